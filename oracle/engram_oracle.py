@@ -1,0 +1,148 @@
+"""ctypes front end of the C oracle (``engram_oracle.c``).
+
+TEST INFRASTRUCTURE, NOT PRODUCT CODE: only the test suite, the smoke check
+and the benchmark's CPU-baseline leg may import this module.  It never
+imports the product package and the product package never imports it.
+
+All arrays are host numpy arrays.  bf16 data travels as ``uint16`` bit
+patterns so that nothing here depends on a bf16 numpy dtype.  See the C
+source for the citation of every step and the readings it takes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+SOURCE = _HERE / "engram_oracle.c"
+LIBRARY = _HERE / "libengram_oracle.so"
+
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+
+
+def build(source: Path = SOURCE, output: Path = LIBRARY, extra_flags=()) -> Path:
+    """Compile the oracle with gcc into a shared library and return its path."""
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
+           *extra_flags, str(source), "-o", str(output)]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+def _ptr(arr, ctype):
+    return arr.ctypes.data_as(ctype) if arr is not None else None
+
+
+class Oracle:
+    """One loaded copy of the oracle library."""
+
+    def __init__(self, library: Path | str = LIBRARY):
+        self.path = str(library)
+        lib = ctypes.CDLL(self.path)
+        lib.oracle_hash.restype = ctypes.c_int
+        lib.oracle_hash.argtypes = [_i64p, _i64p, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int64,
+                                    _i64p, _i64p, _i64p, _i64p]
+        lib.oracle_gather.restype = ctypes.c_int64
+        lib.oracle_gather.argtypes = [_i64p, ctypes.c_int64, _u16p, ctypes.c_int64,
+                                      ctypes.c_int64, _u16p]
+        lib.oracle_scatter_add_dense.restype = ctypes.c_int64
+        lib.oracle_scatter_add_dense.argtypes = [_i64p, ctypes.c_int64, _u16p,
+                                                 ctypes.c_int64, _f32p, ctypes.c_int64]
+        lib.oracle_scatter_add_rowsparse.restype = ctypes.c_int64
+        lib.oracle_scatter_add_rowsparse.argtypes = [_i64p, ctypes.c_int64, _u16p,
+                                                     ctypes.c_int64, ctypes.c_int64,
+                                                     _i64p, _f32p, _i64p]
+        self._lib = lib
+
+    # -- hash ---------------------------------------------------------------
+    def hash(self, tokens, ngram_size, heads_per_ngram, eos_id, multipliers,
+             primes, offsets, seq_ids=None):
+        """Row IDs int64 [batch, seq, H] for tokens int64 [batch, seq]."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+        if tokens.ndim != 2:
+            raise ValueError("tokens must be [batch, seq]")
+        batch, seq = tokens.shape
+        heads = (ngram_size - 1) * heads_per_ngram
+        mult = np.ascontiguousarray(multipliers, dtype=np.int64)
+        pr = np.ascontiguousarray(primes, dtype=np.int64)
+        off = np.ascontiguousarray(offsets, dtype=np.int64)
+        if mult.shape != (ngram_size,) or pr.shape != (heads,) or off.shape != (heads,):
+            raise ValueError("multipliers/primes/offsets have the wrong length")
+        seg = None
+        if seq_ids is not None:
+            seg = np.ascontiguousarray(seq_ids, dtype=np.int64)
+            if seg.shape != tokens.shape:
+                raise ValueError("seq_ids must match tokens")
+        out = np.empty((batch, seq, heads), dtype=np.int64)
+        rc = self._lib.oracle_hash(_ptr(tokens, _i64p), _ptr(seg, _i64p), batch, seq,
+                                   int(ngram_size), int(heads_per_ngram), int(eos_id),
+                                   _ptr(mult, _i64p), _ptr(pr, _i64p), _ptr(off, _i64p),
+                                   _ptr(out, _i64p))
+        if rc != 0:
+            raise ValueError("oracle_hash rejected its arguments")
+        return out
+
+    # -- gather -------------------------------------------------------------
+    def gather(self, row_ids, table_bits):
+        """(out uint16 [n, dim], invalid count) for table uint16 [rows, dim]."""
+        ids = np.ascontiguousarray(row_ids, dtype=np.int64).reshape(-1)
+        table = np.ascontiguousarray(table_bits, dtype=np.uint16)
+        rows, dim = table.shape
+        out = np.empty((ids.size, dim), dtype=np.uint16)
+        bad = self._lib.oracle_gather(_ptr(ids, _i64p), ids.size, _ptr(table, _u16p),
+                                      rows, dim, _ptr(out, _u16p))
+        return out, int(bad)
+
+    # -- scatter-add ----------------------------------------------------------
+    def scatter_add_dense(self, row_ids, grad_bits, grad_table):
+        """Accumulate into a copy of grad_table float32 [rows, dim]; returns
+        (new table, invalid count)."""
+        ids = np.ascontiguousarray(row_ids, dtype=np.int64).reshape(-1)
+        grads = np.ascontiguousarray(grad_bits, dtype=np.uint16).reshape(ids.size, -1)
+        table = np.array(grad_table, dtype=np.float32, copy=True, order="C")
+        rows, dim = table.shape
+        if grads.shape[1] != dim:
+            raise ValueError("grad width differs from table width")
+        bad = self._lib.oracle_scatter_add_dense(_ptr(ids, _i64p), ids.size,
+                                                 _ptr(grads, _u16p), dim,
+                                                 _ptr(table, _f32p), rows)
+        if bad < 0:
+            raise MemoryError("oracle_scatter_add_dense ran out of memory")
+        return table, int(bad)
+
+    def scatter_add_rowsparse(self, row_ids, grad_bits, dim, table_rows):
+        """(unique ids int64 [U], sums float32 [U, dim], invalid count)."""
+        ids = np.ascontiguousarray(row_ids, dtype=np.int64).reshape(-1)
+        grads = np.ascontiguousarray(grad_bits, dtype=np.uint16).reshape(ids.size, dim)
+        uid = np.empty(max(ids.size, 1), dtype=np.int64)
+        vals = np.empty((max(ids.size, 1), dim), dtype=np.float32)
+        count = np.zeros(1, dtype=np.int64)
+        bad = self._lib.oracle_scatter_add_rowsparse(_ptr(ids, _i64p), ids.size,
+                                                     _ptr(grads, _u16p), dim, table_rows,
+                                                     _ptr(uid, _i64p), _ptr(vals, _f32p),
+                                                     _ptr(count, _i64p))
+        if bad < 0:
+            raise MemoryError("oracle_scatter_add_rowsparse ran out of memory")
+        u = int(count[0])
+        return uid[:u].copy(), vals[:u].copy(), int(bad)
+
+
+_default = None
+
+
+def default_oracle() -> Oracle:
+    """The oracle built from this directory's source (built on first use if
+    the library is missing or older than its source)."""
+    global _default
+    if _default is None:
+        if (not LIBRARY.exists()
+                or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE)):
+            build()
+        _default = Oracle(LIBRARY)
+    return _default
