@@ -1,0 +1,240 @@
+"""Throughput of the hashed n-gram embedding hot path on one MI355X.
+
+One step = one pass of the whole path over one token batch:
+    engram_hash (tokens -> row ids) -> engram_gather (forward rows)
+    -> engram_scatter_add_rowsparse (backward: per-row fp32 sums)
+on the end-to-end workload: tokens [8, 8192] (Zipf(1.1) ids, EOS w.p.
+1/4096), ngram_size 4, 8 heads per order (24 heads), a 200M x 256 bf16 table
+(102.4 GB, resident in HBM), upstream gradients [8, 8192, 24, 256] bf16.
+Eight distinct token batches are cycled so one step does not warm the next.
+All inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is row lookups per second over the whole
+forward + backward step.  The roofline entry is for the step's dominant
+kernel, timed with HIP events on the stream it runs on.  The CPU baseline
+is the oracle on the host, timed on the same workload's lookups.
+
+    python bench.py [--steps K] [--warmup W] [--workload e2e|full|medium|backward]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("row lookups/s and achieved HBM GB/s (% of peak), "
+          "fwd hash+gather and bwd scatter")
+PEAK_HBM_GBS = 8000.0
+N_BATCHES = 8
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl, unique_rows, with_seg=False):
+    """Bytes the method must move per call (reads + writes), per phase."""
+    N, R, D = wl.tokens_per_batch, wl.lookups, wl.dim
+    out = {"hash": 8 * N + 8 * R + (8 * N if with_seg else 0),
+           "gather": 8 * R + 2 * D * R + 2 * D * R}
+    if wl.grads == "rowsparse":
+        out["scatter"] = 8 * R + 2 * D * R + (4 * D + 8) * unique_rows
+    elif wl.grads == "dense":
+        out["scatter"] = 8 * R + 2 * D * R + 8 * D * unique_rows
+    return out
+
+
+def cpu_baseline(wl, tokens_host, mult, table, grads, budget_s=12.0):
+    """The oracle (single-threaded C) on the host cores, on the e2e batch:
+    hash, gather from a compact host copy of the table rows the batch
+    touches, and the row-sparse scatter-add.  Repeated within a time budget;
+    the median rate is reported."""
+    import torch
+    from oracle import default_oracle
+
+    oracle = default_oracle()
+    rows0 = oracle.hash(tokens_host[0], wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult,
+                        wl.primes, wl.offsets).reshape(-1)
+    uniq, local = np.unique(rows0, return_inverse=True)
+    compact = table.index_select(0, torch.from_numpy(uniq).to(table.device))
+    compact_bits = compact.view(torch.int16).cpu().numpy().view(np.uint16)
+    grad_bits = grads.view(torch.int16).cpu().numpy().view(np.uint16)
+    local = local.astype(np.int64)
+    rates, start = [], time.perf_counter()
+    while len(rates) < 5 and (not rates or time.perf_counter() - start < budget_s):
+        t0 = time.perf_counter()
+        oracle.hash(tokens_host[0], wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult,
+                    wl.primes, wl.offsets)
+        oracle.gather(local, compact_bits)
+        if wl.grads == "rowsparse":
+            oracle.scatter_add_rowsparse(local, grad_bits, wl.dim, uniq.size)
+        rates.append(wl.lookups / (time.perf_counter() - t0))
+    return {"value": float(np.median(rates)), "unit": "lookups/s", "cores": 1,
+            "kind": "oracle",
+            "sample": (f"the full {wl.name} batch ({wl.lookups} lookups), "
+                       f"{len(rates)} runs, median; gather from a compact host copy of "
+                       f"the {uniq.size} table rows it touches; single-threaded C oracle")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="e2e", choices=["e2e", "full", "medium", "backward"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path runs on a single MI355X with the whole table in HBM)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gram_hashed_embedding_amd import engram as E
+    from gram_hashed_embedding_amd import workloads
+
+    wl = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    mult = wl.multipliers()
+    log(f"[bench] workload {wl.describe()}")
+
+    tokens_host = [wl.tokens(k) for k in range(N_BATCHES)]
+    tokens = [torch.from_numpy(t).to(dev) for t in tokens_host]
+    t0 = time.perf_counter()
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] table {tuple(table.shape)} bf16 ready in {time.perf_counter() - t0:.1f}s")
+
+    R, D = wl.lookups, wl.dim
+    rows = torch.empty((wl.batch, wl.seq, wl.heads), dtype=torch.int64, device=dev)
+    out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    backward = wl.grads != "none"
+    if backward:
+        grads = workloads.make_grads(R, D, wl.seed + 2, dev)
+    if wl.grads == "rowsparse":
+        uid = torch.empty(R, dtype=torch.int64, device=dev)
+        uval = torch.empty((R, D), dtype=torch.float32, device=dev)
+        count = torch.zeros(1, dtype=torch.int64, device=dev)
+        mode = E.SCATTER_ROWSPARSE
+    elif wl.grads == "dense":
+        gtab = workloads.make_grad_table(wl.table_rows, D, None, dev)
+        mode = E.SCATTER_SORTED
+    if backward:
+        ws = torch.empty(max(E.engram_scatter_add_workspace(R, wl.table_rows, D, mode), 1),
+                         dtype=torch.uint8, device=dev)
+
+    def step(k, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        E.engram_hash(tokens[k % N_BATCHES], wl.ngram_size, wl.heads_per_ngram, wl.eos_id,
+                      mult, wl.primes, wl.offsets, wl.table_rows, out=rows)
+        if ev is not None:
+            ev[1].record(stream)
+        E.engram_gather(rows, table, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+        if wl.grads == "rowsparse":
+            E.engram_scatter_add_rowsparse(rows.view(-1), grads, wl.table_rows, unique_ids=uid,
+                                           unique_grads=uval, num_unique=count, workspace=ws)
+        elif wl.grads == "dense":
+            E.engram_scatter_add(rows.view(-1), grads, gtab, workspace=ws)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    # whole-step timing: nothing between the kernels
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for k in range(args.steps):
+        step(k)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(stop) / args.steps
+
+    # per-phase timing: events between the calls, same stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    phase_ms = {
+        "hash": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
+        "gather": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
+    }
+    if backward:
+        phase_ms["scatter"] = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    # distinct rows of one batch (the backward's U), read after timing
+    unique_rows = 0
+    if wl.grads == "rowsparse":
+        step(0)
+        torch.cuda.synchronize()
+        unique_rows = int(count.item())
+    elif wl.grads == "dense":
+        step(0)
+        torch.cuda.synchronize()
+        unique_rows = int(torch.unique(rows).numel())
+    nbytes = algorithmic_bytes(wl, unique_rows)
+    phases = {p: {"ms": phase_ms[p], "algorithmic_bytes": nbytes[p],
+                  "gbps": nbytes[p] / (phase_ms[p] * 1e-3) / 1e9,
+                  "frac_of_peak": nbytes[p] / (phase_ms[p] * 1e-3) / 1e9 / PEAK_HBM_GBS}
+              for p in phase_ms}
+    step_bytes = sum(nbytes[p] for p in phase_ms)
+    step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # the gather is one kernel launch per call: its event time is the kernel's
+    dominant = "gather"
+    roofline = {"bound": "hbm", "kernel": "gather_kernel<5>" if D == 256 else "gather_kernel",
+                "achieved": phases[dominant]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS, "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline and wl.grads in ("rowsparse", "none"):
+        try:
+            cpu = cpu_baseline(wl, tokens_host, mult, table,
+                               grads if backward else None)
+        except Exception as exc:  # the baseline must not hide the GPU number
+            log(f"[bench] cpu baseline failed: {exc!r}")
+
+    result = {
+        "metric": METRIC,
+        "value": R / (ms_per_step * 1e-3),
+        "unit": "lookups/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**wl.describe(), "step": "hash+gather" + ("+scatter" if backward else ""),
+                   "backward": wl.grads, "accumulate": "f64" if backward else None,
+                   "unique_rows": unique_rows, "token_batches_cycled": N_BATCHES},
+        "step_algorithmic_bytes": step_bytes,
+        "step_gbps": step_gbps,
+        "step_frac_of_peak": step_gbps / PEAK_HBM_GBS,
+        "phases": phases,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

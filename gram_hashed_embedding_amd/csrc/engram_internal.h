@@ -1,0 +1,51 @@
+// engram_internal.h -- helpers shared by the HIP translation units of
+// libengram.so.  Not part of the public ABI (that is include/engram.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "engram.h"
+
+namespace engram {
+
+// 16-byte vector of four 32-bit words: eight bf16 values, or four fp32.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;  // CDNA wavefront width
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Status of the launches just enqueued on this thread.
+inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
+}
+
+// a * b <= limit for non-negative a, b, without overflow.
+inline bool mul_fits(int64_t a, int64_t b, int64_t limit) {
+  return a == 0 || b <= limit / a;
+}
+
+// bf16 element e (0..7) of a 16-byte chunk, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ void unpack_bf16x8(const u32x4 &v, float (&f)[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// Add a lane's count of invalid ids to *err (when err is not null).  Invalid
+// ids are rare, so one atomic per lane that saw any is cheap.
+__device__ __forceinline__ void count_errors(int bad, int64_t *err) {
+  if (err != nullptr && bad != 0)
+    atomicAdd(reinterpret_cast<unsigned long long *>(err), (unsigned long long)bad);
+}
+
+}  // namespace engram

@@ -1,0 +1,244 @@
+"""Python binding of libengram.so (ctypes; same names as the C ABI).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  Importing this
+module loads the library and raises ImportError when it has not been built
+(``python -m gram_hashed_embedding_amd.build``); there is no fallback path.
+
+All calls are asynchronous on ``torch.cuda.current_stream()`` of the
+tensors' device (or the stream passed in), exactly like the C entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import re
+from pathlib import Path
+
+import torch
+
+_PKG = Path(__file__).resolve().parent
+LIBRARY = _PKG / "libengram.so"
+HEADER = _PKG.parent / "include" / "engram.h"
+
+ENGRAM_OK = 0
+ENGRAM_EINVAL = -1
+ENGRAM_EALIGN = -2
+ENGRAM_EWORKSPACE = -3
+ENGRAM_EHIP = -4
+SCATTER_SORTED = 0
+SCATTER_ATOMIC = 1
+SCATTER_ROWSPARSE = 2
+MAX_NGRAM = 8
+MAX_HEADS = 64
+
+if not LIBRARY.exists():
+    raise ImportError(f"{LIBRARY} is missing: build it with "
+                      "`python -m gram_hashed_embedding_amd.build` (hipcc, gfx950)")
+
+_lib = ctypes.CDLL(str(LIBRARY))
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+_lib.engram_status_string.restype = ctypes.c_char_p
+_lib.engram_status_string.argtypes = [ctypes.c_int]
+_lib.engram_abi_version.restype = ctypes.c_int
+_lib.engram_abi_version.argtypes = []
+_lib.engram_hash.restype = ctypes.c_int
+_lib.engram_hash.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                             ctypes.c_int32, ctypes.c_int64, _i64p, _i64p, _i64p,
+                             ctypes.c_int64, _vp, _vp]
+_lib.engram_gather.restype = ctypes.c_int
+_lib.engram_gather.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
+                               _vp, _vp]
+_lib.engram_scatter_add_workspace.restype = ctypes.c_size_t
+_lib.engram_scatter_add_workspace.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int32]
+_lib.engram_scatter_add.restype = ctypes.c_int
+_lib.engram_scatter_add.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64, _vp,
+                                    ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_size_t, _vp,
+                                    _vp]
+_lib.engram_scatter_add_rowsparse.restype = ctypes.c_int
+_lib.engram_scatter_add_rowsparse.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                                              ctypes.c_int64, _vp, _vp, _vp, _vp,
+                                              ctypes.c_size_t, _vp, _vp]
+
+
+class EngramError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        super().__init__(f"{call}: {engram_status_string(status)} (status {status})")
+
+
+def engram_status_string(status: int) -> str:
+    return _lib.engram_status_string(int(status)).decode()
+
+
+def engram_abi_version() -> int:
+    return int(_lib.engram_abi_version())
+
+
+def declared_symbols() -> list[str]:
+    """Names of the functions include/engram.h declares."""
+    text = HEADER.read_text()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(engram_\w+)\s*\(", text,
+                                 re.MULTILINE)))
+
+
+def _check(status: int, call: str) -> None:
+    if status != ENGRAM_OK:
+        raise EngramError(status, call)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _host_i64(values, length, what):
+    arr = (ctypes.c_int64 * max(length, 1))()
+    vals = [int(v) for v in (values.tolist() if hasattr(values, "tolist") else values)]
+    if len(vals) != length:
+        raise ValueError(f"{what} must have {length} entries, got {len(vals)}")
+    for i, v in enumerate(vals):
+        arr[i] = v
+    return arr
+
+
+def _device_tensor(t, dtype, what):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device (cuda) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def engram_hash(tokens, ngram_size, heads_per_ngram, eos_id, multipliers, primes, offsets,
+                table_rows, seq_ids=None, out=None, stream=None):
+    """Row ids int64 [batch, seq, H] of tokens int64 [batch, seq]."""
+    _device_tensor(tokens, torch.int64, "tokens")
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [batch, seq]")
+    batch, seq = tokens.shape
+    if not 2 <= int(ngram_size) <= MAX_NGRAM:
+        raise ValueError(f"ngram_size must be in [2, {MAX_NGRAM}]")
+    heads = (int(ngram_size) - 1) * int(heads_per_ngram)
+    if seq_ids is not None:
+        _device_tensor(seq_ids, torch.int64, "seq_ids")
+        if seq_ids.shape != tokens.shape:
+            raise ValueError("seq_ids must have the shape of tokens")
+    if out is None:
+        out = torch.empty((batch, seq, heads), dtype=torch.int64, device=tokens.device)
+    _device_tensor(out, torch.int64, "out")
+    if out.numel() != batch * seq * heads:
+        raise ValueError("out must hold batch * seq * H ids")
+    mult = _host_i64(multipliers, int(ngram_size), "multipliers")
+    pr = _host_i64(primes, heads, "primes")
+    off = _host_i64(offsets, heads, "offsets")
+    with torch.cuda.device(tokens.device):
+        status = _lib.engram_hash(_ptr(tokens), _ptr(seq_ids), batch, seq, int(ngram_size),
+                                  int(heads_per_ngram), int(eos_id), mult, pr, off,
+                                  int(table_rows), _ptr(out), _stream(tokens.device, stream))
+    _check(status, "engram_hash")
+    return out
+
+
+def engram_gather(row_ids, table, out=None, err_count=None, stream=None):
+    """bf16 rows table[row_ids] with shape row_ids.shape + (head_dim,)."""
+    _device_tensor(row_ids, torch.int64, "row_ids")
+    _device_tensor(table, torch.bfloat16, "table")
+    if table.dim() != 2:
+        raise ValueError("table must be [rows, head_dim]")
+    rows, dim = table.shape
+    n = row_ids.numel()
+    if out is None:
+        out = torch.empty((*row_ids.shape, dim), dtype=torch.bfloat16, device=row_ids.device)
+    _device_tensor(out, torch.bfloat16, "out")
+    if out.numel() != n * dim:
+        raise ValueError("out must hold n * head_dim values")
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
+    with torch.cuda.device(row_ids.device):
+        status = _lib.engram_gather(_ptr(row_ids), n, _ptr(table), rows, dim, _ptr(out),
+                                    _ptr(err_count), _stream(row_ids.device, stream))
+    _check(status, "engram_gather")
+    return out
+
+
+def engram_scatter_add_workspace(n, table_rows, head_dim, mode=SCATTER_SORTED) -> int:
+    size = _lib.engram_scatter_add_workspace(int(n), int(table_rows), int(head_dim), int(mode))
+    if size == ctypes.c_size_t(-1).value:
+        raise EngramError(ENGRAM_EINVAL, "engram_scatter_add_workspace")
+    return int(size)
+
+
+def _workspace(workspace, n, table_rows, dim, mode, device):
+    need = engram_scatter_add_workspace(n, table_rows, dim, mode)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _device_tensor(workspace, torch.uint8, "workspace")
+    return workspace
+
+
+def engram_scatter_add(row_ids, grads, grad_table, mode=SCATTER_SORTED, workspace=None,
+                       err_count=None, stream=None):
+    """grad_table[r] += sum of grads[i] over row_ids[i] == r (in place)."""
+    _device_tensor(row_ids, torch.int64, "row_ids")
+    _device_tensor(grads, torch.bfloat16, "grads")
+    _device_tensor(grad_table, torch.float32, "grad_table")
+    rows, dim = grad_table.shape
+    n = row_ids.numel()
+    if grads.numel() != n * dim:
+        raise ValueError("grads must hold n * head_dim values")
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
+    ws = None
+    if mode == SCATTER_SORTED:
+        ws = _workspace(workspace, n, rows, dim, mode, row_ids.device)
+    with torch.cuda.device(row_ids.device):
+        status = _lib.engram_scatter_add(_ptr(row_ids), n, _ptr(grads), dim, _ptr(grad_table),
+                                         rows, int(mode), _ptr(ws),
+                                         0 if ws is None else ws.numel(), _ptr(err_count),
+                                         _stream(row_ids.device, stream))
+    _check(status, "engram_scatter_add")
+    return grad_table
+
+
+def engram_scatter_add_rowsparse(row_ids, grads, table_rows, unique_ids=None, unique_grads=None,
+                                 num_unique=None, workspace=None, err_count=None, stream=None):
+    """(unique_ids int64 [n], unique_grads fp32 [n, dim], num_unique int64 [1]);
+    the first num_unique entries are valid (num_unique stays on the device)."""
+    _device_tensor(row_ids, torch.int64, "row_ids")
+    _device_tensor(grads, torch.bfloat16, "grads")
+    n = row_ids.numel()
+    dim = grads.shape[-1]
+    if grads.numel() != n * dim:
+        raise ValueError("grads must hold n * head_dim values")
+    dev = row_ids.device
+    if unique_ids is None:
+        unique_ids = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
+    if unique_grads is None:
+        unique_grads = torch.empty((max(n, 1), dim), dtype=torch.float32, device=dev)
+    if num_unique is None:
+        num_unique = torch.empty(1, dtype=torch.int64, device=dev)
+    _device_tensor(unique_ids, torch.int64, "unique_ids")
+    _device_tensor(unique_grads, torch.float32, "unique_grads")
+    _device_tensor(num_unique, torch.int64, "num_unique")
+    if unique_ids.numel() < n or unique_grads.numel() < n * dim:
+        raise ValueError("unique_ids / unique_grads must hold n entries")
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
+    ws = _workspace(workspace, n, table_rows, dim, SCATTER_ROWSPARSE, dev)
+    with torch.cuda.device(dev):
+        status = _lib.engram_scatter_add_rowsparse(_ptr(row_ids), n, _ptr(grads), dim,
+                                                   int(table_rows), _ptr(unique_ids),
+                                                   _ptr(unique_grads), _ptr(num_unique),
+                                                   _ptr(ws), ws.numel(), _ptr(err_count),
+                                                   _stream(dev, stream))
+    _check(status, "engram_scatter_add_rowsparse")
+    return unique_ids, unique_grads, num_unique

@@ -154,6 +154,14 @@ def packed_documents(rng, batch, seq, zipf_s, mean_len=2048.0, sigma=1.0,
     return tokens, seg
 
 
+def random_segments(shape, mean_length, seed):
+    """Packed segment ids: each position starts a new segment with
+    probability 1/mean_length (ids are running counts along each row)."""
+    rng = np.random.Generator(np.random.PCG64([seed, 99]))
+    starts = rng.random(size=shape) < 1.0 / mean_length
+    return np.cumsum(starts, axis=-1).astype(np.int64)
+
+
 # ---------------------------------------------------------------------------
 # workload descriptions
 # ---------------------------------------------------------------------------

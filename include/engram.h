@@ -1,0 +1,184 @@
+/*
+ * engram.h -- C ABI of libengram.so: the raw-token hashed n-gram embedding
+ * (hash -> row gather -> scatter-add) on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources the operations follow:
+ *   [API] NeMo AutoModel v0.7 API page
+ *         "nemo_automodel.components.models.qwen3_8_flash_next.engram"
+ *   [PR1] prime-rl release notes v0.9.1.dev179, section "Validation"
+ *   [PR2] prime-rl pull request 3434 "feat(models): add native Qwen3.8 Flash
+ *         Next", section "Validation"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named d_* are device pointers (HIP device memory of the current
+ *   device); pointers named h_* are host pointers.  The caller allocates and
+ *   frees every buffer, workspace included.  The library never allocates,
+ *   keeps no state between calls and is re-entrant.
+ * - Host arrays are read during the call only (copied into kernel
+ *   arguments); the caller may reuse them as soon as the call returns.
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *   work is enqueued on it and the call returns without waiting: no entry
+ *   point synchronises with the host or reads device memory on the host.
+ * - Arguments are checked on the host before anything is enqueued; a bad
+ *   argument returns an error code and enqueues nothing.  Codes:
+ *     ENGRAM_OK         success (work enqueued)
+ *     ENGRAM_EINVAL     invalid argument: null required pointer, negative or
+ *                       overflowing size, unsupported shape, bad constants
+ *     ENGRAM_EALIGN     a device data buffer is not 16-byte aligned
+ *     ENGRAM_EWORKSPACE workspace missing or smaller than the query says
+ *     ENGRAM_EHIP       the HIP runtime refused a launch
+ * - Device-side conditions never abort: a row id of -1 is padding (a zero
+ *   row in a gather, skipped in a scatter; the exchange padding of the
+ *   [API] page, _validate_padded_received_ids, uses -1 the same way); any
+ *   other row id outside [0, table_rows) is treated the same way AND adds
+ *   one to *d_err_count when d_err_count is not NULL (an int64 the caller
+ *   zeroes; it stays on the device until the caller reads it).
+ * - Layouts are row-major and contiguous.  bf16 data is passed as void*.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENGRAM_ABI_VERSION 1
+
+#define ENGRAM_OK 0
+#define ENGRAM_EINVAL (-1)
+#define ENGRAM_EALIGN (-2)
+#define ENGRAM_EWORKSPACE (-3)
+#define ENGRAM_EHIP (-4)
+
+/* Largest n-gram order (current token included) and head count accepted. */
+#define ENGRAM_MAX_NGRAM 8
+#define ENGRAM_MAX_HEADS 64
+
+/* Scatter-add modes. */
+#define ENGRAM_SCATTER_SORTED 0    /* deterministic: sort + segmented sum    */
+#define ENGRAM_SCATTER_ATOMIC 1    /* fp32 atomic adds (order not fixed)     */
+#define ENGRAM_SCATTER_ROWSPARSE 2 /* workspace query of the row-sparse call */
+
+/* Human-readable text of a status code (static storage). */
+const char *engram_status_string(int status);
+
+/* ENGRAM_ABI_VERSION of the built library. */
+int engram_abi_version(void);
+
+/*
+ * engram_hash -- global table row of every (batch, position, head).
+ *
+ * Follows [API] Qwen3_8_FlashNextNGramEmbedding (class description and
+ * constructor arguments), _hash_input_ids and _shift_right_after_eos.
+ * With n = ngram_size, J = heads_per_ngram and H = (n - 1) * J:
+ *   - s_0 is the token at (b, t); for k = 1..n-1, s_k is the token k
+ *     positions back if the path back to it crosses no EOS (an EOS ends the
+ *     segment it closes, so the position right after an EOS starts fresh)
+ *     and no change of d_seq_ids, and lies inside the row; otherwise s_k = 0;
+ *   - the order-g mix, g = 2..n, is the int64 sum of s_k * multipliers[k]
+ *     for k < g, every product and sum wrapping modulo 2^64;
+ *   - head h = (g - 2) * J + j (bigram heads first, then trigram, ...) gets
+ *     row offsets[h] + (mix mod primes[h]), the remainder taken in [0, p).
+ * Arguments:
+ *   d_tokens     int64 [batch, seq], raw token ids (any int64 value).
+ *   d_seq_ids    int64 [batch, seq] packed segment ids, or NULL.
+ *   eos_id       the EOS token id.
+ *   h_multipliers int64 [ngram_size]; h_primes, h_offsets int64 [H].
+ *   table_rows   rows of the table the ids address: every head must satisfy
+ *                primes[h] > 0, offsets[h] >= 0, offsets[h]+primes[h] <=
+ *                table_rows.
+ *   d_row_ids    int64 [batch, seq, H], written.
+ * Errors: EINVAL for ngram_size outside [2, ENGRAM_MAX_NGRAM],
+ * heads_per_ngram < 1, H > ENGRAM_MAX_HEADS, a bad prime/offset, a null
+ * pointer or a size overflow.  batch * seq == 0 enqueues nothing.
+ */
+int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids,
+                int64_t batch, int64_t seq, int32_t ngram_size,
+                int32_t heads_per_ngram, int64_t eos_id,
+                const int64_t *h_multipliers, const int64_t *h_primes,
+                const int64_t *h_offsets, int64_t table_rows,
+                int64_t *d_row_ids, void *stream);
+
+/*
+ * engram_gather -- d_out[i, :] = d_table[d_row_ids[i], :] (bitwise bf16 copy).
+ *
+ * Follows [API] _lookup_ngram_ids and Qwen3_8_FlashNextOwnerShardedEmbedding
+ * (with no process group the full table is local and the lookup is a plain
+ * embedding lookup).  For the forward of the layer, pass the hash output
+ * with n = batch * seq * H: d_out [batch, seq, H, head_dim] is then the
+ * page's [batch, sequence, ngram_heads * head_dim] result.
+ *   d_row_ids  int64 [n]; d_table bf16 [table_rows, head_dim];
+ *   d_out      bf16 [n, head_dim], written (zero rows for -1/invalid ids).
+ *   head_dim   a positive multiple of 8; d_table and d_out 16-byte aligned.
+ * Errors: EINVAL (null pointer with n > 0, bad head_dim, negative sizes,
+ * overflow), EALIGN.  n == 0 enqueues nothing.
+ */
+int engram_gather(const int64_t *d_row_ids, int64_t n, const void *d_table,
+                  int64_t table_rows, int64_t head_dim, void *d_out,
+                  int64_t *d_err_count, void *stream);
+
+/*
+ * engram_scatter_add_workspace -- bytes of device workspace that
+ * engram_scatter_add (mode ENGRAM_SCATTER_SORTED or _ATOMIC) or
+ * engram_scatter_add_rowsparse (mode ENGRAM_SCATTER_ROWSPARSE) needs for n
+ * ids.  0 means no workspace is needed.  Returns (size_t)-1 for arguments
+ * the calls would reject.
+ */
+size_t engram_scatter_add_workspace(int64_t n, int64_t table_rows,
+                                    int64_t head_dim, int32_t mode);
+
+/*
+ * engram_scatter_add -- backward of the gather into a dense fp32 gradient
+ * table:  for every distinct valid row r among d_row_ids,
+ *     d_grad_table[r, :] = fp32(d_grad_table[r, :] + S_r),
+ * where S_r is the sum of the bf16 gradient rows d_grads[i, :] with
+ * d_row_ids[i] == r.  Rows not referenced are left unchanged.
+ *
+ * Follows [API] Qwen3_8_FlashNextOwnerShardedEmbedding (the owner alone
+ * accumulates a row's gradient), [PR2] Validation (backward gradient
+ * aggregation per row) and [PR1] Validation (FP32 reduction defaults).
+ *   mode ENGRAM_SCATTER_SORTED: S_r is summed in fp64, rounded once to fp32,
+ *     then added with one fp32 add; deterministic run to run.  Needs the
+ *     workspace and table_rows < 2^32 - 1, n < 2^32.
+ *   mode ENGRAM_SCATTER_ATOMIC: every gradient element is added to the
+ *     table with an fp32 atomic add; the order of additions is not fixed.
+ *     Needs no workspace.
+ *   d_row_ids int64 [n]; d_grads bf16 [n, head_dim]; d_grad_table fp32
+ *   [table_rows, head_dim], accumulated in place.  head_dim a positive
+ *   multiple of 8, at most 2048; d_grads and d_grad_table 16-byte aligned.
+ * Errors: EINVAL, EALIGN, EWORKSPACE.  n == 0 enqueues nothing.
+ */
+int engram_scatter_add(const int64_t *d_row_ids, int64_t n,
+                       const void *d_grads, int64_t head_dim,
+                       float *d_grad_table, int64_t table_rows, int32_t mode,
+                       void *d_workspace, size_t workspace_bytes,
+                       int64_t *d_err_count, void *stream);
+
+/*
+ * engram_scatter_add_rowsparse -- the same sums S_r, emitted row-sparse:
+ * d_unique_ids[u] (ascending distinct valid rows) and d_unique_grads[u, :]
+ * (fp32 S_r, summed in fp64 and rounded once) for u < U, with U written to
+ * *d_num_unique.  Deterministic.  Capacity: the caller provides n entries
+ * (d_unique_ids int64 [n], d_unique_grads fp32 [n, head_dim]); entries at
+ * u >= U are left unchanged.  For tables whose dense fp32 gradient would not
+ * fit beside the table (a 200M x 256 table needs 204.8 GB of fp32).
+ *   Same limits as the sorted mode of engram_scatter_add; needs the
+ *   workspace of mode ENGRAM_SCATTER_ROWSPARSE.
+ * Errors: EINVAL, EALIGN, EWORKSPACE.  n == 0 writes U = 0.
+ */
+int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
+                                 const void *d_grads, int64_t head_dim,
+                                 int64_t table_rows, int64_t *d_unique_ids,
+                                 float *d_unique_grads, int64_t *d_num_unique,
+                                 void *d_workspace, size_t workspace_bytes,
+                                 int64_t *d_err_count, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

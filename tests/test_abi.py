@@ -1,0 +1,123 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch.
+No call here reaches a kernel (each either fails validation or is empty)."""
+import ctypes
+
+import pytest
+
+e = pytest.importorskip("gram_hashed_embedding_amd.engram")
+
+i64arr = ctypes.c_int64 * 64
+
+
+def _arr(vals):
+    a = i64arr()
+    for i, v in enumerate(vals):
+        a[i] = v
+    return a
+
+
+def test_every_declared_symbol_is_exported():
+    names = e.declared_symbols()
+    assert set(names) == {"engram_status_string", "engram_abi_version", "engram_hash",
+                          "engram_gather", "engram_scatter_add_workspace",
+                          "engram_scatter_add", "engram_scatter_add_rowsparse"}
+    for name in names:
+        assert hasattr(e._lib, name), name
+
+
+def test_status_strings_and_version():
+    assert e.engram_abi_version() == 1
+    assert e.engram_status_string(0) == "ok"
+    for code in (-1, -2, -3, -4):
+        assert e.engram_status_string(code) not in ("ok", "unknown status")
+    assert e.engram_status_string(7) == "unknown status"
+
+
+def _hash(tokens=None, seg=None, batch=1, seq=4, n=3, J=2, mult=(1, 2, 3),
+          primes=(5, 7, 11, 13), offs=(0, 5, 12, 23), rows=36, out=None):
+    return e._lib.engram_hash(tokens, seg, batch, seq, n, J, 0, _arr(mult), _arr(primes),
+                              _arr(offs), rows, out, None)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails first
+
+
+@pytest.mark.parametrize("kwargs", [
+    dict(n=1), dict(n=9), dict(J=0), dict(n=8, J=10),            # orders / heads
+    dict(primes=(5, 0, 11, 13)), dict(primes=(5, -7, 11, 13)),    # primes
+    dict(offs=(0, 5, 12, -1)), dict(offs=(0, 5, 12, 30)),         # offsets past the table
+    dict(batch=-1), dict(seq=-2), dict(rows=-5),
+    dict(batch=1 << 40, seq=1 << 40),                            # size overflow
+    dict(tokens=None, out=FAKE), dict(tokens=FAKE, out=None),     # null buffers
+])
+def test_hash_rejects(kwargs):
+    args = dict(tokens=FAKE, out=FAKE)
+    args.update(kwargs)
+    assert _hash(**args) == e.ENGRAM_EINVAL
+
+
+def test_hash_empty_is_ok_without_launch():
+    assert _hash(tokens=None, out=None, batch=0, seq=5) == e.ENGRAM_OK
+    assert _hash(tokens=None, out=None, batch=3, seq=0) == e.ENGRAM_OK
+
+
+def test_hash_accepts_boundary_offsets():
+    # offset + prime == table_rows is allowed; an empty batch stops before launching
+    assert _hash(tokens=None, out=None, batch=0, offs=(0, 5, 12, 23), rows=36) == e.ENGRAM_OK
+    assert _hash(tokens=None, out=None, batch=0, offs=(0, 5, 12, 23), rows=35) == e.ENGRAM_EINVAL
+
+
+ALIGNED = ctypes.c_void_p(0x10000)
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def test_gather_rejects():
+    g = e._lib.engram_gather
+    assert g(ALIGNED, 4, ALIGNED, 10, 12, ALIGNED, None, None) == e.ENGRAM_EINVAL  # dim % 8
+    assert g(ALIGNED, 4, ALIGNED, 10, 0, ALIGNED, None, None) == e.ENGRAM_EINVAL
+    assert g(ALIGNED, -1, ALIGNED, 10, 8, ALIGNED, None, None) == e.ENGRAM_EINVAL
+    assert g(None, 4, ALIGNED, 10, 8, ALIGNED, None, None) == e.ENGRAM_EINVAL
+    assert g(ALIGNED, 4, MISALIGNED, 10, 8, ALIGNED, None, None) == e.ENGRAM_EALIGN
+    assert g(ALIGNED, 4, ALIGNED, 10, 8, MISALIGNED, None, None) == e.ENGRAM_EALIGN
+    assert g(ALIGNED, 1 << 62, ALIGNED, 10, 8, ALIGNED, None, None) == e.ENGRAM_EINVAL
+    assert g(None, 0, None, 10, 8, None, None, None) == e.ENGRAM_OK
+
+
+def test_scatter_workspace_query():
+    w = e.engram_scatter_add_workspace
+    assert w(1000, 5000, 64, e.SCATTER_ATOMIC) == 0
+    sorted_bytes = w(1000, 5000, 64, e.SCATTER_SORTED)
+    assert sorted_bytes == w(1000, 5000, 64, e.SCATTER_ROWSPARSE)
+    assert sorted_bytes >= 16 * 1000            # keys and indices, twice
+    assert w(2000, 5000, 64, e.SCATTER_SORTED) > sorted_bytes
+    assert w(0, 5000, 64, e.SCATTER_SORTED) >= 0
+    for bad in [(10, 50, 12, 0), (10, 50, 4096, 0), (-1, 50, 8, 0), (10, 50, 8, 3),
+                (10, 1 << 33, 8, 0)]:
+        with pytest.raises(e.EngramError):
+            w(*bad)
+    assert w(10, 1 << 33, 8, e.SCATTER_ATOMIC) == 0   # atomic path has no key limit
+
+
+def test_scatter_rejects():
+    s = e._lib.engram_scatter_add
+    ws = e.engram_scatter_add_workspace(100, 50, 8, 0)
+    assert s(ALIGNED, 100, ALIGNED, 8, ALIGNED, 50, 5, ALIGNED, ws, None, None) == e.ENGRAM_EINVAL
+    assert s(ALIGNED, 100, ALIGNED, 12, ALIGNED, 50, 0, ALIGNED, ws, None, None) == e.ENGRAM_EINVAL
+    assert s(ALIGNED, 100, ALIGNED, 8, ALIGNED, 50, 0, ALIGNED, ws - 1, None, None) == \
+        e.ENGRAM_EWORKSPACE
+    assert s(ALIGNED, 100, ALIGNED, 8, ALIGNED, 50, 0, None, 0, None, None) == e.ENGRAM_EWORKSPACE
+    assert s(ALIGNED, 100, MISALIGNED, 8, ALIGNED, 50, 0, ALIGNED, ws, None, None) == \
+        e.ENGRAM_EALIGN
+    assert s(None, 100, ALIGNED, 8, ALIGNED, 50, 1, None, 0, None, None) == e.ENGRAM_EINVAL
+    assert s(ALIGNED, 100, ALIGNED, 8, ALIGNED, 1 << 33, 0, ALIGNED, ws, None, None) == \
+        e.ENGRAM_EINVAL
+    assert s(None, 0, None, 8, None, 50, 0, None, 0, None, None) == e.ENGRAM_OK
+    r = e._lib.engram_scatter_add_rowsparse
+    ws = e.engram_scatter_add_workspace(100, 50, 8, 2)
+    assert r(ALIGNED, 100, ALIGNED, 8, 50, ALIGNED, ALIGNED, None, ALIGNED, ws, None, None) == \
+        e.ENGRAM_EINVAL
+    assert r(ALIGNED, 100, ALIGNED, 8, 50, None, ALIGNED, ALIGNED, ALIGNED, ws, None, None) == \
+        e.ENGRAM_EINVAL
+    assert r(ALIGNED, 100, ALIGNED, 8, 50, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 16, None, None) == \
+        e.ENGRAM_EWORKSPACE

@@ -1,0 +1,93 @@
+"""Parity at full size: the 200M x 256 bf16 table (102.4 GB) resident in HBM.
+
+Row ids are compared with the oracle in full.  Gathered rows are compared
+with the oracle on a sample of outputs (the oracle gathers from a host copy
+of just the table rows those outputs need) and, over every output, with
+torch's index_select on the device.  The e2e backward (row-sparse) is
+compared with the oracle in full.  These use the calls the benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gram_hashed_embedding_amd import workloads
+from tests.gpu_helpers import bits, dev, host_f32, needs_gpu, release
+
+pytestmark = needs_gpu
+E = pytest.importorskip("gram_hashed_embedding_amd.engram")
+
+SAMPLE = 8192
+
+
+def sampled_gather_check(oracle, rows_host, out, table, seed):
+    dim = table.shape[1]
+    flat_rows = rows_host.reshape(-1)
+    pick = np.random.Generator(np.random.PCG64(seed)).choice(flat_rows.size, SAMPLE,
+                                                            replace=False)
+    uniq, local = np.unique(flat_rows[pick], return_inverse=True)
+    small_table = bits(table.index_select(0, dev(uniq)))
+    want, bad = oracle.gather(local.astype(np.int64), small_table)
+    assert bad == 0
+    got = bits(out.view(-1, dim).index_select(0, dev(pick.astype(np.int64))))
+    assert np.array_equal(got, want)
+    # every output row against torch's index_select on the device
+    assert torch.equal(out.view(-1, dim), table.index_select(0, dev(flat_rows)))
+
+
+def forward(wl, tok, seg, table, mult):
+    rows = E.engram_hash(dev(tok), wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult,
+                         wl.primes, wl.offsets, wl.table_rows,
+                         seq_ids=None if seg is None else dev(seg))
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = E.engram_gather(rows, table, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return rows, out
+
+
+def test_full_scale_forward(oracle):
+    wl = workloads.full()
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
+    mult = wl.multipliers()
+    tok, seg = wl.tokens(0, with_segments=True)
+    for s in (None, seg):
+        rows, out = forward(wl, tok, s, table, mult)
+        want = oracle.hash(tok, wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult,
+                           wl.primes, wl.offsets, s)
+        rows_host = rows.cpu().numpy()
+        assert np.array_equal(rows_host, want)
+        assert out.shape == (1, 32768, 32, 256)
+        sampled_gather_check(oracle, rows_host, out, table, wl.seed)
+        del rows, out
+    del table
+    release()
+
+
+def test_e2e_forward_backward(oracle):
+    wl = workloads.e2e()
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
+    mult = wl.multipliers()
+    tok = wl.tokens(0)
+    rows, out = forward(wl, tok, None, table, mult)
+    want = oracle.hash(tok, wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes,
+                       wl.offsets)
+    rows_host = rows.cpu().numpy()
+    assert np.array_equal(rows_host, want)
+    sampled_gather_check(oracle, rows_host, out, table, wl.seed + 1)
+    del out, table
+    release()
+
+    grads = workloads.make_grads(wl.lookups, wl.dim, wl.seed + 2, "cuda")
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    uid, uval, count = E.engram_scatter_add_rowsparse(rows.view(-1), grads, wl.table_rows,
+                                                      err_count=err)
+    u = int(count.item())
+    assert int(err.item()) == 0
+    want_uid, want_val, bad = oracle.scatter_add_rowsparse(rows_host.reshape(-1), bits(grads),
+                                                           wl.dim, wl.table_rows)
+    assert bad == 0 and u == want_uid.size
+    assert 0.5 * wl.lookups < u < wl.lookups
+    assert np.array_equal(uid[:u].cpu().numpy(), want_uid)
+    assert np.array_equal(host_f32(uval[:u]).view(np.uint32), want_val.view(np.uint32))
+    del grads, uid, uval
+    release()

@@ -1,0 +1,190 @@
+"""GPU parity of the backward scatter-add against the oracle.
+
+Sorted (deterministic) dense and row-sparse results must equal the oracle
+bit for bit: both sum each row in fp64 and round once, and fp64 sums of
+bf16 values are exact here.  The fp32 atomic variant adds every term into
+the fp32 table in no fixed order.  Each of its elements must be within
+1e-5 relative / 1e-6 absolute of the oracle, or, where a row has so many
+terms that fp32 rounding alone exceeds that, within the worst-case error of
+fp32 summation in any order: (k + 2) * 2^-24 * (|G| + sum |g_i|) for a row
+with k terms (k roundings of the running sum, plus the oracle's own two).
+"""
+import numpy as np
+import pytest
+import torch
+
+from gram_hashed_embedding_amd import workloads
+from tests.gpu_helpers import bits, dev, host_f32, needs_gpu, release
+from tests.test_oracle_lookup import bits_to_f64
+
+pytestmark = needs_gpu
+E = pytest.importorskip("gram_hashed_embedding_amd.engram")
+
+RTOL, ATOL = 1e-5, 1e-6
+
+
+def run_dense(ids, grads_dev, base_dev, mode):
+    table = base_dev.clone()
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    E.engram_scatter_add(dev(ids), grads_dev, table, mode=mode, err_count=err)
+    torch.cuda.synchronize()
+    return table, int(err.item())
+
+
+def run_sparse(ids, grads_dev, rows):
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    uid, uval, count = E.engram_scatter_add_rowsparse(dev(ids), grads_dev, rows, err_count=err)
+    u = int(count.item())
+    return uid[:u].cpu().numpy(), host_f32(uval[:u]), int(err.item())
+
+
+def check_atomic(ids, gbits, base_h, got, want, rows, dim):
+    valid = (ids >= 0) & (ids < rows)
+    uniq, inv, cnt = np.unique(ids[valid], return_inverse=True, return_counts=True)
+    absg = np.zeros((uniq.size, dim), dtype=np.float64)
+    np.add.at(absg, inv, np.abs(bits_to_f64(gbits[valid])))
+    diff = np.abs(got[uniq].astype(np.float64) - want[uniq])
+    tol = ATOL + RTOL * np.abs(want[uniq].astype(np.float64))
+    bound = (cnt[:, None] + 2) * 2.0 ** -24 * (np.abs(base_h[uniq]) + absg) * 1.01
+    assert (diff <= np.maximum(tol, bound)).all()
+    touched = np.zeros(rows, dtype=bool)
+    touched[uniq] = True
+    assert np.array_equal(got[~touched], base_h[~touched])
+
+
+def check_all_modes(oracle, ids, dim, rows, seed, base_std=1.0):
+    grads = workloads.make_grads(ids.size, dim, seed, "cuda")
+    gbits = bits(grads)
+    base = workloads.make_grad_table(rows, dim, seed + 1 if base_std else None, "cuda")
+    base_h = host_f32(base)
+    want, bad = oracle.scatter_add_dense(ids, gbits, base_h)
+
+    got, err = run_dense(ids, grads, base, E.SCATTER_SORTED)
+    assert err == bad
+    assert np.array_equal(host_f32(got).view(np.uint32), want.view(np.uint32))
+
+    got_a, err_a = run_dense(ids, grads, base, E.SCATTER_ATOMIC)
+    assert err_a == bad
+    check_atomic(ids, gbits, base_h, host_f32(got_a), want, rows, dim)
+
+    uid, uval, err_s = run_sparse(ids, grads, rows)
+    want_uid, want_val, bad_s = oracle.scatter_add_rowsparse(ids, gbits, dim, rows)
+    assert err_s == bad_s == bad
+    assert np.array_equal(uid, want_uid)
+    assert np.array_equal(uval.view(np.uint32), want_val.view(np.uint32))
+
+
+def test_tiny_workload(oracle):
+    wl = workloads.tiny()
+    rows_ids = oracle.hash(wl.tokens(0), 3, 2, 0, wl.multipliers(), wl.primes, wl.offsets)
+    check_all_modes(oracle, rows_ids.reshape(-1), wl.dim, wl.table_rows, 11)
+
+
+def test_backward_workload(oracle):
+    """The backward workload at full size: 262,144 lookups of Zipf(1.2)
+    tokens into a 16.8M x 64 fp32 gradient table."""
+    wl = workloads.backward()
+    tok = wl.tokens(0)
+    ids = oracle.hash(tok, wl.ngram_size, wl.heads_per_ngram, wl.eos_id, wl.multipliers(),
+                      wl.primes, wl.offsets).reshape(-1)
+    counts = np.bincount(ids)
+    assert counts.max() > 100          # hot rows collide heavily
+    check_all_modes(oracle, ids, wl.dim, wl.table_rows, 21)
+    release()
+
+
+@pytest.mark.parametrize("n", [1, 2, 31, 32, 33, 63, 64, 65, 4095, 4096, 4097, 20011])
+def test_ragged_counts(oracle, n):
+    rng = np.random.Generator(np.random.PCG64(n))
+    ids = np.minimum(rng.zipf(1.3, size=n) - 1, 499).astype(np.int64)
+    check_all_modes(oracle, ids, 32, 500, 100 + n)
+
+
+@pytest.mark.parametrize("dim", [8, 16, 24, 40, 128, 256, 520, 1024, 2048])
+def test_dims(oracle, dim):
+    rng = np.random.Generator(np.random.PCG64(dim))
+    ids = np.minimum(rng.zipf(1.2, size=3000) - 1, 799).astype(np.int64)
+    check_all_modes(oracle, ids, dim, 800, 200 + dim)
+
+
+@pytest.mark.parametrize("pattern", ["one_row", "two_rows", "runs_at_range_edges",
+                                     "sorted_runs", "all_distinct", "max_key"])
+def test_run_structure(oracle, pattern):
+    """Runs longer than a walker range, runs ending exactly on range edges,
+    a single hot row spanning thousands of ranges."""
+    rng = np.random.Generator(np.random.PCG64(len(pattern)))
+    rows = 1 << 20
+    if pattern == "one_row":
+        ids = np.full(100_003, 777, dtype=np.int64)
+    elif pattern == "two_rows":
+        ids = rng.choice([5, rows - 1], size=50_000).astype(np.int64)
+    elif pattern == "runs_at_range_edges":
+        lens = rng.choice([1, 31, 32, 33, 64, 65, 96], size=600)
+        ids = np.repeat(rng.permutation(rows)[:600], lens).astype(np.int64)
+        ids = rng.permutation(ids)
+    elif pattern == "sorted_runs":
+        lens = rng.choice([1, 31, 32, 33, 64, 65, 96, 200], size=600)
+        ids = np.repeat(np.sort(rng.permutation(rows)[:600]), lens).astype(np.int64)
+    elif pattern == "all_distinct":
+        ids = rng.permutation(rows)[:70_000].astype(np.int64)
+    else:  # the largest and smallest valid keys only
+        ids = rng.choice([0, rows - 1], size=9_999).astype(np.int64)
+    check_all_modes(oracle, ids, 64, rows, 300)
+
+
+def test_padding_and_invalid_ids(oracle):
+    rng = np.random.Generator(np.random.PCG64(5))
+    rows = 1000
+    ids = rng.integers(0, rows, size=9000).astype(np.int64)
+    ids[::7] = -1
+    ids[::101] = rows
+    ids[::211] = -5
+    ids[::401] = 1 << 40
+    check_all_modes(oracle, ids, 16, rows, 400)
+
+
+def test_only_padding(oracle):
+    ids = np.full(300, -1, dtype=np.int64)
+    check_all_modes(oracle, ids, 16, 50, 401)
+
+
+def test_tiny_tables(oracle):
+    for rows in (1, 2, 3):
+        ids = np.random.Generator(np.random.PCG64(rows)).integers(0, rows, size=777)
+        check_all_modes(oracle, ids.astype(np.int64), 8, rows, 500 + rows)
+
+
+def test_sorted_is_deterministic():
+    wl = workloads.backward()
+    rng = np.random.Generator(np.random.PCG64(9))
+    ids = np.minimum(rng.zipf(1.1, size=200_000) - 1, 50_000).astype(np.int64)
+    grads = workloads.make_grads(ids.size, 64, 9, "cuda")
+    base = workloads.make_grad_table(50_001, 64, 10, "cuda")
+    a, _ = run_dense(ids, grads, base, E.SCATTER_SORTED)
+    b, _ = run_dense(ids, grads, base, E.SCATTER_SORTED)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    u1 = run_sparse(ids, grads, 50_001)
+    u2 = run_sparse(ids, grads, 50_001)
+    assert np.array_equal(u1[0], u2[0]) and np.array_equal(u1[1], u2[1])
+    del wl
+
+
+def test_empty():
+    grads = torch.zeros((0, 8), dtype=torch.bfloat16, device="cuda")
+    table = torch.ones((4, 8), dtype=torch.float32, device="cuda")
+    ids = torch.zeros(0, dtype=torch.int64, device="cuda")
+    E.engram_scatter_add(ids, grads, table)
+    assert torch.equal(table, torch.ones_like(table))
+    count = torch.full((1,), 9, dtype=torch.int64, device="cuda")
+    E.engram_scatter_add_rowsparse(ids, grads, 4, num_unique=count)
+    assert int(count.item()) == 0
+
+
+def test_workspace_too_small_is_rejected():
+    ids = torch.zeros(100, dtype=torch.int64, device="cuda")
+    grads = torch.zeros((100, 8), dtype=torch.bfloat16, device="cuda")
+    table = torch.zeros((4, 8), dtype=torch.float32, device="cuda")
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(E.EngramError) as info:
+        E.engram_scatter_add(ids, grads, table, workspace=ws)
+    assert info.value.status == E.ENGRAM_EWORKSPACE
