@@ -202,6 +202,21 @@ def main():
                 "achieved": phases[dominant]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS, "traffic": None}
 
+    # context: a plain device-to-device copy (torch copy_, 2 GiB read + 2 GiB
+    # written) shows what this GPU's HBM delivers to a streaming kernel
+    src = torch.empty(1 << 30, dtype=torch.int16, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 2 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
+
     cpu = None
     if not args.no_cpu_baseline and wl.grads in ("rowsparse", "none"):
         try:
@@ -231,6 +246,7 @@ def main():
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBS,
         "phases": phases,
         "roofline": roofline,
+        "hbm_copy_ceiling_gbps": copy_gbps,
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -24,18 +24,18 @@
 //     directly: valid rows become 32-bit keys, padding and invalid ids the
 //     key table_rows, which sorts last and is dropped.
 //  2. Segment heads (first position of each distinct row) are counted per
-//     32-position range and scanned: the scan gives every distinct row its
+//     16-position range and scanned: the scan gives every distinct row its
 //     output slot u, and U itself.
-//  3. Range walkers: a group of head_dim/8 lanes (16 bytes of the row per
-//     lane) walks one 32-position range of the sorted order, loading the
-//     gradient rows in sorted order (eight in flight per lane) and keeping
-//     fp64 sums in registers.  A run that starts and ends inside the range
+//  3. Range walkers: a group of head_dim/8 lanes (two 4-value quads of the
+//     row per lane) takes one 16-position range of the sorted order, issues all its
+//     loads at once (keys, flat indices, then the 16 gradient rows) and sums
+//     runs in fp64 registers.  A run that starts and ends inside the range
 //     is written once (dense read-modify-write or row-sparse store).  A run
-//     cut by a range boundary leaves fp64 partials; a fix-up pass, owned by
-//     the range holding the run's first position, adds them in range order
-//     and writes the row.  No work item waits on another, and hot rows
-//     (hundreds of contributions) are spread over many walkers instead of
-//     serialising one.
+//     cut by a range boundary leaves fp64 partials; a fix-up pass adds each
+//     cut run's pieces in a fixed order with a whole block and writes the
+//     row.  No work item waits on another, and hot rows (hundreds of
+//     contributions) are spread over many walkers instead of serialising
+//     one.
 // Atomic path: one fp32 atomic add per gradient element into the dense
 // table (hardware float atomics in L2); order of additions not fixed.
 #include "engram_internal.h"
@@ -51,13 +51,13 @@ constexpr int kMaxBins = 256;
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr int kScanChunk = kScanThreads * kScanItems;
-constexpr int kRange = 32;  // sorted positions per walker
+constexpr int kRange = 16;  // sorted positions per walker
 constexpr int kWalkThreads = 256;
-constexpr int kWalkUnroll = 8;
 constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnroll = 4;
 
-static_assert(kRange == 32, "range_heads_kernel splits each wavefront into two ranges");
+constexpr int kFixupBlocks = 4096;
+static_assert(kWave % kRange == 0 && kRange % 4 == 0, "ranges tile a wavefront");
 
 // ----------------------------------------------------------------- keys ----
 // Valid rows keep their index; -1 (padding) and invalid ids get the key
@@ -236,10 +236,15 @@ __global__ __launch_bounds__(kSortThreads) void radix_downsweep_kernel(
 }
 
 // --------------------------------------------------------- segment heads ---
+// Distinct-row starts per kRange-position range (one ballot per wavefront,
+// kWave / kRange ranges per wavefront).  Also clears the count of cut-run
+// owners that the reduction kernel appends to.
 __global__ __launch_bounds__(256) void range_heads_kernel(const uint32_t *keys, int64_t n,
                                                           uint32_t sentinel, uint32_t *head_count,
-                                                          int64_t num_ranges) {
+                                                          int64_t num_ranges,
+                                                          uint32_t *owner_count) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j == 0) *owner_count = 0;
   bool head = false;
   if (j < n) {
     const uint32_t k = keys[j];
@@ -247,198 +252,252 @@ __global__ __launch_bounds__(256) void range_heads_kernel(const uint32_t *keys, 
   }
   const unsigned long long m = __ballot(head);
   const int lane = __lane_id();
-  if ((lane & (kRange - 1)) == 0) {
+  if ((lane % kRange) == 0) {
     const int64_t r = j / kRange;
-    const unsigned long long half = lane == 0 ? (m & 0xffffffffull) : (m >> 32);
-    if (r < num_ranges) head_count[r] = (uint32_t)__popcll(half);
+    const unsigned long long mine = (m >> lane) & ((1ull << kRange) - 1ull);
+    if (r < num_ranges) head_count[r] = (uint32_t)__popcll(mine);
   }
 }
 
 // ---------------------------------------------------------- range walkers --
+// Lane layout.  A walker is L lanes.  A row of head_dim values is split into
+// quads of 4 values (8 bytes of bf16 input, 16 bytes of fp32 output); lane
+// l owns quads l, l + L, ..., l + (Q - 1) * L (Q = quads per lane).  Every
+// load instruction of a walker thus reads L consecutive 8-byte pieces, and
+// every store instruction writes L consecutive 16-byte pieces: whole
+// cache lines, so no partially written line reaches HBM.
 struct WalkArgs {
-  const uint32_t *keys;  // sorted rows (sentinel last)
+  const uint32_t *keys;  // sorted rows (sentinel last), padded to whole ranges
   const uint32_t *vals;  // flat index of each sorted row
   int64_t n;
   uint32_t sentinel;
-  const u32x4 *grads;  // [n, cpr] chunks of 8 bf16
-  int64_t cpr;         // head_dim / 8
+  const uint2 *grads;  // [n, dim / 4] quads of 4 bf16
+  int64_t quads;       // dim / 4
   int64_t dim;
   const uint32_t *head_count;
   const uint32_t *head_off;
   int64_t num_ranges;
-  float *grad_table;     // dense output
-  int64_t *unique_ids;   // row-sparse output
+  float *grad_table;    // dense output
+  int64_t *unique_ids;  // row-sparse output
   float *unique_grads;
-  double *pfirst;  // [num_ranges, dim]: run entering the range from before
-  double *plast;   // [num_ranges, dim]: run leaving the range, started in it
+  // fp64 partial rows, [num_ranges][2][quads][2]: the first and second
+  // halves of every quad's 4 values in two planes (whole-line stores)
+  double *pfirst;  // run entering the range from before
+  double *plast;   // run leaving the range, started in it
+  uint32_t *run_end;     // [n]: end position of cut runs, by distinct-row slot
+  uint32_t *owner_list;  // [num_ranges]: ranges whose last run is cut
+  uint32_t *owner_count;
 };
 
-template <int CPL>
-__device__ __forceinline__ void zero_acc(double (&acc)[CPL][8]) {
+template <int Q>
+__device__ __forceinline__ void zero_acc(double (&acc)[Q][4]) {
 #pragma unroll
-  for (int c = 0; c < CPL; ++c)
+  for (int k = 0; k < Q; ++k)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[c][e] = 0.0;
+    for (int e = 0; e < 4; ++e) acc[k][e] = 0.0;
 }
 
-template <int CPL>
-__device__ __forceinline__ void add_chunk(double (&acc)[CPL][8], const u32x4 (&g)[CPL]) {
+template <int Q>
+__device__ __forceinline__ void add_quads(double (&acc)[Q][4], const uint2 (&g)[Q]) {
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    float f[8];
-    unpack_bf16x8(g[c], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[c][e] += (double)f[e];
+  for (int k = 0; k < Q; ++k) {
+    acc[k][0] += (double)bf16_lo(g[k].x);
+    acc[k][1] += (double)bf16_hi(g[k].x);
+    acc[k][2] += (double)bf16_lo(g[k].y);
+    acc[k][3] += (double)bf16_hi(g[k].y);
   }
 }
 
-template <int L, int CPL>
+template <int L, int Q>
 __device__ __forceinline__ void store_partial(double *buf, int64_t r, const WalkArgs &a, int lane,
-                                              const double (&acc)[CPL][8]) {
+                                              const double (&acc)[Q][4]) {
+  double *base = buf + r * a.dim;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int64_t col = lane + (int64_t)c * L;
-    if (col < a.cpr) {
-      f64x2 *dst = reinterpret_cast<f64x2 *>(buf + r * a.dim + col * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = f64x2{acc[c][2 * e], acc[c][2 * e + 1]};
+  for (int k = 0; k < Q; ++k) {
+    const int64_t qd = lane + (int64_t)k * L;
+    if (qd < a.quads) {
+      reinterpret_cast<f64x2 *>(base)[qd] = f64x2{acc[k][0], acc[k][1]};
+      reinterpret_cast<f64x2 *>(base)[a.quads + qd] = f64x2{acc[k][2], acc[k][3]};
     }
   }
 }
 
-template <int L, int CPL>
+template <int L, int Q>
 __device__ __forceinline__ void add_partial(const double *buf, int64_t r, const WalkArgs &a,
-                                            int lane, double (&acc)[CPL][8]) {
+                                            int lane, double (&acc)[Q][4]) {
+  const double *base = buf + r * a.dim;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int64_t col = lane + (int64_t)c * L;
-    if (col < a.cpr) {
-      const f64x2 *src = reinterpret_cast<const f64x2 *>(buf + r * a.dim + col * 8);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const f64x2 v = src[e];
-        acc[c][2 * e] += v.x;
-        acc[c][2 * e + 1] += v.y;
-      }
+  for (int k = 0; k < Q; ++k) {
+    const int64_t qd = lane + (int64_t)k * L;
+    if (qd < a.quads) {
+      const f64x2 lo = reinterpret_cast<const f64x2 *>(base)[qd];
+      const f64x2 hi = reinterpret_cast<const f64x2 *>(base)[a.quads + qd];
+      acc[k][0] += lo.x;
+      acc[k][1] += lo.y;
+      acc[k][2] += hi.x;
+      acc[k][3] += hi.y;
     }
   }
 }
 
 // The finished sum of row `key` (distinct-row slot u): one rounding to fp32,
 // then one fp32 add into the dense table, or a row-sparse store.
-template <int L, int CPL, bool SPARSE>
+template <int L, int Q, bool SPARSE>
 __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArgs &a, int lane,
-                                         const double (&acc)[CPL][8]) {
+                                         const double (&acc)[Q][4]) {
   if (SPARSE && lane == 0) a.unique_ids[u] = (int64_t)key;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int64_t col = lane + (int64_t)c * L;
-    if (col >= a.cpr) continue;
-    f32x4 s0 = {(float)acc[c][0], (float)acc[c][1], (float)acc[c][2], (float)acc[c][3]};
-    f32x4 s1 = {(float)acc[c][4], (float)acc[c][5], (float)acc[c][6], (float)acc[c][7]};
+  for (int k = 0; k < Q; ++k) {
+    const int64_t qd = lane + (int64_t)k * L;
+    if (qd >= a.quads) continue;
+    const f32x4 sum = {(float)acc[k][0], (float)acc[k][1], (float)acc[k][2], (float)acc[k][3]};
     if (SPARSE) {
-      f32x4 *dst = reinterpret_cast<f32x4 *>(a.unique_grads + (int64_t)u * a.dim + col * 8);
-      __builtin_nontemporal_store(s0, dst);
-      __builtin_nontemporal_store(s1, dst + 1);
+      f32x4 *dst = reinterpret_cast<f32x4 *>(a.unique_grads + (int64_t)u * a.dim) + qd;
+      __builtin_nontemporal_store(sum, dst);
     } else {
-      f32x4 *dst = reinterpret_cast<f32x4 *>(a.grad_table + (int64_t)key * a.dim + col * 8);
-      const f32x4 g0 = dst[0], g1 = dst[1];
-      dst[0] = g0 + s0;
-      dst[1] = g1 + s1;
+      f32x4 *dst = reinterpret_cast<f32x4 *>(a.grad_table + (int64_t)key * a.dim) + qd;
+      *dst = *dst + sum;
     }
   }
 }
 
-template <int L, int CPL, bool SPARSE>
+// One walker over one kRange-position range of the sorted order.  Every
+// load is issued up front and unconditionally (keys and flat indices as
+// 16-byte vectors, then one gradient row per position; positions past the
+// data read row 0 and are ignored), so a walker costs two memory round
+// trips; only then are runs summed and written.  A run that starts and ends
+// in the range is written here.  A run cut by the range's left edge leaves
+// its partial in pfirst (and, where it ends, its end position); a run cut by
+// the right edge leaves its partial in plast and the range joins the owner
+// list for the fix-up.
+// EXACT: the row is exactly Q * L quads (every power-of-two width), so no
+// lane needs its quad index clamped and the compiler folds the k * L steps
+// into immediate load offsets.
+template <int L, int Q, bool SPARSE, bool EXACT>
 __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
   const int lane = threadIdx.x % L;
   const int64_t w = ((int64_t)blockIdx.x * kWalkThreads + threadIdx.x) / L;
   if (w >= a.num_ranges) return;
   const int64_t beg = w * kRange;
-  const int64_t end = min(a.n, beg + kRange);
-  const uint32_t first = a.keys[beg];
-  if (first == a.sentinel) return;  // only padding / invalid ids from here on
-  const bool left_open = beg > 0 && a.keys[beg - 1] == first;
+  const int cnt = (int)min((int64_t)kRange, a.n - beg);
 
-  uint32_t u = a.head_off[w];
-  uint32_t cur = first;
-  bool first_run = true;
-  bool done = false;
-  double acc[CPL][8];
-  zero_acc<CPL>(acc);
-
-  for (int64_t j0 = beg; j0 < end && !done; j0 += kWalkUnroll) {
-    uint32_t kk[kWalkUnroll];
-    u32x4 g[kWalkUnroll][CPL];
+  uint32_t kk[kRange], vv[kRange];
+  {
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + beg);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(a.vals + beg);
 #pragma unroll
-    for (int q = 0; q < kWalkUnroll; ++q) kk[q] = j0 + q < end ? a.keys[j0 + q] : a.sentinel;
-#pragma unroll
-    for (int q = 0; q < kWalkUnroll; ++q) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) g[q][c] = u32x4{0u, 0u, 0u, 0u};
-      if (kk[q] != a.sentinel) {
-        const int64_t src = (int64_t)a.vals[j0 + q] * a.cpr;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const int64_t col = lane + (int64_t)c * L;
-          if (col < a.cpr) g[q][c] = a.grads[src + col];
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < kWalkUnroll; ++q) {
-      if (done) continue;
-      if (kk[q] == a.sentinel) {
-        done = true;
-        continue;
-      }
-      if (kk[q] != cur) {  // a new distinct row starts at j0 + q
-        if (first_run && left_open) {
-          store_partial<L, CPL>(a.pfirst, w, a, lane, acc);
-        } else {
-          emit_row<L, CPL, SPARSE>(cur, u, a, lane, acc);
-          ++u;
-        }
-        cur = kk[q];
-        first_run = false;
-        zero_acc<CPL>(acc);
-      }
-      add_chunk<CPL>(acc, g[q]);
+    for (int i = 0; i < kRange / 4; ++i) {
+      const u32x4 k4 = kp[i], v4 = vp[i];
+      kk[4 * i] = k4.x; kk[4 * i + 1] = k4.y; kk[4 * i + 2] = k4.z; kk[4 * i + 3] = k4.w;
+      vv[4 * i] = v4.x; vv[4 * i + 1] = v4.y; vv[4 * i + 2] = v4.z; vv[4 * i + 3] = v4.w;
     }
   }
-  const bool right_open = end < a.n && a.keys[end] == cur;
-  if (first_run && left_open)
-    store_partial<L, CPL>(a.pfirst, w, a, lane, acc);
-  else if (right_open)
-    store_partial<L, CPL>(a.plast, w, a, lane, acc);
-  else
-    emit_row<L, CPL, SPARSE>(cur, u, a, lane, acc);
+  const int64_t end = beg + cnt;
+  const uint32_t before = a.keys[beg > 0 ? beg - 1 : 0];
+  const uint32_t after = a.keys[end < a.n ? end : a.n - 1];
+  int live_count = 0;
+#pragma unroll
+  for (int q = 0; q < kRange; ++q) {
+    if (q >= cnt) kk[q] = a.sentinel;
+    live_count += kk[q] != a.sentinel ? 1 : 0;  // sentinels sort last
+  }
+
+  // gradient rows in flight together (rows wider than 512 values: Q / 2
+  // batches, to bound registers)
+  constexpr int B = Q > 2 ? kRange / (Q / 2) : kRange;
+  const bool left_open = beg > 0 && live_count > 0 && before == kk[0];
+  uint32_t u = a.head_off[w];  // slot of the next run that starts here
+  uint32_t cur = kk[0];
+  bool first = true;
+  double acc[Q][4];
+  zero_acc<Q>(acc);
+#pragma unroll
+  for (int b0 = 0; b0 < kRange; b0 += B) {
+    uint2 g[B][Q];
+#pragma unroll
+    for (int qq = 0; qq < B; ++qq) {
+      const int q = b0 + qq;
+      const uint2 *row = a.grads + (int64_t)(kk[q] != a.sentinel ? vv[q] : 0u) * a.quads;
+#pragma unroll
+      for (int k = 0; k < Q; ++k)
+        g[qq][k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
+    }
+#pragma unroll
+    for (int qq = 0; qq < B; ++qq) {
+      const int q = b0 + qq;
+      if (q < live_count) {
+        if (kk[q] != cur) {  // a new distinct row starts at beg + q
+          if (first && left_open) {
+            store_partial<L, Q>(a.pfirst, w, a, lane, acc);
+            if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + q);
+          } else {
+            emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+            ++u;
+          }
+          cur = kk[q];
+          first = false;
+          zero_acc<Q>(acc);
+        }
+        add_quads<Q>(acc, g[qq]);
+      }
+    }
+  }
+  if (live_count == 0) return;  // only padding / invalid ids from here on
+  const bool right_open = end < a.n && after == cur;
+  if (first && left_open) {
+    store_partial<L, Q>(a.pfirst, w, a, lane, acc);
+    if (!right_open && lane == 0) a.run_end[u - 1] = (uint32_t)(beg + live_count);
+  } else if (right_open) {
+    store_partial<L, Q>(a.plast, w, a, lane, acc);
+    if (lane == 0) a.owner_list[atomicAdd(a.owner_count, 1u)] = (uint32_t)w;
+  } else {
+    emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+  }
 }
 
-// Rows cut by range boundaries: the range holding the row's first position
-// adds its own partial and the entering partials of the following ranges,
-// in order, and writes the row.
-template <int L, int CPL, bool SPARSE>
+// Cut runs.  A block takes one owner range c0 at a time (grid-stride over
+// the owner list, whose length is read on the device).  The run's pieces
+// are plast[c0] and pfirst[c0 + 1 .. c1], c1 being the range holding its
+// end; the block's walkers sum interleaved pieces, then walker 0 adds the
+// walkers' sums in walker order and writes the row.  Fixed assignment and
+// fixed order keep the result deterministic.
+template <int L, int Q, bool SPARSE>
 __global__ __launch_bounds__(kWalkThreads) void segment_fixup_kernel(const WalkArgs a) {
-  const int lane = threadIdx.x % L;
-  const int64_t w = ((int64_t)blockIdx.x * kWalkThreads + threadIdx.x) / L;
-  if (w >= a.num_ranges) return;
-  const int64_t end = min(a.n, (w + 1) * kRange);
-  const uint32_t heads = a.head_count[w];
-  if (heads == 0 || end >= a.n) return;
-  const uint32_t key = a.keys[end - 1];
-  if (key == a.sentinel || a.keys[end] != key) return;
-
-  double acc[CPL][8];
-  zero_acc<CPL>(acc);
-  add_partial<L, CPL>(a.plast, w, a, lane, acc);
-  for (int64_t q = w + 1; q < a.num_ranges; ++q) {
-    add_partial<L, CPL>(a.pfirst, q, a, lane, acc);
-    const int64_t qend = min(a.n, (q + 1) * kRange);
-    const bool passes_through = a.head_count[q] == 0 && qend < a.n && a.keys[qend] == key;
-    if (!passes_through) break;
+  constexpr int G = kWalkThreads / L;  // walkers per block
+  __shared__ double s_sum[G][L * Q * 4];
+  const int lane = threadIdx.x % L, g = threadIdx.x / L;
+  const uint32_t owners = *a.owner_count;
+  for (uint32_t i = blockIdx.x; i < owners; i += gridDim.x) {
+    const int64_t c0 = a.owner_list[i];
+    const uint32_t u = a.head_off[c0] + a.head_count[c0] - 1;
+    const uint32_t key = a.keys[(c0 + 1) * kRange - 1];
+    const int64_t c1 = ((int64_t)a.run_end[u] - 1) / kRange;
+    const int64_t pieces = c1 - c0 + 1;
+    double acc[Q][4];
+    zero_acc<Q>(acc);
+#pragma unroll 1
+    for (int64_t p = g; p < pieces; p += G) {
+      if (p == 0)
+        add_partial<L, Q>(a.plast, c0, a, lane, acc);
+      else
+        add_partial<L, Q>(a.pfirst, c0 + p, a, lane, acc);
+    }
+#pragma unroll
+    for (int k = 0; k < Q; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_sum[g][(lane * Q + k) * 4 + e] = acc[k][e];
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll 1
+      for (int h = 1; h < G; ++h)
+#pragma unroll
+        for (int k = 0; k < Q; ++k)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[k][e] += s_sum[h][(lane * Q + k) * 4 + e];
+      emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
+    }
+    __syncthreads();
   }
-  emit_row<L, CPL, SPARSE>(key, a.head_off[w] + heads - 1, a, lane, acc);
 }
 
 __global__ void write_zero_kernel(int64_t *p) { *p = 0; }
@@ -482,7 +541,7 @@ struct Plan {
   int64_t num_tiles, num_ranges, scan_chunks;
   int bits, passes, per_pass;
   size_t keys_a, vals_a, keys_b, vals_b, counts, chunk_sums, head_count, head_off, scalars,
-      pfirst, plast, total;
+      run_end, owner_list, pfirst, plast, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -516,7 +575,9 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
     off += align256(bytes);
     return at;
   };
+  // key / index buffers hold whole ranges (the walkers read 16-byte vectors)
   const size_t nn = (size_t)n;
+  static_assert(256 % (kRange * 4) == 0, "256-byte padding covers a whole range");
   p->keys_a = take(nn * 4);
   p->vals_a = take(nn * 4);
   p->keys_b = take(nn * 4);
@@ -526,6 +587,8 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
   p->head_count = take((size_t)p->num_ranges * 4);
   p->head_off = take((size_t)p->num_ranges * 4);
   p->scalars = take(64);
+  p->run_end = take(nn * 4);
+  p->owner_list = take((size_t)p->num_ranges * 4);
   p->pfirst = take((size_t)p->num_ranges * (size_t)dim * 8);
   p->plast = take((size_t)p->num_ranges * (size_t)dim * 8);
   p->total = off;
@@ -547,28 +610,34 @@ void launch_scan(const uint32_t *in, uint32_t *out, int64_t m, uint32_t *chunk_s
                      chunk_sums, total32, total64);
 }
 
-template <int L, int CPL, bool SPARSE>
+template <int L, int Q, bool SPARSE>
 void launch_walkers(const WalkArgs &a, hipStream_t s) {
   const int64_t threads = a.num_ranges * L;
   const unsigned blocks = (unsigned)((threads + kWalkThreads - 1) / kWalkThreads);
-  hipLaunchKernelGGL((segment_reduce_kernel<L, CPL, SPARSE>), dim3(blocks), dim3(kWalkThreads), 0,
-                     s, a);
-  hipLaunchKernelGGL((segment_fixup_kernel<L, CPL, SPARSE>), dim3(blocks), dim3(kWalkThreads), 0,
-                     s, a);
+  if (a.quads == (int64_t)Q * L)
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, SPARSE, true>), dim3(blocks),
+                       dim3(kWalkThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, SPARSE, false>), dim3(blocks),
+                       dim3(kWalkThreads), 0, s, a);
+  const unsigned fix_blocks =
+      (unsigned)(a.num_ranges < kFixupBlocks ? a.num_ranges : kFixupBlocks);
+  hipLaunchKernelGGL((segment_fixup_kernel<L, Q, SPARSE>), dim3(fix_blocks), dim3(kWalkThreads),
+                     0, s, a);
 }
 
 template <bool SPARSE>
 void dispatch_walkers(const WalkArgs &a, hipStream_t s) {
-  const int64_t cpr = a.cpr;
-  if (cpr <= 1) launch_walkers<1, 1, SPARSE>(a, s);
-  else if (cpr <= 2) launch_walkers<2, 1, SPARSE>(a, s);
-  else if (cpr <= 4) launch_walkers<4, 1, SPARSE>(a, s);
-  else if (cpr <= 8) launch_walkers<8, 1, SPARSE>(a, s);
-  else if (cpr <= 16) launch_walkers<16, 1, SPARSE>(a, s);
-  else if (cpr <= 32) launch_walkers<32, 1, SPARSE>(a, s);
-  else if (cpr <= 64) launch_walkers<64, 1, SPARSE>(a, s);
-  else if (cpr <= 128) launch_walkers<64, 2, SPARSE>(a, s);
-  else launch_walkers<64, 4, SPARSE>(a, s);
+  const int64_t cpr = a.quads / 2;  // 16-byte chunks per row
+  if (cpr <= 1) launch_walkers<1, 2, SPARSE>(a, s);
+  else if (cpr <= 2) launch_walkers<2, 2, SPARSE>(a, s);
+  else if (cpr <= 4) launch_walkers<4, 2, SPARSE>(a, s);
+  else if (cpr <= 8) launch_walkers<8, 2, SPARSE>(a, s);
+  else if (cpr <= 16) launch_walkers<16, 2, SPARSE>(a, s);
+  else if (cpr <= 32) launch_walkers<32, 2, SPARSE>(a, s);
+  else if (cpr <= 64) launch_walkers<64, 2, SPARSE>(a, s);
+  else if (cpr <= 128) launch_walkers<64, 4, SPARSE>(a, s);
+  else launch_walkers<64, 8, SPARSE>(a, s);
 }
 
 int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim,
@@ -588,6 +657,9 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   uint32_t *chunk_sums = reinterpret_cast<uint32_t *>(base + p.chunk_sums);
   uint32_t *head_count = reinterpret_cast<uint32_t *>(base + p.head_count);
   uint32_t *head_off = reinterpret_cast<uint32_t *>(base + p.head_off);
+  uint32_t *owner_count = reinterpret_cast<uint32_t *>(base + p.scalars);
+  uint32_t *run_end = reinterpret_cast<uint32_t *>(base + p.run_end);
+  uint32_t *owner_list = reinterpret_cast<uint32_t *>(base + p.owner_list);
   double *pfirst = reinterpret_cast<double *>(base + p.pfirst);
   double *plast = reinterpret_cast<double *>(base + p.plast);
 
@@ -629,7 +701,7 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   const uint32_t sentinel = (uint32_t)table_rows;
   const unsigned head_blocks = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL(range_heads_kernel, dim3(head_blocks), dim3(256), 0, s, src_k, n, sentinel,
-                     head_count, p.num_ranges);
+                     head_count, p.num_ranges, owner_count);
   launch_scan(head_count, head_off, p.num_ranges, chunk_sums, nullptr,
               sparse ? num_unique : nullptr, s);
 
@@ -639,8 +711,8 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   a.vals = src_v;
   a.n = n;
   a.sentinel = sentinel;
-  a.grads = static_cast<const u32x4 *>(grads);
-  a.cpr = dim / 8;
+  a.grads = static_cast<const uint2 *>(grads);
+  a.quads = dim / 4;
   a.dim = dim;
   a.head_count = head_count;
   a.head_off = head_off;
@@ -650,6 +722,9 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   a.unique_grads = unique_grads;
   a.pfirst = pfirst;
   a.plast = plast;
+  a.run_end = run_end;
+  a.owner_list = owner_list;
+  a.owner_count = owner_count;
   if (sparse)
     dispatch_walkers<true>(a, s);
   else
