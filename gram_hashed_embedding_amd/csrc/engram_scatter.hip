@@ -15,14 +15,15 @@
 //
 // Sorted (deterministic) path, all on the caller's stream:
 //  1. LSD radix sort of (row, flat index) pairs, key width = bit width of
-//     table_rows, at most 8 bits per pass.  Per pass: an upsweep counts each
-//     4096-key tile's digits; a two-kernel scan turns the digit-major count
-//     matrix into output offsets; a downsweep ranks every key inside its
-//     tile with a wavefront multi-split (one ballot per digit bit yields the
-//     mask of lanes holding the same digit, its popcount the stable rank)
-//     and scatters keys and indices.  The first pass reads the int64 ids
-//     directly: valid rows become 32-bit keys, padding and invalid ids the
-//     key table_rows, which sorts last and is dropped.
+//     table_rows, at most 8 bits per pass, one kernel per pass ("one-sweep"):
+//     each 4096-key tile ranks its keys with a wavefront multi-split (one
+//     ballot per digit bit yields the mask of lanes holding the same digit,
+//     its popcount the stable rank), finds its output offsets by decoupled
+//     look-back over earlier tiles' published digit counts, and writes its
+//     keys and indices in coalesced digit runs staged through LDS.  The
+//     first pass reads the int64 ids directly: valid rows become 32-bit
+//     keys, padding and invalid ids the key table_rows, which sorts last and
+//     is dropped.
 //  2. Segment heads (first position of each distinct row) are counted per
 //     16-position range and scanned: the scan gives every distinct row its
 //     output slot u, and U itself.
@@ -57,6 +58,7 @@ constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnroll = 4;
 
 constexpr int kFixupBlocks = 4096;
+constexpr int kSortCounters = 4 * 256 + 4;  // digit totals of up to 4 passes, tickets
 static_assert(kWave % kRange == 0 && kRange % 4 == 0, "ranges tile a wavefront");
 
 // ----------------------------------------------------------------- keys ----
@@ -142,44 +144,76 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(
 }
 
 // ------------------------------------------------------------ radix sort ---
-template <bool FROM_IDS>
-__global__ __launch_bounds__(kSortThreads) void radix_upsweep_kernel(
-    const int64_t *ids, const uint32_t *keys, int64_t n, int64_t table_rows, int shift,
-    uint32_t mask, uint32_t *counts, int64_t num_tiles, int64_t *err) {
-  __shared__ uint32_t hist[kMaxBins];
-  const int tid = threadIdx.x;
-  for (int d = tid; d <= (int)mask; d += kSortThreads) hist[d] = 0;
-  __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kSortTile;
-  int bad = 0;
-  for (int i = 0; i < kSortItems; ++i) {
-    const int64_t p = base + (int64_t)i * kSortThreads + tid;
-    if (p < n) {
-      const uint32_t k = FROM_IDS ? make_key(ids[p], table_rows, bad) : keys[p];
-      atomicAdd(&hist[(k >> shift) & mask], 1u);
-    }
-  }
-  if (FROM_IDS) count_errors(bad, err);
-  __syncthreads();
-  for (int d = tid; d <= (int)mask; d += kSortThreads)
-    counts[(int64_t)d * num_tiles + blockIdx.x] = hist[d];
+// One-sweep LSD radix sort.  One kernel clears the look-back state, one
+// counts every pass's digits over all keys (the global digit totals of a
+// pass do not depend on the order the keys are in), then one kernel per
+// pass: a block takes the next tile by atomic ticket, ranks its keys with a
+// wavefront multi-split, publishes its per-digit counts, learns the counts
+// of all earlier tiles by decoupled look-back, stages the tile in LDS in
+// sorted order and writes it out in coalesced runs.
+constexpr uint64_t kFlagAggregate = 1ull << 32;  // count of this tile only
+constexpr uint64_t kFlagInclusive = 2ull << 32;  // count of tiles 0..this
+constexpr uint32_t kSpinLimit = 1u << 22;        // bound on every look-back wait
+constexpr int64_t kStallMark = int64_t(1) << 40;  // added to err when a wait expires
+
+__global__ __launch_bounds__(256) void sort_clear_kernel(uint64_t *status, int64_t status_len,
+                                                         uint32_t *counters, int counters_len) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < status_len) status[i] = 0;
+  if (i < counters_len) counters[i] = 0;
 }
 
-// Stable scatter of one tile.  Wave w owns tile positions
-// [w * 1024, (w + 1) * 1024), read in 16 rounds of 64 consecutive keys, so
-// (wave, round, lane) is the original order.
-template <bool FROM_IDS>
-__global__ __launch_bounds__(kSortThreads) void radix_downsweep_kernel(
-    const int64_t *ids, const uint32_t *keys_in, const uint32_t *vals_in, int64_t n,
-    int64_t table_rows, int shift, int bits, const uint32_t *offsets, int64_t num_tiles,
-    uint32_t *keys_out, uint32_t *vals_out) {
-  __shared__ uint32_t s_hist[kSortWaves][kMaxBins];
-  const uint32_t mask = (1u << bits) - 1u;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-  for (int d = tid; d < kSortWaves * kMaxBins; d += kSortThreads) (&s_hist[0][0])[d] = 0;
+// hist[pass * kMaxBins + digit] += number of keys with that digit.
+__global__ __launch_bounds__(kSortThreads) void sort_histogram_kernel(
+    const int64_t *ids, int64_t n, int64_t table_rows, int passes, int per_pass, int bits,
+    uint32_t *hist, int64_t *err) {
+  __shared__ uint32_t s_hist[4][kMaxBins];
+  const int tid = threadIdx.x;
+  for (int d = tid; d < 4 * kMaxBins; d += kSortThreads) (&s_hist[0][0])[d] = 0;
   __syncthreads();
+  int bad = 0;
+  for (int64_t p = (int64_t)blockIdx.x * kSortThreads + tid; p < n;
+       p += (int64_t)gridDim.x * kSortThreads) {
+    const uint32_t k = make_key(ids[p], table_rows, bad);
+    for (int q = 0; q < passes; ++q) {
+      const int shift = q * per_pass;
+      const int width = bits - shift < per_pass ? bits - shift : per_pass;
+      atomicAdd(&s_hist[q][(k >> shift) & ((1u << width) - 1u)], 1u);
+    }
+  }
+  count_errors(bad, err);
+  __syncthreads();
+  for (int d = tid; d < passes * kMaxBins; d += kSortThreads) {
+    const uint32_t c = (&s_hist[0][0])[d];
+    if (c != 0) atomicAdd(&hist[d], c);
+  }
+}
 
-  const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)wave * (kSortItems * kWave);
+template <bool FROM_IDS>
+__global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
+    const int64_t *ids, const uint32_t *keys_in, const uint32_t *vals_in, int64_t n,
+    int64_t table_rows, int shift, int bits, const uint32_t *hist, uint64_t *status,
+    uint32_t *ticket, int64_t num_tiles, uint32_t *keys_out, uint32_t *vals_out, int64_t *err) {
+  __shared__ uint32_t s_keys[kSortTile];
+  __shared__ uint32_t s_vals[kSortTile];
+  __shared__ uint32_t s_cnt[kSortWaves][kMaxBins];  // per-wave counts -> wave offsets
+  __shared__ uint32_t s_local[kMaxBins];            // tile-local start of each digit
+  __shared__ uint32_t s_gbase[kMaxBins];            // global position of tile-local 0
+  __shared__ uint32_t s_tile;
+  const uint32_t mask = (1u << bits) - 1u;
+  const int bins = 1 << bits;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+
+  if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+  for (int d = tid; d < kSortWaves * kMaxBins; d += kSortThreads) (&s_cnt[0][0])[d] = 0;
+  __syncthreads();
+  const int64_t tile = s_tile;
+  const int64_t tile0 = tile * kSortTile;
+  const int count = (int)min((int64_t)kSortTile, n - tile0);
+
+  // keys of this tile: wave w owns tile positions [w * 1024, (w + 1) * 1024)
+  // in 16 rounds of 64, so (wave, round, lane) is the original order
+  const int64_t base = tile0 + (int64_t)wave * (kSortItems * kWave);
   const unsigned long long below = (1ull << lane) - 1ull;
   uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
 #pragma unroll
@@ -208,30 +242,78 @@ __global__ __launch_bounds__(kSortThreads) void radix_downsweep_kernel(
       peers &= bit ? bal : ~bal;
     }
     if (valid) {
-      const uint32_t prior = s_hist[wave][d];
+      const uint32_t prior = s_cnt[wave][d];
       rank[i] = prior + (uint32_t)__popcll(peers & below);
-      if ((peers & below) == 0ull) s_hist[wave][d] = prior + (uint32_t)__popcll(peers);
+      if ((peers & below) == 0ull) s_cnt[wave][d] = prior + (uint32_t)__popcll(peers);
     }
   }
   __syncthreads();
-  for (int d = tid; d <= (int)mask; d += kSortThreads) {
-    uint32_t run = offsets[(int64_t)d * num_tiles + blockIdx.x];
+
+  // per digit: tile count, wave offsets; publish the tile's count at once
+  uint32_t tile_count = 0;
+  if (tid < bins) {
     for (int w = 0; w < kSortWaves; ++w) {
-      const uint32_t c = s_hist[w][d];
-      s_hist[w][d] = run;
-      run += c;
+      const uint32_t c = s_cnt[w][tid];
+      s_cnt[w][tid] = tile_count;
+      tile_count += c;
     }
+    const uint64_t word = (tile == 0 ? kFlagInclusive : kFlagAggregate) | tile_count;
+    __hip_atomic_store(&status[tile * kMaxBins + tid], word, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // tile-local digit starts, and global digit starts (keys of all smaller
+  // digits over all tiles), by block scans over the digits
+  uint32_t scan_total;
+  const uint32_t local_start = block_exclusive_scan(tid < bins ? tile_count : 0u, scan_total);
+  const uint32_t digit_start = block_exclusive_scan(tid < bins ? hist[tid] : 0u, scan_total);
+  // decoupled look-back: the keys of this digit in all earlier tiles
+  if (tid < bins) {
+    s_local[tid] = local_start;
+    uint64_t before = 0;
+    bool stalled = false;
+    for (int64_t t = tile - 1; t >= 0; --t) {
+      uint64_t word;
+      uint32_t spins = 0;
+      while (((word = __hip_atomic_load(&status[t * kMaxBins + tid], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)) >> 32) == 0) {
+        if (++spins == kSpinLimit) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if ((word >> 32) == 0) {  // the wait expired: give up, flag the call
+        stalled = true;
+        break;
+      }
+      before += word & 0xffffffffull;
+      if (word & kFlagInclusive) break;
+    }
+    if (tile != 0)
+      __hip_atomic_store(&status[tile * kMaxBins + tid],
+                         kFlagInclusive | (uint32_t)(before + tile_count), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    if (stalled && err != nullptr)
+      atomicAdd(reinterpret_cast<unsigned long long *>(err), (unsigned long long)kStallMark);
+    s_gbase[tid] = digit_start + (uint32_t)before;
   }
   __syncthreads();
+
+  // stage in LDS in tile-sorted order, then write digit runs out coalesced
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const int64_t p = base + (int64_t)i * kWave + lane;
     if (p < n) {
       const uint32_t d = (key[i] >> shift) & mask;
-      const uint32_t dst = s_hist[wave][d] + rank[i];
-      keys_out[dst] = key[i];
-      vals_out[dst] = val[i];
+      const uint32_t at = s_local[d] + s_cnt[wave][d] + rank[i];
+      s_keys[at] = key[i];
+      s_vals[at] = val[i];
     }
+  }
+  __syncthreads();
+  for (int j = tid; j < count; j += kSortThreads) {
+    const uint32_t k = s_keys[j];
+    const uint32_t d = (k >> shift) & mask;
+    const uint32_t dst = s_gbase[d] + (uint32_t)j - s_local[d];
+    keys_out[dst] = k;
+    vals_out[dst] = s_vals[j];
   }
 }
 
@@ -540,8 +622,8 @@ __global__ __launch_bounds__(kAtomicThreads) void scatter_atomic_kernel(
 struct Plan {
   int64_t num_tiles, num_ranges, scan_chunks;
   int bits, passes, per_pass;
-  size_t keys_a, vals_a, keys_b, vals_b, counts, chunk_sums, head_count, head_off, scalars,
-      run_end, owner_list, pfirst, plast, total;
+  size_t keys_a, vals_a, keys_b, vals_b, status, counters, chunk_sums, head_count, head_off,
+      scalars, run_end, owner_list, pfirst, plast, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -562,9 +644,7 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
     return false;
   p->num_tiles = (n + kSortTile - 1) / kSortTile;
   p->num_ranges = (n + kRange - 1) / kRange;
-  const int64_t count_len = (int64_t)kMaxBins * p->num_tiles;
-  const int64_t longest = count_len > p->num_ranges ? count_len : p->num_ranges;
-  p->scan_chunks = (longest + kScanChunk - 1) / kScanChunk;
+  p->scan_chunks = (p->num_ranges + kScanChunk - 1) / kScanChunk;
   p->bits = bit_width_u64((uint64_t)table_rows);  // the key table_rows must fit
   if (p->bits < 1) p->bits = 1;
   p->passes = (p->bits + 7) / 8;
@@ -582,7 +662,8 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
   p->vals_a = take(nn * 4);
   p->keys_b = take(nn * 4);
   p->vals_b = take(nn * 4);
-  p->counts = take((size_t)count_len * 4);
+  p->status = take((size_t)p->passes * (size_t)p->num_tiles * kMaxBins * 8);
+  p->counters = take(kSortCounters * 4);
   p->chunk_sums = take((size_t)(p->scan_chunks > 0 ? p->scan_chunks : 1) * 4);
   p->head_count = take((size_t)p->num_ranges * 4);
   p->head_off = take((size_t)p->num_ranges * 4);
@@ -653,7 +734,6 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   uint32_t *vals_a = reinterpret_cast<uint32_t *>(base + p.vals_a);
   uint32_t *keys_b = reinterpret_cast<uint32_t *>(base + p.keys_b);
   uint32_t *vals_b = reinterpret_cast<uint32_t *>(base + p.vals_b);
-  uint32_t *counts = reinterpret_cast<uint32_t *>(base + p.counts);
   uint32_t *chunk_sums = reinterpret_cast<uint32_t *>(base + p.chunk_sums);
   uint32_t *head_count = reinterpret_cast<uint32_t *>(base + p.head_count);
   uint32_t *head_off = reinterpret_cast<uint32_t *>(base + p.head_off);
@@ -664,30 +744,32 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   double *plast = reinterpret_cast<double *>(base + p.plast);
 
   // 1. radix sort (ping-pong a <-> b; the first pass reads the ids)
+  uint64_t *status = reinterpret_cast<uint64_t *>(base + p.status);
+  uint32_t *counters = reinterpret_cast<uint32_t *>(base + p.counters);
+  uint32_t *hist = counters;                 // [4][kMaxBins]
+  uint32_t *tickets = counters + 4 * kMaxBins;  // [4]
+  const int64_t status_len = (int64_t)p.passes * p.num_tiles * kMaxBins;
+  const int64_t clear_len = status_len > kSortCounters ? status_len : kSortCounters;
+  hipLaunchKernelGGL(sort_clear_kernel, dim3((unsigned)((clear_len + 255) / 256)), dim3(256), 0,
+                     s, status, status_len, counters, kSortCounters);
+  const int64_t hist_blocks = p.num_tiles < 2048 ? p.num_tiles : 2048;
+  hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)hist_blocks), dim3(kSortThreads), 0,
+                     s, ids, n, table_rows, p.passes, p.per_pass, p.bits, hist, err);
   const uint32_t *src_k = nullptr, *src_v = nullptr;
   uint32_t *dst_k = keys_a, *dst_v = vals_a, *spare_k = keys_b, *spare_v = vals_b;
   const unsigned tiles = (unsigned)p.num_tiles;
   for (int pass = 0; pass < p.passes; ++pass) {
     const int shift = pass * p.per_pass;
     const int width = p.bits - shift < p.per_pass ? p.bits - shift : p.per_pass;
-    const uint32_t mask = (1u << width) - 1u;
-    const int64_t bins = (int64_t)mask + 1;
+    uint64_t *pass_status = status + (int64_t)pass * p.num_tiles * kMaxBins;
     if (pass == 0)
-      hipLaunchKernelGGL(radix_upsweep_kernel<true>, dim3(tiles), dim3(kSortThreads), 0, s, ids,
-                         nullptr, n, table_rows, shift, mask, counts, p.num_tiles, err);
+      hipLaunchKernelGGL(onesweep_kernel<true>, dim3(tiles), dim3(kSortThreads), 0, s, ids,
+                         nullptr, nullptr, n, table_rows, shift, width, hist, pass_status,
+                         tickets, p.num_tiles, dst_k, dst_v, err);
     else
-      hipLaunchKernelGGL(radix_upsweep_kernel<false>, dim3(tiles), dim3(kSortThreads), 0, s,
-                         nullptr, src_k, n, table_rows, shift, mask, counts, p.num_tiles,
-                         nullptr);
-    launch_scan(counts, counts, bins * p.num_tiles, chunk_sums, nullptr, nullptr, s);
-    if (pass == 0)
-      hipLaunchKernelGGL(radix_downsweep_kernel<true>, dim3(tiles), dim3(kSortThreads), 0, s,
-                         ids, nullptr, nullptr, n, table_rows, shift, width, counts,
-                         p.num_tiles, dst_k, dst_v);
-    else
-      hipLaunchKernelGGL(radix_downsweep_kernel<false>, dim3(tiles), dim3(kSortThreads), 0, s,
-                         nullptr, src_k, src_v, n, table_rows, shift, width, counts,
-                         p.num_tiles, dst_k, dst_v);
+      hipLaunchKernelGGL(onesweep_kernel<false>, dim3(tiles), dim3(kSortThreads), 0, s, nullptr,
+                         src_k, src_v, n, table_rows, shift, width, hist + pass * kMaxBins,
+                         pass_status, tickets + pass, p.num_tiles, dst_k, dst_v, err);
     src_k = dst_k;
     src_v = dst_v;
     uint32_t *tk = dst_k, *tv = dst_v;
