@@ -32,9 +32,10 @@
 //     loads at once (keys, flat indices, then the 16 gradient rows) and sums
 //     runs in fp64 registers.  A run that starts and ends inside the range
 //     is written once (dense read-modify-write or row-sparse store).  A run
-//     cut by a range boundary leaves fp64 partials; a fix-up pass adds each
-//     cut run's pieces in a fixed order with a whole block and writes the
-//     row.  No work item waits on another, and hot rows (hundreds of
+//     cut by the range's end but ending in the next range is finished by
+//     the same walker; only runs longer than a range (hot rows) leave fp64
+//     partials, which a fix-up pass adds in range order with a whole block
+//     per run before writing the row.  No work item waits on another, and hot rows (hundreds of
 //     contributions) are spread over many walkers instead of serialising
 //     one.
 // Atomic path: one fp32 atomic add per gradient element into the dense
@@ -57,8 +58,12 @@ constexpr int kWalkThreads = 256;
 constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnroll = 4;
 
-constexpr int kFixupBlocks = 4096;
-constexpr int kSortCounters = 4 * 256 + 4;  // digit totals of up to 4 passes, tickets
+constexpr int64_t kFixupBlocks = 1024;  // blocks of the long-run fix-up
+// Global digit totals are kept in kHistCopies copies (a block adds to copy
+// blockIdx % kHistCopies) so the histogram's atomics do not all meet on the
+// same few hundred words; readers add the copies.
+constexpr int kHistCopies = 8;
+constexpr int kSortCounters = kHistCopies * 4 * 256 + 4;  // digit totals, pass tickets
 static_assert(kWave % kRange == 0 && kRange % 4 == 0, "ranges tile a wavefront");
 
 // ----------------------------------------------------------------- keys ----
@@ -155,6 +160,7 @@ constexpr uint64_t kFlagAggregate = 1ull << 32;  // count of this tile only
 constexpr uint64_t kFlagInclusive = 2ull << 32;  // count of tiles 0..this
 constexpr uint32_t kSpinLimit = 1u << 22;        // bound on every look-back wait
 constexpr int64_t kStallMark = int64_t(1) << 40;  // added to err when a wait expires
+constexpr int kLookBatch = 4;                     // predecessor tiles read per look-back step
 
 __global__ __launch_bounds__(256) void sort_clear_kernel(uint64_t *status, int64_t status_len,
                                                          uint32_t *counters, int counters_len) {
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(256) void sort_clear_kernel(uint64_t *status, int64
   if (i < counters_len) counters[i] = 0;
 }
 
-// hist[pass * kMaxBins + digit] += number of keys with that digit.
+// hist[copy][pass][digit] += number of keys with that digit.
 __global__ __launch_bounds__(kSortThreads) void sort_histogram_kernel(
     const int64_t *ids, int64_t n, int64_t table_rows, int passes, int per_pass, int bits,
     uint32_t *hist, int64_t *err) {
@@ -183,9 +189,10 @@ __global__ __launch_bounds__(kSortThreads) void sort_histogram_kernel(
   }
   count_errors(bad, err);
   __syncthreads();
+  uint32_t *copy = hist + (int64_t)(blockIdx.x % kHistCopies) * 4 * kMaxBins;
   for (int d = tid; d < passes * kMaxBins; d += kSortThreads) {
     const uint32_t c = (&s_hist[0][0])[d];
-    if (c != 0) atomicAdd(&hist[d], c);
+    if (c != 0) atomicAdd(&copy[d], c);
   }
 }
 
@@ -265,26 +272,40 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   // digits over all tiles), by block scans over the digits
   uint32_t scan_total;
   const uint32_t local_start = block_exclusive_scan(tid < bins ? tile_count : 0u, scan_total);
-  const uint32_t digit_start = block_exclusive_scan(tid < bins ? hist[tid] : 0u, scan_total);
+  uint32_t digit_total = 0;
+  if (tid < bins)
+    for (int c = 0; c < kHistCopies; ++c) digit_total += hist[(int64_t)c * 4 * kMaxBins + tid];
+  const uint32_t digit_start = block_exclusive_scan(digit_total, scan_total);
   // decoupled look-back: the keys of this digit in all earlier tiles
   if (tid < bins) {
     s_local[tid] = local_start;
     uint64_t before = 0;
-    bool stalled = false;
-    for (int64_t t = tile - 1; t >= 0; --t) {
-      uint64_t word;
-      uint32_t spins = 0;
-      while (((word = __hip_atomic_load(&status[t * kMaxBins + tid], __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT)) >> 32) == 0) {
-        if (++spins == kSpinLimit) break;
-        __builtin_amdgcn_s_sleep(1);
+    bool stalled = false, found = false;
+    // look back kLookBatch tiles per step, all loads in flight together
+    for (int64_t t = tile - 1; t >= 0 && !found && !stalled; t -= kLookBatch) {
+      uint64_t word[kLookBatch];
+#pragma unroll
+      for (int j = 0; j < kLookBatch; ++j)
+        word[j] = t - j >= 0 ? __hip_atomic_load(&status[(t - j) * kMaxBins + tid],
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                             : kFlagInclusive;  // before tile 0: nothing
+#pragma unroll
+      for (int j = 0; j < kLookBatch; ++j) {
+        if (found || stalled) continue;
+        uint32_t spins = 0;
+        while ((word[j] >> 32) == 0) {  // not published yet: wait on this one
+          if (++spins == kSpinLimit) break;
+          __builtin_amdgcn_s_sleep(1);
+          word[j] = __hip_atomic_load(&status[(t - j) * kMaxBins + tid], __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if ((word[j] >> 32) == 0) {  // the wait expired: give up, flag the call
+          stalled = true;
+          continue;
+        }
+        before += word[j] & 0xffffffffull;
+        found = (word[j] & kFlagInclusive) != 0;
       }
-      if ((word >> 32) == 0) {  // the wait expired: give up, flag the call
-        stalled = true;
-        break;
-      }
-      before += word & 0xffffffffull;
-      if (word & kFlagInclusive) break;
     }
     if (tile != 0)
       __hip_atomic_store(&status[tile * kMaxBins + tid],
@@ -446,15 +467,17 @@ __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArg
 // One walker over one kRange-position range of the sorted order.  Every
 // load is issued up front and unconditionally (keys and flat indices as
 // 16-byte vectors, then one gradient row per position; positions past the
-// data read row 0 and are ignored), so a walker costs two memory round
-// trips; only then are runs summed and written.  A run that starts and ends
-// in the range is written here.  A run cut by the range's left edge leaves
-// its partial in pfirst (and, where it ends, its end position); a run cut by
-// the right edge leaves its partial in plast and the range joins the owner
-// list for the fix-up.
-// EXACT: the row is exactly Q * L quads (every power-of-two width), so no
-// lane needs its quad index clamped and the compiler folds the k * L steps
-// into immediate load offsets.
+// data, or owned by the previous walker, read row 0 and are ignored), so a
+// walker costs two memory round trips; only then are runs summed and
+// written.  Run ownership: the walker holding a run's first position owns
+// it.  A run that ends inside its owner's range is written at once.  A run
+// that crosses into the next range but ends there ("short") is finished by
+// its owner, which then reads the next range's keys and the continuation
+// rows; the next walker recognises it (the run did not cover the last
+// position of the range before the previous one) and skips it.  A longer
+// run leaves fp64 partials: plast from its owner, pfirst from every later
+// range it touches (the last one also records where the run ends), and its
+// owner joins the owner list for the fix-up.
 template <int L, int Q, bool SPARSE, bool EXACT>
 __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
   const int lane = threadIdx.x % L;
@@ -476,6 +499,7 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
   }
   const int64_t end = beg + cnt;
   const uint32_t before = a.keys[beg > 0 ? beg - 1 : 0];
+  const uint32_t before2 = a.keys[beg > kRange ? beg - kRange - 1 : 0];
   const uint32_t after = a.keys[end < a.n ? end : a.n - 1];
   int live_count = 0;
 #pragma unroll
@@ -483,11 +507,18 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
     if (q >= cnt) kk[q] = a.sentinel;
     live_count += kk[q] != a.sentinel ? 1 : 0;  // sentinels sort last
   }
+  const bool left_open = beg > 0 && live_count > 0 && before == kk[0];
+  // the entering run started in the previous range: its owner finishes it
+  // if it ends here
+  const bool left_short = left_open && (beg <= kRange || before2 != kk[0]);
+  int lead = 0;  // length of the entering run inside this range
+#pragma unroll
+  for (int q = 0; q < kRange; ++q) lead += (left_open && lead == q && kk[q] == kk[0]) ? 1 : 0;
+  const bool skip_lead = left_short && !(lead == live_count && end < a.n && after == kk[0]);
 
   // gradient rows in flight together (rows wider than 512 values: Q / 2
   // batches, to bound registers)
   constexpr int B = Q > 2 ? kRange / (Q / 2) : kRange;
-  const bool left_open = beg > 0 && live_count > 0 && before == kk[0];
   uint32_t u = a.head_off[w];  // slot of the next run that starts here
   uint32_t cur = kk[0];
   bool first = true;
@@ -499,7 +530,8 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
 #pragma unroll
     for (int qq = 0; qq < B; ++qq) {
       const int q = b0 + qq;
-      const uint2 *row = a.grads + (int64_t)(kk[q] != a.sentinel ? vv[q] : 0u) * a.quads;
+      const bool needed = kk[q] != a.sentinel && !(skip_lead && q < lead);
+      const uint2 *row = a.grads + (int64_t)(needed ? vv[q] : 0u) * a.quads;
 #pragma unroll
       for (int k = 0; k < Q; ++k)
         g[qq][k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
@@ -510,8 +542,10 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
       if (q < live_count) {
         if (kk[q] != cur) {  // a new distinct row starts at beg + q
           if (first && left_open) {
-            store_partial<L, Q>(a.pfirst, w, a, lane, acc);
-            if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + q);
+            if (!skip_lead) {  // last piece of a long run
+              store_partial<L, Q>(a.pfirst, w, a, lane, acc);
+              if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + q);
+            }
           } else {
             emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
             ++u;
@@ -527,22 +561,66 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
   if (live_count == 0) return;  // only padding / invalid ids from here on
   const bool right_open = end < a.n && after == cur;
   if (first && left_open) {
-    store_partial<L, Q>(a.pfirst, w, a, lane, acc);
-    if (!right_open && lane == 0) a.run_end[u - 1] = (uint32_t)(beg + live_count);
-  } else if (right_open) {
+    if (right_open) {  // a long run passes through this range
+      store_partial<L, Q>(a.pfirst, w, a, lane, acc);
+    } else if (!skip_lead) {  // the long run ends here
+      store_partial<L, Q>(a.pfirst, w, a, lane, acc);
+      if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + live_count);
+    }
+    return;
+  }
+  if (!right_open) {
+    emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+    return;
+  }
+  // the last run continues into the next range (right_open: end < n, so
+  // this range is full and the next one starts at end)
+  const int64_t nbeg = end;
+  const int ncnt = (int)min((int64_t)kRange, a.n - nbeg);
+  uint32_t nk[kRange], nv[kRange];
+  {
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + nbeg);
+    const u32x4 *vp = reinterpret_cast<const u32x4 *>(a.vals + nbeg);
+#pragma unroll
+    for (int i = 0; i < kRange / 4; ++i) {
+      const u32x4 k4 = kp[i], v4 = vp[i];
+      nk[4 * i] = k4.x; nk[4 * i + 1] = k4.y; nk[4 * i + 2] = k4.z; nk[4 * i + 3] = k4.w;
+      nv[4 * i] = v4.x; nv[4 * i + 1] = v4.y; nv[4 * i + 2] = v4.z; nv[4 * i + 3] = v4.w;
+    }
+  }
+  int m = 0;  // continuation length
+#pragma unroll
+  for (int q = 0; q < kRange; ++q) m += (m == q && q < ncnt && nk[q] == cur) ? 1 : 0;
+  const int64_t past = nbeg + kRange;
+  const bool is_long = m == kRange && past < a.n && a.keys[past] == cur;
+  if (is_long) {
     store_partial<L, Q>(a.plast, w, a, lane, acc);
     if (lane == 0) a.owner_list[atomicAdd(a.owner_count, 1u)] = (uint32_t)w;
-  } else {
-    emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+    return;
   }
+  for (int q0 = 0; q0 < m; q0 += 4) {
+    uint2 g[4][Q];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const bool live = q0 + b < m;
+      const uint2 *row = a.grads + (int64_t)(live ? nv[q0 + b] : 0u) * a.quads;
+#pragma unroll
+      for (int k = 0; k < Q; ++k)
+        g[b][k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      if (q0 + b < m) add_quads<Q>(acc, g[b]);
+  }
+  emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
 }
 
-// Cut runs.  A block takes one owner range c0 at a time (grid-stride over
-// the owner list, whose length is read on the device).  The run's pieces
-// are plast[c0] and pfirst[c0 + 1 .. c1], c1 being the range holding its
-// end; the block's walkers sum interleaved pieces, then walker 0 adds the
-// walkers' sums in walker order and writes the row.  Fixed assignment and
-// fixed order keep the result deterministic.
+// Long runs (longer than a range; rare hot rows).  A block takes one owner
+// range c0 at a time (grid-stride over the owner list, whose length is read
+// on the device).  The run's pieces are plast[c0] and pfirst[c0 + 1 .. c1],
+// c1 being the range holding its end; the block's walkers sum interleaved
+// pieces, then walker 0 adds the walkers' sums in walker order and writes
+// the row.  Fixed assignment and fixed order keep the result deterministic.
 template <int L, int Q, bool SPARSE>
 __global__ __launch_bounds__(kWalkThreads) void segment_fixup_kernel(const WalkArgs a) {
   constexpr int G = kWalkThreads / L;  // walkers per block
@@ -746,13 +824,14 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   // 1. radix sort (ping-pong a <-> b; the first pass reads the ids)
   uint64_t *status = reinterpret_cast<uint64_t *>(base + p.status);
   uint32_t *counters = reinterpret_cast<uint32_t *>(base + p.counters);
-  uint32_t *hist = counters;                 // [4][kMaxBins]
-  uint32_t *tickets = counters + 4 * kMaxBins;  // [4]
+  uint32_t *hist = counters;                                // [kHistCopies][4][kMaxBins]
+  uint32_t *tickets = counters + kHistCopies * 4 * kMaxBins;  // [4]
   const int64_t status_len = (int64_t)p.passes * p.num_tiles * kMaxBins;
   const int64_t clear_len = status_len > kSortCounters ? status_len : kSortCounters;
   hipLaunchKernelGGL(sort_clear_kernel, dim3((unsigned)((clear_len + 255) / 256)), dim3(256), 0,
                      s, status, status_len, counters, kSortCounters);
-  const int64_t hist_blocks = p.num_tiles < 2048 ? p.num_tiles : 2048;
+  const int64_t hist_want = (n + 4095) / 4096;
+  const int64_t hist_blocks = hist_want < 512 ? hist_want : 512;
   hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)hist_blocks), dim3(kSortThreads), 0,
                      s, ids, n, table_rows, p.passes, p.per_pass, p.bits, hist, err);
   const uint32_t *src_k = nullptr, *src_v = nullptr;

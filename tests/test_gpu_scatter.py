@@ -108,7 +108,8 @@ def test_dims(oracle, dim):
 
 
 @pytest.mark.parametrize("pattern", ["one_row", "two_rows", "runs_at_range_edges",
-                                     "sorted_runs", "all_distinct", "max_key"])
+                                     "sorted_runs", "all_distinct", "max_key",
+                                     "every_length_sorted", "every_length_shuffled"])
 def test_run_structure(oracle, pattern):
     """Runs longer than a walker range, runs ending exactly on range edges,
     a single hot row spanning thousands of ranges."""
@@ -127,6 +128,12 @@ def test_run_structure(oracle, pattern):
         ids = np.repeat(np.sort(rng.permutation(rows)[:600]), lens).astype(np.int64)
     elif pattern == "all_distinct":
         ids = rng.permutation(rows)[:70_000].astype(np.int64)
+    elif pattern.startswith("every_length"):
+        # run lengths 1..50 in every phase against the sorted-order ranges
+        lens = np.tile(np.arange(1, 51), 7)
+        ids = np.repeat(np.sort(rng.permutation(rows)[:lens.size]), lens).astype(np.int64)
+        if pattern.endswith("shuffled"):
+            ids = rng.permutation(ids)
     else:  # the largest and smallest valid keys only
         ids = rng.choice([0, rows - 1], size=9_999).astype(np.int64)
     check_all_modes(oracle, ids, 64, rows, 300)
