@@ -2,7 +2,12 @@
 
 One step = one pass of the whole path over one token batch:
     engram_hash (tokens -> row ids) -> engram_gather (forward rows)
-    -> engram_scatter_add_rowsparse (backward: per-row fp32 sums)
+    -> engram_scatter_plan + engram_scatter_apply (backward: per-row fp32
+       sums, row-sparse; the same work as engram_scatter_add_rowsparse)
+The plan (sorting the row ids) needs only the hash output, so it runs on a
+second stream beside the forward gather, as a training step would schedule
+it; the apply waits for it.  A serial pass of the same calls gives the
+per-phase times.
 on the end-to-end workload: tokens [8, 8192] (Zipf(1.1) ids, EOS w.p.
 1/4096), ngram_size 4, 8 heads per order (24 heads), a 200M x 256 bf16 table
 (102.4 GB, resident in HBM), upstream gradients [8, 8192, 24, 256] bf16.
@@ -44,10 +49,14 @@ def algorithmic_bytes(wl, unique_rows, with_seg=False):
     N, R, D = wl.tokens_per_batch, wl.lookups, wl.dim
     out = {"hash": 8 * N + 8 * R + (8 * N if with_seg else 0),
            "gather": 8 * R + 2 * D * R + 2 * D * R}
+    # the backward's plan (sorting the ids) is overhead: its algorithmic
+    # bytes are the ids it reads; the apply moves the gradients
     if wl.grads == "rowsparse":
-        out["scatter"] = 8 * R + 2 * D * R + (4 * D + 8) * unique_rows
+        out["scatter_plan"] = 8 * R
+        out["scatter_apply"] = 2 * D * R + (4 * D + 8) * unique_rows
     elif wl.grads == "dense":
-        out["scatter"] = 8 * R + 2 * D * R + 8 * D * unique_rows
+        out["scatter_plan"] = 8 * R
+        out["scatter_apply"] = 2 * D * R + 8 * D * unique_rows
     return out
 
 
@@ -134,29 +143,54 @@ def main():
         ws = torch.empty(max(E.engram_scatter_add_workspace(R, wl.table_rows, D, mode), 1),
                          dtype=torch.uint8, device=dev)
 
-    def step(k, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    side = torch.cuda.Stream(dev)  # default priority
+    ev_rows = [torch.cuda.Event() for _ in range(2)]
+    ev_plan = [torch.cuda.Event() for _ in range(2)]
+
+    def step(k):
+        """One step.  The backward's plan (sort of the row ids) needs only the
+        hash output, so it runs on a side stream beside the forward gather; the
+        apply waits for it."""
         E.engram_hash(tokens[k % N_BATCHES], wl.ngram_size, wl.heads_per_ngram, wl.eos_id,
                       mult, wl.primes, wl.offsets, wl.table_rows, out=rows)
-        if ev is not None:
-            ev[1].record(stream)
+        if not backward:
+            E.engram_gather(rows, table, out=out)
+            return
+        ev_rows[k % 2].record(stream)
+        side.wait_event(ev_rows[k % 2])
+        E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws, stream=side)
+        ev_plan[k % 2].record(side)
         E.engram_gather(rows, table, out=out)
-        if ev is not None:
-            ev[2].record(stream)
+        stream.wait_event(ev_plan[k % 2])
+        apply_backward()
+
+    def apply_backward():
         if wl.grads == "rowsparse":
-            E.engram_scatter_add_rowsparse(rows.view(-1), grads, wl.table_rows, unique_ids=uid,
-                                           unique_grads=uval, num_unique=count, workspace=ws)
-        elif wl.grads == "dense":
-            E.engram_scatter_add(rows.view(-1), grads, gtab, workspace=ws)
-        if ev is not None:
+            E.engram_scatter_apply(grads, ws, wl.table_rows, unique_ids=uid, unique_grads=uval,
+                                   num_unique=count)
+        else:
+            E.engram_scatter_apply(grads, ws, wl.table_rows, grad_table=gtab)
+
+    def serial_step(k, ev):
+        """The same calls one after another on one stream, with events between
+        them (per-phase times)."""
+        ev[0].record(stream)
+        E.engram_hash(tokens[k % N_BATCHES], wl.ngram_size, wl.heads_per_ngram, wl.eos_id,
+                      mult, wl.primes, wl.offsets, wl.table_rows, out=rows)
+        ev[1].record(stream)
+        E.engram_gather(rows, table, out=out)
+        ev[2].record(stream)
+        if backward:
+            E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws)
             ev[3].record(stream)
+            apply_backward()
+            ev[4].record(stream)
 
     for k in range(args.warmup):
         step(k)
     torch.cuda.synchronize()
 
-    # whole-step timing: nothing between the kernels
+    # whole-step timing (the driver's step): nothing between the calls
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -166,40 +200,45 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(stop) / args.steps
 
-    # per-phase timing: events between the calls, same stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # per-phase timing: events between the calls, one stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
-        step(k, evs[k])
+        serial_step(k, evs[k])
     torch.cuda.synchronize()
     phase_ms = {
         "hash": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
         "gather": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
     }
     if backward:
-        phase_ms["scatter"] = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        phase_ms["scatter_plan"] = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+        phase_ms["scatter_apply"] = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
+    serial_ms = float(np.mean([e[0].elapsed_time(e[4 if backward else 2]) for e in evs]))
 
     # distinct rows of one batch (the backward's U), read after timing
     unique_rows = 0
-    if wl.grads == "rowsparse":
-        step(0)
+    if backward:
+        serial_step(0, evs[0])
         torch.cuda.synchronize()
-        unique_rows = int(count.item())
-    elif wl.grads == "dense":
-        step(0)
-        torch.cuda.synchronize()
-        unique_rows = int(torch.unique(rows).numel())
+        unique_rows = (int(count.item()) if wl.grads == "rowsparse"
+                       else int(torch.unique(rows).numel()))
     nbytes = algorithmic_bytes(wl, unique_rows)
-    phases = {p: {"ms": phase_ms[p], "algorithmic_bytes": nbytes[p],
-                  "gbps": nbytes[p] / (phase_ms[p] * 1e-3) / 1e9,
-                  "frac_of_peak": nbytes[p] / (phase_ms[p] * 1e-3) / 1e9 / PEAK_HBM_GBS}
-              for p in phase_ms}
-    step_bytes = sum(nbytes[p] for p in phase_ms)
+    phases = {}
+    for p_, ms in phase_ms.items():
+        b_ = nbytes.get(p_, 0)
+        phases[p_] = {"ms": ms, "algorithmic_bytes": b_, "gbps": b_ / (ms * 1e-3) / 1e9,
+                      "frac_of_peak": b_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    step_bytes = sum(nbytes.values())
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # the gather is one kernel launch per call: its event time is the kernel's
+    # roofline of the dominant call: the gather is one kernel; the apply is
+    # the segment-reduce kernel plus the (short) long-run fix-up kernel
     dominant = "gather"
-    roofline = {"bound": "hbm", "kernel": "gather_kernel<5>" if D == 256 else "gather_kernel",
-                "achieved": phases[dominant]["gbps"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+    kernel = "gather_kernel<5>" if D == 256 else "gather_kernel"
+    if backward and phase_ms["scatter_apply"] > phase_ms["gather"]:
+        dominant = "scatter_apply"
+        kernel = "segment_reduce_kernel + segment_fixup_kernel (engram_scatter_apply)"
+    roofline = {"bound": "hbm", "kernel": kernel, "achieved": phases[dominant]["gbps"],
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS, "traffic": None}
 
     # context: a plain device-to-device copy (torch copy_, 2 GiB read + 2 GiB
@@ -238,9 +277,12 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {**wl.describe(), "step": "hash+gather" + ("+scatter" if backward else ""),
+        "config": {**wl.describe(),
+                   "step": "hash+gather" + ("+scatter(plan beside gather, apply)" if backward
+                                            else ""),
                    "backward": wl.grads, "accumulate": "f64" if backward else None,
                    "unique_rows": unique_rows, "token_batches_cycled": N_BATCHES},
+        "serial_ms_per_step": serial_ms,
         "step_algorithmic_bytes": step_bytes,
         "step_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBS,

@@ -340,14 +340,11 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
 
 // --------------------------------------------------------- segment heads ---
 // Distinct-row starts per kRange-position range (one ballot per wavefront,
-// kWave / kRange ranges per wavefront).  Also clears the count of cut-run
-// owners that the reduction kernel appends to.
+// kWave / kRange ranges per wavefront).
 __global__ __launch_bounds__(256) void range_heads_kernel(const uint32_t *keys, int64_t n,
                                                           uint32_t sentinel, uint32_t *head_count,
-                                                          int64_t num_ranges,
-                                                          uint32_t *owner_count) {
+                                                          int64_t num_ranges) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (j == 0) *owner_count = 0;
   bool head = false;
   if (j < n) {
     const uint32_t k = keys[j];
@@ -387,9 +384,10 @@ struct WalkArgs {
   // halves of every quad's 4 values in two planes (whole-line stores)
   double *pfirst;  // run entering the range from before
   double *plast;   // run leaving the range, started in it
-  uint32_t *run_end;     // [n]: end position of cut runs, by distinct-row slot
-  uint32_t *owner_list;  // [num_ranges]: ranges whose last run is cut
-  uint32_t *owner_count;
+  uint32_t *run_end;      // [n]: end position of long runs, by distinct-row slot
+  uint32_t *owner_flag;   // [num_ranges]: 1 where the range owns a long run
+  const uint32_t *unique_total;  // U, from the plan
+  int64_t *num_unique;           // row-sparse output count
 };
 
 template <int Q>
@@ -482,7 +480,9 @@ template <int L, int Q, bool SPARSE, bool EXACT>
 __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
   const int lane = threadIdx.x % L;
   const int64_t w = ((int64_t)blockIdx.x * kWalkThreads + threadIdx.x) / L;
+  if (SPARSE && blockIdx.x == 0 && threadIdx.x == 0) *a.num_unique = (int64_t)*a.unique_total;
   if (w >= a.num_ranges) return;
+  bool owns_long = false;
   const int64_t beg = w * kRange;
   const int cnt = (int)min((int64_t)kRange, a.n - beg);
 
@@ -558,7 +558,10 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
       }
     }
   }
-  if (live_count == 0) return;  // only padding / invalid ids from here on
+  if (live_count == 0) {  // only padding / invalid ids from here on
+    if (lane == 0) a.owner_flag[w] = 0;
+    return;
+  }
   const bool right_open = end < a.n && after == cur;
   if (first && left_open) {
     if (right_open) {  // a long run passes through this range
@@ -567,10 +570,12 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
       store_partial<L, Q>(a.pfirst, w, a, lane, acc);
       if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + live_count);
     }
+    if (lane == 0) a.owner_flag[w] = 0;
     return;
   }
   if (!right_open) {
     emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+    if (lane == 0) a.owner_flag[w] = 0;
     return;
   }
   // the last run continues into the next range (right_open: end < n, so
@@ -592,10 +597,10 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
 #pragma unroll
   for (int q = 0; q < kRange; ++q) m += (m == q && q < ncnt && nk[q] == cur) ? 1 : 0;
   const int64_t past = nbeg + kRange;
-  const bool is_long = m == kRange && past < a.n && a.keys[past] == cur;
-  if (is_long) {
+  owns_long = m == kRange && past < a.n && a.keys[past] == cur;
+  if (lane == 0) a.owner_flag[w] = owns_long ? 1u : 0u;
+  if (owns_long) {
     store_partial<L, Q>(a.plast, w, a, lane, acc);
-    if (lane == 0) a.owner_list[atomicAdd(a.owner_count, 1u)] = (uint32_t)w;
     return;
   }
   for (int q0 = 0; q0 < m; q0 += 4) {
@@ -615,48 +620,76 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
   emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
 }
 
-// Long runs (longer than a range; rare hot rows).  A block takes one owner
-// range c0 at a time (grid-stride over the owner list, whose length is read
-// on the device).  The run's pieces are plast[c0] and pfirst[c0 + 1 .. c1],
-// c1 being the range holding its end; the block's walkers sum interleaved
-// pieces, then walker 0 adds the walkers' sums in walker order and writes
-// the row.  Fixed assignment and fixed order keep the result deterministic.
+// Long runs (longer than a range; rare hot rows).  Block b looks after the
+// owner flags of ranges [b * span, (b + 1) * span); for each owning range c0
+// it sums the run's pieces plast[c0] and pfirst[c0 + 1 .. c1] (c1 is the
+// range holding the run's end): the block's walkers sum interleaved pieces,
+// walker 0 adds the walkers' sums in walker order and writes the row.  Fixed
+// assignment and fixed order keep the result deterministic.
 template <int L, int Q, bool SPARSE>
-__global__ __launch_bounds__(kWalkThreads) void segment_fixup_kernel(const WalkArgs a) {
+__global__ __launch_bounds__(kWalkThreads) void segment_fixup_kernel(const WalkArgs a,
+                                                                     int64_t span) {
   constexpr int G = kWalkThreads / L;  // walkers per block
   __shared__ double s_sum[G][L * Q * 4];
+  __shared__ uint32_t s_owner[kWalkThreads];
+  __shared__ int s_wave_owners[kWalkThreads / kWave];
+  __shared__ int s_owners;
   const int lane = threadIdx.x % L, g = threadIdx.x / L;
-  const uint32_t owners = *a.owner_count;
-  for (uint32_t i = blockIdx.x; i < owners; i += gridDim.x) {
-    const int64_t c0 = a.owner_list[i];
-    const uint32_t u = a.head_off[c0] + a.head_count[c0] - 1;
-    const uint32_t key = a.keys[(c0 + 1) * kRange - 1];
-    const int64_t c1 = ((int64_t)a.run_end[u] - 1) / kRange;
-    const int64_t pieces = c1 - c0 + 1;
-    double acc[Q][4];
-    zero_acc<Q>(acc);
-#pragma unroll 1
-    for (int64_t p = g; p < pieces; p += G) {
-      if (p == 0)
-        add_partial<L, Q>(a.plast, c0, a, lane, acc);
-      else
-        add_partial<L, Q>(a.pfirst, c0 + p, a, lane, acc);
-    }
-#pragma unroll
-    for (int k = 0; k < Q; ++k)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_sum[g][(lane * Q + k) * 4 + e] = acc[k][e];
+  const int64_t first = (int64_t)blockIdx.x * span;
+  const int64_t last = min(a.num_ranges, first + span);
+  for (int64_t r0 = first; r0 < last; r0 += kWalkThreads) {
+    // collect this stretch's owners (in range order)
+    if (threadIdx.x == 0) s_owners = 0;
     __syncthreads();
-    if (g == 0) {
-#pragma unroll 1
-      for (int h = 1; h < G; ++h)
-#pragma unroll
-        for (int k = 0; k < Q; ++k)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[k][e] += s_sum[h][(lane * Q + k) * 4 + e];
-      emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
+    const int64_t r = r0 + threadIdx.x;
+    const bool owner = r < last && a.owner_flag[r] != 0;
+    const unsigned long long bal = __ballot(owner);
+    if (__lane_id() == 0) s_wave_owners[threadIdx.x / kWave] = __popcll(bal);
+    __syncthreads();
+    if (owner) {
+      int at = __popcll(bal & ((1ull << __lane_id()) - 1ull));
+      for (int v = 0; v < (int)(threadIdx.x / kWave); ++v) at += s_wave_owners[v];
+      s_owner[at] = (uint32_t)r;
+    }
+    if (threadIdx.x == 0) {
+      int total = 0;
+      for (int v = 0; v < kWalkThreads / kWave; ++v) total += s_wave_owners[v];
+      s_owners = total;
     }
     __syncthreads();
+    const int owners = s_owners;
+    for (int i = 0; i < owners; ++i) {
+      const int64_t c0 = s_owner[i];
+      const uint32_t u = a.head_off[c0] + a.head_count[c0] - 1;
+      const uint32_t key = a.keys[(c0 + 1) * kRange - 1];
+      const int64_t c1 = ((int64_t)a.run_end[u] - 1) / kRange;
+      const int64_t pieces = c1 - c0 + 1;
+      double acc[Q][4];
+      zero_acc<Q>(acc);
+#pragma unroll 1
+      for (int64_t p = g; p < pieces; p += G) {
+        if (p == 0)
+          add_partial<L, Q>(a.plast, c0, a, lane, acc);
+        else
+          add_partial<L, Q>(a.pfirst, c0 + p, a, lane, acc);
+      }
+#pragma unroll
+      for (int k = 0; k < Q; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_sum[g][(lane * Q + k) * 4 + e] = acc[k][e];
+      __syncthreads();
+      if (g == 0) {
+#pragma unroll 1
+        for (int h = 1; h < G; ++h)
+#pragma unroll
+          for (int k = 0; k < Q; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] += s_sum[h][(lane * Q + k) * 4 + e];
+        emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
+      }
+      __syncthreads();
+    }
+    __syncthreads();  // s_owner / s_owners are rewritten by the next stretch
   }
 }
 
@@ -701,7 +734,7 @@ struct Plan {
   int64_t num_tiles, num_ranges, scan_chunks;
   int bits, passes, per_pass;
   size_t keys_a, vals_a, keys_b, vals_b, status, counters, chunk_sums, head_count, head_off,
-      scalars, run_end, owner_list, pfirst, plast, total;
+      scalars, run_end, owner_flag, pfirst, plast, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -747,7 +780,7 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
   p->head_off = take((size_t)p->num_ranges * 4);
   p->scalars = take(64);
   p->run_end = take(nn * 4);
-  p->owner_list = take((size_t)p->num_ranges * 4);
+  p->owner_flag = take((size_t)p->num_ranges * 4);
   p->pfirst = take((size_t)p->num_ranges * (size_t)dim * 8);
   p->plast = take((size_t)p->num_ranges * (size_t)dim * 8);
   p->total = off;
@@ -779,10 +812,10 @@ void launch_walkers(const WalkArgs &a, hipStream_t s) {
   else
     hipLaunchKernelGGL((segment_reduce_kernel<L, Q, SPARSE, false>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
-  const unsigned fix_blocks =
-      (unsigned)(a.num_ranges < kFixupBlocks ? a.num_ranges : kFixupBlocks);
+  const int64_t span = (a.num_ranges + kFixupBlocks - 1) / kFixupBlocks;
+  const unsigned fix_blocks = (unsigned)((a.num_ranges + span - 1) / span);
   hipLaunchKernelGGL((segment_fixup_kernel<L, Q, SPARSE>), dim3(fix_blocks), dim3(kWalkThreads),
-                     0, s, a);
+                     0, s, a, span);
 }
 
 template <bool SPARSE>
@@ -799,48 +832,60 @@ void dispatch_walkers(const WalkArgs &a, hipStream_t s) {
   else launch_walkers<64, 8, SPARSE>(a, s);
 }
 
-int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim,
-                   int64_t table_rows, bool sparse, float *grad_table, int64_t *unique_ids,
-                   float *unique_grads, int64_t *num_unique, void *ws, size_t ws_bytes,
-                   int64_t *err, hipStream_t s) {
-  Plan p;
-  if (!make_plan(n, table_rows, dim, &p) || !sorted_limits_ok(n, table_rows))
-    return ENGRAM_EINVAL;
-  if (ws == nullptr || ws_bytes < p.total) return ENGRAM_EWORKSPACE;
-  char *base = static_cast<char *>(ws);
-  uint32_t *keys_a = reinterpret_cast<uint32_t *>(base + p.keys_a);
-  uint32_t *vals_a = reinterpret_cast<uint32_t *>(base + p.vals_a);
-  uint32_t *keys_b = reinterpret_cast<uint32_t *>(base + p.keys_b);
-  uint32_t *vals_b = reinterpret_cast<uint32_t *>(base + p.vals_b);
-  uint32_t *chunk_sums = reinterpret_cast<uint32_t *>(base + p.chunk_sums);
-  uint32_t *head_count = reinterpret_cast<uint32_t *>(base + p.head_count);
-  uint32_t *head_off = reinterpret_cast<uint32_t *>(base + p.head_off);
-  uint32_t *owner_count = reinterpret_cast<uint32_t *>(base + p.scalars);
-  uint32_t *run_end = reinterpret_cast<uint32_t *>(base + p.run_end);
-  uint32_t *owner_list = reinterpret_cast<uint32_t *>(base + p.owner_list);
-  double *pfirst = reinterpret_cast<double *>(base + p.pfirst);
-  double *plast = reinterpret_cast<double *>(base + p.plast);
+// Workspace views shared by the plan and the apply.
+struct Views {
+  uint32_t *keys_a, *vals_a, *keys_b, *vals_b;
+  uint64_t *status;
+  uint32_t *counters, *chunk_sums, *head_count, *head_off, *scalars, *run_end, *owner_flag;
+  double *pfirst, *plast;
+  const uint32_t *sorted_keys, *sorted_vals;  // where the last sort pass leaves them
+};
 
-  // 1. radix sort (ping-pong a <-> b; the first pass reads the ids)
-  uint64_t *status = reinterpret_cast<uint64_t *>(base + p.status);
-  uint32_t *counters = reinterpret_cast<uint32_t *>(base + p.counters);
-  uint32_t *hist = counters;                                // [kHistCopies][4][kMaxBins]
-  uint32_t *tickets = counters + kHistCopies * 4 * kMaxBins;  // [4]
+Views views_of(const Plan &p, void *ws) {
+  char *base = static_cast<char *>(ws);
+  Views v;
+  v.keys_a = reinterpret_cast<uint32_t *>(base + p.keys_a);
+  v.vals_a = reinterpret_cast<uint32_t *>(base + p.vals_a);
+  v.keys_b = reinterpret_cast<uint32_t *>(base + p.keys_b);
+  v.vals_b = reinterpret_cast<uint32_t *>(base + p.vals_b);
+  v.status = reinterpret_cast<uint64_t *>(base + p.status);
+  v.counters = reinterpret_cast<uint32_t *>(base + p.counters);
+  v.chunk_sums = reinterpret_cast<uint32_t *>(base + p.chunk_sums);
+  v.head_count = reinterpret_cast<uint32_t *>(base + p.head_count);
+  v.head_off = reinterpret_cast<uint32_t *>(base + p.head_off);
+  v.scalars = reinterpret_cast<uint32_t *>(base + p.scalars);
+  v.run_end = reinterpret_cast<uint32_t *>(base + p.run_end);
+  v.owner_flag = reinterpret_cast<uint32_t *>(base + p.owner_flag);
+  v.pfirst = reinterpret_cast<double *>(base + p.pfirst);
+  v.plast = reinterpret_cast<double *>(base + p.plast);
+  // passes alternate a -> b -> a ...: an odd pass count ends in a
+  v.sorted_keys = (p.passes % 2 == 1) ? v.keys_a : v.keys_b;
+  v.sorted_vals = (p.passes % 2 == 1) ? v.vals_a : v.vals_b;
+  return v;
+}
+
+// Plan: sort the row ids and give every distinct row its slot (U is left
+// in the workspace scalars).  Needs only the ids.
+int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p, void *ws,
+                int64_t *err, hipStream_t s) {
+  const Views v = views_of(p, ws);
+  uint32_t *hist = v.counters;                                // [kHistCopies][4][kMaxBins]
+  uint32_t *tickets = v.counters + kHistCopies * 4 * kMaxBins;  // [4]
   const int64_t status_len = (int64_t)p.passes * p.num_tiles * kMaxBins;
   const int64_t clear_len = status_len > kSortCounters ? status_len : kSortCounters;
   hipLaunchKernelGGL(sort_clear_kernel, dim3((unsigned)((clear_len + 255) / 256)), dim3(256), 0,
-                     s, status, status_len, counters, kSortCounters);
+                     s, v.status, status_len, v.counters, kSortCounters);
   const int64_t hist_want = (n + 4095) / 4096;
   const int64_t hist_blocks = hist_want < 512 ? hist_want : 512;
   hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)hist_blocks), dim3(kSortThreads), 0,
                      s, ids, n, table_rows, p.passes, p.per_pass, p.bits, hist, err);
   const uint32_t *src_k = nullptr, *src_v = nullptr;
-  uint32_t *dst_k = keys_a, *dst_v = vals_a, *spare_k = keys_b, *spare_v = vals_b;
+  uint32_t *dst_k = v.keys_a, *dst_v = v.vals_a, *spare_k = v.keys_b, *spare_v = v.vals_b;
   const unsigned tiles = (unsigned)p.num_tiles;
   for (int pass = 0; pass < p.passes; ++pass) {
     const int shift = pass * p.per_pass;
     const int width = p.bits - shift < p.per_pass ? p.bits - shift : p.per_pass;
-    uint64_t *pass_status = status + (int64_t)pass * p.num_tiles * kMaxBins;
+    uint64_t *pass_status = v.status + (int64_t)pass * p.num_tiles * kMaxBins;
     if (pass == 0)
       hipLaunchKernelGGL(onesweep_kernel<true>, dim3(tiles), dim3(kSortThreads), 0, s, ids,
                          nullptr, nullptr, n, table_rows, shift, width, hist, pass_status,
@@ -857,35 +902,39 @@ int sorted_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
     spare_k = tk;
     spare_v = tv;
   }
-
-  // 2. distinct-row slots
-  const uint32_t sentinel = (uint32_t)table_rows;
+  // distinct-row slots
   const unsigned head_blocks = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(range_heads_kernel, dim3(head_blocks), dim3(256), 0, s, src_k, n, sentinel,
-                     head_count, p.num_ranges, owner_count);
-  launch_scan(head_count, head_off, p.num_ranges, chunk_sums, nullptr,
-              sparse ? num_unique : nullptr, s);
+  hipLaunchKernelGGL(range_heads_kernel, dim3(head_blocks), dim3(256), 0, s, v.sorted_keys, n,
+                     (uint32_t)table_rows, v.head_count, p.num_ranges);
+  launch_scan(v.head_count, v.head_off, p.num_ranges, v.chunk_sums, v.scalars, nullptr, s);
+  return launch_status();
+}
 
-  // 3. range walkers + fix-up
+// Apply: the per-row sums of one gradient tensor, given the plan of its ids.
+int apply_sorted(const void *grads, int64_t n, int64_t dim, int64_t table_rows, const Plan &p,
+                 void *ws, bool sparse, float *grad_table, int64_t *unique_ids,
+                 float *unique_grads, int64_t *num_unique, hipStream_t s) {
+  const Views v = views_of(p, ws);
   WalkArgs a;
-  a.keys = src_k;
-  a.vals = src_v;
+  a.keys = v.sorted_keys;
+  a.vals = v.sorted_vals;
   a.n = n;
-  a.sentinel = sentinel;
+  a.sentinel = (uint32_t)table_rows;
   a.grads = static_cast<const uint2 *>(grads);
   a.quads = dim / 4;
   a.dim = dim;
-  a.head_count = head_count;
-  a.head_off = head_off;
+  a.head_count = v.head_count;
+  a.head_off = v.head_off;
   a.num_ranges = p.num_ranges;
   a.grad_table = grad_table;
   a.unique_ids = unique_ids;
   a.unique_grads = unique_grads;
-  a.pfirst = pfirst;
-  a.plast = plast;
-  a.run_end = run_end;
-  a.owner_list = owner_list;
-  a.owner_count = owner_count;
+  a.pfirst = v.pfirst;
+  a.plast = v.plast;
+  a.run_end = v.run_end;
+  a.owner_flag = v.owner_flag;
+  a.unique_total = v.scalars;
+  a.num_unique = num_unique;
   if (sparse)
     dispatch_walkers<true>(a, s);
   else
@@ -940,6 +989,60 @@ extern "C" size_t engram_scatter_add_workspace(int64_t n, int64_t table_rows, in
   return p.total;
 }
 
+// Shared argument checks; fills the plan.  Returns ENGRAM_OK or an error.
+static int check_sorted(int64_t n, int64_t table_rows, int64_t head_dim, Plan *p) {
+  if (!make_plan(n, table_rows, head_dim, p) || !sorted_limits_ok(n, table_rows))
+    return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
+static int check_workspace(const Plan &p, const void *ws, size_t bytes) {
+  if (ws == nullptr || bytes < p.total || !aligned16(ws)) return ENGRAM_EWORKSPACE;
+  return ENGRAM_OK;
+}
+
+extern "C" int engram_scatter_plan(const int64_t *d_row_ids, int64_t n, int64_t table_rows,
+                                   int64_t head_dim, void *d_workspace, size_t workspace_bytes,
+                                   int64_t *d_err_count, void *stream) {
+  Plan p;
+  int rc = check_sorted(n, table_rows, head_dim, &p);
+  if (rc != ENGRAM_OK) return rc;
+  if (n == 0) return ENGRAM_OK;
+  if (d_row_ids == nullptr) return ENGRAM_EINVAL;
+  if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
+  return plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, as_stream(stream));
+}
+
+extern "C" int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
+                                    int64_t table_rows, float *d_grad_table,
+                                    int64_t *d_unique_ids, float *d_unique_grads,
+                                    int64_t *d_num_unique, void *d_workspace,
+                                    size_t workspace_bytes, void *stream) {
+  Plan p;
+  int rc = check_sorted(n, table_rows, head_dim, &p);
+  if (rc != ENGRAM_OK) return rc;
+  const bool dense = d_grad_table != nullptr;
+  const bool sparse = d_unique_ids != nullptr || d_unique_grads != nullptr || d_num_unique != nullptr;
+  if (dense == sparse) return ENGRAM_EINVAL;  // exactly one output form
+  if (sparse && (d_unique_ids == nullptr || d_unique_grads == nullptr || d_num_unique == nullptr))
+    return ENGRAM_EINVAL;
+  hipStream_t s = as_stream(stream);
+  if (n == 0) {
+    if (sparse) {
+      hipLaunchKernelGGL(write_zero_kernel, dim3(1), dim3(1), 0, s, d_num_unique);
+      return launch_status();
+    }
+    return ENGRAM_OK;
+  }
+  if (d_grads == nullptr) return ENGRAM_EINVAL;
+  if (!aligned16(d_grads) || (dense && !aligned16(d_grad_table)) ||
+      (sparse && !aligned16(d_unique_grads)))
+    return ENGRAM_EALIGN;
+  if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, sparse, d_grad_table,
+                      d_unique_ids, d_unique_grads, d_num_unique, s);
+}
+
 extern "C" int engram_scatter_add(const int64_t *d_row_ids, int64_t n, const void *d_grads,
                                   int64_t head_dim, float *d_grad_table, int64_t table_rows,
                                   int32_t mode, void *d_workspace, size_t workspace_bytes,
@@ -956,9 +1059,12 @@ extern "C" int engram_scatter_add(const int64_t *d_row_ids, int64_t n, const voi
   if (mode == ENGRAM_SCATTER_ATOMIC)
     return atomic_scatter(d_row_ids, n, d_grads, head_dim, d_grad_table, table_rows,
                           d_err_count, s);
-  if (!aligned16(d_workspace)) return ENGRAM_EWORKSPACE;
-  return sorted_scatter(d_row_ids, n, d_grads, head_dim, table_rows, false, d_grad_table,
-                        nullptr, nullptr, nullptr, d_workspace, workspace_bytes, d_err_count, s);
+  int rc = check_workspace(p, d_workspace, workspace_bytes);
+  if (rc != ENGRAM_OK) return rc;
+  if ((rc = plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, s)) != ENGRAM_OK)
+    return rc;
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, false, d_grad_table,
+                      nullptr, nullptr, nullptr, s);
 }
 
 extern "C" int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
@@ -968,8 +1074,8 @@ extern "C" int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
                                             void *d_workspace, size_t workspace_bytes,
                                             int64_t *d_err_count, void *stream) {
   Plan p;
-  if (!make_plan(n, table_rows, head_dim, &p) || !sorted_limits_ok(n, table_rows))
-    return ENGRAM_EINVAL;
+  int rc = check_sorted(n, table_rows, head_dim, &p);
+  if (rc != ENGRAM_OK) return rc;
   if (d_num_unique == nullptr) return ENGRAM_EINVAL;
   hipStream_t s = as_stream(stream);
   if (n == 0) {
@@ -980,8 +1086,9 @@ extern "C" int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
       d_unique_grads == nullptr)
     return ENGRAM_EINVAL;
   if (!aligned16(d_grads) || !aligned16(d_unique_grads)) return ENGRAM_EALIGN;
-  if (!aligned16(d_workspace)) return ENGRAM_EWORKSPACE;
-  return sorted_scatter(d_row_ids, n, d_grads, head_dim, table_rows, true, nullptr, d_unique_ids,
-                        d_unique_grads, d_num_unique, d_workspace, workspace_bytes, d_err_count,
-                        s);
+  if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
+  if ((rc = plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, s)) != ENGRAM_OK)
+    return rc;
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, true, nullptr,
+                      d_unique_ids, d_unique_grads, d_num_unique, s);
 }

@@ -62,6 +62,13 @@ _lib.engram_scatter_add_rowsparse.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c
                                               ctypes.c_int64, _vp, _vp, _vp, _vp,
                                               ctypes.c_size_t, _vp, _vp]
 
+_lib.engram_scatter_plan.restype = ctypes.c_int
+_lib.engram_scatter_plan.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
+                                     ctypes.c_size_t, _vp, _vp]
+_lib.engram_scatter_apply.restype = ctypes.c_int
+_lib.engram_scatter_apply.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
+                                      _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+
 
 class EngramError(RuntimeError):
     def __init__(self, status: int, call: str):
@@ -241,4 +248,58 @@ def engram_scatter_add_rowsparse(row_ids, grads, table_rows, unique_ids=None, un
                                                    _ptr(ws), ws.numel(), _ptr(err_count),
                                                    _stream(dev, stream))
     _check(status, "engram_scatter_add_rowsparse")
+    return unique_ids, unique_grads, num_unique
+
+
+def engram_scatter_plan(row_ids, table_rows, head_dim, workspace=None, err_count=None,
+                        stream=None):
+    """Sort the row ids and slot their distinct rows into `workspace`
+    (allocated when not given); returns the workspace."""
+    _device_tensor(row_ids, torch.int64, "row_ids")
+    n = row_ids.numel()
+    ws = _workspace(workspace, n, table_rows, head_dim, SCATTER_ROWSPARSE, row_ids.device)
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
+    with torch.cuda.device(row_ids.device):
+        status = _lib.engram_scatter_plan(_ptr(row_ids), n, int(table_rows), int(head_dim),
+                                          _ptr(ws), ws.numel(), _ptr(err_count),
+                                          _stream(row_ids.device, stream))
+    _check(status, "engram_scatter_plan")
+    return ws
+
+
+def engram_scatter_apply(grads, workspace, table_rows, grad_table=None, unique_ids=None,
+                         unique_grads=None, num_unique=None, stream=None):
+    """Sums of `grads` (bf16 [n, head_dim]) per the plan in `workspace`: into
+    grad_table (dense, in place) when given, else row-sparse (allocated when
+    not given); returns grad_table or (unique_ids, unique_grads, num_unique)."""
+    _device_tensor(grads, torch.bfloat16, "grads")
+    _device_tensor(workspace, torch.uint8, "workspace")
+    dim = grads.shape[-1]
+    n = grads.numel() // dim if dim else 0
+    dev = grads.device
+    if grad_table is not None:
+        _device_tensor(grad_table, torch.float32, "grad_table")
+        if grad_table.shape[-1] != dim:
+            raise ValueError("grad_table width differs from the gradients")
+    else:
+        if unique_ids is None:
+            unique_ids = torch.empty(max(n, 1), dtype=torch.int64, device=dev)
+        if unique_grads is None:
+            unique_grads = torch.empty((max(n, 1), dim), dtype=torch.float32, device=dev)
+        if num_unique is None:
+            num_unique = torch.empty(1, dtype=torch.int64, device=dev)
+        _device_tensor(unique_ids, torch.int64, "unique_ids")
+        _device_tensor(unique_grads, torch.float32, "unique_grads")
+        _device_tensor(num_unique, torch.int64, "num_unique")
+        if unique_ids.numel() < n or unique_grads.numel() < n * dim:
+            raise ValueError("unique_ids / unique_grads must hold n entries")
+    with torch.cuda.device(dev):
+        status = _lib.engram_scatter_apply(_ptr(grads), n, dim, int(table_rows),
+                                           _ptr(grad_table), _ptr(unique_ids),
+                                           _ptr(unique_grads), _ptr(num_unique), _ptr(workspace),
+                                           workspace.numel(), _stream(dev, stream))
+    _check(status, "engram_scatter_apply")
+    if grad_table is not None:
+        return grad_table
     return unique_ids, unique_grads, num_unique

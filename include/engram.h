@@ -177,6 +177,38 @@ int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
                                  void *d_workspace, size_t workspace_bytes,
                                  int64_t *d_err_count, void *stream);
 
+/*
+ * engram_scatter_plan / engram_scatter_apply -- the sorted backward in two
+ * steps.  The plan needs only the row ids: it sorts them and gives every
+ * distinct valid row its slot, leaving the result in the workspace.  The
+ * apply then computes the same sums as engram_scatter_add (sorted mode; pass
+ * d_grad_table) or engram_scatter_add_rowsparse (pass the three row-sparse
+ * outputs), for one bf16 gradient tensor of those ids.  Splitting them lets
+ * a caller run the plan as soon as the hash is done (for example on another
+ * stream, beside the forward gather) and reuse one plan for several gradient
+ * tensors of the same ids.  The same semantics and citations as the
+ * one-call forms apply.
+ *   engram_scatter_plan: d_row_ids int64 [n]; the workspace must hold at
+ *     least engram_scatter_add_workspace(n, table_rows, head_dim,
+ *     ENGRAM_SCATTER_ROWSPARSE) bytes; d_err_count as elsewhere.
+ *   engram_scatter_apply: the same n, head_dim, table_rows and workspace as
+ *     the plan, with the plan's work ordered before it (same stream, or an
+ *     event).  Exactly one output form: d_grad_table (dense, accumulated), or
+ *     all of d_unique_ids / d_unique_grads / d_num_unique (row-sparse).  The
+ *     apply does not change the plan; it may run again on the same plan.  A
+ *     workspace that holds no plan of these ids gives undefined results.
+ * Errors: EINVAL (sizes, output form), EALIGN, EWORKSPACE.  n == 0: the plan
+ * enqueues nothing; a row-sparse apply writes U = 0.
+ */
+int engram_scatter_plan(const int64_t *d_row_ids, int64_t n, int64_t table_rows,
+                        int64_t head_dim, void *d_workspace, size_t workspace_bytes,
+                        int64_t *d_err_count, void *stream);
+
+int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
+                         int64_t table_rows, float *d_grad_table, int64_t *d_unique_ids,
+                         float *d_unique_grads, int64_t *d_num_unique, void *d_workspace,
+                         size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

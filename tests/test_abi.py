@@ -21,7 +21,8 @@ def test_every_declared_symbol_is_exported():
     names = e.declared_symbols()
     assert set(names) == {"engram_status_string", "engram_abi_version", "engram_hash",
                           "engram_gather", "engram_scatter_add_workspace",
-                          "engram_scatter_add", "engram_scatter_add_rowsparse"}
+                          "engram_scatter_add", "engram_scatter_add_rowsparse",
+                          "engram_scatter_plan", "engram_scatter_apply"}
     for name in names:
         assert hasattr(e._lib, name), name
 
@@ -121,3 +122,24 @@ def test_scatter_rejects():
         e.ENGRAM_EINVAL
     assert r(ALIGNED, 100, ALIGNED, 8, 50, ALIGNED, ALIGNED, ALIGNED, ALIGNED, 16, None, None) == \
         e.ENGRAM_EWORKSPACE
+
+
+def test_plan_apply_reject():
+    ws = e.engram_scatter_add_workspace(100, 50, 8, 2)
+    pl, ap = e._lib.engram_scatter_plan, e._lib.engram_scatter_apply
+    assert pl(ALIGNED, 100, 50, 12, ALIGNED, ws, None, None) == e.ENGRAM_EINVAL   # dim % 8
+    assert pl(None, 100, 50, 8, ALIGNED, ws, None, None) == e.ENGRAM_EINVAL
+    assert pl(ALIGNED, 100, 50, 8, ALIGNED, ws - 1, None, None) == e.ENGRAM_EWORKSPACE
+    assert pl(ALIGNED, 100, 50, 8, MISALIGNED, ws, None, None) == e.ENGRAM_EWORKSPACE
+    assert pl(None, 0, 50, 8, None, 0, None, None) == e.ENGRAM_OK
+    # exactly one output form
+    assert ap(ALIGNED, 100, 8, 50, None, None, None, None, ALIGNED, ws, None) == e.ENGRAM_EINVAL
+    assert ap(ALIGNED, 100, 8, 50, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ALIGNED, ws, None) == \
+        e.ENGRAM_EINVAL
+    assert ap(ALIGNED, 100, 8, 50, None, ALIGNED, None, ALIGNED, ALIGNED, ws, None) == \
+        e.ENGRAM_EINVAL
+    assert ap(MISALIGNED, 100, 8, 50, ALIGNED, None, None, None, ALIGNED, ws, None) == \
+        e.ENGRAM_EALIGN
+    assert ap(ALIGNED, 100, 8, 50, ALIGNED, None, None, None, ALIGNED, 16, None) == \
+        e.ENGRAM_EWORKSPACE
+    assert ap(None, 0, 8, 50, ALIGNED, None, None, None, None, 0, None) == e.ENGRAM_OK

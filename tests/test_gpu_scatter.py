@@ -195,3 +195,51 @@ def test_workspace_too_small_is_rejected():
     with pytest.raises(E.EngramError) as info:
         E.engram_scatter_add(ids, grads, table, workspace=ws)
     assert info.value.status == E.ENGRAM_EWORKSPACE
+
+
+def test_plan_apply_matches_one_call_and_reuses_plan(oracle):
+    """The two-step form gives the one-call results bit for bit, and one plan
+    serves several gradient tensors of the same ids (dense and row-sparse)."""
+    wl = workloads.backward()
+    ids = oracle.hash(wl.tokens(1), wl.ngram_size, wl.heads_per_ngram, wl.eos_id,
+                      wl.multipliers(), wl.primes, wl.offsets).reshape(-1)
+    ids_dev = dev(ids)
+    rows, dim = wl.table_rows, wl.dim
+    plan = E.engram_scatter_plan(ids_dev, rows, dim)
+    for seed in (31, 32):
+        grads = workloads.make_grads(ids.size, dim, seed, "cuda")
+        base = workloads.make_grad_table(rows, dim, seed + 100, "cuda")
+        one = base.clone()
+        E.engram_scatter_add(ids_dev, grads, one)
+        two = E.engram_scatter_apply(grads, plan, rows, grad_table=base.clone())
+        assert torch.equal(one.view(torch.int32), two.view(torch.int32))
+        u1, v1, c1 = E.engram_scatter_add_rowsparse(ids_dev, grads, rows)
+        u2, v2, c2 = E.engram_scatter_apply(grads, plan, rows)
+        n = int(c1.item())
+        assert n == int(c2.item())
+        assert torch.equal(u1[:n], u2[:n])
+        assert torch.equal(v1[:n].view(torch.int32), v2[:n].view(torch.int32))
+        want_uid, want_val, _ = oracle.scatter_add_rowsparse(ids, bits(grads), dim, rows)
+        assert np.array_equal(u2[:n].cpu().numpy(), want_uid)
+        assert np.array_equal(host_f32(v2[:n]).view(np.uint32), want_val.view(np.uint32))
+    release()
+
+
+def test_plan_on_side_stream(oracle):
+    """Plan on a second stream, apply on the main one after an event."""
+    wl = workloads.tiny()
+    ids = oracle.hash(wl.tokens(2), 3, 2, 0, wl.multipliers(), wl.primes, wl.offsets).reshape(-1)
+    ids_dev = dev(ids)
+    grads = workloads.make_grads(ids.size, wl.dim, 77, "cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan = E.engram_scatter_plan(ids_dev, wl.table_rows, wl.dim)
+        done = torch.cuda.Event()
+        done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    uid, uval, count = E.engram_scatter_apply(grads, plan, wl.table_rows)
+    n = int(count.item())
+    want_uid, want_val, _ = oracle.scatter_add_rowsparse(ids, bits(grads), wl.dim, wl.table_rows)
+    assert np.array_equal(uid[:n].cpu().numpy(), want_uid)
+    assert np.array_equal(host_f32(uval[:n]).view(np.uint32), want_val.view(np.uint32))
