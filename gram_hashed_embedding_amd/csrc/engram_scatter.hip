@@ -27,8 +27,8 @@
 //  2. Segment heads (first position of each distinct row) are counted per
 //     16-position range and scanned: the scan gives every distinct row its
 //     output slot u, and U itself.
-//  3. Range walkers: a group of head_dim/8 lanes (two 4-value quads of the
-//     row per lane) takes one 16-position range of the sorted order, issues all its
+//  3. Range walkers: a group of head_dim/4 lanes (one 4-value quad of the
+//     row per lane, up to a whole wavefront) takes one 16-position range of the sorted order, issues all its
 //     loads at once (keys, flat indices, then the 16 gradient rows) and sums
 //     runs in fp64 registers.  A run that starts and ends inside the range
 //     is written once (dense read-modify-write or row-sparse store).  A run
@@ -818,17 +818,21 @@ void launch_walkers(const WalkArgs &a, hipStream_t s) {
                      0, s, a, span);
 }
 
+// One quad (4 values) per lane: a walker is quads lanes wide, up to a whole
+// wavefront (head_dim 256: one 64-lane walker per wavefront, each load
+// instruction one 512-byte bf16 row, each store one 1 KB fp32 row); wider
+// rows give each lane 2, 4 or 8 quads.
 template <bool SPARSE>
 void dispatch_walkers(const WalkArgs &a, hipStream_t s) {
-  const int64_t cpr = a.quads / 2;  // 16-byte chunks per row
-  if (cpr <= 1) launch_walkers<1, 2, SPARSE>(a, s);
-  else if (cpr <= 2) launch_walkers<2, 2, SPARSE>(a, s);
-  else if (cpr <= 4) launch_walkers<4, 2, SPARSE>(a, s);
-  else if (cpr <= 8) launch_walkers<8, 2, SPARSE>(a, s);
-  else if (cpr <= 16) launch_walkers<16, 2, SPARSE>(a, s);
-  else if (cpr <= 32) launch_walkers<32, 2, SPARSE>(a, s);
-  else if (cpr <= 64) launch_walkers<64, 2, SPARSE>(a, s);
-  else if (cpr <= 128) launch_walkers<64, 4, SPARSE>(a, s);
+  const int64_t q = a.quads;
+  if (q <= 2) launch_walkers<2, 1, SPARSE>(a, s);
+  else if (q <= 4) launch_walkers<4, 1, SPARSE>(a, s);
+  else if (q <= 8) launch_walkers<8, 1, SPARSE>(a, s);
+  else if (q <= 16) launch_walkers<16, 1, SPARSE>(a, s);
+  else if (q <= 32) launch_walkers<32, 1, SPARSE>(a, s);
+  else if (q <= 64) launch_walkers<64, 1, SPARSE>(a, s);
+  else if (q <= 128) launch_walkers<64, 2, SPARSE>(a, s);
+  else if (q <= 256) launch_walkers<64, 4, SPARSE>(a, s);
   else launch_walkers<64, 8, SPARSE>(a, s);
 }
 
