@@ -16,7 +16,7 @@
 // Sorted (deterministic) path, all on the caller's stream:
 //  1. LSD radix sort of (row, flat index) pairs, key width = bit width of
 //     table_rows, at most 8 bits per pass, one kernel per pass ("one-sweep"):
-//     each 4096-key tile ranks its keys with a wavefront multi-split (one
+//     each 8192-key tile (512 threads) ranks its keys with a wavefront multi-split (one
 //     ballot per digit bit yields the mask of lanes holding the same digit,
 //     its popcount the stable rank), finds its output offsets by decoupled
 //     look-back over earlier tiles' published digit counts, and writes its
@@ -45,7 +45,7 @@
 namespace engram {
 namespace {
 
-constexpr int kSortThreads = 256;
+constexpr int kSortThreads = 512;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per tile
@@ -77,9 +77,10 @@ __device__ __forceinline__ uint32_t make_key(int64_t id, int64_t table_rows, int
 }
 
 // ------------------------------------------------------------ block scan ---
-// Exclusive scan of one value per thread over a 256-thread block.
+// Exclusive scan of one value per thread over an NT-thread block.
+template <int NT>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t &total) {
-  __shared__ uint32_t s_wave[kScanThreads / kWave];
+  __shared__ uint32_t s_wave[NT / kWave];
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   uint32_t x = v;
 #pragma unroll
@@ -91,7 +92,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t &t
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < kScanThreads / kWave; ++w) {
+  for (int w = 0; w < NT / kWave; ++w) {
     const uint32_t t = s_wave[w];
     before += w < wave ? t : 0u;
     all += t;
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_reduce_kernel(const uint32_
     if (p < m) s += in[p];
   }
   uint32_t total;
-  block_exclusive_scan(s, total);
+  block_exclusive_scan<kScanThreads>(s, total);
   if (threadIdx.x == 0) chunk_sums[blockIdx.x] = total;
 }
 
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(
   uint32_t carry = 0;
   for (int64_t b = threadIdx.x; b < (int64_t)blockIdx.x; b += kScanThreads) carry += chunk_sums[b];
   uint32_t carry_total;
-  block_exclusive_scan(carry, carry_total);
+  block_exclusive_scan<kScanThreads>(carry, carry_total);
 
   const int64_t base = (int64_t)blockIdx.x * kScanChunk + (int64_t)threadIdx.x * kScanItems;
   uint32_t v[kScanItems];
@@ -135,7 +136,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(
     s += v[i];
   }
   uint32_t block_total;
-  uint32_t run = carry_total + block_exclusive_scan(s, block_total);
+  uint32_t run = carry_total + block_exclusive_scan<kScanThreads>(s, block_total);
 #pragma unroll
   for (int i = 0; i < kScanItems; ++i) {
     if (base + i < m) out[base + i] = run;
@@ -219,7 +220,8 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   const int count = (int)min((int64_t)kSortTile, n - tile0);
 
   // keys of this tile: wave w owns tile positions [w * 1024, (w + 1) * 1024)
-  // in 16 rounds of 64, so (wave, round, lane) is the original order
+  // in 16 rounds of 64, so (wave, round, lane) is the original order; then
+  // the global digit totals (their latency overlaps the ranking)
   const int64_t base = tile0 + (int64_t)wave * (kSortItems * kWave);
   const unsigned long long below = (1ull << lane) - 1ull;
   uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
@@ -237,6 +239,10 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
     }
     rank[i] = 0;
   }
+  uint32_t copies[kHistCopies];
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c)
+    copies[c] = tid < bins ? hist[(int64_t)c * 4 * kMaxBins + tid] : 0u;
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const int64_t p = base + (int64_t)i * kWave + lane;
@@ -271,11 +277,12 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   // tile-local digit starts, and global digit starts (keys of all smaller
   // digits over all tiles), by block scans over the digits
   uint32_t scan_total;
-  const uint32_t local_start = block_exclusive_scan(tid < bins ? tile_count : 0u, scan_total);
+  const uint32_t local_start =
+      block_exclusive_scan<kSortThreads>(tid < bins ? tile_count : 0u, scan_total);
   uint32_t digit_total = 0;
-  if (tid < bins)
-    for (int c = 0; c < kHistCopies; ++c) digit_total += hist[(int64_t)c * 4 * kMaxBins + tid];
-  const uint32_t digit_start = block_exclusive_scan(digit_total, scan_total);
+#pragma unroll
+  for (int c = 0; c < kHistCopies; ++c) digit_total += copies[c];
+  const uint32_t digit_start = block_exclusive_scan<kSortThreads>(digit_total, scan_total);
   // decoupled look-back: the keys of this digit in all earlier tiles
   if (tid < bins) {
     s_local[tid] = local_start;
