@@ -16,7 +16,7 @@
 // Sorted (deterministic) path, all on the caller's stream:
 //  1. LSD radix sort of (row, flat index) pairs, key width = bit width of
 //     table_rows, at most 8 bits per pass, one kernel per pass ("one-sweep"):
-//     each 8192-key tile (512 threads) ranks its keys with a wavefront multi-split (one
+//     each 4096-key tile ranks its keys with a wavefront multi-split (one
 //     ballot per digit bit yields the mask of lanes holding the same digit,
 //     its popcount the stable rank), finds its output offsets by decoupled
 //     look-back over earlier tiles' published digit counts, and writes its
@@ -45,7 +45,7 @@
 namespace engram {
 namespace {
 
-constexpr int kSortThreads = 512;
+constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per tile
