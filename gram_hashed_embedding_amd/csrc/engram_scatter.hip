@@ -630,9 +630,12 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
 // Long runs (longer than a range; rare hot rows).  Block b looks after the
 // owner flags of ranges [b * span, (b + 1) * span); for each owning range c0
 // it sums the run's pieces plast[c0] and pfirst[c0 + 1 .. c1] (c1 is the
-// range holding the run's end): the block's walkers sum interleaved pieces,
-// walker 0 adds the walkers' sums in walker order and writes the row.  Fixed
+// range holding the run's end): the block's walkers sum interleaved pieces
+// (several loads in flight each), walker 0 adds the walkers' sums in walker
+// order and writes the row.  Fixed
 // assignment and fixed order keep the result deterministic.
+constexpr int kFixBatch = 4;
+
 template <int L, int Q, bool SPARSE>
 __global__ __launch_bounds__(kWalkThreads) void segment_fixup_kernel(const WalkArgs a,
                                                                      int64_t span) {
@@ -671,14 +674,25 @@ __global__ __launch_bounds__(kWalkThreads) void segment_fixup_kernel(const WalkA
       const uint32_t key = a.keys[(c0 + 1) * kRange - 1];
       const int64_t c1 = ((int64_t)a.run_end[u] - 1) / kRange;
       const int64_t pieces = c1 - c0 + 1;
+      // walker g sums pieces g, g + G, g + 2G, ... in that order,
+      // kFixBatch pieces in flight
       double acc[Q][4];
       zero_acc<Q>(acc);
 #pragma unroll 1
-      for (int64_t p = g; p < pieces; p += G) {
-        if (p == 0)
-          add_partial<L, Q>(a.plast, c0, a, lane, acc);
-        else
-          add_partial<L, Q>(a.pfirst, c0 + p, a, lane, acc);
+      for (int64_t p0 = g; p0 < pieces; p0 += (int64_t)G * kFixBatch) {
+        double part[kFixBatch][Q][4];
+#pragma unroll
+        for (int b = 0; b < kFixBatch; ++b) {
+          const int64_t p = p0 + (int64_t)b * G;
+          zero_acc<Q>(part[b]);
+          if (p < pieces) add_partial<L, Q>(p == 0 ? a.plast : a.pfirst, c0 + p, a, lane, part[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < kFixBatch; ++b)
+#pragma unroll
+          for (int k = 0; k < Q; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[k][e] += part[b][k][e];
       }
 #pragma unroll
       for (int k = 0; k < Q; ++k)
