@@ -416,6 +416,17 @@ __device__ __forceinline__ void add_quads(double (&acc)[Q][4], const uint2 (&g)[
   }
 }
 
+template <int Q>
+__device__ __forceinline__ void add_quads_if(double (&acc)[Q][4], const uint2 (&g)[Q], bool live) {
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    acc[k][0] += live ? (double)bf16_lo(g[k].x) : 0.0;
+    acc[k][1] += live ? (double)bf16_hi(g[k].x) : 0.0;
+    acc[k][2] += live ? (double)bf16_lo(g[k].y) : 0.0;
+    acc[k][3] += live ? (double)bf16_hi(g[k].y) : 0.0;
+  }
+}
+
 template <int L, int Q>
 __device__ __forceinline__ void store_partial(double *buf, int64_t r, const WalkArgs &a, int lane,
                                               const double (&acc)[Q][4]) {
@@ -546,23 +557,24 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
 #pragma unroll
     for (int qq = 0; qq < B; ++qq) {
       const int q = b0 + qq;
-      if (q < live_count) {
-        if (kk[q] != cur) {  // a new distinct row starts at beg + q
-          if (first && left_open) {
-            if (!skip_lead) {  // last piece of a long run
-              store_partial<L, Q>(a.pfirst, w, a, lane, acc);
-              if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + q);
-            }
-          } else {
-            emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
-            ++u;
+      const bool live = q < live_count;
+      if (live && kk[q] != cur) {  // a new distinct row starts at beg + q
+        if (first && left_open) {
+          if (!skip_lead) {  // last piece of a long run
+            store_partial<L, Q>(a.pfirst, w, a, lane, acc);
+            if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + q);
           }
-          cur = kk[q];
-          first = false;
-          zero_acc<Q>(acc);
+        } else {
+          emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+          ++u;
         }
-        add_quads<Q>(acc, g[qq]);
+        cur = kk[q];
+        first = false;
+        zero_acc<Q>(acc);
       }
+      // the row is used on every path, so its load stays with the others
+      // (issued in order, consumed in order as each one arrives)
+      add_quads_if<Q>(acc, g[qq], live);
     }
   }
   if (live_count == 0) {  // only padding / invalid ids from here on
