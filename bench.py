@@ -60,6 +60,28 @@ def algorithmic_bytes(wl, unique_rows, with_seg=False):
     return out
 
 
+def measured_traffic(call, wl):
+    """HBM bytes per launch of `call` from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic.json), or None when it was taken on another
+    workload or the kernel's source has changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if wl.name != "e2e" or not os.path.exists(path):
+        return None
+    rec = json.load(open(path))["kernels"]
+    parts = {"gather": ["gather"], "scatter_apply": ["reduce", "fixup"]}.get(call)
+    if parts is None:
+        return None
+    total = 0.0
+    for key in parts:
+        k = rec[key]
+        src = os.path.join(ROOT, k["source"])
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != k["source_sha256"]:
+            return None
+        total += k["fetch_bytes"] + k["write_bytes"]
+    return total
+
+
 def cpu_baseline(wl, tokens_host, mult, table, grads, budget_s=12.0):
     """The oracle (single-threaded C) on the host cores, on the e2e batch:
     hash, gather from a compact host copy of the table rows the batch
@@ -239,7 +261,8 @@ def main():
         kernel = "segment_reduce_kernel + segment_fixup_kernel (engram_scatter_apply)"
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": phases[dominant]["gbps"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS, "traffic": None}
+                "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS,
+                "traffic": measured_traffic(dominant, wl)}
 
     # context: a plain device-to-device copy (torch copy_, 2 GiB read + 2 GiB
     # written) shows what this GPU's HBM delivers to a streaming kernel
