@@ -69,7 +69,7 @@ def measured_traffic(call, wl):
     if wl.name != "e2e" or not os.path.exists(path):
         return None
     rec = json.load(open(path))["kernels"]
-    parts = {"gather": ["gather"], "scatter_apply": ["reduce", "fixup"]}.get(call)
+    parts = {"gather": ["gather"], "scatter_apply": ["reduce"]}.get(call)
     if parts is None:
         return None
     total = 0.0
@@ -258,7 +258,7 @@ def main():
     kernel = "gather_kernel<5>" if D == 256 else "gather_kernel"
     if backward and phase_ms["scatter_apply"] > phase_ms["gather"]:
         dominant = "scatter_apply"
-        kernel = "segment_reduce_kernel + segment_fixup_kernel (engram_scatter_apply)"
+        kernel = "segment_reduce_kernel (engram_scatter_apply)"
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": phases[dominant]["gbps"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS,

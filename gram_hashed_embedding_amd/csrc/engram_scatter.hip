@@ -28,16 +28,17 @@
 //     16-position range and scanned: the scan gives every distinct row its
 //     output slot u, and U itself.
 //  3. Range walkers: a group of head_dim/4 lanes (one 4-value quad of the
-//     row per lane, up to a whole wavefront) takes one 16-position range of the sorted order, issues all its
-//     loads at once (keys, flat indices, then the 16 gradient rows) and sums
-//     runs in fp64 registers.  A run that starts and ends inside the range
-//     is written once (dense read-modify-write or row-sparse store).  A run
-//     cut by the range's end but ending in the next range is finished by
-//     the same walker; only runs longer than a range (hot rows) leave fp64
-//     partials, which a fix-up pass adds in range order with a whole block
-//     per run before writing the row.  No work item waits on another, and hot rows (hundreds of
-//     contributions) are spread over many walkers instead of serialising
-//     one.
+//     row per lane, up to a whole wavefront) takes one 16-position range of
+//     the sorted order, issues all its loads at once (keys, flat indices,
+//     then the gradient rows) and sums runs in fp64 registers.  A run that
+//     starts and ends inside the range is written once (dense
+//     read-modify-write or row-sparse store); a run cut by the range's end
+//     but ending in the next range is finished by the same walker.  Runs
+//     longer than that (hot rows; the plan lists them) are summed whole by
+//     the leading blocks of the same launch, a block per run, its walkers
+//     taking interleaved ranges of the run and adding their sums in a fixed
+//     order.  No work item waits on another, and hot rows (hundreds of
+//     contributions) do not serialise a walker.
 // Atomic path: one fp32 atomic add per gradient element into the dense
 // table (hardware float atomics in L2); order of additions not fixed.
 #include "engram_internal.h"
@@ -58,12 +59,14 @@ constexpr int kWalkThreads = 256;
 constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnroll = 4;
 
-constexpr int64_t kFixupBlocks = 1024;  // blocks of the long-run fix-up
+constexpr int64_t kLongBlocks = 1024;  // most blocks that sum long runs
 // Global digit totals are kept in kHistCopies copies (a block adds to copy
 // blockIdx % kHistCopies) so the histogram's atomics do not all meet on the
 // same few hundred words; readers add the copies.
 constexpr int kHistCopies = 8;
-constexpr int kSortCounters = kHistCopies * 4 * 256 + 4;  // digit totals, pass tickets
+// counters: digit totals, 4 pass tickets, the long-run count (and padding)
+constexpr int kSortCounters = kHistCopies * 4 * 256 + 8;
+constexpr int kLongCountAt = kHistCopies * 4 * 256 + 4;
 static_assert(kWave % kRange == 0 && kRange % 4 == 0, "ranges tile a wavefront");
 
 // ----------------------------------------------------------------- keys ----
@@ -347,9 +350,15 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
 
 // --------------------------------------------------------- segment heads ---
 // Distinct-row starts per kRange-position range (one ballot per wavefront,
-// kWave / kRange ranges per wavefront).
+// kWave / kRange ranges per wavefront), and the long runs: a run is long when
+// it starts in range c and still holds position 16 (c + 2), so it covers
+// the whole of range c + 1 and reaches beyond.  Every range whose last run is
+// long is flagged and appended to the long-run list (list order is
+// immaterial: each long run is summed the same way whoever takes it).
 __global__ __launch_bounds__(256) void range_heads_kernel(const uint32_t *keys, int64_t n,
                                                           uint32_t sentinel, uint32_t *head_count,
+                                                          uint32_t *long_flag, uint32_t *long_list,
+                                                          uint32_t *long_count,
                                                           int64_t num_ranges) {
   const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   bool head = false;
@@ -362,7 +371,16 @@ __global__ __launch_bounds__(256) void range_heads_kernel(const uint32_t *keys, 
   if ((lane % kRange) == 0) {
     const int64_t r = j / kRange;
     const unsigned long long mine = (m >> lane) & ((1ull << kRange) - 1ull);
-    if (r < num_ranges) head_count[r] = (uint32_t)__popcll(mine);
+    if (r < num_ranges) {
+      head_count[r] = (uint32_t)__popcll(mine);
+      bool lng = false;
+      if (j + 2 * kRange < n) {
+        const uint32_t k = keys[j + kRange - 1];
+        lng = k != sentinel && keys[j + 2 * kRange] == k && (j == 0 || keys[j - 1] != k);
+      }
+      long_flag[r] = lng ? 1u : 0u;
+      if (lng) long_list[atomicAdd(long_count, 1u)] = (uint32_t)r;
+    }
   }
 }
 
@@ -387,12 +405,10 @@ struct WalkArgs {
   float *grad_table;    // dense output
   int64_t *unique_ids;  // row-sparse output
   float *unique_grads;
-  // fp64 partial rows, [num_ranges][2][quads][2]: the first and second
-  // halves of every quad's 4 values in two planes (whole-line stores)
-  double *pfirst;  // run entering the range from before
-  double *plast;   // run leaving the range, started in it
-  uint32_t *run_end;      // [n]: end position of long runs, by distinct-row slot
-  uint32_t *owner_flag;   // [num_ranges]: 1 where the range owns a long run
+  const uint32_t *long_flag;   // [num_ranges]: 1 where the range's last run is long
+  const uint32_t *long_list;   // ranges whose last run is long
+  const uint32_t *long_count;  // length of long_list
+  uint32_t long_blocks;        // leading blocks of the grid that sum long runs
   const uint32_t *unique_total;  // U, from the plan
   int64_t *num_unique;           // row-sparse output count
 };
@@ -427,35 +443,38 @@ __device__ __forceinline__ void add_quads_if(double (&acc)[Q][4], const uint2 (&
   }
 }
 
-template <int L, int Q>
-__device__ __forceinline__ void store_partial(double *buf, int64_t r, const WalkArgs &a, int lane,
-                                              const double (&acc)[Q][4]) {
-  double *base = buf + r * a.dim;
+// This lane's quads of one gradient row.
+template <int L, int Q, bool EXACT>
+__device__ __forceinline__ void load_row(const WalkArgs &a, uint32_t idx, int lane,
+                                         uint2 (&g)[Q]) {
+  const uint2 *row = a.grads + (int64_t)idx * a.quads;
 #pragma unroll
-  for (int k = 0; k < Q; ++k) {
-    const int64_t qd = lane + (int64_t)k * L;
-    if (qd < a.quads) {
-      reinterpret_cast<f64x2 *>(base)[qd] = f64x2{acc[k][0], acc[k][1]};
-      reinterpret_cast<f64x2 *>(base)[a.quads + qd] = f64x2{acc[k][2], acc[k][3]};
-    }
+  for (int k = 0; k < Q; ++k)
+    g[k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
+}
+
+// Keys and flat indices of one range as 16-byte vectors.
+__device__ __forceinline__ void load_range(const uint32_t *keys, const uint32_t *vals,
+                                           int64_t beg, uint32_t (&kk)[kRange],
+                                           uint32_t (&vv)[kRange]) {
+  const u32x4 *kp = reinterpret_cast<const u32x4 *>(keys + beg);
+  const u32x4 *vp = reinterpret_cast<const u32x4 *>(vals + beg);
+#pragma unroll
+  for (int i = 0; i < kRange / 4; ++i) {
+    const u32x4 k4 = kp[i], v4 = vp[i];
+    kk[4 * i] = k4.x; kk[4 * i + 1] = k4.y; kk[4 * i + 2] = k4.z; kk[4 * i + 3] = k4.w;
+    vv[4 * i] = v4.x; vv[4 * i + 1] = v4.y; vv[4 * i + 2] = v4.z; vv[4 * i + 3] = v4.w;
   }
 }
 
-template <int L, int Q>
-__device__ __forceinline__ void add_partial(const double *buf, int64_t r, const WalkArgs &a,
-                                            int lane, double (&acc)[Q][4]) {
-  const double *base = buf + r * a.dim;
+// Flat indices of one range as 16-byte vectors.
+__device__ __forceinline__ void load_vals(const uint32_t *vals, int64_t beg,
+                                          uint32_t (&vv)[kRange]) {
+  const u32x4 *vp = reinterpret_cast<const u32x4 *>(vals + beg);
 #pragma unroll
-  for (int k = 0; k < Q; ++k) {
-    const int64_t qd = lane + (int64_t)k * L;
-    if (qd < a.quads) {
-      const f64x2 lo = reinterpret_cast<const f64x2 *>(base)[qd];
-      const f64x2 hi = reinterpret_cast<const f64x2 *>(base)[a.quads + qd];
-      acc[k][0] += lo.x;
-      acc[k][1] += lo.y;
-      acc[k][2] += hi.x;
-      acc[k][3] += hi.y;
-    }
+  for (int i = 0; i < kRange / 4; ++i) {
+    const u32x4 v4 = vp[i];
+    vv[4 * i] = v4.x; vv[4 * i + 1] = v4.y; vv[4 * i + 2] = v4.z; vv[4 * i + 3] = v4.w;
   }
 }
 
@@ -480,66 +499,56 @@ __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArg
   }
 }
 
-// One walker over one kRange-position range of the sorted order.  Every
-// load is issued up front and unconditionally (keys and flat indices as
-// 16-byte vectors, then one gradient row per position; positions past the
-// data, or owned by the previous walker, read row 0 and are ignored), so a
-// walker costs two memory round trips; only then are runs summed and
-// written.  Run ownership: the walker holding a run's first position owns
-// it.  A run that ends inside its owner's range is written at once.  A run
-// that crosses into the next range but ends there ("short") is finished by
-// its owner, which then reads the next range's keys and the continuation
-// rows; the next walker recognises it (the run did not cover the last
-// position of the range before the previous one) and skips it.  A longer
-// run leaves fp64 partials: plast from its owner, pfirst from every later
-// range it touches (the last one also records where the run ends), and its
-// owner joins the owner list for the fix-up.
+// One walker over one kRange-position range of the sorted order.  Run
+// ownership: the walker holding a run's first position owns it, unless the
+// run is long (then a long-run block sums it whole).  Positions of a run
+// that entered from the previous range are never summed here: that run is
+// either long or was finished by its owner.  Every load of the positions the
+// walker sums is issued up front and unconditionally (keys and flat indices
+// as 16-byte vectors, then one gradient row per position; other positions
+// read row 0 and are ignored), so a walker costs two memory round trips;
+// only then are runs summed and written.  A run that crosses into the next
+// range (and, not being long, ends there) is finished by its owner, which
+// then reads the next range's keys and the continuation rows.
 template <int L, int Q, bool SPARSE, bool EXACT>
-__global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
+__device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
   const int lane = threadIdx.x % L;
-  const int64_t w = ((int64_t)blockIdx.x * kWalkThreads + threadIdx.x) / L;
-  if (SPARSE && blockIdx.x == 0 && threadIdx.x == 0) *a.num_unique = (int64_t)*a.unique_total;
+  const int64_t w = (blk * kWalkThreads + threadIdx.x) / L;
   if (w >= a.num_ranges) return;
-  bool owns_long = false;
   const int64_t beg = w * kRange;
   const int cnt = (int)min((int64_t)kRange, a.n - beg);
 
   uint32_t kk[kRange], vv[kRange];
-  {
-    const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + beg);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(a.vals + beg);
-#pragma unroll
-    for (int i = 0; i < kRange / 4; ++i) {
-      const u32x4 k4 = kp[i], v4 = vp[i];
-      kk[4 * i] = k4.x; kk[4 * i + 1] = k4.y; kk[4 * i + 2] = k4.z; kk[4 * i + 3] = k4.w;
-      vv[4 * i] = v4.x; vv[4 * i + 1] = v4.y; vv[4 * i + 2] = v4.z; vv[4 * i + 3] = v4.w;
-    }
-  }
+  load_range(a.keys, a.vals, beg, kk, vv);
   const int64_t end = beg + cnt;
   const uint32_t before = a.keys[beg > 0 ? beg - 1 : 0];
-  const uint32_t before2 = a.keys[beg > kRange ? beg - kRange - 1 : 0];
   const uint32_t after = a.keys[end < a.n ? end : a.n - 1];
+  const bool last_long = a.long_flag[w] != 0;
   int live_count = 0;
 #pragma unroll
   for (int q = 0; q < kRange; ++q) {
     if (q >= cnt) kk[q] = a.sentinel;
     live_count += kk[q] != a.sentinel ? 1 : 0;  // sentinels sort last
   }
+  // [lead, tail): the positions this walker sums.  lead skips the run that
+  // entered from before; a long last run (it started here) ends the span.
   const bool left_open = beg > 0 && live_count > 0 && before == kk[0];
-  // the entering run started in the previous range: its owner finishes it
-  // if it ends here
-  const bool left_short = left_open && (beg <= kRange || before2 != kk[0]);
-  int lead = 0;  // length of the entering run inside this range
+  int lead = 0;
 #pragma unroll
   for (int q = 0; q < kRange; ++q) lead += (left_open && lead == q && kk[q] == kk[0]) ? 1 : 0;
-  const bool skip_lead = left_short && !(lead == live_count && end < a.n && after == kk[0]);
+  uint32_t klast = kk[0];
+#pragma unroll
+  for (int q = 1; q < kRange; ++q) klast = q < live_count ? kk[q] : klast;
+  int tail = 0;
+#pragma unroll
+  for (int q = 0; q < kRange; ++q) tail += (q < live_count && !(last_long && kk[q] == klast)) ? 1 : 0;
 
   // gradient rows in flight together (rows wider than 512 values: Q / 2
   // batches, to bound registers)
   constexpr int B = Q > 2 ? kRange / (Q / 2) : kRange;
-  uint32_t u = a.head_off[w];  // slot of the next run that starts here
-  uint32_t cur = kk[0];
-  bool first = true;
+  uint32_t u = a.head_off[w];  // slot of the first run that starts here
+  uint32_t cur = a.sentinel;
+  bool started = false;
   double acc[Q][4];
   zero_acc<Q>(acc);
 #pragma unroll
@@ -548,182 +557,144 @@ __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const Walk
 #pragma unroll
     for (int qq = 0; qq < B; ++qq) {
       const int q = b0 + qq;
-      const bool needed = kk[q] != a.sentinel && !(skip_lead && q < lead);
-      const uint2 *row = a.grads + (int64_t)(needed ? vv[q] : 0u) * a.quads;
-#pragma unroll
-      for (int k = 0; k < Q; ++k)
-        g[qq][k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
+      load_row<L, Q, EXACT>(a, (q >= lead && q < tail) ? vv[q] : 0u, lane, g[qq]);
     }
 #pragma unroll
     for (int qq = 0; qq < B; ++qq) {
       const int q = b0 + qq;
-      const bool live = q < live_count;
-      if (live && kk[q] != cur) {  // a new distinct row starts at beg + q
-        if (first && left_open) {
-          if (!skip_lead) {  // last piece of a long run
-            store_partial<L, Q>(a.pfirst, w, a, lane, acc);
-            if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + q);
-          }
-        } else {
-          emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
-          ++u;
-        }
-        cur = kk[q];
-        first = false;
+      const bool live = q >= lead && q < tail;
+      if (live && started && kk[q] != cur) {  // a new distinct row starts at beg + q
+        emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+        ++u;
         zero_acc<Q>(acc);
+      }
+      if (live) {
+        cur = kk[q];
+        started = true;
       }
       // the row is used on every path, so its load stays with the others
       // (issued in order, consumed in order as each one arrives)
       add_quads_if<Q>(acc, g[qq], live);
     }
   }
-  if (live_count == 0) {  // only padding / invalid ids from here on
-    if (lane == 0) a.owner_flag[w] = 0;
-    return;
-  }
-  const bool right_open = end < a.n && after == cur;
-  if (first && left_open) {
-    if (right_open) {  // a long run passes through this range
-      store_partial<L, Q>(a.pfirst, w, a, lane, acc);
-    } else if (!skip_lead) {  // the long run ends here
-      store_partial<L, Q>(a.pfirst, w, a, lane, acc);
-      if (lane == 0) a.run_end[u - 1] = (uint32_t)(beg + live_count);
+  if (!started) return;
+  // the last run continues into the next range (this range is full, the
+  // next one starts at end); not being long, it ends there
+  if (!last_long && live_count == kRange && end < a.n && after == cur) {
+    const int ncnt = (int)min((int64_t)kRange, a.n - end);
+    uint32_t nk[kRange], nv[kRange];
+    load_range(a.keys, a.vals, end, nk, nv);
+    int m = 0;  // continuation length
+#pragma unroll
+    for (int q = 0; q < kRange; ++q) m += (m == q && q < ncnt && nk[q] == cur) ? 1 : 0;
+    for (int q0 = 0; q0 < m; q0 += 4) {
+      uint2 g[4][Q];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) load_row<L, Q, EXACT>(a, q0 + b < m ? nv[q0 + b] : 0u, lane, g[b]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        if (q0 + b < m) add_quads<Q>(acc, g[b]);
     }
-    if (lane == 0) a.owner_flag[w] = 0;
-    return;
-  }
-  if (!right_open) {
-    emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
-    if (lane == 0) a.owner_flag[w] = 0;
-    return;
-  }
-  // the last run continues into the next range (right_open: end < n, so
-  // this range is full and the next one starts at end)
-  const int64_t nbeg = end;
-  const int ncnt = (int)min((int64_t)kRange, a.n - nbeg);
-  uint32_t nk[kRange], nv[kRange];
-  {
-    const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + nbeg);
-    const u32x4 *vp = reinterpret_cast<const u32x4 *>(a.vals + nbeg);
-#pragma unroll
-    for (int i = 0; i < kRange / 4; ++i) {
-      const u32x4 k4 = kp[i], v4 = vp[i];
-      nk[4 * i] = k4.x; nk[4 * i + 1] = k4.y; nk[4 * i + 2] = k4.z; nk[4 * i + 3] = k4.w;
-      nv[4 * i] = v4.x; nv[4 * i + 1] = v4.y; nv[4 * i + 2] = v4.z; nv[4 * i + 3] = v4.w;
-    }
-  }
-  int m = 0;  // continuation length
-#pragma unroll
-  for (int q = 0; q < kRange; ++q) m += (m == q && q < ncnt && nk[q] == cur) ? 1 : 0;
-  const int64_t past = nbeg + kRange;
-  owns_long = m == kRange && past < a.n && a.keys[past] == cur;
-  if (lane == 0) a.owner_flag[w] = owns_long ? 1u : 0u;
-  if (owns_long) {
-    store_partial<L, Q>(a.plast, w, a, lane, acc);
-    return;
-  }
-  for (int q0 = 0; q0 < m; q0 += 4) {
-    uint2 g[4][Q];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const bool live = q0 + b < m;
-      const uint2 *row = a.grads + (int64_t)(live ? nv[q0 + b] : 0u) * a.quads;
-#pragma unroll
-      for (int k = 0; k < Q; ++k)
-        g[b][k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
-    }
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      if (q0 + b < m) add_quads<Q>(acc, g[b]);
   }
   emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
 }
 
-// Long runs (longer than a range; rare hot rows).  Block b looks after the
-// owner flags of ranges [b * span, (b + 1) * span); for each owning range c0
-// it sums the run's pieces plast[c0] and pfirst[c0 + 1 .. c1] (c1 is the
-// range holding the run's end): the block's walkers sum interleaved pieces
-// (several loads in flight each), walker 0 adds the walkers' sums in walker
-// order and writes the row.  Fixed
-// assignment and fixed order keep the result deterministic.
-constexpr int kFixBatch = 4;
-
-template <int L, int Q, bool SPARSE>
-__global__ __launch_bounds__(kWalkThreads) void segment_fixup_kernel(const WalkArgs a,
-                                                                     int64_t span) {
+// Long runs (hot rows, longer than a range).  Each block takes list entries
+// blockIdx.x, blockIdx.x + long_blocks, ...; for the run that starts in
+// range c0 (slot: the last head of c0) it finds the run's end by a scan of
+// the keys, its G walkers sum the run's ranges c0 + g, c0 + g + G, ... (each
+// range's indices fetched one range ahead, its rows all in flight), and
+// walker 0 adds the walkers' sums in walker order before writing the row.
+// The procedure does not depend on which block takes the run, so the result
+// is deterministic.
+template <int L, int Q, bool SPARSE, bool EXACT>
+__device__ __forceinline__ void long_runs(const WalkArgs &a) {
   constexpr int G = kWalkThreads / L;  // walkers per block
-  __shared__ double s_sum[G][L * Q * 4];
-  __shared__ uint32_t s_owner[kWalkThreads];
-  __shared__ int s_wave_owners[kWalkThreads / kWave];
-  __shared__ int s_owners;
+  __shared__ double s_part[G][L * 4];
   const int lane = threadIdx.x % L, g = threadIdx.x / L;
-  const int64_t first = (int64_t)blockIdx.x * span;
-  const int64_t last = min(a.num_ranges, first + span);
-  for (int64_t r0 = first; r0 < last; r0 += kWalkThreads) {
-    // collect this stretch's owners (in range order)
-    if (threadIdx.x == 0) s_owners = 0;
-    __syncthreads();
-    const int64_t r = r0 + threadIdx.x;
-    const bool owner = r < last && a.owner_flag[r] != 0;
-    const unsigned long long bal = __ballot(owner);
-    if (__lane_id() == 0) s_wave_owners[threadIdx.x / kWave] = __popcll(bal);
-    __syncthreads();
-    if (owner) {
-      int at = __popcll(bal & ((1ull << __lane_id()) - 1ull));
-      for (int v = 0; v < (int)(threadIdx.x / kWave); ++v) at += s_wave_owners[v];
-      s_owner[at] = (uint32_t)r;
+  const int wl = __lane_id();
+  const uint32_t count = *a.long_count;
+  for (uint32_t i = blockIdx.x; i < count; i += a.long_blocks) {
+    const int64_t c0 = a.long_list[i];
+    const int64_t r0 = c0 * kRange;
+    const uint32_t u = a.head_off[c0] + a.head_count[c0] - 1;
+    const uint32_t key = a.keys[r0 + kRange - 1];
+    // start: range c0 is sorted, so the run begins after its smaller keys
+    int64_t start = r0;
+    {
+      const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + r0);
+#pragma unroll
+      for (int i = 0; i < kRange / 4; ++i) {
+        const u32x4 k4 = kp[i];
+        start += (k4.x != key) + (k4.y != key) + (k4.z != key) + (k4.w != key);
+      }
     }
-    if (threadIdx.x == 0) {
-      int total = 0;
-      for (int v = 0; v < kWalkThreads / kWave; ++v) total += s_wave_owners[v];
-      s_owners = total;
+    // end: the first position past r0 + 2 * kRange (which holds key) whose
+    // key differs, 4 * kWave positions per step, each wavefront on its own
+    int64_t stop = -1;
+    for (int64_t p0 = r0 + 2 * kRange + 1; stop < 0; p0 += 4 * kWave) {
+      int first = 4;  // first of this lane's 4 positions that leaves the run
+#pragma unroll
+      for (int e = 3; e >= 0; --e) {
+        const int64_t p = p0 + 4 * wl + e;
+        first = (p >= a.n || a.keys[p] != key) ? e : first;
+      }
+      const unsigned long long leave = __ballot(first < 4);
+      if (leave != 0ull) {
+        const int src = __ffsll((long long)leave) - 1;
+        stop = p0 + 4 * src + __shfl(first, src, kWave);
+      }
     }
-    __syncthreads();
-    const int owners = s_owners;
-    for (int i = 0; i < owners; ++i) {
-      const int64_t c0 = s_owner[i];
-      const uint32_t u = a.head_off[c0] + a.head_count[c0] - 1;
-      const uint32_t key = a.keys[(c0 + 1) * kRange - 1];
-      const int64_t c1 = ((int64_t)a.run_end[u] - 1) / kRange;
-      const int64_t pieces = c1 - c0 + 1;
-      // walker g sums pieces g, g + G, g + 2G, ... in that order,
-      // kFixBatch pieces in flight
-      double acc[Q][4];
-      zero_acc<Q>(acc);
+    const int64_t c1 = (stop - 1) / kRange;  // range of the run's last position
+    double acc[Q][4];
+    zero_acc<Q>(acc);
+    int64_t c = c0 + g;
+    uint32_t vv[kRange];
+    if (c <= c1) load_vals(a.vals, c * kRange, vv);
 #pragma unroll 1
-      for (int64_t p0 = g; p0 < pieces; p0 += (int64_t)G * kFixBatch) {
-        double part[kFixBatch][Q][4];
+    for (; c <= c1; c += G) {
+      uint32_t cv[kRange];
 #pragma unroll
-        for (int b = 0; b < kFixBatch; ++b) {
-          const int64_t p = p0 + (int64_t)b * G;
-          zero_acc<Q>(part[b]);
-          if (p < pieces) add_partial<L, Q>(p == 0 ? a.plast : a.pfirst, c0 + p, a, lane, part[b]);
-        }
+      for (int q = 0; q < kRange; ++q) cv[q] = vv[q];
+      if (c + G <= c1) load_vals(a.vals, (c + G) * kRange, vv);
+      uint2 rows[kRange][Q];
 #pragma unroll
-        for (int b = 0; b < kFixBatch; ++b)
-#pragma unroll
-          for (int k = 0; k < Q; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[k][e] += part[b][k][e];
+      for (int q = 0; q < kRange; ++q) {
+        const int64_t p = c * kRange + q;
+        load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? cv[q] : 0u, lane, rows[q]);
       }
 #pragma unroll
-      for (int k = 0; k < Q; ++k)
+      for (int q = 0; q < kRange; ++q) {
+        const int64_t p = c * kRange + q;
+        add_quads_if<Q>(acc, rows[q], p >= start && p < stop);
+      }
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s_sum[g][(lane * Q + k) * 4 + e] = acc[k][e];
+    for (int k = 0; k < Q; ++k) {
+      if (g > 0)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s_part[g][lane * 4 + e] = acc[k][e];
       __syncthreads();
-      if (g == 0) {
+      if (g == 0)
 #pragma unroll 1
         for (int h = 1; h < G; ++h)
 #pragma unroll
-          for (int k = 0; k < Q; ++k)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[k][e] += s_sum[h][(lane * Q + k) * 4 + e];
-        emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
-      }
+          for (int e = 0; e < 4; ++e) acc[k][e] += s_part[h][lane * 4 + e];
       __syncthreads();
     }
-    __syncthreads();  // s_owner / s_owners are rewritten by the next stretch
+    if (g == 0) emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
   }
+}
+
+// The apply kernel: blocks [0, long_blocks) sum the long runs, the rest are
+// range walkers, kWalkThreads / L walkers per block.
+template <int L, int Q, bool SPARSE, bool EXACT>
+__global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
+  if (SPARSE && blockIdx.x == 0 && threadIdx.x == 0) *a.num_unique = (int64_t)*a.unique_total;
+  if (blockIdx.x < a.long_blocks)
+    long_runs<L, Q, SPARSE, EXACT>(a);
+  else
+    walk_range<L, Q, SPARSE, EXACT>(a, (int64_t)blockIdx.x - a.long_blocks);
 }
 
 __global__ void write_zero_kernel(int64_t *p) { *p = 0; }
@@ -767,7 +738,7 @@ struct Plan {
   int64_t num_tiles, num_ranges, scan_chunks;
   int bits, passes, per_pass;
   size_t keys_a, vals_a, keys_b, vals_b, status, counters, chunk_sums, head_count, head_off,
-      scalars, run_end, owner_flag, pfirst, plast, total;
+      scalars, long_flag, long_list, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -812,10 +783,8 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
   p->head_count = take((size_t)p->num_ranges * 4);
   p->head_off = take((size_t)p->num_ranges * 4);
   p->scalars = take(64);
-  p->run_end = take(nn * 4);
-  p->owner_flag = take((size_t)p->num_ranges * 4);
-  p->pfirst = take((size_t)p->num_ranges * (size_t)dim * 8);
-  p->plast = take((size_t)p->num_ranges * (size_t)dim * 8);
+  p->long_flag = take((size_t)p->num_ranges * 4);
+  p->long_list = take((size_t)(p->num_ranges / 2 + 1) * 4);  // a long run spans 3+ ranges
   p->total = off;
   return true;
 }
@@ -838,17 +807,14 @@ void launch_scan(const uint32_t *in, uint32_t *out, int64_t m, uint32_t *chunk_s
 template <int L, int Q, bool SPARSE>
 void launch_walkers(const WalkArgs &a, hipStream_t s) {
   const int64_t threads = a.num_ranges * L;
-  const unsigned blocks = (unsigned)((threads + kWalkThreads - 1) / kWalkThreads);
+  const unsigned blocks =
+      a.long_blocks + (unsigned)((threads + kWalkThreads - 1) / kWalkThreads);
   if (a.quads == (int64_t)Q * L)
     hipLaunchKernelGGL((segment_reduce_kernel<L, Q, SPARSE, true>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
   else
     hipLaunchKernelGGL((segment_reduce_kernel<L, Q, SPARSE, false>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
-  const int64_t span = (a.num_ranges + kFixupBlocks - 1) / kFixupBlocks;
-  const unsigned fix_blocks = (unsigned)((a.num_ranges + span - 1) / span);
-  hipLaunchKernelGGL((segment_fixup_kernel<L, Q, SPARSE>), dim3(fix_blocks), dim3(kWalkThreads),
-                     0, s, a, span);
 }
 
 // One quad (4 values) per lane: a walker is quads lanes wide, up to a whole
@@ -873,8 +839,7 @@ void dispatch_walkers(const WalkArgs &a, hipStream_t s) {
 struct Views {
   uint32_t *keys_a, *vals_a, *keys_b, *vals_b;
   uint64_t *status;
-  uint32_t *counters, *chunk_sums, *head_count, *head_off, *scalars, *run_end, *owner_flag;
-  double *pfirst, *plast;
+  uint32_t *counters, *chunk_sums, *head_count, *head_off, *scalars, *long_flag, *long_list;
   const uint32_t *sorted_keys, *sorted_vals;  // where the last sort pass leaves them
 };
 
@@ -891,10 +856,8 @@ Views views_of(const Plan &p, void *ws) {
   v.head_count = reinterpret_cast<uint32_t *>(base + p.head_count);
   v.head_off = reinterpret_cast<uint32_t *>(base + p.head_off);
   v.scalars = reinterpret_cast<uint32_t *>(base + p.scalars);
-  v.run_end = reinterpret_cast<uint32_t *>(base + p.run_end);
-  v.owner_flag = reinterpret_cast<uint32_t *>(base + p.owner_flag);
-  v.pfirst = reinterpret_cast<double *>(base + p.pfirst);
-  v.plast = reinterpret_cast<double *>(base + p.plast);
+  v.long_flag = reinterpret_cast<uint32_t *>(base + p.long_flag);
+  v.long_list = reinterpret_cast<uint32_t *>(base + p.long_list);
   // passes alternate a -> b -> a ...: an odd pass count ends in a
   v.sorted_keys = (p.passes % 2 == 1) ? v.keys_a : v.keys_b;
   v.sorted_vals = (p.passes % 2 == 1) ? v.vals_a : v.vals_b;
@@ -942,7 +905,8 @@ int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p
   // distinct-row slots
   const unsigned head_blocks = (unsigned)((n + 255) / 256);
   hipLaunchKernelGGL(range_heads_kernel, dim3(head_blocks), dim3(256), 0, s, v.sorted_keys, n,
-                     (uint32_t)table_rows, v.head_count, p.num_ranges);
+                     (uint32_t)table_rows, v.head_count, v.long_flag, v.long_list,
+                     v.counters + kLongCountAt, p.num_ranges);
   launch_scan(v.head_count, v.head_off, p.num_ranges, v.chunk_sums, v.scalars, nullptr, s);
   return launch_status();
 }
@@ -966,10 +930,12 @@ int apply_sorted(const void *grads, int64_t n, int64_t dim, int64_t table_rows, 
   a.grad_table = grad_table;
   a.unique_ids = unique_ids;
   a.unique_grads = unique_grads;
-  a.pfirst = v.pfirst;
-  a.plast = v.plast;
-  a.run_end = v.run_end;
-  a.owner_flag = v.owner_flag;
+  a.long_flag = v.long_flag;
+  a.long_list = v.long_list;
+  a.long_count = v.counters + kLongCountAt;
+  // a long run spans at least 3 ranges
+  const int64_t most_long = p.num_ranges / 2;
+  a.long_blocks = (uint32_t)(most_long < kLongBlocks ? most_long : kLongBlocks);
   a.unique_total = v.scalars;
   a.num_unique = num_unique;
   if (sparse)
