@@ -25,8 +25,9 @@
 //     keys, padding and invalid ids the key table_rows, which sorts last and
 //     is dropped.
 //  2. Segment heads (first position of each distinct row) are counted per
-//     16-position range and scanned: the scan gives every distinct row its
-//     output slot u, and U itself.
+//     16-position range and scanned in one kernel (decoupled look-back over
+//     tiles of ranges): the scan gives every distinct row its output slot u,
+//     and U itself.
 //  3. Range walkers: a group of head_dim/4 lanes (one 4-value quad of the
 //     row per lane, up to a whole wavefront) takes one 16-position range of
 //     the sorted order, issues all its loads at once (keys, flat indices,
@@ -51,22 +52,21 @@ constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortThreads * kSortItems;  // keys per tile
 constexpr int kMaxBins = 256;
-constexpr int kScanThreads = 256;
-constexpr int kScanItems = 16;
-constexpr int kScanChunk = kScanThreads * kScanItems;
+constexpr int kSlotThreads = 256;  // ranges per tile of the slot scan
 constexpr int kRange = 16;  // sorted positions per walker
 constexpr int kWalkThreads = 256;
 constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnroll = 4;
 
 constexpr int64_t kLongBlocks = 1024;  // most blocks that sum long runs
+constexpr int64_t kLongSpan = 64;      // fewest ranges per such block
 // Global digit totals are kept in kHistCopies copies (a block adds to copy
 // blockIdx % kHistCopies) so the histogram's atomics do not all meet on the
 // same few hundred words; readers add the copies.
 constexpr int kHistCopies = 8;
-// counters: digit totals, 4 pass tickets, the long-run count (and padding)
+// counters: digit totals, 4 pass tickets, the slot scan's ticket (and padding)
 constexpr int kSortCounters = kHistCopies * 4 * 256 + 8;
-constexpr int kLongCountAt = kHistCopies * 4 * 256 + 4;
+constexpr int kSlotTicketAt = kHistCopies * 4 * 256 + 4;
 static_assert(kWave % kRange == 0 && kRange % 4 == 0, "ranges tile a wavefront");
 
 // ----------------------------------------------------------------- keys ----
@@ -105,53 +105,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t &t
   return before + x - v;
 }
 
-// Scan, step 1: the sum of every kScanChunk-element chunk.
-__global__ __launch_bounds__(kScanThreads) void scan_reduce_kernel(const uint32_t *in, int64_t m,
-                                                                    uint32_t *chunk_sums) {
-  const int64_t base = (int64_t)blockIdx.x * kScanChunk;
-  uint32_t s = 0;
-  for (int i = 0; i < kScanItems; ++i) {
-    const int64_t p = base + (int64_t)i * kScanThreads + threadIdx.x;
-    if (p < m) s += in[p];
-  }
-  uint32_t total;
-  block_exclusive_scan<kScanThreads>(s, total);
-  if (threadIdx.x == 0) chunk_sums[blockIdx.x] = total;
-}
-
-// Scan, step 2: each chunk adds the sums of the chunks before it (at most a
-// few hundred) and writes its exclusive prefix.  The last chunk also writes
-// the grand total (as uint32 and/or int64) when asked.
-__global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(
-    const uint32_t *in, uint32_t *out, int64_t m, const uint32_t *chunk_sums, uint32_t *total32,
-    int64_t *total64) {
-  uint32_t carry = 0;
-  for (int64_t b = threadIdx.x; b < (int64_t)blockIdx.x; b += kScanThreads) carry += chunk_sums[b];
-  uint32_t carry_total;
-  block_exclusive_scan<kScanThreads>(carry, carry_total);
-
-  const int64_t base = (int64_t)blockIdx.x * kScanChunk + (int64_t)threadIdx.x * kScanItems;
-  uint32_t v[kScanItems];
-  uint32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    v[i] = base + i < m ? in[base + i] : 0u;
-    s += v[i];
-  }
-  uint32_t block_total;
-  uint32_t run = carry_total + block_exclusive_scan<kScanThreads>(s, block_total);
-#pragma unroll
-  for (int i = 0; i < kScanItems; ++i) {
-    if (base + i < m) out[base + i] = run;
-    run += v[i];
-  }
-  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
-    const uint32_t grand = carry_total + block_total;
-    if (total32 != nullptr) *total32 = grand;
-    if (total64 != nullptr) *total64 = (int64_t)grand;
-  }
-}
-
 // ------------------------------------------------------------ radix sort ---
 // One-sweep LSD radix sort.  One kernel clears the look-back state, one
 // counts every pass's digits over all keys (the global digit totals of a
@@ -173,18 +126,24 @@ __global__ __launch_bounds__(256) void sort_clear_kernel(uint64_t *status, int64
   if (i < counters_len) counters[i] = 0;
 }
 
-// hist[copy][pass][digit] += number of keys with that digit.
+// hist[copy][pass][digit] += number of keys with that digit.  One block per
+// kSortTile ids, all of a thread's loads in flight before any is counted.
 __global__ __launch_bounds__(kSortThreads) void sort_histogram_kernel(
     const int64_t *ids, int64_t n, int64_t table_rows, int passes, int per_pass, int bits,
     uint32_t *hist, int64_t *err) {
   __shared__ uint32_t s_hist[4][kMaxBins];
   const int tid = threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * kSortTile + tid;
+  int64_t id[kSortItems];  // loads at clamped positions, so none waits behind a branch
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) id[i] = ids[min(base + (int64_t)i * kSortThreads, n - 1)];
   for (int d = tid; d < 4 * kMaxBins; d += kSortThreads) (&s_hist[0][0])[d] = 0;
   __syncthreads();
   int bad = 0;
-  for (int64_t p = (int64_t)blockIdx.x * kSortThreads + tid; p < n;
-       p += (int64_t)gridDim.x * kSortThreads) {
-    const uint32_t k = make_key(ids[p], table_rows, bad);
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) {
+    if (base + (int64_t)i * kSortThreads >= n) continue;
+    const uint32_t k = make_key(id[i], table_rows, bad);
     for (int q = 0; q < passes; ++q) {
       const int shift = q * per_pass;
       const int width = bits - shift < per_pass ? bits - shift : per_pass;
@@ -227,25 +186,37 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   // the global digit totals (their latency overlaps the ranking)
   const int64_t base = tile0 + (int64_t)wave * (kSortItems * kWave);
   const unsigned long long below = (1ull << lane) - 1ull;
-  uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
-#pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
-    const int64_t p = base + (int64_t)i * kWave + lane;
-    const bool valid = p < n;
-    int ignored = 0;
-    if (FROM_IDS) {
-      key[i] = valid ? make_key(ids[p], table_rows, ignored) : 0u;
-      val[i] = (uint32_t)p;
-    } else {
-      key[i] = valid ? keys_in[p] : 0u;
-      val[i] = valid ? vals_in[p] : 0u;
-    }
-    rank[i] = 0;
-  }
+  // (loads at clamped positions, so none waits behind a branch)
   uint32_t copies[kHistCopies];
 #pragma unroll
   for (int c = 0; c < kHistCopies; ++c)
-    copies[c] = tid < bins ? hist[(int64_t)c * 4 * kMaxBins + tid] : 0u;
+    copies[c] = hist[(int64_t)c * 4 * kMaxBins + (tid < bins ? tid : 0)];
+  uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+  if (FROM_IDS) {
+    int64_t id[kSortItems];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i)
+      id[i] = ids[min(base + (int64_t)i * kWave + lane, n - 1)];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+      const int64_t p = base + (int64_t)i * kWave + lane;
+      int ignored = 0;
+      key[i] = p < n ? make_key(id[i], table_rows, ignored) : 0u;
+      val[i] = (uint32_t)p;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+      const int64_t p = min(base + (int64_t)i * kWave + lane, n - 1);
+      key[i] = keys_in[p];
+      val[i] = vals_in[p];
+    }
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i)
+      if (base + (int64_t)i * kWave + lane >= n) key[i] = val[i] = 0u;
+  }
+#pragma unroll
+  for (int i = 0; i < kSortItems; ++i) rank[i] = 0;
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const int64_t p = base + (int64_t)i * kWave + lane;
@@ -284,7 +255,7 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
       block_exclusive_scan<kSortThreads>(tid < bins ? tile_count : 0u, scan_total);
   uint32_t digit_total = 0;
 #pragma unroll
-  for (int c = 0; c < kHistCopies; ++c) digit_total += copies[c];
+  for (int c = 0; c < kHistCopies; ++c) digit_total += tid < bins ? copies[c] : 0u;
   const uint32_t digit_start = block_exclusive_scan<kSortThreads>(digit_total, scan_total);
   // decoupled look-back: the keys of this digit in all earlier tiles
   if (tid < bins) {
@@ -348,40 +319,89 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   }
 }
 
-// --------------------------------------------------------- segment heads ---
-// Distinct-row starts per kRange-position range (one ballot per wavefront,
-// kWave / kRange ranges per wavefront), and the long runs: a run is long when
-// it starts in range c and still holds position 16 (c + 2), so it covers
-// the whole of range c + 1 and reaches beyond.  Every range whose last run is
-// long is flagged and appended to the long-run list (list order is
-// immaterial: each long run is summed the same way whoever takes it).
-__global__ __launch_bounds__(256) void range_heads_kernel(const uint32_t *keys, int64_t n,
-                                                          uint32_t sentinel, uint32_t *head_count,
-                                                          uint32_t *long_flag, uint32_t *long_list,
-                                                          uint32_t *long_count,
-                                                          int64_t num_ranges) {
-  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  bool head = false;
-  if (j < n) {
-    const uint32_t k = keys[j];
-    head = k != sentinel && (j == 0 || keys[j - 1] != k);
-  }
-  const unsigned long long m = __ballot(head);
-  const int lane = __lane_id();
-  if ((lane % kRange) == 0) {
-    const int64_t r = j / kRange;
-    const unsigned long long mine = (m >> lane) & ((1ull << kRange) - 1ull);
-    if (r < num_ranges) {
-      head_count[r] = (uint32_t)__popcll(mine);
-      bool lng = false;
-      if (j + 2 * kRange < n) {
-        const uint32_t k = keys[j + kRange - 1];
-        lng = k != sentinel && keys[j + 2 * kRange] == k && (j == 0 || keys[j - 1] != k);
+// ------------------------------------------------------------ row slots ---
+// Slot of every range's first distinct row: the number of distinct-row heads
+// (first positions of a valid row) in all earlier ranges; the last tile also
+// writes U, the number of distinct valid rows.  One thread per range, a tile
+// of kSlotThreads ranges per block (taken by atomic ticket): heads counted
+// from the range's keys, a block scan, then the tile's offset by decoupled
+// look-back, wavefront 0 reading 64 earlier tiles' published words at a time.
+__global__ __launch_bounds__(kSlotThreads) void range_slots_kernel(
+    const uint32_t *keys, int64_t n, uint32_t sentinel, int64_t num_ranges, uint64_t *status,
+    uint32_t *ticket, uint32_t *head_off, uint32_t *total, int64_t *err) {
+  __shared__ uint32_t s_tile, s_prefix;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  if (tid == 0) s_tile = atomicAdd(ticket, 1u);
+  __syncthreads();
+  const int64_t tile = s_tile;
+  const int64_t r = tile * kSlotThreads + tid;
+  uint32_t heads = 0;
+  if (r < num_ranges) {
+    const int64_t beg = r * kRange;
+    const int cnt = (int)min((int64_t)kRange, n - beg);
+    uint32_t prev = beg > 0 ? keys[beg - 1] : sentinel;
+    const u32x4 *kp = reinterpret_cast<const u32x4 *>(keys + beg);
+#pragma unroll
+    for (int i = 0; i < kRange / 4; ++i) {
+      const u32x4 k4 = kp[i];
+      const uint32_t k[4] = {k4.x, k4.y, k4.z, k4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        heads += (4 * i + e < cnt && k[e] != sentinel && k[e] != prev) ? 1u : 0u;
+        prev = k[e];
       }
-      long_flag[r] = lng ? 1u : 0u;
-      if (lng) long_list[atomicAdd(long_count, 1u)] = (uint32_t)r;
     }
   }
+  uint32_t tile_total;
+  const uint32_t local = block_exclusive_scan<kSlotThreads>(heads, tile_total);
+  if (tid < kWave) {
+    if (tid == 0)
+      __hip_atomic_store(&status[tile], (tile == 0 ? kFlagInclusive : kFlagAggregate) | tile_total,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t before = 0;
+    bool stalled = false;
+    for (int64_t t0 = tile - 1; t0 >= 0;) {
+      // lane l reads tile t0 - l; tiles before 0 read as an empty inclusive
+      const int64_t t = t0 - lane;
+      uint64_t word = t >= 0 ? __hip_atomic_load(&status[t], __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : kFlagInclusive;
+      unsigned long long incl, need;
+      uint32_t spins = 0;
+      for (;;) {  // wait for every word up to the nearest inclusive one
+        incl = __ballot((word & kFlagInclusive) != 0);
+        const int upto = incl != 0ull ? __ffsll((long long)incl) - 1 : kWave - 1;
+        need = upto == kWave - 1 ? ~0ull : ((2ull << upto) - 1ull);
+        const unsigned long long pending = __ballot((word >> 32) == 0) & need;
+        if (pending == 0ull) break;
+        if (++spins == kSpinLimit) {
+          stalled = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if ((pending >> lane) & 1ull)
+          word = __hip_atomic_load(&status[t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (stalled) break;
+      uint64_t c = ((need >> lane) & 1ull) ? (word & 0xffffffffull) : 0ull;
+#pragma unroll
+      for (int d = kWave / 2; d > 0; d >>= 1) c += __shfl_xor(c, d, kWave);
+      before += c;
+      if (incl != 0ull) break;
+      t0 -= kWave;
+    }
+    if (tid == 0) {
+      if (tile != 0)
+        __hip_atomic_store(&status[tile], kFlagInclusive | (uint32_t)(before + tile_total),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (stalled && err != nullptr)
+        atomicAdd(reinterpret_cast<unsigned long long *>(err), (unsigned long long)kStallMark);
+      s_prefix = (uint32_t)before;
+    }
+  }
+  __syncthreads();
+  if (r < num_ranges) head_off[r] = s_prefix + local;
+  if (tile == (int64_t)gridDim.x - 1 && tid == 0) *total = s_prefix + tile_total;
 }
 
 // ---------------------------------------------------------- range walkers --
@@ -399,16 +419,13 @@ struct WalkArgs {
   const uint2 *grads;  // [n, dim / 4] quads of 4 bf16
   int64_t quads;       // dim / 4
   int64_t dim;
-  const uint32_t *head_count;
-  const uint32_t *head_off;
+  const uint32_t *head_off;  // slot of each range's first distinct row
   int64_t num_ranges;
   float *grad_table;    // dense output
   int64_t *unique_ids;  // row-sparse output
   float *unique_grads;
-  const uint32_t *long_flag;   // [num_ranges]: 1 where the range's last run is long
-  const uint32_t *long_list;   // ranges whose last run is long
-  const uint32_t *long_count;  // length of long_list
-  uint32_t long_blocks;        // leading blocks of the grid that sum long runs
+  uint32_t long_blocks;  // leading blocks of the grid: they sum the long runs
+  int64_t long_span;     // ranges each of those blocks looks after
   const uint32_t *unique_total;  // U, from the plan
   int64_t *num_unique;           // row-sparse output count
 };
@@ -478,6 +495,15 @@ __device__ __forceinline__ void load_vals(const uint32_t *vals, int64_t beg,
   }
 }
 
+// A run is long when it starts in range c and still holds position
+// 16 (c + 2): it covers the whole of range c + 1 and reaches beyond.  Given
+// the keys at 16 c - 1 (`before`), 16 c + 15 (`k15`) and 16 (c + 2) (`far`),
+// whether range c's last run is long.
+__device__ __forceinline__ bool last_run_long(int64_t c, int64_t n, uint32_t sentinel,
+                                              uint32_t before, uint32_t k15, uint32_t far) {
+  return (c + 2) * kRange < n && k15 != sentinel && far == k15 && (c == 0 || before != k15);
+}
+
 // The finished sum of row `key` (distinct-row slot u): one rounding to fp32,
 // then one fp32 add into the dense table, or a row-sparse store.
 template <int L, int Q, bool SPARSE>
@@ -523,7 +549,8 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
   const int64_t end = beg + cnt;
   const uint32_t before = a.keys[beg > 0 ? beg - 1 : 0];
   const uint32_t after = a.keys[end < a.n ? end : a.n - 1];
-  const bool last_long = a.long_flag[w] != 0;
+  const uint32_t far = a.keys[min(beg + 2 * kRange, a.n - 1)];
+  const bool last_long = last_run_long(w, a.n, a.sentinel, before, kk[kRange - 1], far);
   int live_count = 0;
 #pragma unroll
   for (int q = 0; q < kRange; ++q) {
@@ -599,90 +626,115 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
   emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
 }
 
-// Long runs (hot rows, longer than a range).  Each block takes list entries
-// blockIdx.x, blockIdx.x + long_blocks, ...; for the run that starts in
-// range c0 (slot: the last head of c0) it finds the run's end by a scan of
-// the keys, its G walkers sum the run's ranges c0 + g, c0 + g + G, ... (each
-// range's indices fetched one range ahead, its rows all in flight), and
-// walker 0 adds the walkers' sums in walker order before writing the row.
-// The procedure does not depend on which block takes the run, so the result
-// is deterministic.
+// One long run: the run that starts in range c0 and reaches range c0 + 2.
+template <int L, int Q, bool SPARSE, bool EXACT>
+__device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
+                                         double (&s_part)[kWalkThreads / L][L * 4]) {
+  constexpr int G = kWalkThreads / L;  // walkers per block
+  const int lane = threadIdx.x % L, g = threadIdx.x / L, wl = __lane_id();
+  const int64_t r0 = c0 * kRange;
+  const uint32_t u = a.head_off[c0 + 1] - 1;  // the last head of c0 (c0 + 2 exists)
+  const uint32_t key = a.keys[r0 + kRange - 1];
+  // start: range c0 is sorted, so the run begins after its smaller keys
+  int64_t start = r0;
+  const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + r0);
+#pragma unroll
+  for (int j = 0; j < kRange / 4; ++j) {
+    const u32x4 k4 = kp[j];
+    start += (k4.x != key) + (k4.y != key) + (k4.z != key) + (k4.w != key);
+  }
+  // stop: the first position past r0 + 2 * kRange (which holds key) whose
+  // key differs, 4 * kWave positions per step, each wavefront on its own
+  int64_t stop = -1;
+  for (int64_t p0 = r0 + 2 * kRange + 1; stop < 0; p0 += 4 * kWave) {
+    int leave_at = 4;  // first of this lane's 4 positions past the run
+#pragma unroll
+    for (int e = 3; e >= 0; --e) {
+      const int64_t p = p0 + 4 * wl + e;
+      leave_at = (p >= a.n || a.keys[p] != key) ? e : leave_at;
+    }
+    const unsigned long long leave = __ballot(leave_at < 4);
+    if (leave != 0ull) {
+      const int src = __ffsll((long long)leave) - 1;
+      stop = p0 + 4 * src + __shfl(leave_at, src, kWave);
+    }
+  }
+  const int64_t c1 = (stop - 1) / kRange;  // range of the run's last position
+  double acc[Q][4];
+  zero_acc<Q>(acc);
+  uint32_t vv[kRange];
+  if (c0 + g <= c1) load_vals(a.vals, (c0 + g) * kRange, vv);
+#pragma unroll 1
+  for (int64_t c = c0 + g; c <= c1; c += G) {
+    uint2 rows[kRange][Q];
+#pragma unroll
+    for (int q = 0; q < kRange; ++q) {
+      const int64_t p = c * kRange + q;
+      load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? vv[q] : 0u, lane, rows[q]);
+    }
+    if (c + G <= c1) load_vals(a.vals, (c + G) * kRange, vv);  // the next range's indices
+#pragma unroll
+    for (int q = 0; q < kRange; ++q) {
+      const int64_t p = c * kRange + q;
+      add_quads_if<Q>(acc, rows[q], p >= start && p < stop);
+    }
+  }
+  // walker 0 adds the other walkers' sums in walker order
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    if (g > 0)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_part[g][lane * 4 + e] = acc[k][e];
+    __syncthreads();
+    if (g == 0)
+#pragma unroll 1
+      for (int h = 1; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[k][e] += s_part[h][lane * 4 + e];
+    __syncthreads();
+  }
+  if (g == 0) emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
+}
+
+// Long runs (hot rows, longer than a range).  Block b checks which of the
+// ranges [b * long_span, (b + 1) * long_span) end in a long run (three keys
+// per range) and sums those runs in range order, the whole block on one run:
+// the run's end is found by a scan of the keys, the block's G walkers sum the
+// run's ranges c0 + g, c0 + g + G, ... (each range's indices fetched one
+// range ahead, its rows all in flight), and walker 0 adds the walkers' sums
+// in walker order before writing the row.  Fixed assignment and fixed order keep the result
+// deterministic.
 template <int L, int Q, bool SPARSE, bool EXACT>
 __device__ __forceinline__ void long_runs(const WalkArgs &a) {
-  constexpr int G = kWalkThreads / L;  // walkers per block
-  __shared__ double s_part[G][L * 4];
-  const int lane = threadIdx.x % L, g = threadIdx.x / L;
-  const int wl = __lane_id();
-  const uint32_t count = *a.long_count;
-  for (uint32_t i = blockIdx.x; i < count; i += a.long_blocks) {
-    const int64_t c0 = a.long_list[i];
-    const int64_t r0 = c0 * kRange;
-    const uint32_t u = a.head_off[c0] + a.head_count[c0] - 1;
-    const uint32_t key = a.keys[r0 + kRange - 1];
-    // start: range c0 is sorted, so the run begins after its smaller keys
-    int64_t start = r0;
-    {
-      const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + r0);
-#pragma unroll
-      for (int i = 0; i < kRange / 4; ++i) {
-        const u32x4 k4 = kp[i];
-        start += (k4.x != key) + (k4.y != key) + (k4.z != key) + (k4.w != key);
-      }
+  __shared__ double s_part[kWalkThreads / L][L * 4];
+  __shared__ uint32_t s_list[kWalkThreads];
+  __shared__ int s_wave_count[kWalkThreads / kWave];
+  const int wl = __lane_id(), wave = threadIdx.x / kWave;
+  const int64_t first = (int64_t)blockIdx.x * a.long_span;
+  const int64_t last = min(a.num_ranges, first + a.long_span);
+  for (int64_t b0 = first; b0 < last; b0 += kWalkThreads) {
+    // this stretch's flagged ranges, in range order
+    const int64_t r = b0 + threadIdx.x;
+    bool flagged = false;
+    if (r < last) {
+      const int64_t at = r * kRange;
+      flagged = last_run_long(r, a.n, a.sentinel, a.keys[at > 0 ? at - 1 : 0],
+                              a.keys[min(at + kRange - 1, a.n - 1)],
+                              a.keys[min(at + 2 * kRange, a.n - 1)]);
     }
-    // end: the first position past r0 + 2 * kRange (which holds key) whose
-    // key differs, 4 * kWave positions per step, each wavefront on its own
-    int64_t stop = -1;
-    for (int64_t p0 = r0 + 2 * kRange + 1; stop < 0; p0 += 4 * kWave) {
-      int first = 4;  // first of this lane's 4 positions that leaves the run
+    const unsigned long long bal = __ballot(flagged);
+    if (wl == 0) s_wave_count[wave] = __popcll(bal);
+    __syncthreads();
+    int at = __popcll(bal & ((1ull << wl) - 1ull)), count = 0;
 #pragma unroll
-      for (int e = 3; e >= 0; --e) {
-        const int64_t p = p0 + 4 * wl + e;
-        first = (p >= a.n || a.keys[p] != key) ? e : first;
-      }
-      const unsigned long long leave = __ballot(first < 4);
-      if (leave != 0ull) {
-        const int src = __ffsll((long long)leave) - 1;
-        stop = p0 + 4 * src + __shfl(first, src, kWave);
-      }
+    for (int v = 0; v < kWalkThreads / kWave; ++v) {
+      at += v < wave ? s_wave_count[v] : 0;
+      count += s_wave_count[v];
     }
-    const int64_t c1 = (stop - 1) / kRange;  // range of the run's last position
-    double acc[Q][4];
-    zero_acc<Q>(acc);
-    int64_t c = c0 + g;
-    uint32_t vv[kRange];
-    if (c <= c1) load_vals(a.vals, c * kRange, vv);
-#pragma unroll 1
-    for (; c <= c1; c += G) {
-      uint32_t cv[kRange];
-#pragma unroll
-      for (int q = 0; q < kRange; ++q) cv[q] = vv[q];
-      if (c + G <= c1) load_vals(a.vals, (c + G) * kRange, vv);
-      uint2 rows[kRange][Q];
-#pragma unroll
-      for (int q = 0; q < kRange; ++q) {
-        const int64_t p = c * kRange + q;
-        load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? cv[q] : 0u, lane, rows[q]);
-      }
-#pragma unroll
-      for (int q = 0; q < kRange; ++q) {
-        const int64_t p = c * kRange + q;
-        add_quads_if<Q>(acc, rows[q], p >= start && p < stop);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < Q; ++k) {
-      if (g > 0)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_part[g][lane * 4 + e] = acc[k][e];
-      __syncthreads();
-      if (g == 0)
-#pragma unroll 1
-        for (int h = 1; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[k][e] += s_part[h][lane * 4 + e];
-      __syncthreads();
-    }
-    if (g == 0) emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
+    if (flagged) s_list[at] = (uint32_t)r;
+    __syncthreads();
+    for (int i = 0; i < count; ++i) long_run<L, Q, SPARSE, EXACT>(a, s_list[i], s_part);
+    __syncthreads();  // s_list and s_wave_count are rewritten for the next stretch
   }
 }
 
@@ -735,10 +787,10 @@ __global__ __launch_bounds__(kAtomicThreads) void scatter_atomic_kernel(
 
 // ------------------------------------------------------------------ host ---
 struct Plan {
-  int64_t num_tiles, num_ranges, scan_chunks;
+  int64_t num_tiles, num_ranges, slot_tiles;
   int bits, passes, per_pass;
-  size_t keys_a, vals_a, keys_b, vals_b, status, counters, chunk_sums, head_count, head_off,
-      scalars, long_flag, long_list, total;
+  size_t keys_a, vals_a, keys_b, vals_b, status, counters, head_off,
+      scalars, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -759,7 +811,7 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
     return false;
   p->num_tiles = (n + kSortTile - 1) / kSortTile;
   p->num_ranges = (n + kRange - 1) / kRange;
-  p->scan_chunks = (p->num_ranges + kScanChunk - 1) / kScanChunk;
+  p->slot_tiles = (p->num_ranges + kSlotThreads - 1) / kSlotThreads;
   p->bits = bit_width_u64((uint64_t)table_rows);  // the key table_rows must fit
   if (p->bits < 1) p->bits = 1;
   p->passes = (p->bits + 7) / 8;
@@ -777,14 +829,11 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
   p->vals_a = take(nn * 4);
   p->keys_b = take(nn * 4);
   p->vals_b = take(nn * 4);
-  p->status = take((size_t)p->passes * (size_t)p->num_tiles * kMaxBins * 8);
+  // look-back words: every sort pass's, then the slot scan's
+  p->status = take(((size_t)p->passes * (size_t)p->num_tiles * kMaxBins + (size_t)p->slot_tiles) * 8);
   p->counters = take(kSortCounters * 4);
-  p->chunk_sums = take((size_t)(p->scan_chunks > 0 ? p->scan_chunks : 1) * 4);
-  p->head_count = take((size_t)p->num_ranges * 4);
   p->head_off = take((size_t)p->num_ranges * 4);
   p->scalars = take(64);
-  p->long_flag = take((size_t)p->num_ranges * 4);
-  p->long_list = take((size_t)(p->num_ranges / 2 + 1) * 4);  // a long run spans 3+ ranges
   p->total = off;
   return true;
 }
@@ -793,15 +842,6 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
 // 32-bit flat indices.
 inline bool sorted_limits_ok(int64_t n, int64_t table_rows) {
   return table_rows < (int64_t)UINT32_MAX && n < (int64_t)UINT32_MAX;
-}
-
-void launch_scan(const uint32_t *in, uint32_t *out, int64_t m, uint32_t *chunk_sums,
-                 uint32_t *total32, int64_t *total64, hipStream_t s) {
-  const unsigned chunks = (unsigned)((m + kScanChunk - 1) / kScanChunk);
-  hipLaunchKernelGGL(scan_reduce_kernel, dim3(chunks), dim3(kScanThreads), 0, s, in, m,
-                     chunk_sums);
-  hipLaunchKernelGGL(scan_apply_kernel, dim3(chunks), dim3(kScanThreads), 0, s, in, out, m,
-                     chunk_sums, total32, total64);
 }
 
 template <int L, int Q, bool SPARSE>
@@ -839,7 +879,7 @@ void dispatch_walkers(const WalkArgs &a, hipStream_t s) {
 struct Views {
   uint32_t *keys_a, *vals_a, *keys_b, *vals_b;
   uint64_t *status;
-  uint32_t *counters, *chunk_sums, *head_count, *head_off, *scalars, *long_flag, *long_list;
+  uint32_t *counters, *head_off, *scalars;
   const uint32_t *sorted_keys, *sorted_vals;  // where the last sort pass leaves them
 };
 
@@ -852,12 +892,8 @@ Views views_of(const Plan &p, void *ws) {
   v.vals_b = reinterpret_cast<uint32_t *>(base + p.vals_b);
   v.status = reinterpret_cast<uint64_t *>(base + p.status);
   v.counters = reinterpret_cast<uint32_t *>(base + p.counters);
-  v.chunk_sums = reinterpret_cast<uint32_t *>(base + p.chunk_sums);
-  v.head_count = reinterpret_cast<uint32_t *>(base + p.head_count);
   v.head_off = reinterpret_cast<uint32_t *>(base + p.head_off);
   v.scalars = reinterpret_cast<uint32_t *>(base + p.scalars);
-  v.long_flag = reinterpret_cast<uint32_t *>(base + p.long_flag);
-  v.long_list = reinterpret_cast<uint32_t *>(base + p.long_list);
   // passes alternate a -> b -> a ...: an odd pass count ends in a
   v.sorted_keys = (p.passes % 2 == 1) ? v.keys_a : v.keys_b;
   v.sorted_vals = (p.passes % 2 == 1) ? v.vals_a : v.vals_b;
@@ -871,13 +907,11 @@ int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p
   const Views v = views_of(p, ws);
   uint32_t *hist = v.counters;                                // [kHistCopies][4][kMaxBins]
   uint32_t *tickets = v.counters + kHistCopies * 4 * kMaxBins;  // [4]
-  const int64_t status_len = (int64_t)p.passes * p.num_tiles * kMaxBins;
+  const int64_t status_len = (int64_t)p.passes * p.num_tiles * kMaxBins + p.slot_tiles;
   const int64_t clear_len = status_len > kSortCounters ? status_len : kSortCounters;
   hipLaunchKernelGGL(sort_clear_kernel, dim3((unsigned)((clear_len + 255) / 256)), dim3(256), 0,
                      s, v.status, status_len, v.counters, kSortCounters);
-  const int64_t hist_want = (n + 4095) / 4096;
-  const int64_t hist_blocks = hist_want < 512 ? hist_want : 512;
-  hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)hist_blocks), dim3(kSortThreads), 0,
+  hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)p.num_tiles), dim3(kSortThreads), 0,
                      s, ids, n, table_rows, p.passes, p.per_pass, p.bits, hist, err);
   const uint32_t *src_k = nullptr, *src_v = nullptr;
   uint32_t *dst_k = v.keys_a, *dst_v = v.vals_a, *spare_k = v.keys_b, *spare_v = v.vals_b;
@@ -903,11 +937,10 @@ int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p
     spare_v = tv;
   }
   // distinct-row slots
-  const unsigned head_blocks = (unsigned)((n + 255) / 256);
-  hipLaunchKernelGGL(range_heads_kernel, dim3(head_blocks), dim3(256), 0, s, v.sorted_keys, n,
-                     (uint32_t)table_rows, v.head_count, v.long_flag, v.long_list,
-                     v.counters + kLongCountAt, p.num_ranges);
-  launch_scan(v.head_count, v.head_off, p.num_ranges, v.chunk_sums, v.scalars, nullptr, s);
+  hipLaunchKernelGGL(range_slots_kernel, dim3((unsigned)p.slot_tiles), dim3(kSlotThreads), 0, s,
+                     v.sorted_keys, n, (uint32_t)table_rows, p.num_ranges,
+                     v.status + (int64_t)p.passes * p.num_tiles * kMaxBins,
+                     v.counters + kSlotTicketAt, v.head_off, v.scalars, err);
   return launch_status();
 }
 
@@ -924,18 +957,17 @@ int apply_sorted(const void *grads, int64_t n, int64_t dim, int64_t table_rows, 
   a.grads = static_cast<const uint2 *>(grads);
   a.quads = dim / 4;
   a.dim = dim;
-  a.head_count = v.head_count;
   a.head_off = v.head_off;
   a.num_ranges = p.num_ranges;
   a.grad_table = grad_table;
   a.unique_ids = unique_ids;
   a.unique_grads = unique_grads;
-  a.long_flag = v.long_flag;
-  a.long_list = v.long_list;
-  a.long_count = v.counters + kLongCountAt;
-  // a long run spans at least 3 ranges
-  const int64_t most_long = p.num_ranges / 2;
-  a.long_blocks = (uint32_t)(most_long < kLongBlocks ? most_long : kLongBlocks);
+  // long-run blocks: at most kLongBlocks, each looking after at least
+  // kLongSpan ranges (a long run spans 3 ranges or more)
+  int64_t lb = p.num_ranges >= 3 ? (p.num_ranges + kLongSpan - 1) / kLongSpan : 0;
+  lb = lb < kLongBlocks ? lb : kLongBlocks;
+  a.long_blocks = (uint32_t)lb;
+  a.long_span = lb > 0 ? (p.num_ranges + lb - 1) / lb : 0;
   a.unique_total = v.scalars;
   a.num_unique = num_unique;
   if (sparse)
