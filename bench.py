@@ -19,7 +19,12 @@ forward + backward step.  The roofline entry is for the step's dominant
 kernel, timed with HIP events on the stream it runs on.  The CPU baseline
 is the oracle on the host, timed on the same workload's lookups.
 
-    python bench.py [--steps K] [--warmup W] [--workload e2e|full|medium|backward]
+    python bench.py [--steps K] [--warmup W] [--workload e2e|full|medium|backward|cp_slice]
+
+--workload cp_slice times one context-parallel rank's forward on the
+full-scale workload (tokens [1, 32768], 32 heads, the 200M x 256 table):
+engram_hash_slice over the last of 8 equal slices of the replicated
+sequence (with its packed-segment ids), then engram_gather of that slice.
 """
 from __future__ import annotations
 
@@ -114,12 +119,107 @@ def cpu_baseline(wl, tokens_host, mult, table, grads, budget_s=12.0):
                        f"the {uniq.size} table rows it touches; single-threaded C oracle")}
 
 
+def bench_cp_slice(args, torch, E, workloads, ranks=8):
+    """One context-parallel rank's forward: hash its slice of the replicated
+    sequence (history read across the slice boundary), gather the slice."""
+    wl = workloads.full()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    mult = wl.multipliers()
+    S = wl.seq
+    a, b = (ranks - 1) * S // ranks, S
+    local = b - a
+    log(f"[bench] cp_slice: workload {wl.describe()}, slice [{a}, {b}) of {ranks}")
+    host = [wl.tokens(k, with_segments=True) for k in range(N_BATCHES)]
+    tokens = [torch.from_numpy(t).to(dev) for t, _ in host]
+    segs = [torch.from_numpy(s_).to(dev) for _, s_ in host]
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, dev)
+    R, D = wl.batch * local * wl.heads, wl.dim
+    rows = torch.empty((wl.batch, local, wl.heads), dtype=torch.int64, device=dev)
+    out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+
+    def step(k, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        E.engram_hash_slice(tokens[k % N_BATCHES], a, b, wl.ngram_size, wl.heads_per_ngram,
+                            wl.eos_id, mult, wl.primes, wl.offsets, wl.table_rows,
+                            seq_ids=segs[k % N_BATCHES], out=rows)
+        if ev is not None:
+            ev[1].record(stream)
+        E.engram_gather(rows, table, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for k in range(args.steps):
+        step(k)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(k, evs[k])
+    torch.cuda.synchronize()
+    hist = wl.ngram_size - 1
+    nbytes = {"hash": 8 * wl.batch * (local + hist) * 2 + 8 * R,   # tokens + seg ids, rows
+              "gather": 8 * R + 4 * D * R}
+    phases = {}
+    for i, p_ in enumerate(("hash", "gather")):
+        pm = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+        g = nbytes[p_] / (pm * 1e-3) / 1e9
+        phases[p_] = {"ms": pm, "algorithmic_bytes": nbytes[p_], "gbps": g,
+                      "frac_of_peak": g / PEAK_HBM_GBS}
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import default_oracle
+        oracle = default_oracle()
+        t_host, s_host = host[0]
+        rates, start = [], time.perf_counter()
+        ids = rows.cpu().numpy()
+        uniq, loc = np.unique(ids.reshape(-1), return_inverse=True)
+        compact = table.index_select(0, torch.from_numpy(uniq).to(dev))
+        compact_bits = compact.view(torch.int16).cpu().numpy().view(np.uint16)
+        while len(rates) < 5 and (not rates or time.perf_counter() - start < 12.0):
+            c0 = time.perf_counter()
+            oracle.hash_global_slice(t_host, a, b, wl.ngram_size, wl.heads_per_ngram,
+                                     wl.eos_id, mult, wl.primes, wl.offsets, s_host)
+            oracle.gather(loc.astype(np.int64), compact_bits)
+            rates.append(R / (time.perf_counter() - c0))
+        cpu = {"value": float(np.median(rates)), "unit": "lookups/s", "cores": 1,
+               "kind": "oracle",
+               "sample": (f"one rank's slice ({R} lookups), {len(rates)} runs, median; the "
+                          "oracle hashes the whole replicated sequence and keeps the slice; "
+                          "gather from a compact host copy of the rows it touches")}
+    result = {
+        "metric": METRIC, "value": R / (ms * 1e-3), "unit": "lookups/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**wl.describe(), "workload": "cp_slice", "cp_ranks": ranks,
+                   "slice": [a, b], "lookups": R, "segments": True,
+                   "step": "hash_slice+gather"},
+        "phases": phases,
+        "roofline": {"bound": "hbm", "kernel": "gather_kernel<5>",
+                     "achieved": phases["gather"]["gbps"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": phases["gather"]["gbps"] / PEAK_HBM_GBS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="e2e", choices=["e2e", "full", "medium", "backward"])
+    ap.add_argument("--workload", default="e2e",
+                    choices=["e2e", "full", "medium", "backward", "cp_slice"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -133,6 +233,8 @@ def main():
     from gram_hashed_embedding_amd import engram as E
     from gram_hashed_embedding_amd import workloads
 
+    if args.workload == "cp_slice":
+        return bench_cp_slice(args, torch, E, workloads)
     wl = workloads.get(args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -8,18 +8,24 @@
 // _shift_right_after_eos (history never crosses an EOS or a packed-segment
 // boundary) and _hash_input_ids (output [batch, sequence, ngram_heads]).
 //
+// The slice form follows _forward_global_slice on the same page: the
+// complete (replicated) sequence is available, and only positions
+// [seq_start, seq_end) of every row are hashed, so their history may reach
+// back before seq_start (the two preceding raw tokens and the EOS resets
+// survive a context-parallel boundary).
+//
 // Readings taken where the page is silent: the tokens of an order are
 // combined by a wrapping sum of token * multiplier; multiplier k scales the
 // token k positions back; a position with no valid history token reads 0.
 //
 // Design.  One block covers 64 consecutive tokens of the flattened
-// [batch, seq] array.  Phase 1: one lane per token walks back at most
-// ngram_size - 1 positions (the whole history an n-gram can see, so no scan
-// over the sequence is needed), stopping at the row start, an EOS or a
-// segment change, and keeps the running order mixes M_2..M_n (a prefix sum,
-// so every order costs one multiply-add) in LDS.  Phase 2: the block's
-// 64 * H outputs are one contiguous span of the row-id array, so lane i
-// writes output i: the stores are fully coalesced.  Each output reduces its
+// [batch, slice] array.  Phase 1: one lane per token loads its last
+// ngram_size positions at once (the whole history an n-gram can see, so no
+// scan over the sequence is needed) and walks back through them, stopping
+// at the row start, an EOS or a segment change; it keeps the running order
+// mixes M_2..M_n (a prefix sum, so every order costs one multiply-add) in
+// LDS.  Phase 2: the block's 64 * H outputs are one contiguous span of the
+// row-id array, so lane i writes output i: the stores are fully coalesced.  Each output reduces its
 // order's mix by its head's prime with a Barrett step on |mix| (one 64x64
 // high multiply, one correction) and adds the head offset.  The arithmetic
 // is integer-only and tiny next to the 8 bytes written per output; the
@@ -34,11 +40,13 @@ constexpr int kHashTokens = 64;
 constexpr int64_t kFill = 0;  // history token read where none is valid
 
 struct HashArgs {
-  const int64_t *tokens;
-  const int64_t *seg;  // may be null
-  int64_t *rows;
-  int64_t total_tokens;  // batch * seq
-  int64_t seq;
+  const int64_t *tokens;  // [batch, stride]
+  const int64_t *seg;     // [batch, stride], may be null
+  int64_t *rows;          // [batch, local, H]
+  int64_t total_tokens;   // batch * local
+  int64_t stride;         // positions per row of tokens / seg
+  int64_t start;          // first hashed position of every row
+  int64_t local;          // hashed positions per row
   int64_t eos;
   int32_t n;  // ngram_size
   int32_t J;  // heads_per_ngram
@@ -77,27 +85,32 @@ __global__ __launch_bounds__(kHashThreads) void hash_kernel(const HashArgs a) {
     s_off[h] = a.offset[h];
   }
 
-  // Phase 1: the order mixes of one token per lane.
+  // Phase 1: the order mixes of one token per lane.  The lane's whole
+  // history (and its segment ids) is loaded at once, positions before the
+  // row start reading the lane's own token (never used), so the walk back
+  // below costs one memory round trip.
   if (tid < kHashTokens && tok0 + tid < a.total_tokens) {
     const int64_t f = tok0 + tid;
-    const int64_t t = f % a.seq;  // position inside its row
-    const int64_t *tp = a.tokens + f;
-    const int64_t *sp = a.seg != nullptr ? a.seg + f : nullptr;
-    uint64_t mix = (uint64_t)tp[0] * a.mult[0];  // wraps modulo 2^64
+    const int64_t b = f / a.local;
+    const int64_t t = a.start + (f - b * a.local);  // position inside its row
+    const int64_t *tp = a.tokens + b * a.stride + t;
+    const int64_t *sp = a.seg != nullptr ? a.seg + b * a.stride + t : nullptr;
+    int64_t hist[ENGRAM_MAX_NGRAM], segs[ENGRAM_MAX_NGRAM];
+#pragma unroll
+    for (int k = 0; k < ENGRAM_MAX_NGRAM; ++k) {
+      const int64_t back = (k < a.n && t - k >= 0) ? k : 0;
+      hist[k] = tp[-back];
+      segs[k] = sp != nullptr ? sp[-back] : 0;
+    }
+    uint64_t mix = (uint64_t)hist[0] * a.mult[0];  // wraps modulo 2^64
     bool valid = true;
-    for (int k = 1; k < a.n; ++k) {
+#pragma unroll
+    for (int k = 1; k < ENGRAM_MAX_NGRAM; ++k) {
+      if (k >= a.n) break;
       // Step back from t-k+1 to t-k: stop at the row start, at an EOS
       // (which closes the segment before t-k+1) or at a segment change.
-      if (valid) {
-        if (t - k < 0) {
-          valid = false;
-        } else {
-          const int64_t prev = tp[-k];
-          if (prev == a.eos) valid = false;
-          else if (sp != nullptr && sp[-k] != sp[-k + 1]) valid = false;
-        }
-      }
-      const int64_t s_k = valid ? tp[-k] : kFill;
+      valid = valid && t - k >= 0 && hist[k] != a.eos && segs[k] == segs[k - 1];
+      const int64_t s_k = valid ? hist[k] : kFill;
       mix += (uint64_t)s_k * a.mult[k];
       s_mix[tid][k - 1] = mix;  // mix of order k + 1
     }
@@ -120,22 +133,25 @@ __global__ __launch_bounds__(kHashThreads) void hash_kernel(const HashArgs a) {
 }  // namespace
 }  // namespace engram
 
-using namespace engram;
+namespace engram {
+namespace {
 
-extern "C" int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
-                           int64_t seq, int32_t ngram_size, int32_t heads_per_ngram,
-                           int64_t eos_id, const int64_t *h_multipliers,
-                           const int64_t *h_primes, const int64_t *h_offsets,
-                           int64_t table_rows, int64_t *d_row_ids, void *stream) {
-  if (batch < 0 || seq < 0 || table_rows < 0) return ENGRAM_EINVAL;
+int hash_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch, int64_t stride,
+                int64_t start, int64_t end, int32_t ngram_size, int32_t heads_per_ngram,
+                int64_t eos_id, const int64_t *h_multipliers, const int64_t *h_primes,
+                const int64_t *h_offsets, int64_t table_rows, int64_t *d_row_ids,
+                void *stream) {
+  if (batch < 0 || stride < 0 || table_rows < 0) return ENGRAM_EINVAL;
+  if (start < 0 || end < start || end > stride) return ENGRAM_EINVAL;
   if (ngram_size < 2 || ngram_size > ENGRAM_MAX_NGRAM || heads_per_ngram < 1)
     return ENGRAM_EINVAL;
   const int64_t H = (int64_t)(ngram_size - 1) * heads_per_ngram;
   if (H > ENGRAM_MAX_HEADS) return ENGRAM_EINVAL;
   if (h_multipliers == nullptr || h_primes == nullptr || h_offsets == nullptr)
     return ENGRAM_EINVAL;
-  if (!mul_fits(batch, seq, INT64_MAX)) return ENGRAM_EINVAL;
-  const int64_t total = batch * seq;
+  if (!mul_fits(batch, stride, INT64_MAX)) return ENGRAM_EINVAL;
+  const int64_t local = end - start;
+  const int64_t total = batch * local;
   if (!mul_fits(total, H * 8, INT64_MAX)) return ENGRAM_EINVAL;
   if ((total + kHashTokens - 1) / kHashTokens > INT32_MAX) return ENGRAM_EINVAL;
 
@@ -155,7 +171,9 @@ extern "C" int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids, in
   a.seg = d_seq_ids;
   a.rows = d_row_ids;
   a.total_tokens = total;
-  a.seq = seq;
+  a.stride = stride;
+  a.start = start;
+  a.local = local;
   a.eos = eos_id;
   a.n = ngram_size;
   a.J = heads_per_ngram;
@@ -163,4 +181,30 @@ extern "C" int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids, in
   const unsigned blocks = (unsigned)((total + kHashTokens - 1) / kHashTokens);
   hipLaunchKernelGGL(hash_kernel, dim3(blocks), dim3(kHashThreads), 0, as_stream(stream), a);
   return launch_status();
+}
+
+}  // namespace
+}  // namespace engram
+
+using namespace engram;
+
+extern "C" int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
+                           int64_t seq, int32_t ngram_size, int32_t heads_per_ngram,
+                           int64_t eos_id, const int64_t *h_multipliers,
+                           const int64_t *h_primes, const int64_t *h_offsets,
+                           int64_t table_rows, int64_t *d_row_ids, void *stream) {
+  if (seq < 0) return ENGRAM_EINVAL;
+  return hash_window(d_tokens, d_seq_ids, batch, seq, 0, seq, ngram_size, heads_per_ngram,
+                     eos_id, h_multipliers, h_primes, h_offsets, table_rows, d_row_ids, stream);
+}
+
+extern "C" int engram_hash_slice(const int64_t *d_tokens, const int64_t *d_seq_ids,
+                                 int64_t batch, int64_t global_seq, int64_t seq_start,
+                                 int64_t seq_end, int32_t ngram_size, int32_t heads_per_ngram,
+                                 int64_t eos_id, const int64_t *h_multipliers,
+                                 const int64_t *h_primes, const int64_t *h_offsets,
+                                 int64_t table_rows, int64_t *d_row_ids, void *stream) {
+  return hash_window(d_tokens, d_seq_ids, batch, global_seq, seq_start, seq_end, ngram_size,
+                     heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets, table_rows,
+                     d_row_ids, stream);
 }

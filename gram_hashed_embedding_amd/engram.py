@@ -47,6 +47,11 @@ _lib.engram_hash.restype = ctypes.c_int
 _lib.engram_hash.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                              ctypes.c_int32, ctypes.c_int64, _i64p, _i64p, _i64p,
                              ctypes.c_int64, _vp, _vp]
+_lib.engram_hash_slice.restype = ctypes.c_int
+_lib.engram_hash_slice.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_int64, _i64p, _i64p, _i64p, ctypes.c_int64, _vp,
+                                   _vp]
 _lib.engram_gather.restype = ctypes.c_int
 _lib.engram_gather.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
                                _vp, _vp]
@@ -153,6 +158,54 @@ def engram_hash(tokens, ngram_size, heads_per_ngram, eos_id, multipliers, primes
                                   int(table_rows), _ptr(out), _stream(tokens.device, stream))
     _check(status, "engram_hash")
     return out
+
+
+def engram_hash_slice(tokens, seq_start, seq_end, ngram_size, heads_per_ngram, eos_id,
+                      multipliers, primes, offsets, table_rows, seq_ids=None, out=None,
+                      stream=None):
+    """Row ids int64 [batch, seq_end - seq_start, H] of positions
+    [seq_start, seq_end) of the complete sequence tokens int64
+    [batch, global_seq] (history may reach back before seq_start)."""
+    _device_tensor(tokens, torch.int64, "tokens")
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [batch, global_seq]")
+    batch, gseq = tokens.shape
+    start, end = int(seq_start), int(seq_end)
+    if not 0 <= start <= end <= gseq:
+        raise ValueError(f"slice [{start}, {end}) is not inside [0, {gseq})")
+    if not 2 <= int(ngram_size) <= MAX_NGRAM:
+        raise ValueError(f"ngram_size must be in [2, {MAX_NGRAM}]")
+    heads = (int(ngram_size) - 1) * int(heads_per_ngram)
+    if seq_ids is not None:
+        _device_tensor(seq_ids, torch.int64, "seq_ids")
+        if seq_ids.shape != tokens.shape:
+            raise ValueError("seq_ids must have the shape of tokens")
+    if out is None:
+        out = torch.empty((batch, end - start, heads), dtype=torch.int64, device=tokens.device)
+    _device_tensor(out, torch.int64, "out")
+    if out.numel() != batch * (end - start) * heads:
+        raise ValueError("out must hold batch * (seq_end - seq_start) * H ids")
+    mult = _host_i64(multipliers, int(ngram_size), "multipliers")
+    pr = _host_i64(primes, heads, "primes")
+    off = _host_i64(offsets, heads, "offsets")
+    with torch.cuda.device(tokens.device):
+        status = _lib.engram_hash_slice(_ptr(tokens), _ptr(seq_ids), batch, gseq, start, end,
+                                        int(ngram_size), int(heads_per_ngram), int(eos_id),
+                                        mult, pr, off, int(table_rows), _ptr(out),
+                                        _stream(tokens.device, stream))
+    _check(status, "engram_hash_slice")
+    return out
+
+
+def forward_global_slice(tokens, seq_start, seq_end, table, ngram_size, heads_per_ngram,
+                         eos_id, multipliers, primes, offsets, seq_ids=None, stream=None):
+    """The slice's values bf16 [batch, seq_end - seq_start, H * head_dim]:
+    engram_hash_slice, then engram_gather (two library calls)."""
+    rows = engram_hash_slice(tokens, seq_start, seq_end, ngram_size, heads_per_ngram, eos_id,
+                             multipliers, primes, offsets, table.shape[0], seq_ids=seq_ids,
+                             stream=stream)
+    out = engram_gather(rows, table, stream=stream)
+    return out.reshape(rows.shape[0], rows.shape[1], -1)
 
 
 def engram_gather(row_ids, table, out=None, err_count=None, stream=None):

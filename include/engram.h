@@ -104,6 +104,31 @@ int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids,
                 int64_t *d_row_ids, void *stream);
 
 /*
+ * engram_hash_slice -- the rows of positions [seq_start, seq_end) of every row
+ * of a complete sequence: d_row_ids[b, t - seq_start, h] equals what
+ * engram_hash gives at (b, t, h) for the whole [batch, global_seq] input.
+ *
+ * Follows [API] Qwen3_8_FlashNextNGramEmbedding._forward_global_slice: the
+ * replicated global ids are hashed so that a slice keeps the preceding raw
+ * tokens and the EOS resets across a context-parallel boundary; only the
+ * requested slice is computed (history is read from before seq_start).
+ * Arguments as for engram_hash, with:
+ *   d_tokens, d_seq_ids  int64 [batch, global_seq] (d_seq_ids may be NULL).
+ *   seq_start, seq_end   the slice, 0 <= seq_start <= seq_end <= global_seq.
+ *   d_row_ids            int64 [batch, seq_end - seq_start, H], written.
+ * Errors: those of engram_hash, and EINVAL for a slice outside the sequence.
+ * An empty slice (or batch 0) enqueues nothing.  Pass the result to
+ * engram_gather for the slice's values ([batch, local, H, head_dim]).
+ */
+int engram_hash_slice(const int64_t *d_tokens, const int64_t *d_seq_ids,
+                      int64_t batch, int64_t global_seq, int64_t seq_start,
+                      int64_t seq_end, int32_t ngram_size,
+                      int32_t heads_per_ngram, int64_t eos_id,
+                      const int64_t *h_multipliers, const int64_t *h_primes,
+                      const int64_t *h_offsets, int64_t table_rows,
+                      int64_t *d_row_ids, void *stream);
+
+/*
  * engram_gather -- d_out[i, :] = d_table[d_row_ids[i], :] (bitwise bf16 copy).
  *
  * Follows [API] _lookup_ngram_ids and Qwen3_8_FlashNextOwnerShardedEmbedding

@@ -88,6 +88,20 @@ class Oracle:
             raise ValueError("oracle_hash rejected its arguments")
         return out
 
+    def hash_global_slice(self, tokens, seq_start, seq_end, ngram_size, heads_per_ngram,
+                          eos_id, multipliers, primes, offsets, seq_ids=None):
+        """Row IDs int64 [batch, seq_end - seq_start, H] of one slice of a
+        complete sequence.  Follows the NeMo AutoModel v0.7 API page
+        (qwen3_8_flash_next.engram), Qwen3_8_FlashNextNGramEmbedding.
+        _forward_global_slice: the whole replicated sequence is hashed, then
+        the positions [seq_start, seq_end) are kept."""
+        tokens = np.asarray(tokens)
+        if not 0 <= seq_start <= seq_end <= tokens.shape[1]:
+            raise ValueError("slice outside the sequence")
+        full = self.hash(tokens, ngram_size, heads_per_ngram, eos_id, multipliers, primes,
+                         offsets, seq_ids=seq_ids)
+        return full[:, seq_start:seq_end, :].copy()
+
     # -- gather -------------------------------------------------------------
     def gather(self, row_ids, table_bits):
         """(out uint16 [n, dim], invalid count) for table uint16 [rows, dim]."""

@@ -22,7 +22,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"engram_status_string", "engram_abi_version", "engram_hash",
                           "engram_gather", "engram_scatter_add_workspace",
                           "engram_scatter_add", "engram_scatter_add_rowsparse",
-                          "engram_scatter_plan", "engram_scatter_apply"}
+                          "engram_scatter_plan", "engram_scatter_apply",
+                          "engram_hash_slice"}
     for name in names:
         assert hasattr(e._lib, name), name
 
@@ -143,3 +144,15 @@ def test_plan_apply_reject():
     assert ap(ALIGNED, 100, 8, 50, ALIGNED, None, None, None, ALIGNED, 16, None) == \
         e.ENGRAM_EWORKSPACE
     assert ap(None, 0, 8, 50, ALIGNED, None, None, None, None, 0, None) == e.ENGRAM_OK
+
+
+def test_hash_slice_rejects():
+    hs = e._lib.engram_hash_slice
+    def call(start, end, gseq=8, batch=1, tokens=FAKE, out=FAKE):
+        return hs(tokens, None, batch, gseq, start, end, 3, 2, 0, _arr((1, 2, 3)),
+                  _arr((5, 7, 11, 13)), _arr((0, 5, 12, 23)), 36, out, None)
+    for start, end in [(-1, 4), (5, 4), (0, 9), (9, 9)]:
+        assert call(start, end) == e.ENGRAM_EINVAL, (start, end)
+    assert call(3, 3, tokens=None, out=None) == e.ENGRAM_OK   # empty slice: no launch
+    assert call(0, 8, batch=0, tokens=None, out=None) == e.ENGRAM_OK
+    assert call(0, 4, tokens=None) == e.ENGRAM_EINVAL

@@ -59,6 +59,19 @@ def test_full_scale_forward(oracle):
         assert out.shape == (1, 32768, 32, 256)
         sampled_gather_check(oracle, rows_host, out, table, wl.seed)
         del rows, out
+    # the 8-way context-parallel split: each slice's forward reads its history
+    # across the boundary and equals the same slice of the whole forward
+    step = tok.shape[1] // 8
+    for r in range(8):
+        a, b = r * step, (r + 1) * step
+        sl = E.forward_global_slice(dev(tok), a, b, table, wl.ngram_size, wl.heads_per_ngram,
+                                    wl.eos_id, mult, wl.primes, wl.offsets, seq_ids=dev(seg))
+        torch.cuda.synchronize()
+        want = oracle.hash_global_slice(tok, a, b, wl.ngram_size, wl.heads_per_ngram,
+                                        wl.eos_id, mult, wl.primes, wl.offsets, seg)
+        assert sl.shape == (1, step, 32 * 256)
+        sampled_gather_check(oracle, want, sl.view(1, step, 32, 256), table, wl.seed + r)
+        del sl
     del table
     release()
 

@@ -1,0 +1,92 @@
+"""GPU parity of the global-slice hash (engram_hash_slice) and of the slice
+forward (hash slice, then gather) against the oracle: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from gram_hashed_embedding_amd import workloads
+from tests.gpu_helpers import bits, dev, needs_gpu
+from tests.test_oracle_hash import WINDOW_CASES
+
+pytestmark = needs_gpu
+E = pytest.importorskip("gram_hashed_embedding_amd.engram")
+
+
+def gpu_slice(tok, start, end, n, J, eos, mult, primes, offs, rows, seg=None):
+    out = E.engram_hash_slice(dev(tok), start, end, n, J, eos, mult, primes, offs, rows,
+                              seq_ids=None if seg is None else dev(seg))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def slices_of(S, seed):
+    """Slices near the edges, ragged ones and the 8-way context-parallel split."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = [(0, S), (0, 1), (S - 1, S), (1, 3), (S // 2, S // 2)]
+    for _ in range(6):
+        a, b = sorted(int(x) for x in rng.integers(0, S + 1, 2))
+        out.append((a, b))
+    step = S // 8
+    out += [(r * step, (r + 1) * step) for r in range(8)]
+    return out
+
+
+@pytest.mark.parametrize("name", ["tiny", "medium", "e2e"])
+@pytest.mark.parametrize("segments", [False, True])
+def test_slices_match_oracle(oracle, name, segments):
+    wl = workloads.get(name)
+    tok = wl.tokens(3)
+    seg = workloads.random_segments(tok.shape, 300, wl.seed) if segments else None
+    mult = wl.multipliers()
+    args = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+    full = oracle.hash(tok, *args, seg)
+    for a, b in slices_of(tok.shape[1], wl.seed):
+        got = gpu_slice(tok, a, b, *args, wl.table_rows, seg)
+        assert got.shape == (tok.shape[0], b - a, len(wl.primes))
+        assert np.array_equal(got, full[:, a:b]), (a, b)
+        if name == "tiny":
+            assert np.array_equal(got, oracle.hash_global_slice(tok, a, b, *args, seg))
+
+
+@pytest.mark.parametrize("case", [c for c in WINDOW_CASES if c["slice"]],
+                         ids=lambda c: c["name"])
+def test_golden_slices(oracle, case):
+    n, J = case["n"], 2
+    tok = np.array([case["tokens"]], dtype=np.int64)
+    seg = None if case["seg"] is None else np.array([case["seg"]], dtype=np.int64)
+    primes = [1009, 1013] * (n - 1)
+    offs = workloads.cumulative_offsets(primes)
+    a, b = case["slice"]
+    for variant in range(3):
+        mult = workloads.seeded_multipliers(n, 700 + variant)
+        want = oracle.hash_global_slice(tok, a, b, n, J, case["eos"], mult, primes, offs, seg)
+        got = gpu_slice(tok, a, b, n, J, case["eos"], mult, primes, offs, sum(primes), seg)
+        assert np.array_equal(got, want), variant
+
+
+def test_slice_forward_tiny(oracle):
+    """Hash slice + gather, every output against the oracle."""
+    wl = workloads.tiny()
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
+    tok = wl.tokens(2)
+    mult = wl.multipliers()
+    args = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+    for a, b in [(0, 128), (17, 80), (64, 128), (127, 128)]:
+        out = E.forward_global_slice(dev(tok), a, b, table, *args)
+        torch.cuda.synchronize()
+        ids = oracle.hash_global_slice(tok, a, b, *args)
+        want, bad = oracle.gather(ids, bits(table))
+        assert bad == 0
+        assert out.shape == (tok.shape[0], b - a, len(wl.primes) * wl.dim)
+        assert np.array_equal(bits(out).reshape(-1, wl.dim), want)
+
+
+def test_empty_slice_and_rejects():
+    wl = workloads.tiny()
+    tok = dev(wl.tokens(0))
+    args = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, wl.multipliers(), wl.primes,
+            wl.offsets, wl.table_rows)
+    assert E.engram_hash_slice(tok, 9, 9, *args).shape == (2, 0, 4)
+    for a, b in [(-1, 4), (5, 4), (0, 129)]:
+        with pytest.raises(ValueError):
+            E.engram_hash_slice(tok, a, b, *args)

@@ -43,8 +43,9 @@ def load_window_cases(path=GOLDEN):
         seg = None if c["seg"] == "-" else [int(x) for x in c["seg"].split()]
         exp = {k: [0 if x == "F" else int(x) for x in c[f"s{k}"].split()]
                for k in range(1, n)}
+        sl = tuple(int(x) for x in c["slice"].split()) if "slice" in c else None
         out.append(dict(name=c["case"], n=n, eos=int(c["eos"]), tokens=toks,
-                        seg=seg, expected=exp))
+                        seg=seg, expected=exp, slice=sl))
     return out
 
 
