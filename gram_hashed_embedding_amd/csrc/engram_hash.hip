@@ -3,16 +3,17 @@
 // Computes the global row of every (batch, position, head) as described on
 // the NeMo AutoModel v0.7 API page "qwen3_8_flash_next.engram":
 // Qwen3_8_FlashNextNGramEmbedding (class description: bigram heads first,
-// then trigram, ...; context resets after an EOS; wrapping signed int64
-// arithmetic; positive remainders; checkpoint head offsets),
+// then trigram, ...; the history is cleared after an EOS; signed int64
+// arithmetic that wraps; non-negative remainders; head offsets from the
+// checkpoint),
 // _shift_right_after_eos (history never crosses an EOS or a packed-segment
 // boundary) and _hash_input_ids (output [batch, sequence, ngram_heads]).
 //
 // The slice form follows _forward_global_slice on the same page: the
 // complete (replicated) sequence is available, and only positions
 // [seq_start, seq_end) of every row are hashed, so their history may reach
-// back before seq_start (the two preceding raw tokens and the EOS resets
-// survive a context-parallel boundary).
+// back before seq_start (a context-parallel cut keeps the tokens before it
+// and the EOS resets at it).
 //
 // Readings taken where the page is silent: the tokens of an order are
 // combined by a wrapping sum of token * multiplier; multiplier k scales the

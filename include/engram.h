@@ -54,7 +54,7 @@ extern "C" {
 #define ENGRAM_EWORKSPACE (-3)
 #define ENGRAM_EHIP (-4)
 
-/* Largest n-gram order (current token included) and head count accepted. */
+/* Highest n-gram order accepted (the current token counts) and most heads. */
 #define ENGRAM_MAX_NGRAM 8
 #define ENGRAM_MAX_HEADS 64
 
@@ -109,9 +109,9 @@ int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids,
  * engram_hash gives at (b, t, h) for the whole [batch, global_seq] input.
  *
  * Follows [API] Qwen3_8_FlashNextNGramEmbedding._forward_global_slice: the
- * replicated global ids are hashed so that a slice keeps the preceding raw
- * tokens and the EOS resets across a context-parallel boundary; only the
- * requested slice is computed (history is read from before seq_start).
+ * whole replicated sequence is the input, so a context-parallel slice still
+ * sees the tokens before its first position and the EOS resets there; only
+ * the requested slice is computed (history is read from before seq_start).
  * Arguments as for engram_hash, with:
  *   d_tokens, d_seq_ids  int64 [batch, global_seq] (d_seq_ids may be NULL).
  *   seq_start, seq_end   the slice, 0 <= seq_start <= seq_end <= global_seq.

@@ -45,8 +45,8 @@
 #define ORACLE_MAX_ORDER 8
 
 /* ---------------------------------------------------------------------- */
-/* Two's-complement int64 arithmetic without undefined behaviour.          */
-/* "Hashing intentionally uses signed int64 overflow" ([API],              */
+/* Two's-complement int64 arithmetic without undefined behaviour.  The     */
+/* hash relies on signed int64 overflow on purpose ([API],                 */
 /* Qwen3_8_FlashNextNGramEmbedding, class description): products and sums  */
 /* wrap modulo 2^64.  C leaves signed overflow undefined, so the wrap is   */
 /* done on uint64_t and the bits are reinterpreted.                        */
@@ -68,9 +68,9 @@ static int64_t wrapping_add(int64_t a, int64_t b)
     return bits_to_i64((uint64_t)a + (uint64_t)b);
 }
 
-/* "positive remainders" ([API], class description): the floor remainder,
- * in [0, p) for p > 0.  C's % truncates toward zero, so a negative result
- * is moved up by p. */
+/* Remainders are taken non-negative ([API], class description): the floor
+ * remainder, in [0, p) for p > 0.  C's % truncates toward zero, so a
+ * negative result is moved up by p. */
 static int64_t positive_remainder(int64_t x, int64_t p)
 {
     int64_t r = x % p;
@@ -80,13 +80,13 @@ static int64_t positive_remainder(int64_t x, int64_t p)
 }
 
 /* ---------------------------------------------------------------------- */
-/* History read: "Read an earlier token without crossing an EOS or         */
-/* packed-segment boundary" ([API], _shift_right_after_eos).               */
+/* History read ([API], _shift_right_after_eos): an earlier token is only  */
+/* read if the way back to it passes no EOS and no packed-segment border.  */
 /* Walks back from position t one step at a time.  Stepping from j+1 to j  */
-/* crosses a boundary when tok[j] is EOS (the EOS "terminates the          */
-/* preceding segment", [API] constructor argument eos_token_id, so the     */
-/* next position starts fresh) or when the packed segment IDs of j and j+1 */
-/* differ ("n-gram history stays inside a segment", [API] _hash_input_ids, */
+/* crosses a boundary when tok[j] is EOS (an EOS closes the segment before */
+/* it, [API] constructor argument eos_token_id, so the position after it   */
+/* starts fresh) or when the packed segment IDs of j and j+1 differ (a     */
+/* token's history never leaves its own segment, [API] _hash_input_ids,    */
 /* argument sequence_ids).  Running off the start of the row also has no   */
 /* valid token.  A missing token reads FILL.                               */
 /* ---------------------------------------------------------------------- */
