@@ -26,12 +26,15 @@
  *     history, the position after it starts fresh;
  *   - backward: each unique row's contributions are summed in fp64 in
  *     ascending flat index, rounded once to fp32, then added to the fp32
- *     gradient row with one fp32 add.
+ *     gradient row with one fp32 add;
+ *   - optimizer step (SignSGD on the touched rows): fp32(w) - lr * sign(g)
+ *     in fp32, rounded once to bf16 (nearest, ties to even), sign(0) = 0.
  *
  * Parity status: every function here is pinned by CPU tests (brute force
  * over exhaustive tiny inputs with an independent big-integer formulation,
  * closed-form unit-multiplier cases written from the pages' EOS and segment
- * rules, degenerate cases, and library routines for gather and scatter).
+ * rules, degenerate cases, and library routines for gather, scatter and
+ * the SignSGD step's fp32 -> bf16 rounding).
  * Parity with the released checkpoint's hash is unpinned: the pages do not
  * fix the combining operation or the fill value, and no checkpoint is here.
  *
@@ -320,5 +323,53 @@ int64_t oracle_scatter_add_rowsparse(const int64_t *row_ids, int64_t n,
     *num_unique = u;
     free(acc);
     free(refs);
+    return bad;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Row-sparse SignSGD step into the bf16 table.  The RL runs on the pages  */
+/* trained with SignSGD at learning rate 1e-6 and the default FP32         */
+/* optimizer math ([PR1] Validation; [PR2] Validation).  Reading (the      */
+/* pages give no formula): for every listed row r with gradient sum S_r    */
+/* (fp32, the row-sparse backward's output), every element becomes         */
+/*     w <- bf16( fp32(w) - lr * sign(S_r[e]) )                            */
+/* with the subtraction in fp32, sign(0) = 0, and one rounding to bf16,    */
+/* to nearest with ties to even.  Rows not listed keep their values.       */
+/* The listed ids are taken one after another; ids outside [0, rows) are  */
+/* skipped and counted (the return value).                                 */
+/* ---------------------------------------------------------------------- */
+static uint16_t float_to_bf16_bits(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);          /* NaN stays a quiet NaN */
+    /* round to nearest, ties to even: add just under half of the dropped
+     * range, plus one when the kept part is odd, then truncate */
+    const uint32_t keep_odd = (u >> 16) & 1u;
+    u += 0x7fffu + keep_odd;
+    return (uint16_t)(u >> 16);
+}
+
+int64_t oracle_signsgd_rowsparse(const int64_t *unique_ids, const float *unique_grads,
+                                 int64_t count, int64_t dim, uint16_t *table,
+                                 int64_t table_rows, float lr)
+{
+    int64_t bad = 0;
+    for (int64_t u = 0; u < count; ++u) {
+        const int64_t r = unique_ids[u];
+        if (r < 0 || r >= table_rows) {
+            bad += r != -1 ? 1 : 0;
+            continue;
+        }
+        for (int64_t e = 0; e < dim; ++e) {
+            const float g = unique_grads[u * dim + e];
+            const float sign = g > 0.0f ? 1.0f : (g < 0.0f ? -1.0f : 0.0f);
+            const float w = bf16_bits_to_float(table[r * dim + e]);
+            const float step = lr * sign;
+            const float updated = w - step;
+            table[r * dim + e] = float_to_bf16_bits(updated);
+        }
+    }
     return bad;
 }

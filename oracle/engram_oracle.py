@@ -58,6 +58,9 @@ class Oracle:
         lib.oracle_scatter_add_rowsparse.argtypes = [_i64p, ctypes.c_int64, _u16p,
                                                      ctypes.c_int64, ctypes.c_int64,
                                                      _i64p, _f32p, _i64p]
+        lib.oracle_signsgd_rowsparse.restype = ctypes.c_int64
+        lib.oracle_signsgd_rowsparse.argtypes = [_i64p, _f32p, ctypes.c_int64, ctypes.c_int64,
+                                                 _u16p, ctypes.c_int64, ctypes.c_float]
         self._lib = lib
 
     # -- hash ---------------------------------------------------------------
@@ -145,6 +148,19 @@ class Oracle:
             raise MemoryError("oracle_scatter_add_rowsparse ran out of memory")
         u = int(count[0])
         return uid[:u].copy(), vals[:u].copy(), int(bad)
+
+    # -- optimizer step -------------------------------------------------------
+    def signsgd_rowsparse(self, unique_ids, unique_grads, table_bits, lr):
+        """SignSGD on the listed rows of a copy of the bf16 table (uint16
+        [rows, dim]); returns (new table bits, invalid count)."""
+        ids = np.ascontiguousarray(unique_ids, dtype=np.int64).reshape(-1)
+        table = np.array(table_bits, dtype=np.uint16, copy=True, order="C")
+        rows, dim = table.shape
+        grads = np.ascontiguousarray(unique_grads, dtype=np.float32).reshape(ids.size, dim)
+        bad = self._lib.oracle_signsgd_rowsparse(_ptr(ids, _i64p), _ptr(grads, _f32p),
+                                                 ids.size, dim, _ptr(table, _u16p), rows,
+                                                 float(lr))
+        return table, int(bad)
 
 
 _default = None

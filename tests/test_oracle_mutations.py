@@ -15,6 +15,8 @@ from oracle import Oracle, build
 from oracle.engram_oracle import SOURCE
 from tests import test_oracle_hash as H
 from tests import test_oracle_lookup as L
+from tests import test_oracle_signsgd as G
+from tests import test_oracle_slice as SL
 
 MUTANTS = {
     "drop_current_token": ("for (int k = 0; k < g; ++k)", "for (int k = 1; k < g; ++k)"),
@@ -42,6 +44,10 @@ MUTANTS = {
     "overwrite_not_add": ("dst[e] = dst[e] + s;", "dst[e] = s;"),
     "no_grouping": ("while (end < m && refs[end].row == refs[begin].row)",
                     "while (end < m && 0)"),
+    "sgd_ascent": ("const float updated = w - step;", "const float updated = w + step;"),
+    "sgd_truncating_bf16": ("u += 0x7fffu + keep_odd;", "u += 0u * keep_odd;"),
+    "sgd_ties_away": ("u += 0x7fffu + keep_odd;", "u += 0x8000u + 0u * keep_odd;"),
+    "sgd_sign_of_zero_is_one": ("g < 0.0f ? -1.0f : 0.0f", "g < 0.0f ? -1.0f : 1.0f"),
 }
 
 # Every pin, called directly with the mutant in place of the oracle fixture.
@@ -62,6 +68,10 @@ PINS = [
     lambda o: L.test_dense_one_shared_row(o),
     lambda o: L.test_dense_skips_padding_and_counts_invalid(o),
     lambda o: L.test_rowsparse_matches_dense(o),
+    lambda o: [G.test_matches_torch_rounding(o, lr) for lr in (2.0 ** -8, 0.3)],
+    lambda o: G.test_hand_cases_and_ties(o),
+    lambda o: G.test_unlisted_rows_and_invalid_ids(o),
+    lambda o: [SL.test_slice_reads_history_across_the_boundary(o, c) for c in SL.SLICE_CASES],
 ]
 
 
