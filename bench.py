@@ -19,7 +19,14 @@ forward + backward step.  The roofline entry is for the step's dominant
 kernel, timed with HIP events on the stream it runs on.  The CPU baseline
 is the oracle on the host, timed on the same workload's lookups.
 
-    python bench.py [--steps K] [--warmup W] [--workload e2e|full|medium|backward|cp_slice]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload e2e|e2e_signsgd|full|medium|backward|cp_slice]
+
+--workload e2e_signsgd is the e2e step with the optimizer: the apply is
+engram_scatter_apply_signsgd, which sums each distinct row's gradients and
+applies one SignSGD step to that row of the bf16 table in the same pass
+(the fp32 sums are never written).  The line also reports the same step
+done in two calls (row-sparse apply, then engram_signsgd_rowsparse).
 
 --workload cp_slice times one context-parallel rank's forward on the
 full-scale workload (tokens [1, 32768], 32 heads, the 200M x 256 table):
@@ -219,7 +226,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="e2e",
-                    choices=["e2e", "full", "medium", "backward", "cp_slice"])
+                    choices=["e2e", "e2e_signsgd", "full", "medium", "backward", "cp_slice"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -235,7 +242,9 @@ def main():
 
     if args.workload == "cp_slice":
         return bench_cp_slice(args, torch, E, workloads)
-    wl = workloads.get(args.workload)
+    signsgd = args.workload == "e2e_signsgd"
+    lr = 1e-6  # the learning rate of the pages' SignSGD runs
+    wl = workloads.get("e2e" if signsgd else args.workload)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -255,7 +264,7 @@ def main():
     backward = wl.grads != "none"
     if backward:
         grads = workloads.make_grads(R, D, wl.seed + 2, dev)
-    if wl.grads == "rowsparse":
+    if wl.grads == "rowsparse":  # (the SignSGD step's comparison uses these too)
         uid = torch.empty(R, dtype=torch.int64, device=dev)
         uval = torch.empty((R, D), dtype=torch.float32, device=dev)
         count = torch.zeros(1, dtype=torch.int64, device=dev)
@@ -289,7 +298,9 @@ def main():
         apply_backward()
 
     def apply_backward():
-        if wl.grads == "rowsparse":
+        if signsgd:
+            E.engram_scatter_apply_signsgd(grads, ws, table, lr)
+        elif wl.grads == "rowsparse":
             E.engram_scatter_apply(grads, ws, wl.table_rows, unique_ids=uid, unique_grads=uval,
                                    num_unique=count)
         else:
@@ -343,9 +354,32 @@ def main():
     if backward:
         serial_step(0, evs[0])
         torch.cuda.synchronize()
-        unique_rows = (int(count.item()) if wl.grads == "rowsparse"
+        unique_rows = (int(count.item()) if wl.grads == "rowsparse" and not signsgd
                        else int(torch.unique(rows).numel()))
     nbytes = algorithmic_bytes(wl, unique_rows)
+    unfused = None
+    if signsgd:
+        # the fused apply reads the gradient rows and reads + writes each
+        # distinct row of the bf16 table once
+        nbytes["scatter_apply"] = 2 * D * R + 4 * D * unique_rows
+        # the same step in two calls, for comparison (same plan, same stream)
+        u0, u1, u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws)
+        tw = []
+        for k in range(max(args.steps // 2, 3)):
+            u0.record(stream)
+            E.engram_scatter_apply(grads, ws, wl.table_rows, unique_ids=uid, unique_grads=uval,
+                                   num_unique=count)
+            u1.record(stream)
+            E.engram_signsgd_rowsparse(uid, uval, count, table, lr)
+            u2.record(stream)
+            torch.cuda.synchronize()
+            tw.append((u0.elapsed_time(u1), u1.elapsed_time(u2)))
+        a_ms, s_ms = (float(np.median([t[i] for t in tw])) for i in range(2))
+        unfused = {"scatter_apply_ms": a_ms, "engram_signsgd_rowsparse_ms": s_ms,
+                   "total_ms": a_ms + s_ms,
+                   "algorithmic_bytes": 2 * D * R + (4 * D + 8) * unique_rows
+                   + (8 + 4 * D + 4 * D) * unique_rows}
     phases = {}
     for p_, ms in phase_ms.items():
         b_ = nbytes.get(p_, 0)
@@ -360,11 +394,12 @@ def main():
     kernel = "gather_kernel<5>" if D == 256 else "gather_kernel"
     if backward and phase_ms["scatter_apply"] > phase_ms["gather"]:
         dominant = "scatter_apply"
-        kernel = "segment_reduce_kernel (engram_scatter_apply)"
+        kernel = ("segment_reduce_kernel, SignSGD output (engram_scatter_apply_signsgd)"
+                  if signsgd else "segment_reduce_kernel (engram_scatter_apply)")
     roofline = {"bound": "hbm", "kernel": kernel, "achieved": phases[dominant]["gbps"],
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS,
-                "traffic": measured_traffic(dominant, wl)}
+                "traffic": None if signsgd else measured_traffic(dominant, wl)}
 
     # context: a plain device-to-device copy (torch copy_, 2 GiB read + 2 GiB
     # written) shows what this GPU's HBM delivers to a streaming kernel
@@ -403,8 +438,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {**wl.describe(),
+                   **({"workload": "e2e_signsgd", "optimizer": "signsgd", "lr": lr}
+                      if signsgd else {}),
                    "step": "hash+gather" + ("+scatter(plan beside gather, apply)" if backward
-                                            else ""),
+                                            else "")
+                   + ("+signsgd(fused into the apply)" if signsgd else ""),
                    "backward": wl.grads, "accumulate": "f64" if backward else None,
                    "unique_rows": unique_rows, "token_batches_cycled": N_BATCHES},
         "serial_ms_per_step": serial_ms,
@@ -412,6 +450,7 @@ def main():
         "step_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBS,
         "phases": phases,
+        **({"two_call_apply_and_signsgd": unfused} if unfused else {}),
         "roofline": roofline,
         "hbm_copy_ceiling_gbps": copy_gbps,
         "cpu_baseline": cpu,

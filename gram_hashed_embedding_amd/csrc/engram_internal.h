@@ -41,6 +41,21 @@ __device__ __forceinline__ void unpack_bf16x8(const u32x4 &v, float (&f)[8]) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
+// fp32 -> bf16 bits, rounded to nearest with ties to even (a NaN stays a
+// quiet NaN): add just under half of the dropped low half, plus one when the
+// kept half is odd, and keep the high half.
+__device__ __forceinline__ uint32_t bf16_bits_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// One SignSGD element in fp32: w - lr * sign(g), sign(0) = 0, as bf16 bits.
+__device__ __forceinline__ uint32_t signsgd_bf16(float w, float g, float lr) {
+  const float s = g > 0.0f ? 1.0f : (g < 0.0f ? -1.0f : 0.0f);
+  return bf16_bits_rne(w - lr * s);
+}
+
 // Add a lane's count of invalid ids to *err (when err is not null).  Invalid
 // ids are rare, so one atomic per lane that saw any is cheap.
 __device__ __forceinline__ void count_errors(int bad, int64_t *err) {

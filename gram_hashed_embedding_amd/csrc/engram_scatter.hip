@@ -424,6 +424,8 @@ struct WalkArgs {
   float *grad_table;    // dense output
   int64_t *unique_ids;  // row-sparse output
   float *unique_grads;
+  uint2 *table;         // SignSGD output: the bf16 table, [rows, dim / 4] quads
+  float lr;
   uint32_t long_blocks;  // leading blocks of the grid: they sum the long runs
   int64_t long_span;     // ranges each of those blocks looks after
   const uint32_t *unique_total;  // U, from the plan
@@ -460,14 +462,26 @@ __device__ __forceinline__ void add_quads_if(double (&acc)[Q][4], const uint2 (&
   }
 }
 
+// What the apply writes for each distinct row r with sum S_r.
+constexpr int kOutDense = 0;    // grad_table[r] += fp32(S_r)
+constexpr int kOutSparse = 1;   // unique_ids[u] = r, unique_grads[u] = fp32(S_r)
+constexpr int kOutSignSGD = 2;  // table[r] = bf16(fp32(table[r]) - lr * sign(fp32(S_r)))
+
+// This lane's quads of row idx of a [rows, quads] array of 4-value quads.
+template <int L, int Q, bool EXACT>
+__device__ __forceinline__ void load_quads(const uint2 *base, uint32_t idx, int64_t quads,
+                                           int lane, uint2 (&g)[Q]) {
+  const uint2 *row = base + (int64_t)idx * quads;
+#pragma unroll
+  for (int k = 0; k < Q; ++k)
+    g[k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, quads - 1)];
+}
+
 // This lane's quads of one gradient row.
 template <int L, int Q, bool EXACT>
 __device__ __forceinline__ void load_row(const WalkArgs &a, uint32_t idx, int lane,
                                          uint2 (&g)[Q]) {
-  const uint2 *row = a.grads + (int64_t)idx * a.quads;
-#pragma unroll
-  for (int k = 0; k < Q; ++k)
-    g[k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
+  load_quads<L, Q, EXACT>(a.grads, idx, a.quads, lane, g);
 }
 
 // Keys and flat indices of one range as 16-byte vectors.
@@ -505,22 +519,29 @@ __device__ __forceinline__ bool last_run_long(int64_t c, int64_t n, uint32_t sen
 }
 
 // The finished sum of row `key` (distinct-row slot u): one rounding to fp32,
-// then one fp32 add into the dense table, or a row-sparse store.
-template <int L, int Q, bool SPARSE>
+// then one fp32 add into the dense table, a row-sparse store, or the SignSGD
+// step on the table row (w: this lane's quads of that row, loaded earlier).
+template <int L, int Q, int OUT>
 __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArgs &a, int lane,
-                                         const double (&acc)[Q][4]) {
-  if (SPARSE && lane == 0) a.unique_ids[u] = (int64_t)key;
+                                         const double (&acc)[Q][4], const uint2 (&w)[Q]) {
+  if (OUT == kOutSparse && lane == 0) a.unique_ids[u] = (int64_t)key;
 #pragma unroll
   for (int k = 0; k < Q; ++k) {
     const int64_t qd = lane + (int64_t)k * L;
     if (qd >= a.quads) continue;
     const f32x4 sum = {(float)acc[k][0], (float)acc[k][1], (float)acc[k][2], (float)acc[k][3]};
-    if (SPARSE) {
+    if (OUT == kOutSparse) {
       f32x4 *dst = reinterpret_cast<f32x4 *>(a.unique_grads + (int64_t)u * a.dim) + qd;
       __builtin_nontemporal_store(sum, dst);
-    } else {
+    } else if (OUT == kOutDense) {
       f32x4 *dst = reinterpret_cast<f32x4 *>(a.grad_table + (int64_t)key * a.dim) + qd;
       *dst = *dst + sum;
+    } else {
+      const uint32_t b0 = signsgd_bf16(bf16_lo(w[k].x), sum.x, a.lr);
+      const uint32_t b1 = signsgd_bf16(bf16_hi(w[k].x), sum.y, a.lr);
+      const uint32_t b2 = signsgd_bf16(bf16_lo(w[k].y), sum.z, a.lr);
+      const uint32_t b3 = signsgd_bf16(bf16_hi(w[k].y), sum.w, a.lr);
+      a.table[(int64_t)key * a.quads + qd] = uint2{b0 | (b1 << 16), b2 | (b3 << 16)};
     }
   }
 }
@@ -536,7 +557,7 @@ __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArg
 // only then are runs summed and written.  A run that crosses into the next
 // range (and, not being long, ends there) is finished by its owner, which
 // then reads the next range's keys and the continuation rows.
-template <int L, int Q, bool SPARSE, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT>
 __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
   const int lane = threadIdx.x % L;
   const int64_t w = (blk * kWalkThreads + threadIdx.x) / L;
@@ -570,6 +591,20 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
 #pragma unroll
   for (int q = 0; q < kRange; ++q) tail += (q < live_count && !(last_long && kk[q] == klast)) ? 1 : 0;
 
+  // SignSGD: the table row of every run that starts in [lead, tail), loaded
+  // beside the gradient rows (other positions re-read the first key's row)
+  uint2 tw[OUT == kOutSignSGD ? kRange : 1][Q];
+  uint2 cw[Q];  // the current run's table row
+  if constexpr (OUT == kOutSignSGD) {
+    if (tail > lead) {
+#pragma unroll
+      for (int q = 0; q < kRange; ++q) {
+        const bool head = q >= lead && q < tail && (q == lead || kk[q] != kk[q > 0 ? q - 1 : 0]);
+        load_quads<L, Q, EXACT>(a.table, head ? kk[q] : kk[0], a.quads, lane, tw[q]);
+      }
+    }
+  }
+
   // gradient rows in flight together (rows wider than 512 values: Q / 2
   // batches, to bound registers)
   constexpr int B = Q > 2 ? kRange / (Q / 2) : kRange;
@@ -590,12 +625,17 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
     for (int qq = 0; qq < B; ++qq) {
       const int q = b0 + qq;
       const bool live = q >= lead && q < tail;
-      if (live && started && kk[q] != cur) {  // a new distinct row starts at beg + q
-        emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+      const bool head = live && (!started || kk[q] != cur);  // a distinct row starts at beg + q
+      if (head && started) {
+        emit_row<L, Q, OUT>(cur, u, a, lane, acc, cw);
         ++u;
         zero_acc<Q>(acc);
       }
-      if (live) {
+      if (head) {
+        if constexpr (OUT == kOutSignSGD) {
+#pragma unroll
+          for (int k = 0; k < Q; ++k) cw[k] = tw[q][k];
+        }
         cur = kk[q];
         started = true;
       }
@@ -623,11 +663,11 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
         if (q0 + b < m) add_quads<Q>(acc, g[b]);
     }
   }
-  emit_row<L, Q, SPARSE>(cur, u, a, lane, acc);
+  emit_row<L, Q, OUT>(cur, u, a, lane, acc, cw);
 }
 
 // One long run: the run that starts in range c0 and reaches range c0 + 2.
-template <int L, int Q, bool SPARSE, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT>
 __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
                                          double (&s_part)[kWalkThreads / L][L * 4]) {
   constexpr int G = kWalkThreads / L;  // walkers per block
@@ -635,6 +675,8 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
   const int64_t r0 = c0 * kRange;
   const uint32_t u = a.head_off[c0 + 1] - 1;  // the last head of c0 (c0 + 2 exists)
   const uint32_t key = a.keys[r0 + kRange - 1];
+  uint2 tw[Q];  // SignSGD: the run's table row
+  if constexpr (OUT == kOutSignSGD) load_quads<L, Q, EXACT>(a.table, key, a.quads, lane, tw);
   // start: range c0 is sorted, so the run begins after its smaller keys
   int64_t start = r0;
   const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + r0);
@@ -663,20 +705,48 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
   double acc[Q][4];
   zero_acc<Q>(acc);
   uint32_t vv[kRange];
-  if (c0 + g <= c1) load_vals(a.vals, (c0 + g) * kRange, vv);
+  if (Q == 1 && c0 + g <= c1) load_vals(a.vals, (c0 + g) * kRange, vv);
+  if constexpr (Q == 1) {
+    // a whole range of rows in flight, the next range's indices fetched
+    // while they arrive
 #pragma unroll 1
-  for (int64_t c = c0 + g; c <= c1; c += G) {
-    uint2 rows[kRange][Q];
+    for (int64_t c = c0 + g; c <= c1; c += G) {
+      uint2 rows[kRange][Q];
 #pragma unroll
-    for (int q = 0; q < kRange; ++q) {
-      const int64_t p = c * kRange + q;
-      load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? vv[q] : 0u, lane, rows[q]);
+      for (int q = 0; q < kRange; ++q) {
+        const int64_t p = c * kRange + q;
+        load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? vv[q] : 0u, lane, rows[q]);
+      }
+      if (c + G <= c1) load_vals(a.vals, (c + G) * kRange, vv);
+#pragma unroll
+      for (int q = 0; q < kRange; ++q) {
+        const int64_t p = c * kRange + q;
+        add_quads_if<Q>(acc, rows[q], p >= start && p < stop);
+      }
     }
-    if (c + G <= c1) load_vals(a.vals, (c + G) * kRange, vv);  // the next range's indices
+  } else {
+    // wide rows: batches of kRange / Q rows, one batch at a time (a loop the
+    // compiler keeps rolled, so it cannot hoist every batch's loads at once)
+    constexpr int B = kRange / Q > 0 ? kRange / Q : 1;
+#pragma unroll 1
+    for (int64_t p0 = (c0 + g) * kRange; p0 <= c1 * kRange; p0 += (int64_t)G * kRange) {
+#pragma unroll 1
+      for (int b0 = 0; b0 < kRange; b0 += B) {
+        uint32_t idx[B];
 #pragma unroll
-    for (int q = 0; q < kRange; ++q) {
-      const int64_t p = c * kRange + q;
-      add_quads_if<Q>(acc, rows[q], p >= start && p < stop);
+        for (int qq = 0; qq < B; ++qq) idx[qq] = a.vals[p0 + b0 + qq];
+        uint2 rows[B][Q];
+#pragma unroll
+        for (int qq = 0; qq < B; ++qq) {
+          const int64_t p = p0 + b0 + qq;
+          load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? idx[qq] : 0u, lane, rows[qq]);
+        }
+#pragma unroll
+        for (int qq = 0; qq < B; ++qq) {
+          const int64_t p = p0 + b0 + qq;
+          add_quads_if<Q>(acc, rows[qq], p >= start && p < stop);
+        }
+      }
     }
   }
   // walker 0 adds the other walkers' sums in walker order
@@ -693,7 +763,7 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
         for (int e = 0; e < 4; ++e) acc[k][e] += s_part[h][lane * 4 + e];
     __syncthreads();
   }
-  if (g == 0) emit_row<L, Q, SPARSE>(key, u, a, lane, acc);
+  if (g == 0) emit_row<L, Q, OUT>(key, u, a, lane, acc, tw);
 }
 
 // Long runs (hot rows, longer than a range).  Block b checks which of the
@@ -704,7 +774,7 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
 // range ahead, its rows all in flight), and walker 0 adds the walkers' sums
 // in walker order before writing the row.  Fixed assignment and fixed order keep the result
 // deterministic.
-template <int L, int Q, bool SPARSE, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT>
 __device__ __forceinline__ void long_runs(const WalkArgs &a) {
   __shared__ double s_part[kWalkThreads / L][L * 4];
   __shared__ uint32_t s_list[kWalkThreads];
@@ -733,20 +803,21 @@ __device__ __forceinline__ void long_runs(const WalkArgs &a) {
     }
     if (flagged) s_list[at] = (uint32_t)r;
     __syncthreads();
-    for (int i = 0; i < count; ++i) long_run<L, Q, SPARSE, EXACT>(a, s_list[i], s_part);
+    for (int i = 0; i < count; ++i) long_run<L, Q, OUT, EXACT>(a, s_list[i], s_part);
     __syncthreads();  // s_list and s_wave_count are rewritten for the next stretch
   }
 }
 
 // The apply kernel: blocks [0, long_blocks) sum the long runs, the rest are
 // range walkers, kWalkThreads / L walkers per block.
-template <int L, int Q, bool SPARSE, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT>
 __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
-  if (SPARSE && blockIdx.x == 0 && threadIdx.x == 0) *a.num_unique = (int64_t)*a.unique_total;
+  if (OUT == kOutSparse && blockIdx.x == 0 && threadIdx.x == 0)
+    *a.num_unique = (int64_t)*a.unique_total;
   if (blockIdx.x < a.long_blocks)
-    long_runs<L, Q, SPARSE, EXACT>(a);
+    long_runs<L, Q, OUT, EXACT>(a);
   else
-    walk_range<L, Q, SPARSE, EXACT>(a, (int64_t)blockIdx.x - a.long_blocks);
+    walk_range<L, Q, OUT, EXACT>(a, (int64_t)blockIdx.x - a.long_blocks);
 }
 
 __global__ void write_zero_kernel(int64_t *p) { *p = 0; }
@@ -844,16 +915,16 @@ inline bool sorted_limits_ok(int64_t n, int64_t table_rows) {
   return table_rows < (int64_t)UINT32_MAX && n < (int64_t)UINT32_MAX;
 }
 
-template <int L, int Q, bool SPARSE>
+template <int L, int Q, int OUT>
 void launch_walkers(const WalkArgs &a, hipStream_t s) {
   const int64_t threads = a.num_ranges * L;
   const unsigned blocks =
       a.long_blocks + (unsigned)((threads + kWalkThreads - 1) / kWalkThreads);
   if (a.quads == (int64_t)Q * L)
-    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, SPARSE, true>), dim3(blocks),
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, true>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, SPARSE, false>), dim3(blocks),
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, false>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
 }
 
@@ -861,18 +932,18 @@ void launch_walkers(const WalkArgs &a, hipStream_t s) {
 // wavefront (head_dim 256: one 64-lane walker per wavefront, each load
 // instruction one 512-byte bf16 row, each store one 1 KB fp32 row); wider
 // rows give each lane 2, 4 or 8 quads.
-template <bool SPARSE>
+template <int OUT>
 void dispatch_walkers(const WalkArgs &a, hipStream_t s) {
   const int64_t q = a.quads;
-  if (q <= 2) launch_walkers<2, 1, SPARSE>(a, s);
-  else if (q <= 4) launch_walkers<4, 1, SPARSE>(a, s);
-  else if (q <= 8) launch_walkers<8, 1, SPARSE>(a, s);
-  else if (q <= 16) launch_walkers<16, 1, SPARSE>(a, s);
-  else if (q <= 32) launch_walkers<32, 1, SPARSE>(a, s);
-  else if (q <= 64) launch_walkers<64, 1, SPARSE>(a, s);
-  else if (q <= 128) launch_walkers<64, 2, SPARSE>(a, s);
-  else if (q <= 256) launch_walkers<64, 4, SPARSE>(a, s);
-  else launch_walkers<64, 8, SPARSE>(a, s);
+  if (q <= 2) launch_walkers<2, 1, OUT>(a, s);
+  else if (q <= 4) launch_walkers<4, 1, OUT>(a, s);
+  else if (q <= 8) launch_walkers<8, 1, OUT>(a, s);
+  else if (q <= 16) launch_walkers<16, 1, OUT>(a, s);
+  else if (q <= 32) launch_walkers<32, 1, OUT>(a, s);
+  else if (q <= 64) launch_walkers<64, 1, OUT>(a, s);
+  else if (q <= 128) launch_walkers<64, 2, OUT>(a, s);
+  else if (q <= 256) launch_walkers<64, 4, OUT>(a, s);
+  else launch_walkers<64, 8, OUT>(a, s);
 }
 
 // Workspace views shared by the plan and the apply.
@@ -944,10 +1015,20 @@ int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p
   return launch_status();
 }
 
+// Outputs of an apply; the ones the output mode does not use are null.
+struct ApplyOut {
+  int mode;  // kOutDense, kOutSparse or kOutSignSGD
+  float *grad_table;
+  int64_t *unique_ids;
+  float *unique_grads;
+  int64_t *num_unique;
+  void *table;  // bf16
+  float lr;
+};
+
 // Apply: the per-row sums of one gradient tensor, given the plan of its ids.
 int apply_sorted(const void *grads, int64_t n, int64_t dim, int64_t table_rows, const Plan &p,
-                 void *ws, bool sparse, float *grad_table, int64_t *unique_ids,
-                 float *unique_grads, int64_t *num_unique, hipStream_t s) {
+                 void *ws, const ApplyOut &o, hipStream_t s) {
   const Views v = views_of(p, ws);
   WalkArgs a;
   a.keys = v.sorted_keys;
@@ -959,9 +1040,11 @@ int apply_sorted(const void *grads, int64_t n, int64_t dim, int64_t table_rows, 
   a.dim = dim;
   a.head_off = v.head_off;
   a.num_ranges = p.num_ranges;
-  a.grad_table = grad_table;
-  a.unique_ids = unique_ids;
-  a.unique_grads = unique_grads;
+  a.grad_table = o.grad_table;
+  a.unique_ids = o.unique_ids;
+  a.unique_grads = o.unique_grads;
+  a.table = static_cast<uint2 *>(o.table);
+  a.lr = o.lr;
   // long-run blocks: at most kLongBlocks, each looking after at least
   // kLongSpan ranges (a long run spans 3 ranges or more)
   int64_t lb = p.num_ranges >= 3 ? (p.num_ranges + kLongSpan - 1) / kLongSpan : 0;
@@ -969,11 +1052,13 @@ int apply_sorted(const void *grads, int64_t n, int64_t dim, int64_t table_rows, 
   a.long_blocks = (uint32_t)lb;
   a.long_span = lb > 0 ? (p.num_ranges + lb - 1) / lb : 0;
   a.unique_total = v.scalars;
-  a.num_unique = num_unique;
-  if (sparse)
-    dispatch_walkers<true>(a, s);
+  a.num_unique = o.num_unique;
+  if (o.mode == kOutSparse)
+    dispatch_walkers<kOutSparse>(a, s);
+  else if (o.mode == kOutDense)
+    dispatch_walkers<kOutDense>(a, s);
   else
-    dispatch_walkers<false>(a, s);
+    dispatch_walkers<kOutSignSGD>(a, s);
   return launch_status();
 }
 
@@ -1074,8 +1159,9 @@ extern "C" int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head
       (sparse && !aligned16(d_unique_grads)))
     return ENGRAM_EALIGN;
   if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
-  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, sparse, d_grad_table,
-                      d_unique_ids, d_unique_grads, d_num_unique, s);
+  const ApplyOut o = {sparse ? kOutSparse : kOutDense, d_grad_table, d_unique_ids,
+                      d_unique_grads, d_num_unique, nullptr, 0.0f};
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, o, s);
 }
 
 extern "C" int engram_scatter_add(const int64_t *d_row_ids, int64_t n, const void *d_grads,
@@ -1098,8 +1184,8 @@ extern "C" int engram_scatter_add(const int64_t *d_row_ids, int64_t n, const voi
   if (rc != ENGRAM_OK) return rc;
   if ((rc = plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, s)) != ENGRAM_OK)
     return rc;
-  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, false, d_grad_table,
-                      nullptr, nullptr, nullptr, s);
+  const ApplyOut o = {kOutDense, d_grad_table, nullptr, nullptr, nullptr, nullptr, 0.0f};
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, o, s);
 }
 
 extern "C" int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
@@ -1124,6 +1210,22 @@ extern "C" int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
   if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
   if ((rc = plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, s)) != ENGRAM_OK)
     return rc;
-  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, true, nullptr,
-                      d_unique_ids, d_unique_grads, d_num_unique, s);
+  const ApplyOut o = {kOutSparse, nullptr, d_unique_ids, d_unique_grads, d_num_unique, nullptr,
+                      0.0f};
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, o, s);
+}
+
+extern "C" int engram_scatter_apply_signsgd(const void *d_grads, int64_t n, int64_t head_dim,
+                                            int64_t table_rows, void *d_table, float lr,
+                                            void *d_workspace, size_t workspace_bytes,
+                                            void *stream) {
+  Plan p;
+  int rc = check_sorted(n, table_rows, head_dim, &p);
+  if (rc != ENGRAM_OK) return rc;
+  if (n == 0) return ENGRAM_OK;
+  if (d_grads == nullptr || d_table == nullptr) return ENGRAM_EINVAL;
+  if (!aligned16(d_grads) || !aligned16(d_table)) return ENGRAM_EALIGN;
+  if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
+  const ApplyOut o = {kOutSignSGD, nullptr, nullptr, nullptr, nullptr, d_table, lr};
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, o, as_stream(stream));
 }

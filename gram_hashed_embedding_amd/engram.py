@@ -73,6 +73,13 @@ _lib.engram_scatter_plan.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes
 _lib.engram_scatter_apply.restype = ctypes.c_int
 _lib.engram_scatter_apply.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
                                       _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.engram_signsgd_rowsparse.restype = ctypes.c_int
+_lib.engram_signsgd_rowsparse.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
+                                          ctypes.c_int64, ctypes.c_float, _vp, _vp]
+_lib.engram_scatter_apply_signsgd.restype = ctypes.c_int
+_lib.engram_scatter_apply_signsgd.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_int64, _vp, ctypes.c_float, _vp,
+                                              ctypes.c_size_t, _vp]
 
 
 class EngramError(RuntimeError):
@@ -356,3 +363,47 @@ def engram_scatter_apply(grads, workspace, table_rows, grad_table=None, unique_i
     if grad_table is not None:
         return grad_table
     return unique_ids, unique_grads, num_unique
+
+
+def engram_signsgd_rowsparse(unique_ids, unique_grads, num_unique, table, lr, err_count=None,
+                             stream=None):
+    """SignSGD on the rows a row-sparse gradient lists, in place on the bf16
+    table [rows, head_dim]; num_unique is the device count U."""
+    _device_tensor(unique_ids, torch.int64, "unique_ids")
+    _device_tensor(unique_grads, torch.float32, "unique_grads")
+    _device_tensor(num_unique, torch.int64, "num_unique")
+    _device_tensor(table, torch.bfloat16, "table")
+    if table.dim() != 2:
+        raise ValueError("table must be [rows, head_dim]")
+    rows, dim = table.shape
+    cap = unique_ids.numel()
+    if unique_grads.numel() != cap * dim:
+        raise ValueError("unique_grads must be [capacity, head_dim]")
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
+    with torch.cuda.device(table.device):
+        status = _lib.engram_signsgd_rowsparse(_ptr(unique_ids), _ptr(unique_grads),
+                                               _ptr(num_unique), cap, dim, _ptr(table), rows,
+                                               float(lr), _ptr(err_count),
+                                               _stream(table.device, stream))
+    _check(status, "engram_signsgd_rowsparse")
+    return table
+
+
+def engram_scatter_apply_signsgd(grads, workspace, table, lr, stream=None):
+    """The planned backward of bf16 grads [n, head_dim] fused with one
+    SignSGD step on the bf16 table (in place)."""
+    _device_tensor(grads, torch.bfloat16, "grads")
+    _device_tensor(workspace, torch.uint8, "workspace")
+    _device_tensor(table, torch.bfloat16, "table")
+    rows, dim = table.shape
+    n = grads.numel() // dim
+    if grads.numel() != n * dim:
+        raise ValueError("grads must be [n, head_dim] with the table's head_dim")
+    with torch.cuda.device(table.device):
+        status = _lib.engram_scatter_apply_signsgd(_ptr(grads), n, dim, rows, _ptr(table),
+                                                   float(lr), _ptr(workspace),
+                                                   workspace.numel(),
+                                                   _stream(table.device, stream))
+    _check(status, "engram_scatter_apply_signsgd")
+    return table

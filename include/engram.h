@@ -234,6 +234,50 @@ int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
                          float *d_unique_grads, int64_t *d_num_unique, void *d_workspace,
                          size_t workspace_bytes, void *stream);
 
+/*
+ * engram_signsgd_rowsparse -- one SignSGD step on the rows a row-sparse
+ * gradient lists: for u < *d_num_unique (read on the device; at most
+ * capacity) and r = d_unique_ids[u] in [0, table_rows), every element of
+ * row r of the bf16 table becomes
+ *     bf16( fp32(w) - lr * sign(d_unique_grads[u, e]) )
+ * (the subtraction in fp32, sign(0) = 0, one rounding to bf16 to nearest
+ * with ties to even).  Rows not listed keep their values.
+ *
+ * Follows [PR1] Validation and [PR2] Validation (the RL runs trained with
+ * SignSGD, learning rate 1e-6, FP32 optimizer defaults); the pages give no
+ * formula, and the one above is the reading taken.
+ *   d_unique_ids int64 [capacity], distinct (as engram_scatter_add_rowsparse
+ *   writes them; a repeated id would be updated twice, in no fixed order);
+ *   d_unique_grads fp32 [capacity, head_dim]; d_num_unique int64 [1];
+ *   d_table bf16 [table_rows, head_dim], updated in place.  head_dim a
+ *   positive multiple of 8; d_unique_grads and d_table 16-byte aligned.
+ *   Ids of -1 are skipped; other ids outside the table are skipped and
+ *   counted in *d_err_count (when not NULL).
+ * Errors: EINVAL, EALIGN.  capacity == 0 enqueues nothing.
+ */
+int engram_signsgd_rowsparse(const int64_t *d_unique_ids, const float *d_unique_grads,
+                             const int64_t *d_num_unique, int64_t capacity,
+                             int64_t head_dim, void *d_table, int64_t table_rows,
+                             float lr, int64_t *d_err_count, void *stream);
+
+/*
+ * engram_scatter_apply_signsgd -- the backward and the SignSGD step in one
+ * pass: for every distinct valid row r of the planned ids, with S_r the
+ * fp32 sum engram_scatter_apply would produce (summed in fp64, rounded once),
+ *     d_table[r, e] = bf16( fp32(d_table[r, e]) - lr * sign(S_r[e]) ).
+ * The same result as engram_scatter_apply (row-sparse) followed by
+ * engram_signsgd_rowsparse, without writing or reading the fp32 sums.
+ * Citations as for those two calls.
+ *   d_grads bf16 [n, head_dim]; d_table bf16 [table_rows, head_dim], updated
+ *   in place; lr the learning rate; the workspace holds a plan of the n ids
+ *   made by engram_scatter_plan (same n, head_dim and table_rows), ordered
+ *   before this call.  d_grads and d_table 16-byte aligned.
+ * Errors: EINVAL, EALIGN, EWORKSPACE.  n == 0 enqueues nothing.
+ */
+int engram_scatter_apply_signsgd(const void *d_grads, int64_t n, int64_t head_dim,
+                                 int64_t table_rows, void *d_table, float lr,
+                                 void *d_workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,7 +23,8 @@ def test_every_declared_symbol_is_exported():
                           "engram_gather", "engram_scatter_add_workspace",
                           "engram_scatter_add", "engram_scatter_add_rowsparse",
                           "engram_scatter_plan", "engram_scatter_apply",
-                          "engram_hash_slice"}
+                          "engram_hash_slice", "engram_signsgd_rowsparse",
+                          "engram_scatter_apply_signsgd"}
     for name in names:
         assert hasattr(e._lib, name), name
 
@@ -156,3 +157,20 @@ def test_hash_slice_rejects():
     assert call(3, 3, tokens=None, out=None) == e.ENGRAM_OK   # empty slice: no launch
     assert call(0, 8, batch=0, tokens=None, out=None) == e.ENGRAM_OK
     assert call(0, 4, tokens=None) == e.ENGRAM_EINVAL
+
+
+def test_signsgd_rejects():
+    sg = e._lib.engram_signsgd_rowsparse
+    assert sg(ALIGNED, ALIGNED, ALIGNED, 10, 12, ALIGNED, 50, 0.1, None, None) == e.ENGRAM_EINVAL
+    assert sg(ALIGNED, ALIGNED, ALIGNED, -1, 8, ALIGNED, 50, 0.1, None, None) == e.ENGRAM_EINVAL
+    assert sg(None, ALIGNED, ALIGNED, 10, 8, ALIGNED, 50, 0.1, None, None) == e.ENGRAM_EINVAL
+    assert sg(ALIGNED, MISALIGNED, ALIGNED, 10, 8, ALIGNED, 50, 0.1, None, None) == e.ENGRAM_EALIGN
+    assert sg(ALIGNED, ALIGNED, ALIGNED, 10, 8, MISALIGNED, 50, 0.1, None, None) == e.ENGRAM_EALIGN
+    assert sg(None, None, None, 0, 8, None, 50, 0.1, None, None) == e.ENGRAM_OK
+    ap = e._lib.engram_scatter_apply_signsgd
+    ws = e.engram_scatter_add_workspace(100, 50, 8, 2)
+    assert ap(ALIGNED, 100, 12, 50, ALIGNED, 0.1, ALIGNED, ws, None) == e.ENGRAM_EINVAL
+    assert ap(ALIGNED, 100, 8, 50, None, 0.1, ALIGNED, ws, None) == e.ENGRAM_EINVAL
+    assert ap(ALIGNED, 100, 8, 50, MISALIGNED, 0.1, ALIGNED, ws, None) == e.ENGRAM_EALIGN
+    assert ap(ALIGNED, 100, 8, 50, ALIGNED, 0.1, ALIGNED, 16, None) == e.ENGRAM_EWORKSPACE
+    assert ap(None, 0, 8, 50, None, 0.1, None, 0, None) == e.ENGRAM_OK

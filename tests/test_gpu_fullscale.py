@@ -102,5 +102,21 @@ def test_e2e_forward_backward(oracle):
     assert 0.5 * wl.lookups < u < wl.lookups
     assert np.array_equal(uid[:u].cpu().numpy(), want_uid)
     assert np.array_equal(host_f32(uval[:u]).view(np.uint32), want_val.view(np.uint32))
-    del grads, uid, uval
+    del uid, uval
+    release()
+
+    # the backward fused with one SignSGD step on the 102.4 GB table: every
+    # touched row against the oracle's step on a host copy of those rows
+    lr = 2.0 ** -6
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
+    touched = dev(want_uid)
+    before = bits(table.index_select(0, touched))
+    want_rows, bad = oracle.signsgd_rowsparse(np.arange(u, dtype=np.int64), want_val, before, lr)
+    assert bad == 0
+    ws = E.engram_scatter_plan(rows.view(-1), wl.table_rows, wl.dim)
+    E.engram_scatter_apply_signsgd(grads, ws, table, lr)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(table.index_select(0, touched)), want_rows)
+    assert not np.array_equal(want_rows, before)
+    del grads, table, ws
     release()

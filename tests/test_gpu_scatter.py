@@ -73,6 +73,26 @@ def check_all_modes(oracle, ids, dim, rows, seed, base_std=1.0):
     assert np.array_equal(uid, want_uid)
     assert np.array_equal(uval.view(np.uint32), want_val.view(np.uint32))
 
+    check_signsgd(oracle, ids, grads, want_uid, want_val, dim, rows, seed)
+
+
+def check_signsgd(oracle, ids, grads, want_uid, want_val, dim, rows, seed, lr=2.0 ** -6):
+    """The SignSGD step on a bf16 N(0, 0.02) table, fused into the apply and
+    standalone on the row-sparse output, against the oracle bit for bit."""
+    table0 = workloads.make_table(rows, dim, seed + 5, "cuda")
+    want_t, _ = oracle.signsgd_rowsparse(want_uid, want_val, bits(table0), lr)
+    fused = table0.clone()
+    ws = E.engram_scatter_plan(dev(ids), rows, dim)
+    E.engram_scatter_apply_signsgd(grads, ws, fused, lr)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(fused), want_t)
+    del fused
+    two_step = table0.clone()
+    uid_d, uval_d, cnt_d = E.engram_scatter_add_rowsparse(dev(ids), grads, rows)
+    E.engram_signsgd_rowsparse(uid_d, uval_d, cnt_d, two_step, lr)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(two_step), want_t)
+
 
 def test_tiny_workload(oracle):
     wl = workloads.tiny()
@@ -243,3 +263,34 @@ def test_plan_on_side_stream(oracle):
     want_uid, want_val, _ = oracle.scatter_add_rowsparse(ids, bits(grads), wl.dim, wl.table_rows)
     assert np.array_equal(uid[:n].cpu().numpy(), want_uid)
     assert np.array_equal(host_f32(uval[:n]).view(np.uint32), want_val.view(np.uint32))
+
+
+@pytest.mark.parametrize("dim", [8, 24, 256])
+@pytest.mark.parametrize("lr", [1e-6, 2.0 ** -8, 0.3])
+def test_signsgd_standalone(oracle, dim, lr):
+    """Given row-sparse input: fewer rows than the capacity, padding and
+    out-of-range ids (skipped and counted), zero gradients (sign 0)."""
+    rows, cap, u = 3000, 700, 611
+    rng = np.random.Generator(np.random.PCG64(dim))
+    ids = rng.choice(rows, cap, replace=False).astype(np.int64)
+    ids[[3, 50]] = -1
+    ids[[7, 400, 610]] = [rows, rows + 5, -9]
+    ids[650] = 5        # past U: never read
+    g = rng.normal(0, 1, (cap, dim)).astype(np.float32)
+    g[rng.random((cap, dim)) < 0.2] = 0.0
+    table = workloads.make_table(rows, dim, dim + 1, "cuda")
+    want, bad = oracle.signsgd_rowsparse(ids[:u], g[:u], bits(table), lr)
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    count = torch.tensor([u], dtype=torch.int64, device="cuda")
+    E.engram_signsgd_rowsparse(dev(ids), dev(g), count, table, lr, err_count=err)
+    torch.cuda.synchronize()
+    assert bad == 3 and int(err.item()) == bad
+    assert np.array_equal(bits(table), want)
+
+
+def test_signsgd_rejects():
+    t = torch.zeros((10, 12), dtype=torch.bfloat16, device="cuda")   # 12 is not a multiple of 8
+    ids = torch.zeros(4, dtype=torch.int64, device="cuda")
+    with pytest.raises(E.EngramError):
+        E.engram_signsgd_rowsparse(ids, torch.zeros((4, 12), device="cuda"),
+                                   torch.zeros(1, dtype=torch.int64, device="cuda"), t, 0.1)
