@@ -373,3 +373,61 @@ int64_t oracle_signsgd_rowsparse(const int64_t *unique_ids, const float *unique_
     }
     return bad;
 }
+
+/* ---------------------------------------------------------------------- */
+/* PLE causal depthwise convolution with per-segment zero history.         */
+/* [API] Qwen3_8_FlashNextPLELayer: _causal_short_conv (a causal depthwise */
+/* convolution over [batch, sequence, channels] with zeros as the history  */
+/* on the left), _segmented_conv (every packed segment is convolved as if  */
+/* it began a fresh row: zeros ahead of it, its own convolution, so no tap */
+/* reads another segment), constructor conv_kernel_size (4) and the        */
+/* attribute short_conv_dilation (= ngram_size).  Under context            */
+/* parallelism the layer receives the preceding (K - 1) * dilation         */
+/* positions from the previous rank; `halo` holds them (NULL: none).       */
+/* Readings (the pages do not fix them): the taps follow F.conv1d, so      */
+/*     out[t, c] = bias[c] + sum_k w[c, k] * x[t - (K - 1 - k) * dilation, c]*/
+/* a tap reads 0 before the (halo-extended) row start or across a change   */
+/* of segment id between it and t; bf16 data, the sum accumulated in fp32  */
+/* from the bias in tap order k = 0 .. K-1, rounded once to bf16 (nearest, */
+/* ties to even).                                                          */
+/* Layout: x, out bf16 [batch, seq, channels]; halo bf16                   */
+/* [batch, halo_len, channels]; seq_ids int64 [batch, halo_len + seq]      */
+/* (covering the halo first); weight bf16 [channels, K]; bias bf16         */
+/* [channels] or NULL.  Returns 0, or -1 on an invalid argument.           */
+/* ---------------------------------------------------------------------- */
+int oracle_ple_conv(const uint16_t *x, const uint16_t *halo, int64_t halo_len,
+                    const int64_t *seq_ids, const uint16_t *weight, const uint16_t *bias,
+                    int64_t batch, int64_t seq, int64_t channels, int kernel_size,
+                    int dilation, uint16_t *out)
+{
+    if (kernel_size < 1 || dilation < 1 || halo_len < 0 || (halo_len > 0 && halo == NULL))
+        return -1;
+    const int64_t len = halo_len + seq;          /* positions of the extended row */
+    for (int64_t b = 0; b < batch; ++b) {
+        const int64_t *seg = seq_ids ? seq_ids + b * len : NULL;
+        for (int64_t t = 0; t < seq; ++t) {
+            const int64_t pos = halo_len + t;    /* t in the extended row */
+            for (int64_t c = 0; c < channels; ++c) {
+                float acc = bias ? bf16_bits_to_float(bias[c]) : 0.0f;
+                for (int k = 0; k < kernel_size; ++k) {
+                    const int64_t p = pos - (int64_t)(kernel_size - 1 - k) * dilation;
+                    int inside = p >= 0;
+                    /* the tap's segment must reach from p to pos unbroken */
+                    for (int64_t j = p; inside && seg != NULL && j < pos; ++j)
+                        if (seg[j] != seg[j + 1])
+                            inside = 0;
+                    float v = 0.0f;
+                    if (inside)
+                        v = p < halo_len
+                                ? bf16_bits_to_float(halo[(b * halo_len + p) * channels + c])
+                                : bf16_bits_to_float(x[(b * seq + (p - halo_len)) * channels + c]);
+                    const float wk = bf16_bits_to_float(weight[c * kernel_size + k]);
+                    const float prod = wk * v;
+                    acc = acc + prod;
+                }
+                out[(b * seq + t) * channels + c] = float_to_bf16_bits(acc);
+            }
+        }
+    }
+    return 0;
+}

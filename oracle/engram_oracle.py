@@ -58,6 +58,10 @@ class Oracle:
         lib.oracle_scatter_add_rowsparse.argtypes = [_i64p, ctypes.c_int64, _u16p,
                                                      ctypes.c_int64, ctypes.c_int64,
                                                      _i64p, _f32p, _i64p]
+        lib.oracle_ple_conv.restype = ctypes.c_int
+        lib.oracle_ple_conv.argtypes = [_u16p, _u16p, ctypes.c_int64, _i64p, _u16p, _u16p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                        ctypes.c_int, ctypes.c_int, _u16p]
         lib.oracle_signsgd_rowsparse.restype = ctypes.c_int64
         lib.oracle_signsgd_rowsparse.argtypes = [_i64p, _f32p, ctypes.c_int64, ctypes.c_int64,
                                                  _u16p, ctypes.c_int64, ctypes.c_float]
@@ -161,6 +165,34 @@ class Oracle:
                                                  ids.size, dim, _ptr(table, _u16p), rows,
                                                  float(lr))
         return table, int(bad)
+
+
+    # -- PLE convolution ------------------------------------------------------
+    def ple_conv(self, x_bits, weight_bits, dilation, bias_bits=None, seq_ids=None,
+                 halo_bits=None):
+        """Causal depthwise conv with per-segment zero history: x uint16
+        (bf16 bits) [batch, seq, channels], weight [channels, K], bias
+        [channels] or None, seq_ids int64 [batch, halo + seq] or None, halo
+        [batch, halo, channels] or None; returns uint16 [batch, seq, channels]."""
+        x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        batch, seq, channels = x.shape
+        w = np.ascontiguousarray(weight_bits, dtype=np.uint16)
+        if w.ndim != 2 or w.shape[0] != channels:
+            raise ValueError("weight must be [channels, K]")
+        K = w.shape[1]
+        bias = None if bias_bits is None else np.ascontiguousarray(bias_bits, dtype=np.uint16)
+        halo = None if halo_bits is None else np.ascontiguousarray(halo_bits, dtype=np.uint16)
+        hl = 0 if halo is None else halo.shape[1]
+        seg = None if seq_ids is None else np.ascontiguousarray(seq_ids, dtype=np.int64)
+        if seg is not None and seg.shape != (batch, hl + seq):
+            raise ValueError("seq_ids must be [batch, halo + seq]")
+        out = np.empty_like(x)
+        rc = self._lib.oracle_ple_conv(_ptr(x, _u16p), _ptr(halo, _u16p), hl, _ptr(seg, _i64p),
+                                       _ptr(w, _u16p), _ptr(bias, _u16p), batch, seq, channels,
+                                       K, int(dilation), _ptr(out, _u16p))
+        if rc != 0:
+            raise ValueError("oracle_ple_conv rejected its arguments")
+        return out
 
 
 _default = None

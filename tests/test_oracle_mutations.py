@@ -15,6 +15,7 @@ from oracle import Oracle, build
 from oracle.engram_oracle import SOURCE
 from tests import test_oracle_hash as H
 from tests import test_oracle_lookup as L
+from tests import test_oracle_conv as CV
 from tests import test_oracle_signsgd as G
 from tests import test_oracle_slice as SL
 
@@ -48,6 +49,18 @@ MUTANTS = {
     "sgd_truncating_bf16": ("u += 0x7fffu + keep_odd;", "u += 0u * keep_odd;"),
     "sgd_ties_away": ("u += 0x7fffu + keep_odd;", "u += 0x8000u + 0u * keep_odd;"),
     "sgd_sign_of_zero_is_one": ("g < 0.0f ? -1.0f : 0.0f", "g < 0.0f ? -1.0f : 1.0f"),
+    "conv_taps_reversed": ("weight[c * kernel_size + k]",
+                           "weight[c * kernel_size + (kernel_size - 1 - k)]"),
+    "conv_dilation_off_by_one": ("(int64_t)(kernel_size - 1 - k) * dilation;",
+                                 "(int64_t)(kernel_size - 1 - k) * (dilation + 1);"),
+    "conv_ignores_segments": ("if (seg[j] != seg[j + 1])\n                            inside = 0;",
+                              "if (0)\n                            inside = 0;"),
+    "conv_drops_bias": ("float acc = bias ? bf16_bits_to_float(bias[c]) : 0.0f;",
+                        "float acc = 0.0f;"),
+    "conv_ignores_halo": ("? bf16_bits_to_float(halo[(b * halo_len + p) * channels + c])",
+                          "? 0.0f"),
+    "conv_not_causal": ("const int64_t p = pos - (int64_t)(kernel_size - 1 - k) * dilation;",
+                        "const int64_t p = pos - (int64_t)(kernel_size - 1 - k) * dilation + dilation;"),
 }
 
 # Every pin, called directly with the mutant in place of the oracle fixture.
@@ -72,6 +85,11 @@ PINS = [
     lambda o: G.test_hand_cases_and_ties(o),
     lambda o: G.test_unlisted_rows_and_invalid_ids(o),
     lambda o: [SL.test_slice_reads_history_across_the_boundary(o, c) for c in SL.SLICE_CASES],
+    lambda o: CV.test_matches_conv1d_on_exact_data(o, 4, 3, True),
+    lambda o: CV.test_segments_match_one_conv1d_per_segment(o),
+    lambda o: CV.test_impulse_response_spans_nine_positions(o),
+    lambda o: CV.test_halo_equals_joined_row(o, True),
+    lambda o: CV.test_rounding_ties_to_even(o),
 ]
 
 
