@@ -20,7 +20,11 @@ kernel, timed with HIP events on the stream it runs on.  The CPU baseline
 is the oracle on the host, timed on the same workload's lookups.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload e2e|e2e_signsgd|full|medium|backward|cp_slice]
+                    [--workload e2e|e2e_signsgd|full|medium|backward|cp_slice|ple_conv]
+
+--workload ple_conv times the PLE causal dilated depthwise convolution
+(engram_ple_conv) on bf16 [8, 8192, 8192] with packed-document segment ids,
+kernel 4, dilation 4 (the metric is then positions x channels per second).
 
 --workload e2e_signsgd is the e2e step with the optimizer: the apply is
 engram_scatter_apply_signsgd, which sums each distinct row's gradients and
@@ -220,13 +224,88 @@ def bench_cp_slice(args, torch, E, workloads, ranks=8):
     print(json.dumps(result), flush=True)
 
 
+def bench_ple_conv(args, torch, E, workloads):
+    """The PLE convolution over one batch of hidden states; a second pass
+    with the context-parallel halo (the preceding (K-1) * dilation rows)."""
+    wl = workloads.ple_conv()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    B, S, C, K, d = wl.batch, wl.seq, wl.channels, wl.kernel_size, wl.dilation
+    log(f"[bench] ple_conv: {wl.describe()}")
+    x = workloads.make_bf16((B, S, C), wl.seed, dev)
+    w = workloads.make_bf16((C, K), wl.seed + 1, dev, std=0.5)
+    bias = workloads.make_bf16((C,), wl.seed + 2, dev, std=0.5)
+    seg = torch.from_numpy(wl.segments()).to(dev)
+    H = wl.history
+    halo = workloads.make_bf16((B, H, C), wl.seed + 3, dev)
+    seg_h = torch.from_numpy(wl.segments(halo=H)).to(dev)
+    out = torch.empty_like(x)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / max(steps, 1)
+
+    plain = lambda: E.engram_ple_conv(x, w, d, bias=bias, seq_ids=seg, out=out)
+    with_halo = lambda: E.engram_ple_conv(x, w, d, bias=bias, seq_ids=seg_h, halo=halo, out=out)
+    timed(plain, 0, 20)       # bring the clocks up before either timing
+    timed(with_halo, 0, 20)
+    ms = timed(plain, args.steps, args.warmup)
+    ms_h = timed(with_halo, args.steps, args.warmup)
+    nbytes = 2 * B * S * C * 2 + 8 * B * S + 2 * C * (K + 1)
+    nbytes_h = nbytes + 2 * B * H * C + 8 * B * H
+    gbps, gbps_h = nbytes / (ms * 1e-3) / 1e9, nbytes_h / (ms_h * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import default_oracle
+        oracle = default_oracle()
+        xs = x[0:1, :, :256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        ws_ = w[:256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        bs = bias[:256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        sg = seg[0:1].cpu().numpy()
+        rates, start = [], time.perf_counter()
+        while len(rates) < 5 and (not rates or time.perf_counter() - start < 12.0):
+            c0 = time.perf_counter()
+            oracle.ple_conv(xs, ws_, d, bs, sg)
+            rates.append(S * 256 / (time.perf_counter() - c0))
+        cpu = {"value": float(np.median(rates)), "unit": "position-channels/s", "cores": 1,
+               "kind": "oracle",
+               "sample": f"one row x 256 channels ({S * 256} outputs), {len(rates)} runs, "
+                         "median; single-threaded C oracle"}
+    result = {
+        "metric": "PLE conv position-channels/s and achieved HBM GB/s (% of peak)",
+        "value": B * S * C / (ms * 1e-3), "unit": "position-channels/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**wl.describe(), "segments": "packed documents", "bias": True},
+        "algorithmic_bytes": nbytes, "gbps": gbps,
+        "with_cp_halo": {"halo_rows": H, "ms": ms_h, "algorithmic_bytes": nbytes_h,
+                         "gbps": gbps_h},
+        "roofline": {"bound": "hbm", "kernel": f"ple_conv_k4_kernel<{d}>", "achieved": gbps,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="e2e",
-                    choices=["e2e", "e2e_signsgd", "full", "medium", "backward", "cp_slice"])
+                    choices=["e2e", "e2e_signsgd", "full", "medium", "backward", "cp_slice",
+                             "ple_conv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -242,6 +321,8 @@ def main():
 
     if args.workload == "cp_slice":
         return bench_cp_slice(args, torch, E, workloads)
+    if args.workload == "ple_conv":
+        return bench_ple_conv(args, torch, E, workloads)
     signsgd = args.workload == "e2e_signsgd"
     lr = 1e-6  # the learning rate of the pages' SignSGD runs
     wl = workloads.get("e2e" if signsgd else args.workload)

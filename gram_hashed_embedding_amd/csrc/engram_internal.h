@@ -13,6 +13,7 @@ namespace engram {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // four bf16 values
 
 constexpr int kWave = 64;  // CDNA wavefront width
 

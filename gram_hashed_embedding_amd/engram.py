@@ -80,6 +80,10 @@ _lib.engram_scatter_apply_signsgd.restype = ctypes.c_int
 _lib.engram_scatter_apply_signsgd.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64,
                                               ctypes.c_int64, _vp, ctypes.c_float, _vp,
                                               ctypes.c_size_t, _vp]
+_lib.engram_ple_conv.restype = ctypes.c_int
+_lib.engram_ple_conv.argtypes = [_vp, _vp, ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64,
+                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                 _vp, _vp]
 
 
 class EngramError(RuntimeError):
@@ -407,3 +411,42 @@ def engram_scatter_apply_signsgd(grads, workspace, table, lr, stream=None):
                                                    _stream(table.device, stream))
     _check(status, "engram_scatter_apply_signsgd")
     return table
+
+
+def engram_ple_conv(x, weight, dilation, bias=None, seq_ids=None, halo=None, out=None,
+                    stream=None):
+    """Causal dilated depthwise conv of bf16 x [batch, seq, channels] with
+    weight [channels, K] (bf16), optional bias [channels], packed-segment ids
+    [batch, halo + seq] and a halo [batch, halo, channels] of preceding
+    positions; returns bf16 [batch, seq, channels]."""
+    _device_tensor(x, torch.bfloat16, "x")
+    _device_tensor(weight, torch.bfloat16, "weight")
+    if x.dim() != 3 or weight.dim() != 2 or weight.shape[0] != x.shape[2]:
+        raise ValueError("x must be [batch, seq, channels] and weight [channels, K]")
+    batch, seq, ch = x.shape
+    hl = 0
+    if halo is not None:
+        _device_tensor(halo, torch.bfloat16, "halo")
+        if halo.dim() != 3 or halo.shape[0] != batch or halo.shape[2] != ch:
+            raise ValueError("halo must be [batch, halo_len, channels]")
+        hl = halo.shape[1]
+    if bias is not None:
+        _device_tensor(bias, torch.bfloat16, "bias")
+        if bias.numel() != ch:
+            raise ValueError("bias must have one value per channel")
+    if seq_ids is not None:
+        _device_tensor(seq_ids, torch.int64, "seq_ids")
+        if tuple(seq_ids.shape) != (batch, hl + seq):
+            raise ValueError("seq_ids must be [batch, halo_len + seq]")
+    if out is None:
+        out = torch.empty_like(x)
+    _device_tensor(out, torch.bfloat16, "out")
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    with torch.cuda.device(x.device):
+        status = _lib.engram_ple_conv(_ptr(x), _ptr(halo), hl, _ptr(seq_ids), _ptr(weight),
+                                      _ptr(bias), batch, seq, ch, weight.shape[1],
+                                      int(dilation), _ptr(out), _stream(x.device, stream))
+    _check(status, "engram_ple_conv")
+    return out
+

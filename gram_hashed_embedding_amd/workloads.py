@@ -312,3 +312,55 @@ def make_grad_table(rows: int, dim: int, seed: Optional[int], device,
     for start in range(0, rows, chunk_rows):
         t[start:start + chunk_rows].normal_(0.0, 1.0, generator=gen)
     return t
+
+
+# ---------------------------------------------------------------------------
+# the PLE convolution's workload
+# ---------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class ConvWorkload:
+    """Inputs of the PLE causal depthwise convolution.  The pages print no
+    model widths: channels = hc_count * hidden_size is taken as 4 * 2048, a
+    stand-in; kernel 4 and dilation = ngram_size follow the API page (the
+    e2e workload's ngram_size is 4).  Rows are packed documents as in the
+    full-scale workload (segment ids = document index)."""
+    name: str
+    batch: int
+    seq: int
+    channels: int
+    kernel_size: int
+    dilation: int
+    seed: int
+
+    @property
+    def history(self) -> int:
+        return (self.kernel_size - 1) * self.dilation
+
+    def segments(self, variant: int = 0, halo: int = 0) -> np.ndarray:
+        """Segment ids int64 [batch, halo + seq]."""
+        rng = np.random.Generator(np.random.PCG64([self.seed, 77, variant]))
+        _, seg = packed_documents(rng, self.batch, halo + self.seq, 1.1)
+        return seg
+
+    def describe(self) -> dict:
+        return {"workload": self.name, "batch": self.batch, "seq": self.seq,
+                "channels": self.channels, "kernel_size": self.kernel_size,
+                "dilation": self.dilation, "seed": self.seed}
+
+
+def ple_conv() -> ConvWorkload:
+    return ConvWorkload("ple_conv", batch=8, seq=8192, channels=8192, kernel_size=4,
+                        dilation=4, seed=1006)
+
+
+def make_bf16(shape, seed: int, device, std: float = 1.0):
+    """bf16 tensor of the given shape ~ N(0, std), from a seeded generator."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    t = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = t.view(-1)
+    step = 1 << 26
+    for start in range(0, flat.numel(), step):
+        flat[start:start + step].normal_(0.0, std, generator=gen)
+    return t

@@ -278,6 +278,39 @@ int engram_scatter_apply_signsgd(const void *d_grads, int64_t n, int64_t head_di
                                  int64_t table_rows, void *d_table, float lr,
                                  void *d_workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * engram_ple_conv -- the PLE causal dilated depthwise convolution with zero
+ * history per packed segment:
+ *     out[b, t, c] = bias[c] + sum_{k < K} w[c, k] * x[b, t - (K-1-k)*dilation, c]
+ * where a tap reads 0 before the start of the row (the row starts halo_len
+ * positions before x when a halo is given) and when the segment id changes
+ * between the tap's position and t.  The sum is accumulated in fp32 from the
+ * bias in tap order and rounded once to bf16 (nearest, ties to even).
+ *
+ * Follows [API] Qwen3_8_FlashNextPLELayer: _causal_short_conv (causal
+ * depthwise convolution with zeros as the left history; under context
+ * parallelism the preceding (K - 1) * dilation positions come from the
+ * previous rank), _segmented_conv (every packed segment convolved as if it
+ * began a row), conv_kernel_size (4) and short_conv_dilation (= ngram_size).
+ * The tap order (F.conv1d's), fp32 accumulation and the rounding are
+ * readings; the pages do not fix them.
+ *   d_x bf16 [batch, seq, channels]; d_out bf16 [batch, seq, channels],
+ *   written (must not overlap d_x).
+ *   d_halo bf16 [batch, halo_len, channels] (the positions just before x),
+ *   or NULL with halo_len 0.
+ *   d_seq_ids int64 [batch, halo_len + seq] (covering the halo first), or
+ *   NULL (no packed segments).
+ *   d_weight bf16 [channels, kernel_size]; d_bias bf16 [channels] or NULL.
+ *   channels a positive multiple of 8; kernel_size 1..16; dilation >= 1;
+ *   d_x, d_halo and d_out 16-byte aligned.  kernel_size 4 with dilation up
+ *   to 8 runs the tiled kernel; other shapes a plain one.
+ * Errors: EINVAL, EALIGN.  batch * seq == 0 enqueues nothing.
+ */
+int engram_ple_conv(const void *d_x, const void *d_halo, int64_t halo_len,
+                    const int64_t *d_seq_ids, const void *d_weight, const void *d_bias,
+                    int64_t batch, int64_t seq, int64_t channels, int32_t kernel_size,
+                    int32_t dilation, void *d_out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

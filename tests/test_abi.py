@@ -24,7 +24,7 @@ def test_every_declared_symbol_is_exported():
                           "engram_scatter_add", "engram_scatter_add_rowsparse",
                           "engram_scatter_plan", "engram_scatter_apply",
                           "engram_hash_slice", "engram_signsgd_rowsparse",
-                          "engram_scatter_apply_signsgd"}
+                          "engram_scatter_apply_signsgd", "engram_ple_conv"}
     for name in names:
         assert hasattr(e._lib, name), name
 
@@ -174,3 +174,20 @@ def test_signsgd_rejects():
     assert ap(ALIGNED, 100, 8, 50, MISALIGNED, 0.1, ALIGNED, ws, None) == e.ENGRAM_EALIGN
     assert ap(ALIGNED, 100, 8, 50, ALIGNED, 0.1, ALIGNED, 16, None) == e.ENGRAM_EWORKSPACE
     assert ap(None, 0, 8, 50, None, 0.1, None, 0, None) == e.ENGRAM_OK
+
+
+def test_ple_conv_rejects():
+    cv = e._lib.engram_ple_conv
+    def call(halo=None, halo_len=0, batch=2, seq=16, ch=16, K=4, d=3, x=ALIGNED, out=ALIGNED):
+        return cv(x, halo, halo_len, None, ALIGNED, None, batch, seq, ch, K, d, out, None)
+    assert call(ch=12) == e.ENGRAM_EINVAL          # channels % 8
+    assert call(ch=0) == e.ENGRAM_EINVAL
+    assert call(K=0) == e.ENGRAM_EINVAL
+    assert call(K=17) == e.ENGRAM_EINVAL
+    assert call(d=0) == e.ENGRAM_EINVAL
+    assert call(halo_len=9) == e.ENGRAM_EINVAL     # a halo length without a halo
+    assert call(halo_len=-1) == e.ENGRAM_EINVAL
+    assert call(x=None) == e.ENGRAM_EINVAL
+    assert call(x=MISALIGNED) == e.ENGRAM_EALIGN
+    assert call(halo=MISALIGNED, halo_len=9) == e.ENGRAM_EALIGN
+    assert call(seq=0, x=None, out=None) == e.ENGRAM_OK
