@@ -319,7 +319,7 @@ def make_grad_table(rows: int, dim: int, seed: Optional[int], device,
 # ---------------------------------------------------------------------------
 @dataclasses.dataclass(frozen=True)
 class ConvWorkload:
-    """Inputs of the PLE causal depthwise convolution.  The pages print no
+    """Inputs of the causal depthwise PLE convolution.  The pages print no
     model widths: channels = hc_count * hidden_size is taken as 4 * 2048, a
     stand-in; kernel 4 and dilation = ngram_size follow the API page (the
     e2e workload's ngram_size is 4).  Rows are packed documents as in the

@@ -375,7 +375,7 @@ int64_t oracle_signsgd_rowsparse(const int64_t *unique_ids, const float *unique_
 }
 
 /* ---------------------------------------------------------------------- */
-/* PLE causal depthwise convolution with per-segment zero history.         */
+/* Causal depthwise PLE convolution, zero history per packed segment.     */
 /* [API] Qwen3_8_FlashNextPLELayer: _causal_short_conv (a causal depthwise */
 /* convolution over [batch, sequence, channels] with zeros as the history  */
 /* on the left), _segmented_conv (every packed segment is convolved as if  */

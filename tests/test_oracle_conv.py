@@ -1,4 +1,4 @@
-"""CPU pins for the oracle's PLE causal depthwise convolution (no GPU, no
+"""CPU pins for the oracle's causal depthwise PLE convolution (no GPU, no
 HIP code).
 
 Source: NeMo AutoModel v0.7 API page (qwen3_8_flash_next.engram),
@@ -60,7 +60,7 @@ def test_matches_conv1d_on_exact_data(oracle, K, d, with_bias):
 
 
 def test_segments_match_one_conv1d_per_segment(oracle):
-    """The page's procedure: each run of one segment id gets its own conv1d
+    """The page's procedure: every segment is convolved alone by its own conv1d
     with zeros ahead of it."""
     rng = np.random.Generator(np.random.PCG64(5))
     K, d, S = 4, 3, 50
