@@ -477,6 +477,16 @@ __device__ __forceinline__ void load_quads(const uint2 *base, uint32_t idx, int6
     g[k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, quads - 1)];
 }
 
+// This lane's fp32 quads of row idx of the dense gradient table.
+template <int L, int Q, bool EXACT>
+__device__ __forceinline__ void load_grad_row(const WalkArgs &a, uint32_t idx, int lane,
+                                              f32x4 (&g)[Q]) {
+  const f32x4 *row = reinterpret_cast<const f32x4 *>(a.grad_table + (int64_t)idx * a.dim);
+#pragma unroll
+  for (int k = 0; k < Q; ++k)
+    g[k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
+}
+
 // This lane's quads of one gradient row.
 template <int L, int Q, bool EXACT>
 __device__ __forceinline__ void load_row(const WalkArgs &a, uint32_t idx, int lane,
@@ -519,11 +529,13 @@ __device__ __forceinline__ bool last_run_long(int64_t c, int64_t n, uint32_t sen
 }
 
 // The finished sum of row `key` (distinct-row slot u): one rounding to fp32,
-// then one fp32 add into the dense table, a row-sparse store, or the SignSGD
-// step on the table row (w: this lane's quads of that row, loaded earlier).
+// then one fp32 add into the dense table (gt: this lane's quads of the fp32
+// row, loaded earlier), a row-sparse store, or the SignSGD step on the bf16
+// table row (w: this lane's quads of that row, loaded earlier).
 template <int L, int Q, int OUT>
 __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArgs &a, int lane,
-                                         const double (&acc)[Q][4], const uint2 (&w)[Q]) {
+                                         const double (&acc)[Q][4], const uint2 (&w)[Q],
+                                         const f32x4 (&gt)[Q]) {
   if (OUT == kOutSparse && lane == 0) a.unique_ids[u] = (int64_t)key;
 #pragma unroll
   for (int k = 0; k < Q; ++k) {
@@ -535,7 +547,7 @@ __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArg
       __builtin_nontemporal_store(sum, dst);
     } else if (OUT == kOutDense) {
       f32x4 *dst = reinterpret_cast<f32x4 *>(a.grad_table + (int64_t)key * a.dim) + qd;
-      *dst = *dst + sum;
+      *dst = (Q == 1 ? gt[k] : *dst) + sum;  // wide rows are read here, not prefetched
     } else {
       const uint32_t b0 = signsgd_bf16(bf16_lo(w[k].x), sum.x, a.lr);
       const uint32_t b1 = signsgd_bf16(bf16_hi(w[k].x), sum.y, a.lr);
@@ -591,16 +603,25 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
 #pragma unroll
   for (int q = 0; q < kRange; ++q) tail += (q < live_count && !(last_long && kk[q] == klast)) ? 1 : 0;
 
-  // SignSGD: the table row of every run that starts in [lead, tail), loaded
-  // beside the gradient rows (other positions re-read the first key's row)
+  // The output row of every run that starts in [lead, tail), loaded beside
+  // the gradient rows, so no write waits on a read (other positions re-read
+  // the first key's row): the bf16 table row (SignSGD) or the fp32 gradient
+  // table row (dense, rows up to 256 values: wider fp32 rows would not fit
+  // in registers 16 at a time).
+  constexpr bool kPrefetchDense = OUT == kOutDense && Q == 1;
   uint2 tw[OUT == kOutSignSGD ? kRange : 1][Q];
-  uint2 cw[Q];  // the current run's table row
-  if constexpr (OUT == kOutSignSGD) {
+  f32x4 tg[kPrefetchDense ? kRange : 1][Q];
+  uint2 cw[Q];   // the current run's bf16 table row
+  f32x4 cg[Q];   // the current run's fp32 gradient table row
+  if constexpr (OUT == kOutSignSGD || kPrefetchDense) {
     if (tail > lead) {
 #pragma unroll
       for (int q = 0; q < kRange; ++q) {
         const bool head = q >= lead && q < tail && (q == lead || kk[q] != kk[q > 0 ? q - 1 : 0]);
-        load_quads<L, Q, EXACT>(a.table, head ? kk[q] : kk[0], a.quads, lane, tw[q]);
+        if constexpr (OUT == kOutSignSGD)
+          load_quads<L, Q, EXACT>(a.table, head ? kk[q] : kk[0], a.quads, lane, tw[q]);
+        else
+          load_grad_row<L, Q, EXACT>(a, head ? kk[q] : kk[0], lane, tg[q]);
       }
     }
   }
@@ -627,7 +648,7 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
       const bool live = q >= lead && q < tail;
       const bool head = live && (!started || kk[q] != cur);  // a distinct row starts at beg + q
       if (head && started) {
-        emit_row<L, Q, OUT>(cur, u, a, lane, acc, cw);
+        emit_row<L, Q, OUT>(cur, u, a, lane, acc, cw, cg);
         ++u;
         zero_acc<Q>(acc);
       }
@@ -635,6 +656,10 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
         if constexpr (OUT == kOutSignSGD) {
 #pragma unroll
           for (int k = 0; k < Q; ++k) cw[k] = tw[q][k];
+        }
+        if constexpr (kPrefetchDense) {
+#pragma unroll
+          for (int k = 0; k < Q; ++k) cg[k] = tg[q][k];
         }
         cur = kk[q];
         started = true;
@@ -663,7 +688,7 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
         if (q0 + b < m) add_quads<Q>(acc, g[b]);
     }
   }
-  emit_row<L, Q, OUT>(cur, u, a, lane, acc, cw);
+  emit_row<L, Q, OUT>(cur, u, a, lane, acc, cw, cg);
 }
 
 // One long run: the run that starts in range c0 and reaches range c0 + 2.
@@ -675,8 +700,10 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
   const int64_t r0 = c0 * kRange;
   const uint32_t u = a.head_off[c0 + 1] - 1;  // the last head of c0 (c0 + 2 exists)
   const uint32_t key = a.keys[r0 + kRange - 1];
-  uint2 tw[Q];  // SignSGD: the run's table row
+  uint2 tw[Q];   // SignSGD: the run's bf16 table row
+  f32x4 tg[Q];   // dense: the run's fp32 gradient table row
   if constexpr (OUT == kOutSignSGD) load_quads<L, Q, EXACT>(a.table, key, a.quads, lane, tw);
+  if constexpr (OUT == kOutDense && Q == 1) load_grad_row<L, Q, EXACT>(a, key, lane, tg);
   // start: range c0 is sorted, so the run begins after its smaller keys
   int64_t start = r0;
   const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + r0);
@@ -763,7 +790,7 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
         for (int e = 0; e < 4; ++e) acc[k][e] += s_part[h][lane * 4 + e];
     __syncthreads();
   }
-  if (g == 0) emit_row<L, Q, OUT>(key, u, a, lane, acc, tw);
+  if (g == 0) emit_row<L, Q, OUT>(key, u, a, lane, acc, tw, tg);
 }
 
 // Long runs (hot rows, longer than a range).  Block b checks which of the
