@@ -1,13 +1,16 @@
 """Throughput of the hashed n-gram embedding hot path on one MI355X.
 
 One step = one pass of the whole path over one token batch:
-    engram_hash (tokens -> row ids) -> engram_gather (forward rows)
-    -> engram_scatter_plan + engram_scatter_apply (backward: per-row fp32
-       sums, row-sparse; the same work as engram_scatter_add_rowsparse)
-The plan (sorting the row ids) needs only the hash output, so it runs on a
-second stream beside the forward gather, as a training step would schedule
-it; the apply waits for it.  A serial pass of the same calls gives the
-per-phase times.
+    engram_lookup (forward: the row ids hashed from the tokens and their
+       table rows gathered, in one kernel)
+    -> engram_scatter_plan_tokens + engram_scatter_apply (backward: per-row
+       fp32 sums, row-sparse; the same work as hashing, then
+       engram_scatter_add_rowsparse)
+The plan (sorting the row ids) needs only the tokens, so it runs on a second
+stream beside the forward, as a training step would schedule it; the apply
+waits for the forward and the plan.  A serial pass of the same calls gives
+the per-phase times, and the same step with separate calls (engram_hash,
+engram_gather, engram_scatter_plan of the ids, apply) is timed beside it.
 on the end-to-end workload: tokens [8, 8192] (Zipf(1.1) ids, EOS w.p.
 1/4096), ngram_size 4, 8 heads per order (24 heads), a 200M x 256 bf16 table
 (102.4 GB, resident in HBM), upstream gradients [8, 8192, 24, 256] bf16.
@@ -60,18 +63,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(wl, unique_rows, with_seg=False):
-    """Bytes the method must move per call (reads + writes), per phase."""
+def algorithmic_bytes(wl, unique_rows, separate=False):
+    """Bytes the method must move per call (reads + writes), per phase.  The
+    fused forward (engram_lookup) reads the tokens and the table rows and
+    writes the output; the row ids never reach memory.  With separate calls
+    (engram_hash, engram_gather, engram_scatter_plan) the ids are written
+    once and read twice."""
     N, R, D = wl.tokens_per_batch, wl.lookups, wl.dim
-    out = {"hash": 8 * N + 8 * R + (8 * N if with_seg else 0),
-           "gather": 8 * R + 2 * D * R + 2 * D * R}
+    if separate:
+        out = {"hash": 8 * N + 8 * R, "gather": 8 * R + 2 * D * R + 2 * D * R}
+    else:
+        out = {"lookup": 8 * N + 2 * D * R + 2 * D * R}
     # the backward's plan (sorting the ids) is overhead: its algorithmic
-    # bytes are the ids it reads; the apply moves the gradients
+    # bytes are what it reads (the ids, or the tokens it hashes again); the
+    # apply moves the gradients
+    if wl.grads != "none":
+        out["scatter_plan"] = 8 * R if separate else 8 * N
     if wl.grads == "rowsparse":
-        out["scatter_plan"] = 8 * R
         out["scatter_apply"] = 2 * D * R + (4 * D + 8) * unique_rows
     elif wl.grads == "dense":
-        out["scatter_plan"] = 8 * R
         out["scatter_apply"] = 2 * D * R + 8 * D * unique_rows
     return out
 
@@ -85,7 +95,7 @@ def measured_traffic(call, wl):
     if wl.name != "e2e" or not os.path.exists(path):
         return None
     rec = json.load(open(path))["kernels"]
-    parts = {"gather": ["gather"], "scatter_apply": ["reduce"]}.get(call)
+    parts = {"lookup": ["lookup"], "gather": ["gather"], "scatter_apply": ["reduce"]}.get(call)
     if parts is None:
         return None
     total = 0.0
@@ -358,15 +368,33 @@ def main():
                          dtype=torch.uint8, device=dev)
 
     side = torch.cuda.Stream(dev)  # default priority
-    ev_rows = [torch.cuda.Event() for _ in range(2)]
+    hargs = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
     ev_plan = [torch.cuda.Event() for _ in range(2)]
+    ev_apply = [torch.cuda.Event() for _ in range(2)]
+    ev_rows = [torch.cuda.Event() for _ in range(2)]
 
     def step(k):
-        """One step.  The backward's plan (sort of the row ids) needs only the
-        hash output, so it runs on a side stream beside the forward gather; the
-        apply waits for it."""
-        E.engram_hash(tokens[k % N_BATCHES], wl.ngram_size, wl.heads_per_ngram, wl.eos_id,
-                      mult, wl.primes, wl.offsets, wl.table_rows, out=rows)
+        """One step.  The forward is one pass (engram_lookup: hash and gather
+        fused).  The backward's plan needs only the tokens, so it is made
+        from them (engram_scatter_plan_tokens) on a side stream beside the
+        forward, once the previous step's apply has released the workspace;
+        the apply follows the forward and waits for the plan."""
+        tok = tokens[k % N_BATCHES]
+        if not backward:
+            E.engram_lookup(tok, table, *hargs, out=out)
+            return
+        side.wait_event(ev_apply[(k - 1) % 2])
+        E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, workspace=ws, stream=side)
+        ev_plan[k % 2].record(side)
+        E.engram_lookup(tok, table, *hargs, out=out)
+        stream.wait_event(ev_plan[k % 2])
+        apply_backward()
+        ev_apply[k % 2].record(stream)
+
+    def step_separate(k):
+        """The same step with separate calls (hash, then the plan of the ids
+        beside the gather), for comparison."""
+        E.engram_hash(tokens[k % N_BATCHES], *hargs, wl.table_rows, out=rows)
         if not backward:
             E.engram_gather(rows, table, out=out)
             return
@@ -387,62 +415,75 @@ def main():
         else:
             E.engram_scatter_apply(grads, ws, wl.table_rows, grad_table=gtab)
 
-    def serial_step(k, ev):
-        """The same calls one after another on one stream, with events between
-        them (per-phase times)."""
+    def serial_step(k, ev, separate=False):
+        """The calls of a step one after another on one stream, with events
+        between them (per-phase times)."""
+        tok = tokens[k % N_BATCHES]
         ev[0].record(stream)
-        E.engram_hash(tokens[k % N_BATCHES], wl.ngram_size, wl.heads_per_ngram, wl.eos_id,
-                      mult, wl.primes, wl.offsets, wl.table_rows, out=rows)
-        ev[1].record(stream)
-        E.engram_gather(rows, table, out=out)
+        if separate:
+            E.engram_hash(tok, *hargs, wl.table_rows, out=rows)
+            ev[1].record(stream)
+            E.engram_gather(rows, table, out=out)
+        else:
+            E.engram_lookup(tok, table, *hargs, out=out)
+            ev[1].record(stream)
         ev[2].record(stream)
         if backward:
-            E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws)
+            if separate:
+                E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws)
+            else:
+                E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, workspace=ws)
             ev[3].record(stream)
             apply_backward()
             ev[4].record(stream)
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
+    def timed_steps(fn):
+        for k in range(args.warmup):
+            fn(k)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for k in range(args.steps):
+            fn(k)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    def serial_phases(separate):
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+               for _ in range(args.steps)]
+        for k in range(args.steps):
+            serial_step(k, evs[k], separate)
+        torch.cuda.synchronize()
+        mean = lambda i, j: float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
+        ph = ({"hash": mean(0, 1), "gather": mean(1, 2)} if separate
+              else {"lookup": mean(0, 2)})
+        if backward:
+            ph["scatter_plan"] = mean(2, 3)
+            ph["scatter_apply"] = mean(3, 4)
+        return ph, mean(0, 4 if backward else 2)
 
     # whole-step timing (the driver's step): nothing between the calls
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for k in range(args.steps):
-        step(k)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
-
-    # per-phase timing: events between the calls, one stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        serial_step(k, evs[k])
-    torch.cuda.synchronize()
-    phase_ms = {
-        "hash": float(np.mean([e[0].elapsed_time(e[1]) for e in evs])),
-        "gather": float(np.mean([e[1].elapsed_time(e[2]) for e in evs])),
-    }
-    if backward:
-        phase_ms["scatter_plan"] = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-        phase_ms["scatter_apply"] = float(np.mean([e[3].elapsed_time(e[4]) for e in evs]))
-    serial_ms = float(np.mean([e[0].elapsed_time(e[4 if backward else 2]) for e in evs]))
+    ms_per_step = timed_steps(step)
+    phase_ms, serial_ms = serial_phases(False)
+    # the same work with separate calls, timed in the same process
+    sep_ms = timed_steps(step_separate)
+    sep_phase_ms, _ = serial_phases(True)
 
     # distinct rows of one batch (the backward's U), read after timing
     unique_rows = 0
     if backward:
-        serial_step(0, evs[0])
-        torch.cuda.synchronize()
-        unique_rows = (int(count.item()) if wl.grads == "rowsparse" and not signsgd
-                       else int(torch.unique(rows).numel()))
+        E.engram_hash(tokens[0], *hargs, wl.table_rows, out=rows)
+        unique_rows = int(torch.unique(rows).numel())
     nbytes = algorithmic_bytes(wl, unique_rows)
+    sep_bytes = algorithmic_bytes(wl, unique_rows, separate=True)
     unfused = None
     if signsgd:
         # the fused apply reads the gradient rows and reads + writes each
         # distinct row of the bf16 table once
         nbytes["scatter_apply"] = 2 * D * R + 4 * D * unique_rows
+        sep_bytes["scatter_apply"] = nbytes["scatter_apply"]
         # the same step in two calls, for comparison (same plan, same stream)
         u0, u1, u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
         E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws)
@@ -461,19 +502,26 @@ def main():
                    "total_ms": a_ms + s_ms,
                    "algorithmic_bytes": 2 * D * R + (4 * D + 8) * unique_rows
                    + (8 + 4 * D + 4 * D) * unique_rows}
-    phases = {}
-    for p_, ms in phase_ms.items():
-        b_ = nbytes.get(p_, 0)
-        phases[p_] = {"ms": ms, "algorithmic_bytes": b_, "gbps": b_ / (ms * 1e-3) / 1e9,
-                      "frac_of_peak": b_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    def phase_table(pm, nb):
+        out_ = {}
+        for p_, ms in pm.items():
+            b_ = nb.get(p_, 0)
+            out_[p_] = {"ms": ms, "algorithmic_bytes": b_, "gbps": b_ / (ms * 1e-3) / 1e9,
+                        "frac_of_peak": b_ / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        return out_
+
+    phases = phase_table(phase_ms, nbytes)
     step_bytes = sum(nbytes.values())
     step_gbps = step_bytes / (ms_per_step * 1e-3) / 1e9
+    separate_calls = {"ms_per_step": sep_ms, "value": R / (sep_ms * 1e-3),
+                      "step_algorithmic_bytes": sum(sep_bytes.values()),
+                      "phases": phase_table(sep_phase_ms, sep_bytes)}
 
-    # roofline of the dominant call: the gather is one kernel; the apply is
-    # the segment-reduce kernel plus the (short) long-run fix-up kernel
-    dominant = "gather"
-    kernel = "gather_kernel<5>" if D == 256 else "gather_kernel"
-    if backward and phase_ms["scatter_apply"] > phase_ms["gather"]:
+    # roofline of the dominant call: the fused forward and the apply are one
+    # kernel launch each, so their event times are the kernels' times
+    dominant = "lookup"
+    kernel = f"lookup_kernel<{wl.ngram_size}> (engram_lookup)"
+    if backward and phase_ms["scatter_apply"] > phase_ms["lookup"]:
         dominant = "scatter_apply"
         kernel = ("segment_reduce_kernel, SignSGD output (engram_scatter_apply_signsgd)"
                   if signsgd else "segment_reduce_kernel (engram_scatter_apply)")
@@ -521,8 +569,8 @@ def main():
         "config": {**wl.describe(),
                    **({"workload": "e2e_signsgd", "optimizer": "signsgd", "lr": lr}
                       if signsgd else {}),
-                   "step": "hash+gather" + ("+scatter(plan beside gather, apply)" if backward
-                                            else "")
+                   "step": "lookup(hash+gather fused)"
+                   + ("+scatter(plan from tokens beside the lookup, apply)" if backward else "")
                    + ("+signsgd(fused into the apply)" if signsgd else ""),
                    "backward": wl.grads, "accumulate": "f64" if backward else None,
                    "unique_rows": unique_rows, "token_batches_cycled": N_BATCHES},
@@ -531,6 +579,7 @@ def main():
         "step_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBS,
         "phases": phases,
+        "separate_calls": separate_calls,
         **({"two_call_apply_and_signsgd": unfused} if unfused else {}),
         "roofline": roofline,
         "hbm_copy_ceiling_gbps": copy_gbps,

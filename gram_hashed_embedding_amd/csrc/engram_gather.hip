@@ -19,7 +19,7 @@
 // 64-bit: a 200M x 256 table is 102.4 GB.  Output stores are non-temporal
 // so the streaming output does not evict hot (Zipf-frequent) table rows
 // from L2 and the Infinity Cache; table loads stay cacheable.
-#include "engram_internal.h"
+#include "engram_hash_dev.h"
 
 namespace engram {
 namespace {
@@ -100,6 +100,48 @@ __global__ __launch_bounds__(kGatherThreads) void zero_rows_kernel(const int64_t
   if (c % cpr == 0) count_errors(ids[c / cpr] != -1 ? 1 : 0, err);
 }
 
+// The fused forward (engram_lookup).  A block takes kLookRows consecutive
+// lookups.  Phase 1: its first kLookRows lanes compute one row each from the
+// tokens (lookup_row: the token's history in one round of loads, the order
+// mix, a Barrett remainder), so the hash costs one lane per row, and keep
+// them in LDS (and write them out when the caller asks).  Phase 2: as
+// gather_kernel, every lane moves 16-byte chunks of those rows, kUnroll at
+// a time (all loads before the stores).  The row ids never go through
+// memory.  N = ngram_size at compile time, so the history takes no more
+// registers than the order needs.
+constexpr int kLookRows = 32;
+
+template <int N>
+__global__ __launch_bounds__(kGatherThreads) void lookup_kernel(
+    const HashParams h, int64_t n, const u32x4 *__restrict__ table, int64_t cpr, int log2_cpr,
+    u32x4 *__restrict__ out, int64_t *__restrict__ rows_out) {
+  __shared__ int64_t s_row[kLookRows];
+  const int64_t row0 = (int64_t)blockIdx.x * kLookRows;
+  const int nrows = (int)min((int64_t)kLookRows, n - row0);
+  if ((int)threadIdx.x < nrows) {
+    const int64_t r = lookup_row<N>(h, row0 + threadIdx.x);  // inside its head's rows
+    s_row[threadIdx.x] = r;
+    if (rows_out != nullptr) rows_out[row0 + threadIdx.x] = r;
+  }
+  __syncthreads();
+  const int64_t nchunks = (int64_t)nrows * cpr;
+  u32x4 *dst = out + row0 * cpr;
+  for (int64_t k0 = threadIdx.x; k0 < nchunks; k0 += (int64_t)kGatherThreads * kUnroll) {
+    u32x4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t k = min(k0 + (int64_t)u * kGatherThreads, nchunks - 1);
+      const int64_t rl = log2_cpr >= 0 ? k >> log2_cpr : k / cpr;
+      v[u] = table[s_row[rl] * cpr + (k - rl * cpr)];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t k = k0 + (int64_t)u * kGatherThreads;
+      if (k < nchunks) __builtin_nontemporal_store(v[u], &dst[k]);
+    }
+  }
+}
+
 }  // namespace
 }  // namespace engram
 
@@ -151,6 +193,53 @@ extern "C" int engram_gather(const int64_t *d_row_ids, int64_t n, const void *d_
     default:
       hipLaunchKernelGGL(gather_kernel<-1>, grid, block, 0, s, d_row_ids, n, tab, table_rows,
                          cpr, out, d_err_count);
+  }
+  return launch_status();
+}
+
+extern "C" int engram_lookup(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
+                             int64_t seq, int32_t ngram_size, int32_t heads_per_ngram,
+                             int64_t eos_id, const int64_t *h_multipliers,
+                             const int64_t *h_primes, const int64_t *h_offsets,
+                             const void *d_table, int64_t table_rows, int64_t head_dim,
+                             void *d_out, int64_t *d_row_ids, void *stream) {
+  if (seq < 0 || head_dim <= 0 || head_dim % 8 != 0) return ENGRAM_EINVAL;
+  HashParams h;
+  int64_t tokens = 0;
+  const int rc = make_hash_params(d_tokens, d_seq_ids, batch, seq, 0, seq, ngram_size,
+                                  heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets,
+                                  table_rows, &h, &tokens);
+  if (rc != ENGRAM_OK) return rc;
+  const int64_t n = tokens * h.H;
+  if (!mul_fits(table_rows, head_dim * 2, INT64_MAX) || !mul_fits(n, head_dim * 2, INT64_MAX))
+    return ENGRAM_EINVAL;
+  if (n == 0) return ENGRAM_OK;
+  if (d_table == nullptr || d_out == nullptr) return ENGRAM_EINVAL;
+  if (!aligned16(d_table) || !aligned16(d_out)) return ENGRAM_EALIGN;
+  const int64_t cpr = head_dim / 8;
+  const int64_t blocks = (n + kLookRows - 1) / kLookRows;
+  if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+  const u32x4 *tab = static_cast<const u32x4 *>(d_table);
+  u32x4 *out = static_cast<u32x4 *>(d_out);
+  const dim3 grid((unsigned)blocks), block(kGatherThreads);
+  hipStream_t s = as_stream(stream);
+  int log2_cpr = -1;
+  for (int b = 0; b < 62; ++b)
+    if (cpr == (int64_t)1 << b) log2_cpr = b;
+  switch (ngram_size) {
+#define ENGRAM_LOOKUP_CASE(N)                                                                 \
+  case N:                                                                                     \
+    hipLaunchKernelGGL(lookup_kernel<N>, grid, block, 0, s, h, n, tab, cpr, log2_cpr, out,     \
+                       d_row_ids);                                                            \
+    break;
+    ENGRAM_LOOKUP_CASE(2)
+    ENGRAM_LOOKUP_CASE(3)
+    ENGRAM_LOOKUP_CASE(4)
+    ENGRAM_LOOKUP_CASE(5)
+    ENGRAM_LOOKUP_CASE(6)
+    ENGRAM_LOOKUP_CASE(7)
+    ENGRAM_LOOKUP_CASE(8)
+#undef ENGRAM_LOOKUP_CASE
   }
   return launch_status();
 }

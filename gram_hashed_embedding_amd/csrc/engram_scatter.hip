@@ -42,7 +42,7 @@
 //     contributions) do not serialise a walker.
 // Atomic path: one fp32 atomic add per gradient element into the dense
 // table (hardware float atomics in L2); order of additions not fixed.
-#include "engram_internal.h"
+#include "engram_hash_dev.h"
 
 namespace engram {
 namespace {
@@ -159,7 +159,12 @@ __global__ __launch_bounds__(kSortThreads) void sort_histogram_kernel(
   }
 }
 
-template <bool FROM_IDS>
+// Where a sort pass takes its input from.
+constexpr int kSrcIds = 0;        // int64 row ids (first pass of a plan from ids)
+constexpr int kSrcKeys = 1;       // 32-bit keys and flat indices (later passes)
+constexpr int kSrcKeysIota = 2;   // 32-bit keys in flat order (first pass of a plan from tokens)
+
+template <int SRC>
 __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
     const int64_t *ids, const uint32_t *keys_in, const uint32_t *vals_in, int64_t n,
     int64_t table_rows, int shift, int bits, const uint32_t *hist, uint64_t *status,
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   for (int c = 0; c < kHistCopies; ++c)
     copies[c] = hist[(int64_t)c * 4 * kMaxBins + (tid < bins ? tid : 0)];
   uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
-  if (FROM_IDS) {
+  if (SRC == kSrcIds) {
     int64_t id[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i)
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
     for (int i = 0; i < kSortItems; ++i) {
       const int64_t p = min(base + (int64_t)i * kWave + lane, n - 1);
       key[i] = keys_in[p];
-      val[i] = vals_in[p];
+      val[i] = SRC == kSrcKeysIota ? (uint32_t)p : vals_in[p];
     }
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i)
@@ -316,6 +321,53 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
     const uint32_t dst = s_gbase[d] + (uint32_t)j - s_local[d];
     keys_out[dst] = k;
     vals_out[dst] = s_vals[j];
+  }
+}
+
+// ---------------------------------------------------------- plan from tokens
+// The first kernel of a plan made from the tokens: the row of every lookup
+// is computed as the hash kernel does (64 tokens per block; one lane per
+// token computes its order mixes, then the block's 64 * H outputs in flat
+// order), written as its 32-bit sort key, and counted into every pass's
+// digit histogram.  Hashed rows are always inside the table.
+__global__ __launch_bounds__(kSortThreads) void plan_hash_kernel(const HashParams hp,
+                                                                 int64_t total_tokens,
+                                                                 int passes, int per_pass,
+                                                                 int bits, uint32_t *keys,
+                                                                 uint32_t *hist) {
+  constexpr int kTokens = 64;
+  __shared__ uint64_t s_mix[kTokens][ENGRAM_MAX_NGRAM - 1];
+  __shared__ uint32_t s_hist[4][kMaxBins];
+  const int tid = threadIdx.x;
+  const int64_t tok0 = (int64_t)blockIdx.x * kTokens;
+  for (int d = tid; d < 4 * kMaxBins; d += kSortThreads) (&s_hist[0][0])[d] = 0;
+  if (tid < kTokens && tok0 + tid < total_tokens) {
+    uint64_t mix[ENGRAM_MAX_NGRAM - 1];
+    token_mixes(hp, tok0 + tid, mix);
+#pragma unroll
+    for (int k = 0; k < ENGRAM_MAX_NGRAM - 1; ++k)
+      if (k < hp.n - 1) s_mix[tid][k] = mix[k];
+  }
+  __syncthreads();
+  const int ntok = (int)min((int64_t)kTokens, total_tokens - tok0);
+  const int nout = ntok * hp.H;
+  uint32_t *out = keys + tok0 * hp.H;
+  for (int o = tid; o < nout; o += kSortThreads) {
+    const int tl = o / hp.H;
+    const int h = o - tl * hp.H;
+    const uint32_t k = (uint32_t)head_row(hp, s_mix[tl][h / hp.J], h);
+    out[o] = k;
+    for (int q = 0; q < passes; ++q) {
+      const int shift = q * per_pass;
+      const int width = bits - shift < per_pass ? bits - shift : per_pass;
+      atomicAdd(&s_hist[q][(k >> shift) & ((1u << width) - 1u)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t *copy = hist + (int64_t)(blockIdx.x % kHistCopies) * 4 * kMaxBins;
+  for (int d = tid; d < passes * kMaxBins; d += kSortThreads) {
+    const uint32_t c = (&s_hist[0][0])[d];
+    if (c != 0) atomicAdd(&copy[d], c);
   }
 }
 
@@ -999,9 +1051,10 @@ Views views_of(const Plan &p, void *ws) {
 }
 
 // Plan: sort the row ids and give every distinct row its slot (U is left
-// in the workspace scalars).  Needs only the ids.
-int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p, void *ws,
-                int64_t *err, hipStream_t s) {
+// in the workspace scalars).  Needs only the ids: given (ids), or computed
+// from the tokens (hp, when ids is null).
+int plan_sorted(const int64_t *ids, const HashParams *hp, int64_t n, int64_t table_rows,
+                const Plan &p, void *ws, int64_t *err, hipStream_t s) {
   const Views v = views_of(p, ws);
   uint32_t *hist = v.counters;                                // [kHistCopies][4][kMaxBins]
   uint32_t *tickets = v.counters + kHistCopies * 4 * kMaxBins;  // [4]
@@ -1009,8 +1062,15 @@ int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p
   const int64_t clear_len = status_len > kSortCounters ? status_len : kSortCounters;
   hipLaunchKernelGGL(sort_clear_kernel, dim3((unsigned)((clear_len + 255) / 256)), dim3(256), 0,
                      s, v.status, status_len, v.counters, kSortCounters);
-  hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)p.num_tiles), dim3(kSortThreads), 0,
-                     s, ids, n, table_rows, p.passes, p.per_pass, p.bits, hist, err);
+  if (ids != nullptr) {
+    hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)p.num_tiles), dim3(kSortThreads), 0,
+                       s, ids, n, table_rows, p.passes, p.per_pass, p.bits, hist, err);
+  } else {  // keys in flat order go to keys_b, which the first pass reads
+    const int64_t tokens = n / hp->H;
+    hipLaunchKernelGGL(plan_hash_kernel, dim3((unsigned)((tokens + 63) / 64)),
+                       dim3(kSortThreads), 0, s, *hp, tokens, p.passes, p.per_pass, p.bits,
+                       v.keys_b, hist);
+  }
   const uint32_t *src_k = nullptr, *src_v = nullptr;
   uint32_t *dst_k = v.keys_a, *dst_v = v.vals_a, *spare_k = v.keys_b, *spare_v = v.vals_b;
   const unsigned tiles = (unsigned)p.num_tiles;
@@ -1018,14 +1078,19 @@ int plan_sorted(const int64_t *ids, int64_t n, int64_t table_rows, const Plan &p
     const int shift = pass * p.per_pass;
     const int width = p.bits - shift < p.per_pass ? p.bits - shift : p.per_pass;
     uint64_t *pass_status = v.status + (int64_t)pass * p.num_tiles * kMaxBins;
-    if (pass == 0)
-      hipLaunchKernelGGL(onesweep_kernel<true>, dim3(tiles), dim3(kSortThreads), 0, s, ids,
+    if (pass == 0 && ids != nullptr)
+      hipLaunchKernelGGL(onesweep_kernel<kSrcIds>, dim3(tiles), dim3(kSortThreads), 0, s, ids,
                          nullptr, nullptr, n, table_rows, shift, width, hist, pass_status,
                          tickets, p.num_tiles, dst_k, dst_v, err);
+    else if (pass == 0)
+      hipLaunchKernelGGL(onesweep_kernel<kSrcKeysIota>, dim3(tiles), dim3(kSortThreads), 0, s,
+                         nullptr, v.keys_b, nullptr, n, table_rows, shift, width, hist,
+                         pass_status, tickets, p.num_tiles, dst_k, dst_v, err);
     else
-      hipLaunchKernelGGL(onesweep_kernel<false>, dim3(tiles), dim3(kSortThreads), 0, s, nullptr,
-                         src_k, src_v, n, table_rows, shift, width, hist + pass * kMaxBins,
-                         pass_status, tickets + pass, p.num_tiles, dst_k, dst_v, err);
+      hipLaunchKernelGGL(onesweep_kernel<kSrcKeys>, dim3(tiles), dim3(kSortThreads), 0, s,
+                         nullptr, src_k, src_v, n, table_rows, shift, width,
+                         hist + pass * kMaxBins, pass_status, tickets + pass, p.num_tiles, dst_k,
+                         dst_v, err);
     src_k = dst_k;
     src_v = dst_v;
     uint32_t *tk = dst_k, *tv = dst_v;
@@ -1157,7 +1222,8 @@ extern "C" int engram_scatter_plan(const int64_t *d_row_ids, int64_t n, int64_t 
   if (n == 0) return ENGRAM_OK;
   if (d_row_ids == nullptr) return ENGRAM_EINVAL;
   if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
-  return plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, as_stream(stream));
+  return plan_sorted(d_row_ids, nullptr, n, table_rows, p, d_workspace, d_err_count,
+                     as_stream(stream));
 }
 
 extern "C" int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
@@ -1209,7 +1275,8 @@ extern "C" int engram_scatter_add(const int64_t *d_row_ids, int64_t n, const voi
                           d_err_count, s);
   int rc = check_workspace(p, d_workspace, workspace_bytes);
   if (rc != ENGRAM_OK) return rc;
-  if ((rc = plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, s)) != ENGRAM_OK)
+  if ((rc = plan_sorted(d_row_ids, nullptr, n, table_rows, p, d_workspace, d_err_count, s)) !=
+      ENGRAM_OK)
     return rc;
   const ApplyOut o = {kOutDense, d_grad_table, nullptr, nullptr, nullptr, nullptr, 0.0f};
   return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, o, s);
@@ -1235,7 +1302,8 @@ extern "C" int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
     return ENGRAM_EINVAL;
   if (!aligned16(d_grads) || !aligned16(d_unique_grads)) return ENGRAM_EALIGN;
   if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
-  if ((rc = plan_sorted(d_row_ids, n, table_rows, p, d_workspace, d_err_count, s)) != ENGRAM_OK)
+  if ((rc = plan_sorted(d_row_ids, nullptr, n, table_rows, p, d_workspace, d_err_count, s)) !=
+      ENGRAM_OK)
     return rc;
   const ApplyOut o = {kOutSparse, nullptr, d_unique_ids, d_unique_grads, d_num_unique, nullptr,
                       0.0f};
@@ -1256,3 +1324,28 @@ extern "C" int engram_scatter_apply_signsgd(const void *d_grads, int64_t n, int6
   const ApplyOut o = {kOutSignSGD, nullptr, nullptr, nullptr, nullptr, d_table, lr};
   return apply_sorted(d_grads, n, head_dim, table_rows, p, d_workspace, o, as_stream(stream));
 }
+
+extern "C" int engram_scatter_plan_tokens(const int64_t *d_tokens, const int64_t *d_seq_ids,
+                                          int64_t batch, int64_t seq, int32_t ngram_size,
+                                          int32_t heads_per_ngram, int64_t eos_id,
+                                          const int64_t *h_multipliers, const int64_t *h_primes,
+                                          const int64_t *h_offsets, int64_t table_rows,
+                                          int64_t head_dim, void *d_workspace,
+                                          size_t workspace_bytes, void *stream) {
+  if (seq < 0) return ENGRAM_EINVAL;
+  HashParams hp;
+  int64_t tokens = 0;
+  int rc = make_hash_params(d_tokens, d_seq_ids, batch, seq, 0, seq, ngram_size,
+                            heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets,
+                            table_rows, &hp, &tokens);
+  if (rc != ENGRAM_OK) return rc;
+  if (!mul_fits(tokens, hp.H, INT64_MAX)) return ENGRAM_EINVAL;
+  const int64_t n = tokens * hp.H;
+  Plan p;
+  if ((rc = check_sorted(n, table_rows, head_dim, &p)) != ENGRAM_OK) return rc;
+  if (n == 0) return ENGRAM_OK;
+  if ((tokens + 63) / 64 > INT32_MAX) return ENGRAM_EINVAL;
+  if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
+  return plan_sorted(nullptr, &hp, n, table_rows, p, d_workspace, nullptr, as_stream(stream));
+}
+

@@ -52,6 +52,15 @@ _lib.engram_hash_slice.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, cty
                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_int64, _i64p, _i64p, _i64p, ctypes.c_int64, _vp,
                                    _vp]
+_lib.engram_lookup.restype = ctypes.c_int
+_lib.engram_lookup.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                               ctypes.c_int32, ctypes.c_int64, _i64p, _i64p, _i64p, _vp,
+                               ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
+_lib.engram_scatter_plan_tokens.restype = ctypes.c_int
+_lib.engram_scatter_plan_tokens.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64,
+                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                            _i64p, _i64p, _i64p, ctypes.c_int64,
+                                            ctypes.c_int64, _vp, ctypes.c_size_t, _vp]
 _lib.engram_gather.restype = ctypes.c_int
 _lib.engram_gather.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
                                _vp, _vp]
@@ -449,4 +458,69 @@ def engram_ple_conv(x, weight, dilation, bias=None, seq_ids=None, halo=None, out
                                       int(dilation), _ptr(out), _stream(x.device, stream))
     _check(status, "engram_ple_conv")
     return out
+
+
+def _hash_args(tokens, ngram_size, heads_per_ngram, multipliers, primes, offsets, seq_ids):
+    _device_tensor(tokens, torch.int64, "tokens")
+    if tokens.dim() != 2:
+        raise ValueError("tokens must be [batch, seq]")
+    if not 2 <= int(ngram_size) <= MAX_NGRAM:
+        raise ValueError(f"ngram_size must be in [2, {MAX_NGRAM}]")
+    heads = (int(ngram_size) - 1) * int(heads_per_ngram)
+    if seq_ids is not None:
+        _device_tensor(seq_ids, torch.int64, "seq_ids")
+        if seq_ids.shape != tokens.shape:
+            raise ValueError("seq_ids must have the shape of tokens")
+    return (heads, _host_i64(multipliers, int(ngram_size), "multipliers"),
+            _host_i64(primes, heads, "primes"), _host_i64(offsets, heads, "offsets"))
+
+
+def engram_lookup(tokens, table, ngram_size, heads_per_ngram, eos_id, multipliers, primes,
+                  offsets, seq_ids=None, out=None, row_ids=None, stream=None):
+    """The forward in one pass: bf16 [batch, seq, H, head_dim] rows of the
+    hashed ids of tokens int64 [batch, seq]; also writes the ids into row_ids
+    (int64 [batch, seq, H]) when given."""
+    heads, mult, pr, off = _hash_args(tokens, ngram_size, heads_per_ngram, multipliers, primes,
+                                      offsets, seq_ids)
+    _device_tensor(table, torch.bfloat16, "table")
+    if table.dim() != 2:
+        raise ValueError("table must be [rows, head_dim]")
+    batch, seq = tokens.shape
+    rows, dim = table.shape
+    if out is None:
+        out = torch.empty((batch, seq, heads, dim), dtype=torch.bfloat16, device=tokens.device)
+    _device_tensor(out, torch.bfloat16, "out")
+    if out.numel() != batch * seq * heads * dim:
+        raise ValueError("out must hold batch * seq * H * head_dim values")
+    if row_ids is not None:
+        _device_tensor(row_ids, torch.int64, "row_ids")
+        if row_ids.numel() != batch * seq * heads:
+            raise ValueError("row_ids must hold batch * seq * H ids")
+    with torch.cuda.device(tokens.device):
+        status = _lib.engram_lookup(_ptr(tokens), _ptr(seq_ids), batch, seq, int(ngram_size),
+                                    int(heads_per_ngram), int(eos_id), mult, pr, off,
+                                    _ptr(table), rows, dim, _ptr(out), _ptr(row_ids),
+                                    _stream(tokens.device, stream))
+    _check(status, "engram_lookup")
+    return out
+
+
+def engram_scatter_plan_tokens(tokens, table_rows, head_dim, ngram_size, heads_per_ngram, eos_id,
+                               multipliers, primes, offsets, seq_ids=None, workspace=None,
+                               stream=None):
+    """The backward's plan for the hashed ids of tokens, made from the tokens;
+    returns the workspace (allocated when not given)."""
+    heads, mult, pr, off = _hash_args(tokens, ngram_size, heads_per_ngram, multipliers, primes,
+                                      offsets, seq_ids)
+    batch, seq = tokens.shape
+    n = batch * seq * heads
+    ws = _workspace(workspace, n, table_rows, head_dim, SCATTER_ROWSPARSE, tokens.device)
+    with torch.cuda.device(tokens.device):
+        status = _lib.engram_scatter_plan_tokens(_ptr(tokens), _ptr(seq_ids), batch, seq,
+                                                 int(ngram_size), int(heads_per_ngram),
+                                                 int(eos_id), mult, pr, off, int(table_rows),
+                                                 int(head_dim), _ptr(ws), ws.numel(),
+                                                 _stream(tokens.device, stream))
+    _check(status, "engram_scatter_plan_tokens")
+    return ws
 

@@ -129,6 +129,27 @@ int engram_hash_slice(const int64_t *d_tokens, const int64_t *d_seq_ids,
                       int64_t *d_row_ids, void *stream);
 
 /*
+ * engram_lookup -- the forward in one pass: the rows engram_hash gives for
+ * tokens [batch, seq] are gathered straight away, without writing or reading
+ * the row ids in between: d_out[b, t, h, :] = d_table[row(b, t, h), :].
+ * Follows the sources of engram_hash and engram_gather (the layer's forward
+ * hashes, then looks up).  Arguments as for engram_hash, with:
+ *   d_table bf16 [table_rows, head_dim]; d_out bf16 [batch, seq, H, head_dim],
+ *   written; head_dim a positive multiple of 8; d_table and d_out 16-byte
+ *   aligned.
+ *   d_row_ids int64 [batch, seq, H], or NULL: when given, the row ids are
+ *   written too (the same values engram_hash writes).
+ * Hashed rows always lie inside the table (every head is checked to fit), so
+ * no id is invalid.  Errors: those of engram_hash and engram_gather.
+ * batch * seq == 0 enqueues nothing.
+ */
+int engram_lookup(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
+                  int64_t seq, int32_t ngram_size, int32_t heads_per_ngram, int64_t eos_id,
+                  const int64_t *h_multipliers, const int64_t *h_primes,
+                  const int64_t *h_offsets, const void *d_table, int64_t table_rows,
+                  int64_t head_dim, void *d_out, int64_t *d_row_ids, void *stream);
+
+/*
  * engram_gather -- d_out[i, :] = d_table[d_row_ids[i], :] (bitwise bf16 copy).
  *
  * Follows [API] _lookup_ngram_ids and Qwen3_8_FlashNextOwnerShardedEmbedding
@@ -228,6 +249,23 @@ int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
 int engram_scatter_plan(const int64_t *d_row_ids, int64_t n, int64_t table_rows,
                         int64_t head_dim, void *d_workspace, size_t workspace_bytes,
                         int64_t *d_err_count, void *stream);
+
+/*
+ * engram_scatter_plan_tokens -- the plan of the row ids of tokens [batch,
+ * seq], computed from the tokens: the same plan engram_scatter_plan makes
+ * from engram_hash's output (n = batch * seq * H ids), without the ids being
+ * written or read.  Arguments as for engram_hash (the hash) and
+ * engram_scatter_plan (table_rows, head_dim, the workspace of n ids).
+ * Lets the backward's plan start from the tokens alone, beside a forward
+ * done with engram_lookup.  Errors: those of both calls.
+ */
+int engram_scatter_plan_tokens(const int64_t *d_tokens, const int64_t *d_seq_ids,
+                               int64_t batch, int64_t seq, int32_t ngram_size,
+                               int32_t heads_per_ngram, int64_t eos_id,
+                               const int64_t *h_multipliers, const int64_t *h_primes,
+                               const int64_t *h_offsets, int64_t table_rows,
+                               int64_t head_dim, void *d_workspace, size_t workspace_bytes,
+                               void *stream);
 
 int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
                          int64_t table_rows, float *d_grad_table, int64_t *d_unique_ids,

@@ -24,7 +24,8 @@ def test_every_declared_symbol_is_exported():
                           "engram_scatter_add", "engram_scatter_add_rowsparse",
                           "engram_scatter_plan", "engram_scatter_apply",
                           "engram_hash_slice", "engram_signsgd_rowsparse",
-                          "engram_scatter_apply_signsgd", "engram_ple_conv"}
+                          "engram_scatter_apply_signsgd", "engram_ple_conv",
+                          "engram_lookup", "engram_scatter_plan_tokens"}
     for name in names:
         assert hasattr(e._lib, name), name
 
@@ -191,3 +192,26 @@ def test_ple_conv_rejects():
     assert call(x=MISALIGNED) == e.ENGRAM_EALIGN
     assert call(halo=MISALIGNED, halo_len=9) == e.ENGRAM_EALIGN
     assert call(seq=0, x=None, out=None) == e.ENGRAM_OK
+
+
+def test_lookup_and_token_plan_reject():
+    lk = e._lib.engram_lookup
+    def look(dim=8, table=ALIGNED, out=ALIGNED, rows=36, primes=(5, 7, 11, 13), tokens=FAKE):
+        return lk(tokens, None, 1, 4, 3, 2, 0, _arr((1, 2, 3)), _arr(primes), _arr((0, 5, 12, 23)),
+                  table, rows, dim, out, None, None)
+    assert look(dim=12) == e.ENGRAM_EINVAL
+    assert look(primes=(5, 0, 11, 13)) == e.ENGRAM_EINVAL
+    assert look(rows=35) == e.ENGRAM_EINVAL           # the last head does not fit
+    assert look(table=None) == e.ENGRAM_EINVAL
+    assert look(tokens=None) == e.ENGRAM_EINVAL
+    assert look(table=MISALIGNED) == e.ENGRAM_EALIGN
+    assert look(out=MISALIGNED) == e.ENGRAM_EALIGN
+    pt = e._lib.engram_scatter_plan_tokens
+    ws = e.engram_scatter_add_workspace(24, 36, 8, 2)
+    def plan(dim=8, wsb=ws, tokens=FAKE, work=ALIGNED):
+        return pt(tokens, None, 1, 4, 3, 2, 0, _arr((1, 2, 3)), _arr((5, 7, 11, 13)),
+                  _arr((0, 5, 12, 23)), 36, dim, work, wsb, None)
+    assert plan(dim=12) == e.ENGRAM_EINVAL
+    assert plan(wsb=ws - 1) == e.ENGRAM_EWORKSPACE
+    assert plan(work=MISALIGNED) == e.ENGRAM_EWORKSPACE
+    assert plan(tokens=None) == e.ENGRAM_EINVAL

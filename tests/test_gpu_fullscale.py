@@ -87,13 +87,31 @@ def test_e2e_forward_backward(oracle):
     rows_host = rows.cpu().numpy()
     assert np.array_equal(rows_host, want)
     sampled_gather_check(oracle, rows_host, out, table, wl.seed + 1)
-    del out, table
+    # the fused forward the benchmark times gives the same rows and values
+    fused_ids = torch.empty_like(rows)
+    fused = E.engram_lookup(dev(tok), table, wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult,
+                            wl.primes, wl.offsets, row_ids=fused_ids)
+    torch.cuda.synchronize()
+    assert torch.equal(fused_ids, rows)
+    assert torch.equal(fused.view(-1), out.view(-1))
+    del out, fused, table
     release()
 
     grads = workloads.make_grads(wl.lookups, wl.dim, wl.seed + 2, "cuda")
     err = torch.zeros(1, dtype=torch.int64, device="cuda")
     uid, uval, count = E.engram_scatter_add_rowsparse(rows.view(-1), grads, wl.table_rows,
                                                       err_count=err)
+    # the plan the benchmark times (from the tokens) gives the same output
+    ws_t = E.engram_scatter_plan_tokens(dev(tok), wl.table_rows, wl.dim, wl.ngram_size,
+                                        wl.heads_per_ngram, wl.eos_id, mult, wl.primes,
+                                        wl.offsets)
+    uid_t, uval_t, count_t = E.engram_scatter_apply(grads, ws_t, wl.table_rows)
+    torch.cuda.synchronize()
+    ut = int(count_t.item())
+    assert ut == int(count.item())
+    assert torch.equal(uid_t[:ut], uid[:ut])
+    assert torch.equal(uval_t[:ut].view(torch.int32), uval[:ut].view(torch.int32))
+    del uid_t, uval_t, ws_t
     u = int(count.item())
     assert int(err.item()) == 0
     want_uid, want_val, bad = oracle.scatter_add_rowsparse(rows_host.reshape(-1), bits(grads),

@@ -1,0 +1,94 @@
+"""GPU parity of the fused forward (engram_lookup: hash and gather in one
+kernel) and of the plan made from the tokens (engram_scatter_plan_tokens)
+against the oracle and against the separate calls: bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from gram_hashed_embedding_amd import workloads
+from tests.gpu_helpers import bits, dev, host_f32, needs_gpu, release
+
+pytestmark = needs_gpu
+E = pytest.importorskip("gram_hashed_embedding_amd.engram")
+
+
+def hash_args(wl, mult):
+    return (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+
+
+def test_lookup_tiny_against_oracle(oracle):
+    wl = workloads.tiny()
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
+    mult = wl.multipliers()
+    for variant, segments in [(0, False), (1, True), (2, False)]:
+        tok = wl.tokens(variant)
+        seg = workloads.random_segments(tok.shape, 20, variant) if segments else None
+        ids = torch.empty((tok.shape[0], tok.shape[1], len(wl.primes)), dtype=torch.int64,
+                          device="cuda")
+        out = E.engram_lookup(dev(tok), table, *hash_args(wl, mult),
+                              seq_ids=None if seg is None else dev(seg), row_ids=ids)
+        torch.cuda.synchronize()
+        want_ids = oracle.hash(tok, *hash_args(wl, mult), seg)
+        assert np.array_equal(ids.cpu().numpy(), want_ids)
+        want, bad = oracle.gather(want_ids, bits(table))
+        assert bad == 0
+        assert np.array_equal(bits(out).reshape(-1, wl.dim), want)
+
+
+@pytest.mark.parametrize("n", range(2, 9))
+@pytest.mark.parametrize("dim", [8, 24, 256])
+def test_lookup_every_order_and_width(oracle, n, dim):
+    """Every ngram size (the kernel is compiled per size) and row widths with
+    1, 3 (not a power of two) and 32 chunks, against the separate calls."""
+    J = 2
+    H = (n - 1) * J
+    primes = workloads.primes_above(3000, H)
+    offs = workloads.cumulative_offsets(primes)
+    rows = sum(primes) + 5
+    mult = workloads.seeded_multipliers(n, 40 + n)
+    rng = np.random.Generator(np.random.PCG64(n * 100 + dim))
+    tok = rng.integers(0, 50, (3, 97)).astype(np.int64)
+    tok[rng.random(tok.shape) < 0.05] = 7
+    seg = workloads.random_segments(tok.shape, 15, n)
+    table = workloads.make_table(rows, dim, n + dim, "cuda")
+    args = (n, J, 7, mult, primes, offs)
+    ids = torch.empty((3, 97, H), dtype=torch.int64, device="cuda")
+    out = E.engram_lookup(dev(tok), table, *args, seq_ids=dev(seg), row_ids=ids)
+    sep_ids = E.engram_hash(dev(tok), *args, rows, seq_ids=dev(seg))
+    sep_out = E.engram_gather(sep_ids, table)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, sep_ids)
+    assert torch.equal(out, sep_out)
+    assert np.array_equal(ids.cpu().numpy(), oracle.hash(tok, *args, seg))
+
+
+@pytest.mark.parametrize("name", ["tiny", "backward", "e2e"])
+@pytest.mark.parametrize("segments", [False, True])
+def test_token_plan_matches_id_plan_and_oracle(oracle, name, segments):
+    wl = workloads.get(name)
+    tok = wl.tokens(4)
+    seg = workloads.random_segments(tok.shape, 200, wl.seed) if segments else None
+    mult = wl.multipliers()
+    args = hash_args(wl, mult)
+    sd = None if seg is None else dev(seg)
+    R = tok.size * len(wl.primes)
+    grads = workloads.make_grads(R, wl.dim, wl.seed + 9, "cuda")
+    ws_t = E.engram_scatter_plan_tokens(dev(tok), wl.table_rows, wl.dim, *args, seq_ids=sd)
+    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, wl.table_rows)
+    ids = E.engram_hash(dev(tok), *args, wl.table_rows, seq_ids=sd)
+    ws_i = E.engram_scatter_plan(ids.view(-1), wl.table_rows, wl.dim)
+    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, wl.table_rows)
+    torch.cuda.synchronize()
+    u = int(cnt_t.item())
+    assert u == int(cnt_i.item())
+    assert torch.equal(uid_t[:u], uid_i[:u])
+    assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
+    if name != "e2e":   # the e2e backward is checked against the oracle at full size elsewhere
+        want_uid, want_val, bad = oracle.scatter_add_rowsparse(ids.cpu().numpy().reshape(-1),
+                                                               bits(grads), wl.dim,
+                                                               wl.table_rows)
+        assert bad == 0 and u == want_uid.size
+        assert np.array_equal(uid_t[:u].cpu().numpy(), want_uid)
+        assert np.array_equal(host_f32(val_t[:u]).view(np.uint32), want_val.view(np.uint32))
+    del grads, ws_t, ws_i
+    release()
