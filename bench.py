@@ -478,6 +478,29 @@ def main():
         unique_rows = int(torch.unique(rows).numel())
     nbytes = algorithmic_bytes(wl, unique_rows)
     sep_bytes = algorithmic_bytes(wl, unique_rows, separate=True)
+    scatter_modes = None
+    if wl.grads == "dense":
+        # the one-call scatter-add, sorted (plan + apply) and fp32-atomic, side
+        # by side on the same ids and gradients (the dense table accumulates)
+        def timed_call(fn, reps=max(args.steps, 3)):
+            fn()
+            torch.cuda.synchronize()
+            a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a_.record(stream)
+            for _ in range(reps):
+                fn()
+            b_.record(stream)
+            torch.cuda.synchronize()
+            return a_.elapsed_time(b_) / reps
+        flat = rows.view(-1)
+        dense_bytes = 8 * R + 2 * D * R + 8 * D * unique_rows
+        scatter_modes = {"algorithmic_bytes": dense_bytes}
+        for name_, mode_ in (("sorted", E.SCATTER_SORTED), ("atomic", E.SCATTER_ATOMIC)):
+            ms_ = timed_call(lambda: E.engram_scatter_add(
+                flat, grads, gtab, mode=mode_,
+                workspace=ws if mode_ == E.SCATTER_SORTED else None))
+            gbps_ = dense_bytes / (ms_ * 1e-3) / 1e9
+            scatter_modes[name_] = {"ms": ms_, "gbps": gbps_, "frac_of_peak": gbps_ / PEAK_HBM_GBS}
     unfused = None
     if signsgd:
         # the fused apply reads the gradient rows and reads + writes each
@@ -581,6 +604,7 @@ def main():
         "phases": phases,
         "separate_calls": separate_calls,
         **({"two_call_apply_and_signsgd": unfused} if unfused else {}),
+        **({"scatter_add_sorted_vs_atomic": scatter_modes} if scatter_modes else {}),
         "roofline": roofline,
         "hbm_copy_ceiling_gbps": copy_gbps,
         "cpu_baseline": cpu,
