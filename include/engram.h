@@ -34,6 +34,11 @@
  *   other row id outside [0, table_rows) is treated the same way AND adds
  *   one to *d_err_count when d_err_count is not NULL (an int64 the caller
  *   zeroes; it stays on the device until the caller reads it).
+ * - The sorted scatter's kernels wait on one another's published counts
+ *   with bounded waits.  Blocks take their tiles in launch order (an atomic
+ *   ticket), so every wait is for a block already running and ends; should
+ *   one ever expire, the call adds 2^40 to *d_err_count (when not NULL)
+ *   instead of hanging, and its results are not valid.
  * - Layouts are row-major and contiguous.  bf16 data is passed as void*.
  */
 #ifndef ENGRAM_H
@@ -257,7 +262,9 @@ int engram_scatter_plan(const int64_t *d_row_ids, int64_t n, int64_t table_rows,
  * written or read.  Arguments as for engram_hash (the hash) and
  * engram_scatter_plan (table_rows, head_dim, the workspace of n ids).
  * Lets the backward's plan start from the tokens alone, beside a forward
- * done with engram_lookup.  Errors: those of both calls.
+ * done with engram_lookup.  Errors: those of both calls.  Hashed rows are
+ * always inside the table, so there is no error counter (nor a place to
+ * report an expired wait).
  */
 int engram_scatter_plan_tokens(const int64_t *d_tokens, const int64_t *d_seq_ids,
                                int64_t batch, int64_t seq, int32_t ngram_size,
