@@ -86,11 +86,30 @@ def algorithmic_bytes(wl, unique_rows, separate=False):
     return out
 
 
+# The sources whose code a kernel of the hot path is built from: the
+# kernel's own file and the device headers it includes.
+KERNEL_HEADERS = ("gram_hashed_embedding_amd/csrc/engram_internal.h",
+                  "gram_hashed_embedding_amd/csrc/engram_hash_dev.h")
+
+
+def code_digest(paths):
+    """sha256 of the code in `paths` (repository-relative) with comments and
+    whitespace removed, so that edits to comments alone keep it."""
+    import hashlib
+    import re
+    h = hashlib.sha256()
+    for rel in paths:
+        text = open(os.path.join(ROOT, rel)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
 def measured_traffic(call, wl):
     """HBM bytes per launch of `call` from the committed rocprofv3 counter
     summary (profiles/hbm_traffic.json), or None when it was taken on another
-    workload or the kernel's source has changed since."""
-    import hashlib
+    workload or the kernel's code has changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if wl.name != "e2e" or not os.path.exists(path):
         return None
@@ -101,8 +120,7 @@ def measured_traffic(call, wl):
     total = 0.0
     for key in parts:
         k = rec[key]
-        src = os.path.join(ROOT, k["source"])
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != k["source_sha256"]:
+        if code_digest([k["source"], *KERNEL_HEADERS]) != k.get("code_sha256"):
             return None
         total += k["fetch_bytes"] + k["write_bytes"]
     return total

@@ -23,7 +23,9 @@
 //     keys and indices in coalesced digit runs staged through LDS.  The
 //     first pass reads the int64 ids directly: valid rows become 32-bit
 //     keys, padding and invalid ids the key table_rows, which sorts last and
-//     is dropped.
+//     is dropped.  A plan made from the tokens first hashes them into
+//     32-bit keys in flat order (counting the digits as it goes), and its
+//     first pass reads those.
 //  2. Segment heads (first position of each distinct row) are counted per
 //     16-position range and scanned in one kernel (decoupled look-back over
 //     tiles of ranges): the scan gives every distinct row its output slot u,
@@ -33,12 +35,13 @@
 //     the sorted order, issues all its loads at once (keys, flat indices,
 //     then the gradient rows) and sums runs in fp64 registers.  A run that
 //     starts and ends inside the range is written once (dense
-//     read-modify-write or row-sparse store); a run cut by the range's end
-//     but ending in the next range is finished by the same walker.  Runs
-//     longer than that (hot rows; the plan lists them) are summed whole by
-//     the leading blocks of the same launch, a block per run, its walkers
-//     taking interleaved ranges of the run and adding their sums in a fixed
-//     order.  No work item waits on another, and hot rows (hundreds of
+//     read-modify-write, row-sparse store, or the SignSGD step on the bf16
+//     table row); a run cut by the range's end but ending in the next range
+//     is finished by the same walker.  Runs longer than that (hot rows,
+//     found from three sorted keys per range) are summed whole by the
+//     leading blocks of the same launch, a block per run, its walkers taking
+//     interleaved ranges of the run and adding their sums in a fixed order.
+//     No work item waits on another, and hot rows (hundreds of
 //     contributions) do not serialise a walker.
 // Atomic path: one fp32 atomic add per gradient element into the dense
 // table (hardware float atomics in L2); order of additions not fixed.
