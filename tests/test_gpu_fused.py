@@ -92,3 +92,34 @@ def test_token_plan_matches_id_plan_and_oracle(oracle, name, segments):
         assert np.array_equal(host_f32(val_t[:u]).view(np.uint32), want_val.view(np.uint32))
     del grads, ws_t, ws_i
     release()
+
+
+@pytest.mark.parametrize("n,J", [(2, 1), (3, 4), (4, 3), (5, 16), (6, 2), (7, 5), (8, 9)])
+def test_token_plan_every_order(n, J):
+    """The plan made from the tokens equals the plan of engram_hash's ids for
+    every ngram size, up to the most heads (64 = 4 orders x 16), with ragged
+    tiles (a batch that is no multiple of the sort tile)."""
+    H = (n - 1) * J
+    primes = workloads.primes_above(5000, H)
+    offs = workloads.cumulative_offsets(primes)
+    rows = sum(primes) + 3
+    mult = workloads.seeded_multipliers(n, 70 + n)
+    rng = np.random.Generator(np.random.PCG64(n * 1000 + J))
+    tok = rng.integers(0, 40, (3, 211)).astype(np.int64)
+    tok[rng.random(tok.shape) < 0.03] = 5
+    seg = workloads.random_segments(tok.shape, 30, n + J)
+    args = (n, J, 5, mult, primes, offs)
+    R = tok.size * H
+    dim = 16
+    grads = workloads.make_grads(R, dim, n + J, "cuda")
+    ws_t = E.engram_scatter_plan_tokens(dev(tok), rows, dim, *args, seq_ids=dev(seg))
+    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, rows)
+    ids = E.engram_hash(dev(tok), *args, rows, seq_ids=dev(seg))
+    ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
+    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, rows)
+    torch.cuda.synchronize()
+    u = int(cnt_t.item())
+    assert u == int(cnt_i.item()) and u > 0
+    assert torch.equal(uid_t[:u], uid_i[:u])
+    assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
+    assert torch.equal(uid_t[:u], torch.unique(ids))
