@@ -108,7 +108,9 @@ __global__ __launch_bounds__(kGatherThreads) void zero_rows_kernel(const int64_t
 // gather_kernel, every lane moves 16-byte chunks of those rows, kUnroll at
 // a time (all loads before the stores).  The row ids never go through
 // memory.  N = ngram_size at compile time, so the history takes no more
-// registers than the order needs.
+// registers than the order needs.  The slice form (one context-parallel
+// rank's forward, _forward_global_slice on the same page) is the same kernel
+// over a window of positions whose history may reach back before it.
 constexpr int kLookRows = 32;
 
 template <int N>
@@ -197,16 +199,22 @@ extern "C" int engram_gather(const int64_t *d_row_ids, int64_t n, const void *d_
   return launch_status();
 }
 
-extern "C" int engram_lookup(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
-                             int64_t seq, int32_t ngram_size, int32_t heads_per_ngram,
-                             int64_t eos_id, const int64_t *h_multipliers,
-                             const int64_t *h_primes, const int64_t *h_offsets,
-                             const void *d_table, int64_t table_rows, int64_t head_dim,
-                             void *d_out, int64_t *d_row_ids, void *stream) {
-  if (seq < 0 || head_dim <= 0 || head_dim % 8 != 0) return ENGRAM_EINVAL;
+namespace engram {
+namespace {
+
+// The fused forward over positions [start, end) of every row of tokens
+// [batch, stride]; shared by engram_lookup (the whole rows) and
+// engram_lookup_slice.
+int lookup_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
+                  int64_t stride, int64_t start, int64_t end, int32_t ngram_size,
+                  int32_t heads_per_ngram, int64_t eos_id, const int64_t *h_multipliers,
+                  const int64_t *h_primes, const int64_t *h_offsets, const void *d_table,
+                  int64_t table_rows, int64_t head_dim, void *d_out, int64_t *d_row_ids,
+                  void *stream) {
+  if (head_dim <= 0 || head_dim % 8 != 0) return ENGRAM_EINVAL;
   HashParams h;
   int64_t tokens = 0;
-  const int rc = make_hash_params(d_tokens, d_seq_ids, batch, seq, 0, seq, ngram_size,
+  const int rc = make_hash_params(d_tokens, d_seq_ids, batch, stride, start, end, ngram_size,
                                   heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets,
                                   table_rows, &h, &tokens);
   if (rc != ENGRAM_OK) return rc;
@@ -242,4 +250,31 @@ extern "C" int engram_lookup(const int64_t *d_tokens, const int64_t *d_seq_ids, 
 #undef ENGRAM_LOOKUP_CASE
   }
   return launch_status();
+}
+
+}  // namespace
+}  // namespace engram
+
+extern "C" int engram_lookup(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
+                             int64_t seq, int32_t ngram_size, int32_t heads_per_ngram,
+                             int64_t eos_id, const int64_t *h_multipliers,
+                             const int64_t *h_primes, const int64_t *h_offsets,
+                             const void *d_table, int64_t table_rows, int64_t head_dim,
+                             void *d_out, int64_t *d_row_ids, void *stream) {
+  if (seq < 0) return ENGRAM_EINVAL;
+  return lookup_window(d_tokens, d_seq_ids, batch, seq, 0, seq, ngram_size, heads_per_ngram,
+                       eos_id, h_multipliers, h_primes, h_offsets, d_table, table_rows, head_dim,
+                       d_out, d_row_ids, stream);
+}
+
+extern "C" int engram_lookup_slice(const int64_t *d_tokens, const int64_t *d_seq_ids,
+                                   int64_t batch, int64_t global_seq, int64_t seq_start,
+                                   int64_t seq_end, int32_t ngram_size, int32_t heads_per_ngram,
+                                   int64_t eos_id, const int64_t *h_multipliers,
+                                   const int64_t *h_primes, const int64_t *h_offsets,
+                                   const void *d_table, int64_t table_rows, int64_t head_dim,
+                                   void *d_out, int64_t *d_row_ids, void *stream) {
+  return lookup_window(d_tokens, d_seq_ids, batch, global_seq, seq_start, seq_end, ngram_size,
+                       heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets, d_table,
+                       table_rows, head_dim, d_out, d_row_ids, stream);
 }

@@ -56,6 +56,11 @@ _lib.engram_lookup.restype = ctypes.c_int
 _lib.engram_lookup.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
                                ctypes.c_int32, ctypes.c_int64, _i64p, _i64p, _i64p, _vp,
                                ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
+_lib.engram_lookup_slice.restype = ctypes.c_int
+_lib.engram_lookup_slice.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int64, _i64p, _i64p, _i64p, _vp, ctypes.c_int64,
+                                     ctypes.c_int64, _vp, _vp, _vp]
 _lib.engram_scatter_plan_tokens.restype = ctypes.c_int
 _lib.engram_scatter_plan_tokens.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64,
                                             ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
@@ -219,13 +224,12 @@ def engram_hash_slice(tokens, seq_start, seq_end, ngram_size, heads_per_ngram, e
 
 def forward_global_slice(tokens, seq_start, seq_end, table, ngram_size, heads_per_ngram,
                          eos_id, multipliers, primes, offsets, seq_ids=None, stream=None):
-    """The slice's values bf16 [batch, seq_end - seq_start, H * head_dim]:
-    engram_hash_slice, then engram_gather (two library calls)."""
-    rows = engram_hash_slice(tokens, seq_start, seq_end, ngram_size, heads_per_ngram, eos_id,
-                             multipliers, primes, offsets, table.shape[0], seq_ids=seq_ids,
-                             stream=stream)
-    out = engram_gather(rows, table, stream=stream)
-    return out.reshape(rows.shape[0], rows.shape[1], -1)
+    """The slice's values bf16 [batch, seq_end - seq_start, H * head_dim]
+    (engram_lookup_slice: one library call)."""
+    out = engram_lookup_slice(tokens, seq_start, seq_end, table, ngram_size, heads_per_ngram,
+                              eos_id, multipliers, primes, offsets, seq_ids=seq_ids,
+                              stream=stream)
+    return out.reshape(out.shape[0], out.shape[1], -1)
 
 
 def engram_gather(row_ids, table, out=None, err_count=None, stream=None):
@@ -502,6 +506,42 @@ def engram_lookup(tokens, table, ngram_size, heads_per_ngram, eos_id, multiplier
                                     _ptr(table), rows, dim, _ptr(out), _ptr(row_ids),
                                     _stream(tokens.device, stream))
     _check(status, "engram_lookup")
+    return out
+
+
+def engram_lookup_slice(tokens, seq_start, seq_end, table, ngram_size, heads_per_ngram, eos_id,
+                        multipliers, primes, offsets, seq_ids=None, out=None, row_ids=None,
+                        stream=None):
+    """engram_lookup for positions [seq_start, seq_end) of the complete
+    sequence tokens int64 [batch, global_seq] (history may reach back before
+    seq_start): bf16 [batch, seq_end - seq_start, H, head_dim]; also writes
+    the ids into row_ids (int64 [batch, seq_end - seq_start, H]) when given."""
+    heads, mult, pr, off = _hash_args(tokens, ngram_size, heads_per_ngram, multipliers, primes,
+                                      offsets, seq_ids)
+    _device_tensor(table, torch.bfloat16, "table")
+    if table.dim() != 2:
+        raise ValueError("table must be [rows, head_dim]")
+    batch, gseq = tokens.shape
+    start, end = int(seq_start), int(seq_end)
+    if not 0 <= start <= end <= gseq:
+        raise ValueError(f"slice [{start}, {end}) is not inside [0, {gseq})")
+    local = end - start
+    rows, dim = table.shape
+    if out is None:
+        out = torch.empty((batch, local, heads, dim), dtype=torch.bfloat16, device=tokens.device)
+    _device_tensor(out, torch.bfloat16, "out")
+    if out.numel() != batch * local * heads * dim:
+        raise ValueError("out must hold batch * (seq_end - seq_start) * H * head_dim values")
+    if row_ids is not None:
+        _device_tensor(row_ids, torch.int64, "row_ids")
+        if row_ids.numel() != batch * local * heads:
+            raise ValueError("row_ids must hold batch * (seq_end - seq_start) * H ids")
+    with torch.cuda.device(tokens.device):
+        status = _lib.engram_lookup_slice(_ptr(tokens), _ptr(seq_ids), batch, gseq, start, end,
+                                          int(ngram_size), int(heads_per_ngram), int(eos_id),
+                                          mult, pr, off, _ptr(table), rows, dim, _ptr(out),
+                                          _ptr(row_ids), _stream(tokens.device, stream))
+    _check(status, "engram_lookup_slice")
     return out
 
 

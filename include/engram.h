@@ -123,7 +123,8 @@ int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids,
  *   d_row_ids            int64 [batch, seq_end - seq_start, H], written.
  * Errors: those of engram_hash, and EINVAL for a slice outside the sequence.
  * An empty slice (or batch 0) enqueues nothing.  Pass the result to
- * engram_gather for the slice's values ([batch, local, H, head_dim]).
+ * engram_gather for the slice's values ([batch, local, H, head_dim]), or use
+ * engram_lookup_slice, which does both in one pass.
  */
 int engram_hash_slice(const int64_t *d_tokens, const int64_t *d_seq_ids,
                       int64_t batch, int64_t global_seq, int64_t seq_start,
@@ -153,6 +154,31 @@ int engram_lookup(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t bat
                   const int64_t *h_multipliers, const int64_t *h_primes,
                   const int64_t *h_offsets, const void *d_table, int64_t table_rows,
                   int64_t head_dim, void *d_out, int64_t *d_row_ids, void *stream);
+
+/*
+ * engram_lookup_slice -- engram_lookup for positions [seq_start, seq_end) of
+ * every row of a complete sequence: one context-parallel rank's forward in
+ * one pass.  d_out[b, t - seq_start, h, :] equals what engram_lookup gives at
+ * (b, t, h) for the whole [batch, global_seq] input.
+ *
+ * Follows [API] Qwen3_8_FlashNextNGramEmbedding._forward_global_slice (the
+ * whole replicated sequence is hashed, so a slice sees the tokens before its
+ * first position and the EOS resets there; only the slice's rows are looked
+ * up) and the sources of engram_lookup.  Arguments as for engram_lookup,
+ * with:
+ *   d_tokens, d_seq_ids  int64 [batch, global_seq] (d_seq_ids may be NULL).
+ *   seq_start, seq_end   the slice, 0 <= seq_start <= seq_end <= global_seq.
+ *   d_out     bf16 [batch, seq_end - seq_start, H, head_dim], written.
+ *   d_row_ids int64 [batch, seq_end - seq_start, H], or NULL.
+ * Errors: those of engram_lookup, and EINVAL for a slice outside the
+ * sequence.  An empty slice (or batch 0) enqueues nothing.
+ */
+int engram_lookup_slice(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
+                        int64_t global_seq, int64_t seq_start, int64_t seq_end,
+                        int32_t ngram_size, int32_t heads_per_ngram, int64_t eos_id,
+                        const int64_t *h_multipliers, const int64_t *h_primes,
+                        const int64_t *h_offsets, const void *d_table, int64_t table_rows,
+                        int64_t head_dim, void *d_out, int64_t *d_row_ids, void *stream);
 
 /*
  * engram_gather -- d_out[i, :] = d_table[d_row_ids[i], :] (bitwise bf16 copy).

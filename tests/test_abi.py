@@ -25,7 +25,8 @@ def test_every_declared_symbol_is_exported():
                           "engram_scatter_plan", "engram_scatter_apply",
                           "engram_hash_slice", "engram_signsgd_rowsparse",
                           "engram_scatter_apply_signsgd", "engram_ple_conv",
-                          "engram_lookup", "engram_scatter_plan_tokens"}
+                          "engram_lookup", "engram_scatter_plan_tokens",
+                          "engram_lookup_slice"}
     for name in names:
         assert hasattr(e._lib, name), name
 
@@ -215,3 +216,20 @@ def test_lookup_and_token_plan_reject():
     assert plan(wsb=ws - 1) == e.ENGRAM_EWORKSPACE
     assert plan(work=MISALIGNED) == e.ENGRAM_EWORKSPACE
     assert plan(tokens=None) == e.ENGRAM_EINVAL
+
+
+def test_lookup_slice_rejects():
+    ls = e._lib.engram_lookup_slice
+    def look(start=1, end=3, gseq=4, dim=8, table=ALIGNED, out=ALIGNED, tokens=FAKE, batch=1):
+        return ls(tokens, None, batch, gseq, start, end, 3, 2, 0, _arr((1, 2, 3)),
+                  _arr((5, 7, 11, 13)), _arr((0, 5, 12, 23)), table, 36, dim, out, None, None)
+    assert look(start=-1) == e.ENGRAM_EINVAL
+    assert look(start=3, end=2) == e.ENGRAM_EINVAL       # slice reversed
+    assert look(end=5) == e.ENGRAM_EINVAL                # past the sequence
+    assert look(dim=12) == e.ENGRAM_EINVAL
+    assert look(table=None) == e.ENGRAM_EINVAL
+    assert look(tokens=None) == e.ENGRAM_EINVAL
+    assert look(out=MISALIGNED) == e.ENGRAM_EALIGN
+    # empty slices and batches enqueue nothing
+    assert look(start=2, end=2, table=None, out=None) == e.ENGRAM_OK
+    assert look(batch=0, tokens=None, table=None, out=None) == e.ENGRAM_OK

@@ -1,5 +1,6 @@
 """GPU parity of the global-slice hash (engram_hash_slice) and of the slice
-forward (hash slice, then gather) against the oracle: bit-exact."""
+forward (engram_lookup_slice, and hash slice then gather) against the oracle:
+bit-exact."""
 import numpy as np
 import pytest
 import torch
@@ -65,7 +66,7 @@ def test_golden_slices(oracle, case):
 
 
 def test_slice_forward_tiny(oracle):
-    """Hash slice + gather, every output against the oracle."""
+    """The fused slice forward, every output against the oracle."""
     wl = workloads.tiny()
     table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
     tok = wl.tokens(2)
@@ -90,3 +91,29 @@ def test_empty_slice_and_rejects():
     for a, b in [(-1, 4), (5, 4), (0, 129)]:
         with pytest.raises(ValueError):
             E.engram_hash_slice(tok, a, b, *args)
+
+
+@pytest.mark.parametrize("name", ["medium", "e2e"])
+@pytest.mark.parametrize("segments", [False, True])
+def test_lookup_slice_matches_hash_slice_and_gather(name, segments):
+    """engram_lookup_slice (one pass, ids also written) equals engram_hash_slice
+    followed by engram_gather on every slice of slices_of, bit for bit."""
+    wl = workloads.get(name)
+    tok = wl.tokens(5)
+    seg = workloads.random_segments(tok.shape, 300, wl.seed + 1) if segments else None
+    sd = None if seg is None else dev(seg)
+    mult = wl.multipliers()
+    args = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
+    td = dev(tok)
+    H = len(wl.primes)
+    for a, b in slices_of(tok.shape[1], wl.seed + 2):
+        ids = torch.empty((tok.shape[0], b - a, H), dtype=torch.int64, device="cuda")
+        out = E.engram_lookup_slice(td, a, b, table, *args, seq_ids=sd, row_ids=ids)
+        want_ids = E.engram_hash_slice(td, a, b, *args, wl.table_rows, seq_ids=sd)
+        want = E.engram_gather(want_ids, table)
+        torch.cuda.synchronize()
+        assert out.shape == (tok.shape[0], b - a, H, wl.dim)
+        assert torch.equal(ids, want_ids), (a, b)
+        assert torch.equal(out.view(torch.int16), want.view(torch.int16)), (a, b)
+    del table
