@@ -187,6 +187,7 @@ extern "C" int engram_ple_conv(const void *d_x, const void *d_halo, int64_t halo
     return ENGRAM_EINVAL;
   if (kernel_size < 1 || kernel_size > kMaxKernel || dilation < 1) return ENGRAM_EINVAL;
   if (halo_len > 0 && d_halo == nullptr) return ENGRAM_EINVAL;
+  if (seq > INT64_MAX / 2 - halo_len || channels > INT64_MAX / 8) return ENGRAM_EINVAL;
   if (!mul_fits(batch, seq + halo_len, INT64_MAX / 8) ||
       !mul_fits(batch * (seq + halo_len), channels * 2, INT64_MAX))
     return ENGRAM_EINVAL;

@@ -152,7 +152,8 @@ using namespace engram;
 extern "C" int engram_gather(const int64_t *d_row_ids, int64_t n, const void *d_table,
                              int64_t table_rows, int64_t head_dim, void *d_out,
                              int64_t *d_err_count, void *stream) {
-  if (n < 0 || table_rows < 0 || head_dim <= 0 || head_dim % 8 != 0) return ENGRAM_EINVAL;
+  if (n < 0 || table_rows < 0 || head_dim <= 0 || head_dim % 8 != 0 || head_dim > kMaxDim)
+    return ENGRAM_EINVAL;
   if (!mul_fits(table_rows, head_dim * 2, INT64_MAX) || !mul_fits(n, head_dim * 2, INT64_MAX))
     return ENGRAM_EINVAL;
   if (n == 0) return ENGRAM_OK;
@@ -211,7 +212,7 @@ int lookup_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t bat
                   const int64_t *h_primes, const int64_t *h_offsets, const void *d_table,
                   int64_t table_rows, int64_t head_dim, void *d_out, int64_t *d_row_ids,
                   void *stream) {
-  if (head_dim <= 0 || head_dim % 8 != 0) return ENGRAM_EINVAL;
+  if (head_dim <= 0 || head_dim % 8 != 0 || head_dim > kMaxDim) return ENGRAM_EINVAL;
   HashParams h;
   int64_t tokens = 0;
   const int rc = make_hash_params(d_tokens, d_seq_ids, batch, stride, start, end, ngram_size,

@@ -26,6 +26,10 @@ inline int launch_status() {
   return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
 }
 
+// Widest row any entry point takes (2^30 values); keeps every byte count of
+// a row far from overflow.
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
 // a * b <= limit for non-negative a, b, without overflow.
 inline bool mul_fits(int64_t a, int64_t b, int64_t limit) {
   return a == 0 || b <= limit / a;

@@ -40,6 +40,8 @@
  *   one ever expire, the call adds 2^40 to *d_err_count (when not NULL)
  *   instead of hanging, and its results are not valid.
  * - Layouts are row-major and contiguous.  bf16 data is passed as void*.
+ * - head_dim, wherever it is taken, is at most 2^30 (the sorted scatter and
+ *   its plan: at most 2048); larger values are EINVAL.
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H

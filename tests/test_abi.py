@@ -169,6 +169,8 @@ def test_signsgd_rejects():
     assert sg(ALIGNED, MISALIGNED, ALIGNED, 10, 8, ALIGNED, 50, 0.1, None, None) == e.ENGRAM_EALIGN
     assert sg(ALIGNED, ALIGNED, ALIGNED, 10, 8, MISALIGNED, 50, 0.1, None, None) == e.ENGRAM_EALIGN
     assert sg(None, None, None, 0, 8, None, 50, 0.1, None, None) == e.ENGRAM_OK
+    assert sg(ALIGNED, ALIGNED, ALIGNED, 10, 8, ALIGNED, 1 << 60, 0.1, None, None) == \
+        e.ENGRAM_EINVAL                                   # table size overflows
     ap = e._lib.engram_scatter_apply_signsgd
     ws = e.engram_scatter_add_workspace(100, 50, 8, 2)
     assert ap(ALIGNED, 100, 12, 50, ALIGNED, 0.1, ALIGNED, ws, None) == e.ENGRAM_EINVAL
@@ -193,6 +195,8 @@ def test_ple_conv_rejects():
     assert call(x=MISALIGNED) == e.ENGRAM_EALIGN
     assert call(halo=MISALIGNED, halo_len=9) == e.ENGRAM_EALIGN
     assert call(seq=0, x=None, out=None) == e.ENGRAM_OK
+    assert call(seq=(1 << 62), halo=ALIGNED, halo_len=(1 << 62)) == e.ENGRAM_EINVAL  # overflow
+    assert call(ch=(1 << 61)) == e.ENGRAM_EINVAL
 
 
 def test_lookup_and_token_plan_reject():
