@@ -195,7 +195,7 @@ extern "C" int engram_ple_conv(const void *d_x, const void *d_halo, int64_t halo
   if (d_x == nullptr || d_weight == nullptr || d_out == nullptr) return ENGRAM_EINVAL;
   if (!aligned16(d_x) || !aligned16(d_out) || (d_halo != nullptr && !aligned16(d_halo)))
     return ENGRAM_EALIGN;
-  ConvArgs a;
+  ConvArgs a = {};
   a.x = static_cast<const uint2 *>(d_x);
   a.halo = static_cast<const uint2 *>(d_halo);
   a.seg = d_seq_ids;
