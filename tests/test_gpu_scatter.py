@@ -294,3 +294,46 @@ def test_signsgd_rejects():
     with pytest.raises(E.EngramError):
         E.engram_signsgd_rowsparse(ids, torch.zeros((4, 12), device="cuda"),
                                    torch.zeros(1, dtype=torch.int64, device="cuda"), t, 0.1)
+
+
+def random_ids(rng, n, rows):
+    """A seeded mix of the id patterns the backward meets: uniform rows,
+    Zipf-like hot rows (long runs after sorting, some spanning several
+    walker ranges), a few rows repeated hundreds of times, padding (-1) and
+    ids outside the table."""
+    kind = rng.integers(0, 4)
+    if kind == 0:
+        ids = rng.integers(0, rows, n)
+    elif kind == 1:
+        ranks = np.minimum(rng.zipf(1.2, n), rows) - 1
+        ids = rng.permutation(rows)[ranks] if rows <= 1 << 22 else ranks
+    elif kind == 2:
+        hot = rng.integers(0, rows, int(rng.integers(1, 6)))
+        ids = np.where(rng.random(n) < 0.6, hot[rng.integers(0, hot.size, n)],
+                       rng.integers(0, rows, n))
+    else:
+        ids = np.sort(rng.integers(0, rows, n))  # already sorted: runs at every boundary
+    ids = ids.astype(np.int64)
+    ids[rng.random(n) < 0.02] = -1
+    bad = rng.random(n) < 0.005
+    ids[bad] = rows + rng.integers(0, 1000, int(bad.sum()))
+    return ids
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_sweep(oracle, seed):
+    """Seeded random shapes: every output mode bit for bit (atomic within its
+    bound), widths from 8 to 1024; even seeds take small tables (rows from 1
+    up, log-uniform: long runs), odd seeds large ones (up to a few million
+    rows: mostly distinct ids)."""
+    rng = np.random.Generator(np.random.PCG64(9000 + seed))
+    dim = int(rng.choice([8, 16, 24, 40, 64, 128, 256, 520, 1024]))
+    max_rows = max(1, (1 << 23) // dim)
+    if seed % 2 == 0:
+        rows = int(min(max_rows, np.exp(rng.uniform(0, np.log(max_rows)))) + 1)
+    else:
+        rows = int(max_rows * rng.uniform(0.5, 1.0))
+    n = int(rng.integers(1, 40000 if dim <= 256 else 6000))
+    ids = random_ids(rng, n, rows)
+    check_all_modes(oracle, ids, dim, rows, 500 + seed)
+    release()
