@@ -62,6 +62,10 @@ constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnroll = 4;
 
 constexpr int64_t kLongBlocks = 1024;  // most blocks that sum long runs
+// Gradient tensors larger than this are read with non-temporal loads: half
+// the MI355X's 256 MB Infinity Cache, so a tensor that could still be cached
+// when the apply runs is read normally.
+constexpr int64_t kStreamGradBytes = int64_t(128) << 20;
 constexpr int64_t kLongSpan = 64;      // fewest ranges per such block
 // Global digit totals are kept in kHistCopies copies (a block adds to copy
 // blockIdx % kHistCopies) so the histogram's atomics do not all meet on the
@@ -472,6 +476,7 @@ struct WalkArgs {
   int64_t n;
   uint32_t sentinel;
   const uint2 *grads;  // [n, dim / 4] quads of 4 bf16
+  bool stream_grads;   // read the gradient rows with non-temporal loads
   int64_t quads;       // dim / 4
   int64_t dim;
   const uint32_t *head_off;  // slot of each range's first distinct row
@@ -542,11 +547,26 @@ __device__ __forceinline__ void load_grad_row(const WalkArgs &a, uint32_t idx, i
     g[k] = EXACT ? row[lane + k * L] : row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)];
 }
 
-// This lane's quads of one gradient row.
-template <int L, int Q, bool EXACT>
+// This lane's quads of one gradient row.  Every gradient row is read exactly
+// once; when the gradients are far larger than the caches (NT, chosen once per
+// launch from stream_grads) the loads are non-temporal, so they do not displace
+// the lines that are reused (keys, indices, the rows being written).  A
+// gradient tensor small enough to stay cached (just written by the layer
+// above, say) is read normally.
+template <int L, int Q, bool EXACT, bool NT>
 __device__ __forceinline__ void load_row(const WalkArgs &a, uint32_t idx, int lane,
                                          uint2 (&g)[Q]) {
-  load_quads<L, Q, EXACT>(a.grads, idx, a.quads, lane, g);
+  if constexpr (!NT) {
+    load_quads<L, Q, EXACT>(a.grads, idx, a.quads, lane, g);
+    return;
+  }
+  const u32x2 *row = reinterpret_cast<const u32x2 *>(a.grads) + (int64_t)idx * a.quads;
+#pragma unroll
+  for (int k = 0; k < Q; ++k) {
+    const u32x2 t = __builtin_nontemporal_load(
+        EXACT ? &row[lane + k * L] : &row[min((int64_t)lane + (int64_t)k * L, a.quads - 1)]);
+    g[k] = uint2{t.x, t.y};
+  }
 }
 
 // Keys and flat indices of one range as 16-byte vectors.
@@ -624,7 +644,7 @@ __device__ __forceinline__ void emit_row(uint32_t key, uint32_t u, const WalkArg
 // only then are runs summed and written.  A run that crosses into the next
 // range (and, not being long, ends there) is finished by its owner, which
 // then reads the next range's keys and the continuation rows.
-template <int L, int Q, int OUT, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT, bool NT>
 __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
   const int lane = threadIdx.x % L;
   const int64_t w = (blk * kWalkThreads + threadIdx.x) / L;
@@ -695,7 +715,7 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
 #pragma unroll
     for (int qq = 0; qq < B; ++qq) {
       const int q = b0 + qq;
-      load_row<L, Q, EXACT>(a, (q >= lead && q < tail) ? vv[q] : 0u, lane, g[qq]);
+      load_row<L, Q, EXACT, NT>(a, (q >= lead && q < tail) ? vv[q] : 0u, lane, g[qq]);
     }
 #pragma unroll
     for (int qq = 0; qq < B; ++qq) {
@@ -737,7 +757,7 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
     for (int q0 = 0; q0 < m; q0 += 4) {
       uint2 g[4][Q];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) load_row<L, Q, EXACT>(a, q0 + b < m ? nv[q0 + b] : 0u, lane, g[b]);
+      for (int b = 0; b < 4; ++b) load_row<L, Q, EXACT, NT>(a, q0 + b < m ? nv[q0 + b] : 0u, lane, g[b]);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         if (q0 + b < m) add_quads<Q>(acc, g[b]);
@@ -747,7 +767,7 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
 }
 
 // One long run: the run that starts in range c0 and reaches range c0 + 2.
-template <int L, int Q, int OUT, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT, bool NT>
 __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
                                          double (&s_part)[kWalkThreads / L][L * 4]) {
   constexpr int G = kWalkThreads / L;  // walkers per block
@@ -797,7 +817,7 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
 #pragma unroll
       for (int q = 0; q < kRange; ++q) {
         const int64_t p = c * kRange + q;
-        load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? vv[q] : 0u, lane, rows[q]);
+        load_row<L, Q, EXACT, NT>(a, (p >= start && p < stop) ? vv[q] : 0u, lane, rows[q]);
       }
       if (c + G <= c1) load_vals(a.vals, (c + G) * kRange, vv);
 #pragma unroll
@@ -821,7 +841,7 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
 #pragma unroll
         for (int qq = 0; qq < B; ++qq) {
           const int64_t p = p0 + b0 + qq;
-          load_row<L, Q, EXACT>(a, (p >= start && p < stop) ? idx[qq] : 0u, lane, rows[qq]);
+          load_row<L, Q, EXACT, NT>(a, (p >= start && p < stop) ? idx[qq] : 0u, lane, rows[qq]);
         }
 #pragma unroll
         for (int qq = 0; qq < B; ++qq) {
@@ -856,7 +876,7 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
 // range ahead, its rows all in flight), and walker 0 adds the walkers' sums
 // in walker order before writing the row.  Fixed assignment and fixed order keep the result
 // deterministic.
-template <int L, int Q, int OUT, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT, bool NT>
 __device__ __forceinline__ void long_runs(const WalkArgs &a) {
   __shared__ double s_part[kWalkThreads / L][L * 4];
   __shared__ uint32_t s_list[kWalkThreads];
@@ -885,21 +905,21 @@ __device__ __forceinline__ void long_runs(const WalkArgs &a) {
     }
     if (flagged) s_list[at] = (uint32_t)r;
     __syncthreads();
-    for (int i = 0; i < count; ++i) long_run<L, Q, OUT, EXACT>(a, s_list[i], s_part);
+    for (int i = 0; i < count; ++i) long_run<L, Q, OUT, EXACT, NT>(a, s_list[i], s_part);
     __syncthreads();  // s_list and s_wave_count are rewritten for the next stretch
   }
 }
 
 // The apply kernel: blocks [0, long_blocks) sum the long runs, the rest are
 // range walkers, kWalkThreads / L walkers per block.
-template <int L, int Q, int OUT, bool EXACT>
+template <int L, int Q, int OUT, bool EXACT, bool NT>
 __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
   if (OUT == kOutSparse && blockIdx.x == 0 && threadIdx.x == 0)
     *a.num_unique = (int64_t)*a.unique_total;
   if (blockIdx.x < a.long_blocks)
-    long_runs<L, Q, OUT, EXACT>(a);
+    long_runs<L, Q, OUT, EXACT, NT>(a);
   else
-    walk_range<L, Q, OUT, EXACT>(a, (int64_t)blockIdx.x - a.long_blocks);
+    walk_range<L, Q, OUT, EXACT, NT>(a, (int64_t)blockIdx.x - a.long_blocks);
 }
 
 __global__ void write_zero_kernel(int64_t *p) { *p = 0; }
@@ -1002,11 +1022,18 @@ void launch_walkers(const WalkArgs &a, hipStream_t s) {
   const int64_t threads = a.num_ranges * L;
   const unsigned blocks =
       a.long_blocks + (unsigned)((threads + kWalkThreads - 1) / kWalkThreads);
-  if (a.quads == (int64_t)Q * L)
-    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, true>), dim3(blocks),
+  const bool exact = a.quads == (int64_t)Q * L;
+  if (exact && a.stream_grads)
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, true, true>), dim3(blocks),
+                       dim3(kWalkThreads), 0, s, a);
+  else if (exact)
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, true, false>), dim3(blocks),
+                       dim3(kWalkThreads), 0, s, a);
+  else if (a.stream_grads)
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, false, true>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, false>), dim3(blocks),
+    hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, false, false>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
 }
 
@@ -1131,6 +1158,7 @@ int apply_sorted(const void *grads, int64_t n, int64_t dim, int64_t table_rows, 
   a.n = n;
   a.sentinel = (uint32_t)table_rows;
   a.grads = static_cast<const uint2 *>(grads);
+  a.stream_grads = n * dim * 2 > kStreamGradBytes;
   a.quads = dim / 4;
   a.dim = dim;
   a.head_off = v.head_off;
