@@ -37,8 +37,10 @@ done in two calls (row-sparse apply, then engram_signsgd_rowsparse).
 
 --workload cp_slice times one context-parallel rank's forward on the
 full-scale workload (tokens [1, 32768], 32 heads, the 200M x 256 table):
-engram_hash_slice over the last of 8 equal slices of the replicated
-sequence (with its packed-segment ids), then engram_gather of that slice.
+engram_lookup_slice over the last of 8 equal slices of the replicated
+sequence (with its packed-segment ids), hashing and gathering the slice in
+one kernel; the two-call form (engram_hash_slice, then engram_gather) is
+timed beside it.
 """
 from __future__ import annotations
 
