@@ -271,8 +271,8 @@ int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
  *     least engram_scatter_add_workspace(n, table_rows, head_dim,
  *     ENGRAM_SCATTER_ROWSPARSE) bytes; d_err_count as elsewhere.
  *   engram_scatter_apply: the same n, head_dim, table_rows and workspace as
- *     the plan, with the plan's work ordered before it (same stream, or an
- *     event).  Exactly one output form: d_grad_table (dense, accumulated), or
+ *     the plan (made by either plan call), with the plan's work ordered
+ *     before it (same stream, or an event).  Exactly one output form: d_grad_table (dense, accumulated), or
  *     all of d_unique_ids / d_unique_grads / d_num_unique (row-sparse).  The
  *     apply does not change the plan; it may run again on the same plan.  A
  *     workspace that holds no plan of these ids gives undefined results.
@@ -343,8 +343,9 @@ int engram_signsgd_rowsparse(const int64_t *d_unique_ids, const float *d_unique_
  * Citations as for those two calls.
  *   d_grads bf16 [n, head_dim]; d_table bf16 [table_rows, head_dim], updated
  *   in place; lr the learning rate; the workspace holds a plan of the n ids
- *   made by engram_scatter_plan (same n, head_dim and table_rows), ordered
- *   before this call.  d_grads and d_table 16-byte aligned.
+ *   made by engram_scatter_plan or engram_scatter_plan_tokens (same n,
+ *   head_dim and table_rows), ordered before this call.  d_grads and d_table
+ *   16-byte aligned.
  * Errors: EINVAL, EALIGN, EWORKSPACE.  n == 0 enqueues nothing.
  */
 int engram_scatter_apply_signsgd(const void *d_grads, int64_t n, int64_t head_dim,
