@@ -23,9 +23,15 @@
 //     keys and indices in coalesced digit runs staged through LDS.  The
 //     first pass reads the int64 ids directly: valid rows become 32-bit
 //     keys, padding and invalid ids the key table_rows, which sorts last and
-//     is dropped.  A plan made from the tokens first hashes them into
-//     32-bit keys in flat order (counting the digits as it goes), and its
-//     first pass reads those.
+//     is dropped.  A plan made from the tokens first hashes them into 32-bit
+//     keys (counting the digits as it goes), and its first pass reads those.
+//     When the heads own disjoint row ranges (as when the offsets pack them
+//     back to back) every row belongs to one head, so the
+//     keys are laid out and sorted per head: one segment per head, in order
+//     of offset, each sorted on the bits of its largest remainder (23 bits
+//     for 8.3M-row heads instead of the 28 of a 200M-row table: 3 passes
+//     instead of 4), with look-back inside the segment.  The segments one
+//     after another are the same sorted order a sort of all the keys gives.
 //  2. Segment heads (first position of each distinct row) are counted per
 //     16-position range and scanned in one kernel (decoupled look-back over
 //     tiles of ranges): the scan gives every distinct row its output slot u,
@@ -71,9 +77,14 @@ constexpr int64_t kLongSpan = 64;      // fewest ranges per such block
 // blockIdx % kHistCopies) so the histogram's atomics do not all meet on the
 // same few hundred words; readers add the copies.
 constexpr int kHistCopies = 8;
-// counters: digit totals, 4 pass tickets, the slot scan's ticket (and padding)
-constexpr int kSortCounters = kHistCopies * 4 * 256 + 8;
-constexpr int kSlotTicketAt = kHistCopies * 4 * 256 + 4;
+// counters: 4 pass tickets and the slot scan's ticket (8 words), then the
+// digit totals, [copy][segment][pass][digit]: kHistCopies copies of one
+// segment for a sort of the whole key array, or one copy per segment for a
+// sort of per-head segments.
+constexpr int kTicketWords = 8;
+constexpr int kSlotTicketAt = 4;
+constexpr int kHistSets = kHistCopies > ENGRAM_MAX_HEADS ? kHistCopies : ENGRAM_MAX_HEADS;
+constexpr int kSortCounters = kTicketWords + kHistSets * 4 * kMaxBins;
 static_assert(kWave % kRange == 0 && kRange % 4 == 0, "ranges tile a wavefront");
 
 // ----------------------------------------------------------------- keys ----
@@ -85,6 +96,26 @@ __device__ __forceinline__ uint32_t make_key(int64_t id, int64_t table_rows, int
   bad += id != -1 ? 1 : 0;
   return (uint32_t)table_rows;
 }
+
+// Segments of a sort: the keys are sorted within `count` consecutive segments
+// of `len` keys each.  A plan from ids, or from tokens whose heads' row ranges
+// overlap, has one segment of all n keys.  A plan from tokens whose heads own
+// disjoint row ranges sorts each head's keys on their own: segment s holds head
+// head[s]'s rows in token order, the heads ordered by row offset, so the
+// segments one after another are sorted as a whole.  A key's digits are taken
+// from key - base[s] (base[s] = the head's offset), so the sort needs only the
+// bits of the largest prime, and a tile's look-back stops at its segment's
+// first tile.
+struct SortSegs {
+  int64_t len;     // keys per segment
+  int64_t tiles;   // tiles per segment
+  int32_t count;   // segments
+  int32_t copies;  // copies of each segment's digit totals
+  int32_t stride;  // the key at position t of segment s has flat index t * stride + head[s]
+  int32_t pad;
+  uint32_t base[ENGRAM_MAX_HEADS];
+  uint32_t head[ENGRAM_MAX_HEADS];
+};
 
 // ------------------------------------------------------------ block scan ---
 // Exclusive scan of one value per thread over an NT-thread block.
@@ -114,14 +145,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t &t
 
 // ------------------------------------------------------------ radix sort ---
 // One-sweep LSD radix sort.  One kernel clears the look-back state, one
-// counts every pass's digits over all keys (the global digit totals of a
-// pass do not depend on the order the keys are in), then one kernel per
-// pass: a block takes the next tile by atomic ticket, ranks its keys with a
-// wavefront multi-split, publishes its per-digit counts, learns the counts
-// of all earlier tiles by decoupled look-back, stages the tile in LDS in
-// sorted order and writes it out in coalesced runs.
+// counts every pass's digits over each segment's keys (a segment's digit
+// totals of a pass do not depend on the order its keys are in), then one
+// kernel per pass: a block takes the next tile by atomic ticket, ranks its
+// keys with a wavefront multi-split, publishes its per-digit counts, learns
+// the counts of its segment's earlier tiles by decoupled look-back, stages
+// the tile in LDS in sorted order and writes it out in coalesced runs.
 constexpr uint64_t kFlagAggregate = 1ull << 32;  // count of this tile only
-constexpr uint64_t kFlagInclusive = 2ull << 32;  // count of tiles 0..this
+constexpr uint64_t kFlagInclusive = 2ull << 32;  // count of the segment's tiles up to this
 constexpr uint32_t kSpinLimit = 1u << 22;        // bound on every look-back wait
 constexpr int64_t kStallMark = int64_t(1) << 40;  // added to err when a wait expires
 constexpr int kLookBatch = 4;                     // predecessor tiles read per look-back step
@@ -173,9 +204,9 @@ constexpr int kSrcKeysIota = 2;   // 32-bit keys in flat order (first pass of a 
 
 template <int SRC>
 __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
-    const int64_t *ids, const uint32_t *keys_in, const uint32_t *vals_in, int64_t n,
+    const int64_t *ids, const uint32_t *keys_in, const uint32_t *vals_in, const SortSegs sg,
     int64_t table_rows, int shift, int bits, const uint32_t *hist, uint64_t *status,
-    uint32_t *ticket, int64_t num_tiles, uint32_t *keys_out, uint32_t *vals_out, int64_t *err) {
+    uint32_t *ticket, uint32_t *keys_out, uint32_t *vals_out, int64_t *err) {
   __shared__ uint32_t s_keys[kSortTile];
   __shared__ uint32_t s_vals[kSortTile];
   __shared__ uint32_t s_cnt[kSortWaves][kMaxBins];  // per-wave counts -> wave offsets
@@ -190,50 +221,58 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   for (int d = tid; d < kSortWaves * kMaxBins; d += kSortThreads) (&s_cnt[0][0])[d] = 0;
   __syncthreads();
   const int64_t tile = s_tile;
-  const int64_t tile0 = tile * kSortTile;
-  const int count = (int)min((int64_t)kSortTile, n - tile0);
+  const int64_t seg = tile / sg.tiles;
+  const int64_t first = seg * sg.tiles;  // the segment's first tile
+  const int64_t seg0 = seg * sg.len;     // and its first key
+  const int64_t seg_end = seg0 + sg.len;
+  const int64_t tile0 = seg0 + (tile - first) * kSortTile;
+  const int count = (int)min((int64_t)kSortTile, seg_end - tile0);
+  const uint32_t kbase = sg.base[seg];
 
   // keys of this tile: wave w owns tile positions [w * 1024, (w + 1) * 1024)
   // in 16 rounds of 64, so (wave, round, lane) is the original order; then
-  // the global digit totals (their latency overlaps the ranking)
+  // the segment's digit totals (their latency overlaps the ranking)
   const int64_t base = tile0 + (int64_t)wave * (kSortItems * kWave);
   const unsigned long long below = (1ull << lane) - 1ull;
   // (loads at clamped positions, so none waits behind a branch)
+  const uint32_t *seg_hist = hist + seg * 4 * kMaxBins;
+  const int64_t copy_stride = (int64_t)sg.count * 4 * kMaxBins;
   uint32_t copies[kHistCopies];
 #pragma unroll
   for (int c = 0; c < kHistCopies; ++c)
-    copies[c] = hist[(int64_t)c * 4 * kMaxBins + (tid < bins ? tid : 0)];
+    copies[c] = c < sg.copies ? seg_hist[c * copy_stride + (tid < bins ? tid : 0)] : 0u;
   uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
   if (SRC == kSrcIds) {
     int64_t id[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i)
-      id[i] = ids[min(base + (int64_t)i * kWave + lane, n - 1)];
+      id[i] = ids[min(base + (int64_t)i * kWave + lane, seg_end - 1)];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
       const int64_t p = base + (int64_t)i * kWave + lane;
       int ignored = 0;
-      key[i] = p < n ? make_key(id[i], table_rows, ignored) : 0u;
+      key[i] = p < seg_end ? make_key(id[i], table_rows, ignored) : 0u;
       val[i] = (uint32_t)p;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
-      const int64_t p = min(base + (int64_t)i * kWave + lane, n - 1);
+      const int64_t p = min(base + (int64_t)i * kWave + lane, seg_end - 1);
       key[i] = keys_in[p];
-      val[i] = SRC == kSrcKeysIota ? (uint32_t)p : vals_in[p];
+      val[i] = SRC == kSrcKeysIota ? (uint32_t)((p - seg0) * sg.stride + sg.head[seg])
+                                   : vals_in[p];
     }
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i)
-      if (base + (int64_t)i * kWave + lane >= n) key[i] = val[i] = 0u;
+      if (base + (int64_t)i * kWave + lane >= seg_end) key[i] = val[i] = kbase;
   }
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) rank[i] = 0;
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const int64_t p = base + (int64_t)i * kWave + lane;
-    const bool valid = p < n;
-    const uint32_t d = (key[i] >> shift) & mask;
+    const bool valid = p < seg_end;
+    const uint32_t d = ((key[i] - kbase) >> shift) & mask;
     unsigned long long peers = __ballot(valid);
     for (int b = 0; b < bits; ++b) {
       const bool bit = (d >> b) & 1u;
@@ -256,12 +295,12 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
       s_cnt[w][tid] = tile_count;
       tile_count += c;
     }
-    const uint64_t word = (tile == 0 ? kFlagInclusive : kFlagAggregate) | tile_count;
+    const uint64_t word = (tile == first ? kFlagInclusive : kFlagAggregate) | tile_count;
     __hip_atomic_store(&status[tile * kMaxBins + tid], word, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
-  // tile-local digit starts, and global digit starts (keys of all smaller
-  // digits over all tiles), by block scans over the digits
+  // tile-local digit starts, and the segment's digit starts (keys of all
+  // smaller digits over the segment's tiles), by block scans over the digits
   uint32_t scan_total;
   const uint32_t local_start =
       block_exclusive_scan<kSortThreads>(tid < bins ? tile_count : 0u, scan_total);
@@ -269,19 +308,19 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
 #pragma unroll
   for (int c = 0; c < kHistCopies; ++c) digit_total += tid < bins ? copies[c] : 0u;
   const uint32_t digit_start = block_exclusive_scan<kSortThreads>(digit_total, scan_total);
-  // decoupled look-back: the keys of this digit in all earlier tiles
+  // decoupled look-back: the keys of this digit in the segment's earlier tiles
   if (tid < bins) {
     s_local[tid] = local_start;
     uint64_t before = 0;
     bool stalled = false, found = false;
     // look back kLookBatch tiles per step, all loads in flight together
-    for (int64_t t = tile - 1; t >= 0 && !found && !stalled; t -= kLookBatch) {
+    for (int64_t t = tile - 1; t >= first && !found && !stalled; t -= kLookBatch) {
       uint64_t word[kLookBatch];
 #pragma unroll
       for (int j = 0; j < kLookBatch; ++j)
-        word[j] = t - j >= 0 ? __hip_atomic_load(&status[(t - j) * kMaxBins + tid],
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                             : kFlagInclusive;  // before tile 0: nothing
+        word[j] = t - j >= first ? __hip_atomic_load(&status[(t - j) * kMaxBins + tid],
+                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                 : kFlagInclusive;  // before the segment: nothing
 #pragma unroll
       for (int j = 0; j < kLookBatch; ++j) {
         if (found || stalled) continue;
@@ -300,13 +339,13 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
         found = (word[j] & kFlagInclusive) != 0;
       }
     }
-    if (tile != 0)
+    if (tile != first)
       __hip_atomic_store(&status[tile * kMaxBins + tid],
                          kFlagInclusive | (uint32_t)(before + tile_count), __ATOMIC_RELAXED,
                          __HIP_MEMORY_SCOPE_AGENT);
     if (stalled && err != nullptr)
       atomicAdd(reinterpret_cast<unsigned long long *>(err), (unsigned long long)kStallMark);
-    s_gbase[tid] = digit_start + (uint32_t)before;
+    s_gbase[tid] = (uint32_t)seg0 + digit_start + (uint32_t)before;
   }
   __syncthreads();
 
@@ -314,8 +353,8 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
 #pragma unroll
   for (int i = 0; i < kSortItems; ++i) {
     const int64_t p = base + (int64_t)i * kWave + lane;
-    if (p < n) {
-      const uint32_t d = (key[i] >> shift) & mask;
+    if (p < seg_end) {
+      const uint32_t d = ((key[i] - kbase) >> shift) & mask;
       const uint32_t at = s_local[d] + s_cnt[wave][d] + rank[i];
       s_keys[at] = key[i];
       s_vals[at] = val[i];
@@ -324,7 +363,7 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   __syncthreads();
   for (int j = tid; j < count; j += kSortThreads) {
     const uint32_t k = s_keys[j];
-    const uint32_t d = (k >> shift) & mask;
+    const uint32_t d = ((k - kbase) >> shift) & mask;
     const uint32_t dst = s_gbase[d] + (uint32_t)j - s_local[d];
     keys_out[dst] = k;
     vals_out[dst] = s_vals[j];
@@ -375,6 +414,61 @@ __global__ __launch_bounds__(kSortThreads) void plan_hash_kernel(const HashParam
   for (int d = tid; d < passes * kMaxBins; d += kSortThreads) {
     const uint32_t c = (&s_hist[0][0])[d];
     if (c != 0) atomicAdd(&copy[d], c);
+  }
+}
+
+// The first kernel of a plan from tokens sorted in per-head segments: a
+// block takes kHeadTokens tokens of one head (segment s hashes head head[s];
+// a segment is `chunks` blocks), writes each key at its segment's position
+// (segment s, token t: s * tokens + t) and counts its digits (of key -
+// base[s]) into the segment's histograms, one flush per block.  A thread
+// takes kHeadItems tokens with all their history loads in flight together.
+// Blocks of kSortThreads threads, like the sort's, so the plan gets its
+// share of the GPU beside a forward running on another stream (blocks of
+// 1024 threads wait there for a whole compute unit to drain).  N =
+// ngram_size at compile time, as in the fused lookup.
+constexpr int kHeadThreads = kSortThreads;
+constexpr int kHeadItems = 4;
+constexpr int kHeadTokens = kHeadThreads * kHeadItems;
+
+template <int N>
+__global__ __launch_bounds__(kHeadThreads) void plan_hash_heads_kernel(
+    const HashParams hp, const SortSegs sg, int64_t chunks, int passes, int per_pass, int bits,
+    uint32_t *keys, uint32_t *hist) {
+  __shared__ uint32_t s_hist[4][kMaxBins];
+  const int tid = threadIdx.x;
+  const int64_t seg = blockIdx.x / chunks;
+  const int64_t t0 = ((int64_t)blockIdx.x - seg * chunks) * kHeadTokens + tid;
+  const int h = (int)sg.head[seg];
+  const int order = h / hp.J;  // g - 2
+  const uint32_t kbase = sg.base[seg];
+  uint32_t *out = keys + seg * sg.len;
+  for (int d = tid; d < 4 * kMaxBins; d += kHeadThreads) (&s_hist[0][0])[d] = 0;
+  uint64_t mix[kHeadItems][ENGRAM_MAX_NGRAM - 1];
+#pragma unroll
+  for (int i = 0; i < kHeadItems; ++i)
+    token_mixes<N>(hp, min(t0 + (int64_t)i * kHeadThreads, sg.len - 1), mix[i]);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kHeadItems; ++i) {
+    const int64_t t = t0 + (int64_t)i * kHeadThreads;
+    if (t >= sg.len) continue;
+    uint64_t m = mix[i][0];
+#pragma unroll
+    for (int k = 1; k < N - 1; ++k) m = order == k ? mix[i][k] : m;
+    const uint32_t key = (uint32_t)head_row(hp, m, h);
+    out[t] = key;
+    for (int q = 0; q < passes; ++q) {
+      const int shift = q * per_pass;
+      const int width = bits - shift < per_pass ? bits - shift : per_pass;
+      atomicAdd(&s_hist[q][((key - kbase) >> shift) & ((1u << width) - 1u)], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t *dst = hist + seg * 4 * kMaxBins;
+  for (int d = tid; d < passes * kMaxBins; d += kHeadThreads) {
+    const uint32_t c = (&s_hist[0][0])[d];
+    if (c != 0) atomicAdd(&dst[d], c);
   }
 }
 
@@ -962,6 +1056,7 @@ __global__ __launch_bounds__(kAtomicThreads) void scatter_atomic_kernel(
 struct Plan {
   int64_t num_tiles, num_ranges, slot_tiles;
   int bits, passes, per_pass;
+  int64_t status_words;  // look-back words the workspace holds
   size_t keys_a, vals_a, keys_b, vals_b, status, counters, head_off,
       scalars, total;
 };
@@ -1002,8 +1097,11 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
   p->vals_a = take(nn * 4);
   p->keys_b = take(nn * 4);
   p->vals_b = take(nn * 4);
-  // look-back words: every sort pass's, then the slot scan's
-  p->status = take(((size_t)p->passes * (size_t)p->num_tiles * kMaxBins + (size_t)p->slot_tiles) * 8);
+  // look-back words: every sort pass's, then the slot scan's.  A sort in
+  // per-head segments has at most one more (ragged) tile per head.
+  p->status_words =
+      (int64_t)p->passes * (p->num_tiles + ENGRAM_MAX_HEADS) * kMaxBins + p->slot_tiles;
+  p->status = take((size_t)p->status_words * 8);
   p->counters = take(kSortCounters * 4);
   p->head_off = take((size_t)p->num_ranges * 4);
   p->scalars = take(64);
@@ -1080,60 +1178,146 @@ Views views_of(const Plan &p, void *ws) {
   return v;
 }
 
+// How a plan sorts: one segment of all n keys, or one per head.
+struct SortLayout {
+  SortSegs sg;
+  int64_t num_tiles;
+  int bits, passes, per_pass;
+};
+
+SortLayout whole_sort(const Plan &p, int64_t n) {
+  SortLayout L = {};
+  L.sg.len = n;
+  L.sg.tiles = p.num_tiles;
+  L.sg.count = 1;
+  L.sg.copies = kHistCopies;
+  L.sg.stride = 1;
+  L.num_tiles = p.num_tiles;
+  L.bits = p.bits;
+  L.passes = p.passes;
+  L.per_pass = p.per_pass;
+  return L;
+}
+
+// Per-head segments for a plan from tokens: possible when the heads' row
+// ranges [offset, offset + prime) do not overlap (then every row belongs to
+// one head, and the heads ordered by offset are sorted segment after
+// segment), and used when the layout fits the workspace of n keys.
+bool head_sort(const HashParams &hp, int64_t tokens, const Plan &p, SortLayout *out) {
+  int order[ENGRAM_MAX_HEADS];
+  for (int h = 0; h < hp.H; ++h) order[h] = h;
+  for (int i = 1; i < hp.H; ++i)  // heads by row offset (at most 64)
+    for (int j = i; j > 0 && hp.offset[order[j]] < hp.offset[order[j - 1]]; --j) {
+      const int t = order[j];
+      order[j] = order[j - 1];
+      order[j - 1] = t;
+    }
+  uint64_t widest = 1;
+  for (int i = 0; i < hp.H; ++i) {
+    const int h = order[i];
+    if (i + 1 < hp.H && hp.offset[h] + (int64_t)hp.prime[h] > hp.offset[order[i + 1]])
+      return false;
+    widest = hp.prime[h] > widest ? hp.prime[h] : widest;
+  }
+  SortLayout L = {};
+  L.sg.len = tokens;
+  L.sg.tiles = (tokens + kSortTile - 1) / kSortTile;
+  L.sg.count = hp.H;
+  L.sg.copies = 1;
+  L.sg.stride = hp.H;
+  for (int i = 0; i < hp.H; ++i) {
+    L.sg.base[i] = (uint32_t)hp.offset[order[i]];
+    L.sg.head[i] = (uint32_t)order[i];
+  }
+  L.num_tiles = (int64_t)hp.H * L.sg.tiles;
+  L.bits = bit_width_u64(widest - 1);  // digits of key - offset < prime
+  if (L.bits < 1) L.bits = 1;
+  L.passes = (L.bits + 7) / 8;
+  L.per_pass = (L.bits + L.passes - 1) / L.passes;
+  if (L.passes > p.passes ||
+      (int64_t)L.passes * L.num_tiles * kMaxBins + p.slot_tiles > p.status_words)
+    return false;
+  *out = L;
+  return true;
+}
+
 // Plan: sort the row ids and give every distinct row its slot (U is left
 // in the workspace scalars).  Needs only the ids: given (ids), or computed
 // from the tokens (hp, when ids is null).
 int plan_sorted(const int64_t *ids, const HashParams *hp, int64_t n, int64_t table_rows,
                 const Plan &p, void *ws, int64_t *err, hipStream_t s) {
   const Views v = views_of(p, ws);
-  uint32_t *hist = v.counters;                                // [kHistCopies][4][kMaxBins]
-  uint32_t *tickets = v.counters + kHistCopies * 4 * kMaxBins;  // [4]
-  const int64_t status_len = (int64_t)p.passes * p.num_tiles * kMaxBins + p.slot_tiles;
-  const int64_t clear_len = status_len > kSortCounters ? status_len : kSortCounters;
+  uint32_t *tickets = v.counters;              // [4], then the slot scan's
+  uint32_t *hist = v.counters + kTicketWords;  // [copy][segment][4][kMaxBins]
+  SortLayout L = whole_sort(p, n);
+  const bool heads = ids == nullptr && head_sort(*hp, n / hp->H, p, &L);
+  const int64_t sort_words = (int64_t)L.passes * L.num_tiles * kMaxBins;
+  const int64_t status_len = sort_words + p.slot_tiles;
+  const int64_t counters_len = kTicketWords + (int64_t)L.sg.copies * L.sg.count * 4 * kMaxBins;
+  const int64_t clear_len = status_len > counters_len ? status_len : counters_len;
   hipLaunchKernelGGL(sort_clear_kernel, dim3((unsigned)((clear_len + 255) / 256)), dim3(256), 0,
-                     s, v.status, status_len, v.counters, kSortCounters);
+                     s, v.status, status_len, v.counters, (int)counters_len);
+  // The passes alternate between the two key/index buffers and end in the
+  // pair the apply reads; the keys a plan from tokens hashes go to the other
+  // buffer of the first pass.
+  const bool end_in_a = p.passes % 2 == 1;
+  uint32_t *const last_k = end_in_a ? v.keys_a : v.keys_b, *const last_v = end_in_a ? v.vals_a : v.vals_b;
+  uint32_t *const other_k = end_in_a ? v.keys_b : v.keys_a, *const other_v = end_in_a ? v.vals_b : v.vals_a;
+  auto out_k = [&](int pass) { return (L.passes - 1 - pass) % 2 == 0 ? last_k : other_k; };
+  auto out_v = [&](int pass) { return (L.passes - 1 - pass) % 2 == 0 ? last_v : other_v; };
+  uint32_t *const hashed = out_k(0) == last_k ? other_k : last_k;
   if (ids != nullptr) {
-    hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)p.num_tiles), dim3(kSortThreads), 0,
-                       s, ids, n, table_rows, p.passes, p.per_pass, p.bits, hist, err);
-  } else {  // keys in flat order go to keys_b, which the first pass reads
+    hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)L.num_tiles), dim3(kSortThreads), 0,
+                       s, ids, n, table_rows, L.passes, L.per_pass, L.bits, hist, err);
+  } else if (heads) {
+    const int64_t chunks = (L.sg.len + kHeadTokens - 1) / kHeadTokens;
+    const dim3 grid((unsigned)(L.sg.count * chunks));
+    switch (hp->n) {
+#define ENGRAM_PLAN_HEADS_CASE(N)                                                             \
+  case N:                                                                                     \
+    hipLaunchKernelGGL(plan_hash_heads_kernel<N>, grid, dim3(kHeadThreads), 0, s, *hp, L.sg,    \
+                       chunks, L.passes, L.per_pass, L.bits, hashed, hist);                   \
+    break;
+      ENGRAM_PLAN_HEADS_CASE(2)
+      ENGRAM_PLAN_HEADS_CASE(3)
+      ENGRAM_PLAN_HEADS_CASE(4)
+      ENGRAM_PLAN_HEADS_CASE(5)
+      ENGRAM_PLAN_HEADS_CASE(6)
+      ENGRAM_PLAN_HEADS_CASE(7)
+      ENGRAM_PLAN_HEADS_CASE(8)
+#undef ENGRAM_PLAN_HEADS_CASE
+    }
+  } else {  // keys in flat order
     const int64_t tokens = n / hp->H;
     hipLaunchKernelGGL(plan_hash_kernel, dim3((unsigned)((tokens + 63) / 64)),
-                       dim3(kSortThreads), 0, s, *hp, tokens, p.passes, p.per_pass, p.bits,
-                       v.keys_b, hist);
+                       dim3(kSortThreads), 0, s, *hp, tokens, L.passes, L.per_pass, L.bits,
+                       hashed, hist);
   }
-  const uint32_t *src_k = nullptr, *src_v = nullptr;
-  uint32_t *dst_k = v.keys_a, *dst_v = v.vals_a, *spare_k = v.keys_b, *spare_v = v.vals_b;
-  const unsigned tiles = (unsigned)p.num_tiles;
-  for (int pass = 0; pass < p.passes; ++pass) {
-    const int shift = pass * p.per_pass;
-    const int width = p.bits - shift < p.per_pass ? p.bits - shift : p.per_pass;
-    uint64_t *pass_status = v.status + (int64_t)pass * p.num_tiles * kMaxBins;
+  const unsigned tiles = (unsigned)L.num_tiles;
+  for (int pass = 0; pass < L.passes; ++pass) {
+    const int shift = pass * L.per_pass;
+    const int width = L.bits - shift < L.per_pass ? L.bits - shift : L.per_pass;
+    uint64_t *pass_status = v.status + (int64_t)pass * L.num_tiles * kMaxBins;
+    const uint32_t *in_k = pass == 0 ? hashed : out_k(pass - 1);
+    const uint32_t *in_v = pass == 0 ? nullptr : out_v(pass - 1);
     if (pass == 0 && ids != nullptr)
       hipLaunchKernelGGL(onesweep_kernel<kSrcIds>, dim3(tiles), dim3(kSortThreads), 0, s, ids,
-                         nullptr, nullptr, n, table_rows, shift, width, hist, pass_status,
-                         tickets, p.num_tiles, dst_k, dst_v, err);
+                         nullptr, nullptr, L.sg, table_rows, shift, width, hist, pass_status,
+                         tickets, out_k(pass), out_v(pass), err);
     else if (pass == 0)
       hipLaunchKernelGGL(onesweep_kernel<kSrcKeysIota>, dim3(tiles), dim3(kSortThreads), 0, s,
-                         nullptr, v.keys_b, nullptr, n, table_rows, shift, width, hist,
-                         pass_status, tickets, p.num_tiles, dst_k, dst_v, err);
+                         nullptr, in_k, nullptr, L.sg, table_rows, shift, width, hist,
+                         pass_status, tickets, out_k(pass), out_v(pass), err);
     else
       hipLaunchKernelGGL(onesweep_kernel<kSrcKeys>, dim3(tiles), dim3(kSortThreads), 0, s,
-                         nullptr, src_k, src_v, n, table_rows, shift, width,
-                         hist + pass * kMaxBins, pass_status, tickets + pass, p.num_tiles, dst_k,
-                         dst_v, err);
-    src_k = dst_k;
-    src_v = dst_v;
-    uint32_t *tk = dst_k, *tv = dst_v;
-    dst_k = spare_k;
-    dst_v = spare_v;
-    spare_k = tk;
-    spare_v = tv;
+                         nullptr, in_k, in_v, L.sg, table_rows, shift, width,
+                         hist + pass * kMaxBins, pass_status, tickets + pass, out_k(pass),
+                         out_v(pass), err);
   }
   // distinct-row slots
   hipLaunchKernelGGL(range_slots_kernel, dim3((unsigned)p.slot_tiles), dim3(kSlotThreads), 0, s,
-                     v.sorted_keys, n, (uint32_t)table_rows, p.num_ranges,
-                     v.status + (int64_t)p.passes * p.num_tiles * kMaxBins,
-                     v.counters + kSlotTicketAt, v.head_off, v.scalars, err);
+                     v.sorted_keys, n, (uint32_t)table_rows, p.num_ranges, v.status + sort_words,
+                     tickets + kSlotTicketAt, v.head_off, v.scalars, err);
   return launch_status();
 }
 

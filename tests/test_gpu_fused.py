@@ -123,3 +123,53 @@ def test_token_plan_every_order(n, J):
     assert torch.equal(uid_t[:u], uid_i[:u])
     assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
     assert torch.equal(uid_t[:u], torch.unique(ids))
+
+
+@pytest.mark.parametrize("layout", ["ascending", "descending", "shuffled", "gap",
+                                    "overlapping", "shared"])
+def test_token_plan_head_layouts(layout):
+    """The plan from the tokens sorts each head's rows on their own when the
+    heads' row ranges are disjoint (in any order of offsets) and the whole key
+    array otherwise; either way it equals the plan of engram_hash's ids.  Each
+    head has several sort tiles, the last one ragged."""
+    n, J = 3, 4
+    H = (n - 1) * J
+    primes = workloads.primes_above(60000, H)
+    rng = np.random.Generator(np.random.PCG64(7 + len(layout)))
+    order = list(range(H))
+    if layout == "descending":
+        order = order[::-1]
+    elif layout == "shuffled":
+        rng.shuffle(order)
+    offs = [0] * H
+    at = 0
+    for h in order:   # back to back in the chosen order
+        offs[h] = at
+        at += primes[h]
+    rows = at + 11
+    if layout == "gap":   # a gap between two heads, the rest back to back
+        offs = [o + (40 if h >= H // 2 else 0) for h, o in enumerate(offs)]
+        rows += 40
+    elif layout == "overlapping":   # head 1's range starts inside head 0's
+        offs[1] = offs[0] + primes[0] // 2
+    elif layout == "shared":   # two heads share one offset
+        offs[3] = offs[2]
+    mult = workloads.seeded_multipliers(n, 5)
+    tok = rng.integers(0, 3000, (3, 5003)).astype(np.int64)
+    tok[rng.random(tok.shape) < 0.01] = 9
+    seg = workloads.random_segments(tok.shape, 400, 3)
+    args = (n, J, 9, mult, primes, offs)
+    R = tok.size * H
+    dim = 8
+    grads = workloads.make_grads(R, dim, 17, "cuda")
+    ws_t = E.engram_scatter_plan_tokens(dev(tok), rows, dim, *args, seq_ids=dev(seg))
+    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, rows)
+    ids = E.engram_hash(dev(tok), *args, rows, seq_ids=dev(seg))
+    ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
+    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, rows)
+    torch.cuda.synchronize()
+    u = int(cnt_t.item())
+    assert u == int(cnt_i.item()) and u > 0
+    assert torch.equal(uid_t[:u], uid_i[:u])
+    assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
+    assert torch.equal(uid_t[:u], torch.unique(ids))
