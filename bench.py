@@ -6,11 +6,15 @@ One step = one pass of the whole path over one token batch:
     -> engram_scatter_plan_tokens + engram_scatter_apply (backward: per-row
        fp32 sums, row-sparse; the same work as hashing, then
        engram_scatter_add_rowsparse)
-The plan (sorting the row ids) needs only the tokens, so it runs on a second
-stream beside the forward, as a training step would schedule it; the apply
-waits for the forward and the plan.  A serial pass of the same calls gives
-the per-phase times, and the same step with separate calls (engram_hash,
-engram_gather, engram_scatter_plan of the ids, apply) is timed beside it.
+The plan (sorting the row ids) needs only the tokens, so the next batch's
+plan runs on a second stream while the current step's forward and backward
+run (a training loop knows its next batch), into the other of two
+workspaces; the apply waits for the forward and for its batch's plan.  The
+timed region holds exactly one plan, forward and apply per step (it ends
+when the plan made during the last step is done too).  A serial pass of the
+same calls gives the per-phase times, and the same step with separate calls
+(engram_hash, then engram_scatter_plan of the ids beside engram_gather, then
+the apply) is timed beside it.
 on the end-to-end workload: tokens [8, 8192] (Zipf(1.1) ids, EOS w.p.
 1/4096), ngram_size 4, 8 heads per order (24 heads), a 200M x 256 bf16 table
 (102.4 GB, resident in HBM), upstream gradients [8, 8192, 24, 256] bf16.
@@ -400,8 +404,11 @@ def main():
         gtab = workloads.make_grad_table(wl.table_rows, D, None, dev)
         mode = E.SCATTER_SORTED
     if backward:
-        ws = torch.empty(max(E.engram_scatter_add_workspace(R, wl.table_rows, D, mode), 1),
-                         dtype=torch.uint8, device=dev)
+        # two workspaces: the plan of the next batch is made while this
+        # batch's step runs, so consecutive steps use alternate workspaces
+        wss = [torch.empty(max(E.engram_scatter_add_workspace(R, wl.table_rows, D, mode), 1),
+                           dtype=torch.uint8, device=dev) for _ in range(2)]
+        ws = wss[0]
 
     side = torch.cuda.Stream(dev)  # default priority
     hargs = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
@@ -409,22 +416,36 @@ def main():
     ev_apply = [torch.cuda.Event() for _ in range(2)]
     ev_rows = [torch.cuda.Event() for _ in range(2)]
 
+    planned = {"next": None}
+
+    def plan_ahead(k):
+        """The plan of batch k (engram_scatter_plan_tokens: it needs only the
+        tokens) on the side stream, into workspace k % 2, once the apply that
+        last read that workspace (batch k - 2) is done."""
+        side.wait_event(ev_apply[k % 2])
+        E.engram_scatter_plan_tokens(tokens[k % N_BATCHES], wl.table_rows, D, *hargs,
+                                     workspace=wss[k % 2], stream=side)
+        ev_plan[k % 2].record(side)
+        planned["next"] = k
+
     def step(k):
         """One step.  The forward is one pass (engram_lookup: hash and gather
-        fused).  The backward's plan needs only the tokens, so it is made
-        from them (engram_scatter_plan_tokens) on a side stream beside the
-        forward, once the previous step's apply has released the workspace;
-        the apply follows the forward and waits for the plan."""
+        fused).  The backward's plan needs only the tokens, so the next
+        batch's plan is made on a side stream while this step's forward and
+        backward run (a training loop knows its next batch); the apply
+        follows the forward and waits for its own batch's plan, made during
+        the step before.  Every step makes one plan, one forward and one
+        apply."""
         tok = tokens[k % N_BATCHES]
         if not backward:
             E.engram_lookup(tok, table, *hargs, out=out)
             return
-        side.wait_event(ev_apply[(k - 1) % 2])
-        E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, workspace=ws, stream=side)
-        ev_plan[k % 2].record(side)
+        if planned["next"] != k:  # the first step: nothing planned yet
+            plan_ahead(k)
+        plan_ahead(k + 1)
         E.engram_lookup(tok, table, *hargs, out=out)
         stream.wait_event(ev_plan[k % 2])
-        apply_backward()
+        apply_backward(wss[k % 2])
         ev_apply[k % 2].record(stream)
 
     def step_separate(k):
@@ -440,9 +461,9 @@ def main():
         ev_plan[k % 2].record(side)
         E.engram_gather(rows, table, out=out)
         stream.wait_event(ev_plan[k % 2])
-        apply_backward()
+        apply_backward(ws)
 
-    def apply_backward():
+    def apply_backward(ws):
         if signsgd:
             E.engram_scatter_apply_signsgd(grads, ws, table, lr)
         elif wl.grads == "rowsparse":
@@ -470,7 +491,7 @@ def main():
             else:
                 E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, workspace=ws)
             ev[3].record(stream)
-            apply_backward()
+            apply_backward(ws)
             ev[4].record(stream)
 
     def timed_steps(fn):
@@ -480,8 +501,12 @@ def main():
         start = torch.cuda.Event(enable_timing=True)
         stop = torch.cuda.Event(enable_timing=True)
         start.record(stream)
-        for k in range(args.steps):
+        for k in range(args.warmup, args.warmup + args.steps):
             fn(k)
+        if fn is step and backward:
+            # the plan made during the last step (the next batch's) is part
+            # of the timed work: the stop mark waits for it too
+            stream.wait_event(ev_plan[planned["next"] % 2])
         stop.record(stream)
         torch.cuda.synchronize()
         return start.elapsed_time(stop) / args.steps
@@ -629,7 +654,8 @@ def main():
                    **({"workload": "e2e_signsgd", "optimizer": "signsgd", "lr": lr}
                       if signsgd else {}),
                    "step": "lookup(hash+gather fused)"
-                   + ("+scatter(plan from tokens beside the lookup, apply)" if backward else "")
+                   + ("+scatter(plan from tokens, made for the next batch beside this step;"
+                      " apply)" if backward else "")
                    + ("+signsgd(fused into the apply)" if signsgd else ""),
                    "backward": wl.grads, "accumulate": "f64" if backward else None,
                    "unique_rows": unique_rows, "token_batches_cycled": N_BATCHES},
