@@ -59,7 +59,10 @@ namespace {
 constexpr int kSortThreads = 256;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kSortItems = 16;
-constexpr int kSortTile = kSortThreads * kSortItems;  // keys per tile
+constexpr int kSortTile = kSortThreads * kSortItems;  // keys per tile (and per histogram block)
+// A sort with fewer tiles than this takes tiles of half the size: twice the
+// blocks on a GPU of 256 compute units, and half a tile's serial work each.
+constexpr int64_t kSmallSortTiles = 128;
 constexpr int kMaxBins = 256;
 constexpr int kSlotThreads = 256;  // ranges per tile of the slot scan
 constexpr int kRange = 16;  // sorted positions per walker
@@ -202,13 +205,14 @@ constexpr int kSrcIds = 0;        // int64 row ids (first pass of a plan from id
 constexpr int kSrcKeys = 1;       // 32-bit keys and flat indices (later passes)
 constexpr int kSrcKeysIota = 2;   // 32-bit keys in flat order (first pass of a plan from tokens)
 
-template <int SRC>
+template <int SRC, int ITEMS>
 __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
     const int64_t *ids, const uint32_t *keys_in, const uint32_t *vals_in, const SortSegs sg,
     int64_t table_rows, int shift, int bits, const uint32_t *hist, uint64_t *status,
     uint32_t *ticket, uint32_t *keys_out, uint32_t *vals_out, int64_t *err) {
-  __shared__ uint32_t s_keys[kSortTile];
-  __shared__ uint32_t s_vals[kSortTile];
+  constexpr int TILE = kSortThreads * ITEMS;
+  __shared__ uint32_t s_keys[TILE];
+  __shared__ uint32_t s_vals[TILE];
   __shared__ uint32_t s_cnt[kSortWaves][kMaxBins];  // per-wave counts -> wave offsets
   __shared__ uint32_t s_local[kMaxBins];            // tile-local start of each digit
   __shared__ uint32_t s_gbase[kMaxBins];            // global position of tile-local 0
@@ -225,14 +229,14 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
   const int64_t first = seg * sg.tiles;  // the segment's first tile
   const int64_t seg0 = seg * sg.len;     // and its first key
   const int64_t seg_end = seg0 + sg.len;
-  const int64_t tile0 = seg0 + (tile - first) * kSortTile;
-  const int count = (int)min((int64_t)kSortTile, seg_end - tile0);
+  const int64_t tile0 = seg0 + (tile - first) * TILE;
+  const int count = (int)min((int64_t)TILE, seg_end - tile0);
   const uint32_t kbase = sg.base[seg];
 
   // keys of this tile: wave w owns tile positions [w * 1024, (w + 1) * 1024)
   // in 16 rounds of 64, so (wave, round, lane) is the original order; then
   // the segment's digit totals (their latency overlaps the ranking)
-  const int64_t base = tile0 + (int64_t)wave * (kSortItems * kWave);
+  const int64_t base = tile0 + (int64_t)wave * (ITEMS * kWave);
   const unsigned long long below = (1ull << lane) - 1ull;
   // (loads at clamped positions, so none waits behind a branch)
   const uint32_t *seg_hist = hist + seg * 4 * kMaxBins;
@@ -241,14 +245,14 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
 #pragma unroll
   for (int c = 0; c < kHistCopies; ++c)
     copies[c] = c < sg.copies ? seg_hist[c * copy_stride + (tid < bins ? tid : 0)] : 0u;
-  uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+  uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
   if (SRC == kSrcIds) {
-    int64_t id[kSortItems];
+    int64_t id[ITEMS];
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i)
+    for (int i = 0; i < ITEMS; ++i)
       id[i] = ids[min(base + (int64_t)i * kWave + lane, seg_end - 1)];
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
       const int64_t p = base + (int64_t)i * kWave + lane;
       int ignored = 0;
       key[i] = p < seg_end ? make_key(id[i], table_rows, ignored) : 0u;
@@ -256,20 +260,20 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
       const int64_t p = min(base + (int64_t)i * kWave + lane, seg_end - 1);
       key[i] = keys_in[p];
       val[i] = SRC == kSrcKeysIota ? (uint32_t)((p - seg0) * sg.stride + sg.head[seg])
                                    : vals_in[p];
     }
 #pragma unroll
-    for (int i = 0; i < kSortItems; ++i)
+    for (int i = 0; i < ITEMS; ++i)
       if (base + (int64_t)i * kWave + lane >= seg_end) key[i] = val[i] = kbase;
   }
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) rank[i] = 0;
+  for (int i = 0; i < ITEMS; ++i) rank[i] = 0;
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
+  for (int i = 0; i < ITEMS; ++i) {
     const int64_t p = base + (int64_t)i * kWave + lane;
     const bool valid = p < seg_end;
     const uint32_t d = ((key[i] - kbase) >> shift) & mask;
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
 
   // stage in LDS in tile-sorted order, then write digit runs out coalesced
 #pragma unroll
-  for (int i = 0; i < kSortItems; ++i) {
+  for (int i = 0; i < ITEMS; ++i) {
     const int64_t p = base + (int64_t)i * kWave + lane;
     if (p < seg_end) {
       const uint32_t d = ((key[i] - kbase) >> shift) & mask;
@@ -1183,19 +1187,36 @@ struct SortLayout {
   SortSegs sg;
   int64_t num_tiles;
   int bits, passes, per_pass;
+  int items;  // keys per thread of a sort tile
 };
+
+// Tiles of a layout: half-size tiles for a small sort (when its look-back
+// words still fit the workspace), full-size ones otherwise.
+void size_tiles(const Plan &p, SortLayout *L) {
+  auto per_segment = [L](int64_t tile) { return (L->sg.len + tile - 1) / tile; };
+  L->items = kSortItems;
+  int64_t per = per_segment(kSortTile);
+  if ((int64_t)L->sg.count * per < kSmallSortTiles) {
+    const int64_t half = per_segment(kSortTile / 2);
+    if ((int64_t)L->passes * L->sg.count * half * kMaxBins + p.slot_tiles <= p.status_words) {
+      L->items = kSortItems / 2;
+      per = half;
+    }
+  }
+  L->sg.tiles = per;
+  L->num_tiles = (int64_t)L->sg.count * per;
+}
 
 SortLayout whole_sort(const Plan &p, int64_t n) {
   SortLayout L = {};
   L.sg.len = n;
-  L.sg.tiles = p.num_tiles;
   L.sg.count = 1;
   L.sg.copies = kHistCopies;
   L.sg.stride = 1;
-  L.num_tiles = p.num_tiles;
   L.bits = p.bits;
   L.passes = p.passes;
   L.per_pass = p.per_pass;
+  size_tiles(p, &L);
   return L;
 }
 
@@ -1221,7 +1242,6 @@ bool head_sort(const HashParams &hp, int64_t tokens, const Plan &p, SortLayout *
   }
   SortLayout L = {};
   L.sg.len = tokens;
-  L.sg.tiles = (tokens + kSortTile - 1) / kSortTile;
   L.sg.count = hp.H;
   L.sg.copies = 1;
   L.sg.stride = hp.H;
@@ -1229,16 +1249,45 @@ bool head_sort(const HashParams &hp, int64_t tokens, const Plan &p, SortLayout *
     L.sg.base[i] = (uint32_t)hp.offset[order[i]];
     L.sg.head[i] = (uint32_t)order[i];
   }
-  L.num_tiles = (int64_t)hp.H * L.sg.tiles;
   L.bits = bit_width_u64(widest - 1);  // digits of key - offset < prime
   if (L.bits < 1) L.bits = 1;
   L.passes = (L.bits + 7) / 8;
   L.per_pass = (L.bits + L.passes - 1) / L.passes;
+  size_tiles(p, &L);
   if (L.passes > p.passes ||
       (int64_t)L.passes * L.num_tiles * kMaxBins + p.slot_tiles > p.status_words)
     return false;
   *out = L;
   return true;
+}
+
+// One sort pass's buffers and digit, for launch_pass.
+struct PassArgs {
+  const int64_t *ids;
+  const uint32_t *keys_in, *vals_in;
+  int64_t table_rows;
+  int shift, width;
+  const uint32_t *hist;
+  uint64_t *status;
+  uint32_t *ticket, *keys_out, *vals_out;
+  int64_t *err;
+};
+
+template <int ITEMS>
+void launch_pass(int src, const SortLayout &L, const PassArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)L.num_tiles), block(kSortThreads);
+  if (src == kSrcIds)
+    hipLaunchKernelGGL((onesweep_kernel<kSrcIds, ITEMS>), grid, block, 0, s, a.ids, nullptr,
+                       nullptr, L.sg, a.table_rows, a.shift, a.width, a.hist, a.status, a.ticket,
+                       a.keys_out, a.vals_out, a.err);
+  else if (src == kSrcKeysIota)
+    hipLaunchKernelGGL((onesweep_kernel<kSrcKeysIota, ITEMS>), grid, block, 0, s, nullptr,
+                       a.keys_in, nullptr, L.sg, a.table_rows, a.shift, a.width, a.hist, a.status,
+                       a.ticket, a.keys_out, a.vals_out, a.err);
+  else
+    hipLaunchKernelGGL((onesweep_kernel<kSrcKeys, ITEMS>), grid, block, 0, s, nullptr, a.keys_in,
+                       a.vals_in, L.sg, a.table_rows, a.shift, a.width, a.hist, a.status,
+                       a.ticket, a.keys_out, a.vals_out, a.err);
 }
 
 // Plan: sort the row ids and give every distinct row its slot (U is left
@@ -1266,8 +1315,8 @@ int plan_sorted(const int64_t *ids, const HashParams *hp, int64_t n, int64_t tab
   auto out_k = [&](int pass) { return (L.passes - 1 - pass) % 2 == 0 ? last_k : other_k; };
   auto out_v = [&](int pass) { return (L.passes - 1 - pass) % 2 == 0 ? last_v : other_v; };
   uint32_t *const hashed = out_k(0) == last_k ? other_k : last_k;
-  if (ids != nullptr) {
-    hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)L.num_tiles), dim3(kSortThreads), 0,
+  if (ids != nullptr) {  // one block per kSortTile ids, whatever the sort's tiles
+    hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)p.num_tiles), dim3(kSortThreads), 0,
                        s, ids, n, table_rows, L.passes, L.per_pass, L.bits, hist, err);
   } else if (heads) {
     const int64_t chunks = (L.sg.len + kHeadTokens - 1) / kHeadTokens;
@@ -1293,26 +1342,18 @@ int plan_sorted(const int64_t *ids, const HashParams *hp, int64_t n, int64_t tab
                        dim3(kSortThreads), 0, s, *hp, tokens, L.passes, L.per_pass, L.bits,
                        hashed, hist);
   }
-  const unsigned tiles = (unsigned)L.num_tiles;
   for (int pass = 0; pass < L.passes; ++pass) {
     const int shift = pass * L.per_pass;
     const int width = L.bits - shift < L.per_pass ? L.bits - shift : L.per_pass;
-    uint64_t *pass_status = v.status + (int64_t)pass * L.num_tiles * kMaxBins;
-    const uint32_t *in_k = pass == 0 ? hashed : out_k(pass - 1);
-    const uint32_t *in_v = pass == 0 ? nullptr : out_v(pass - 1);
-    if (pass == 0 && ids != nullptr)
-      hipLaunchKernelGGL(onesweep_kernel<kSrcIds>, dim3(tiles), dim3(kSortThreads), 0, s, ids,
-                         nullptr, nullptr, L.sg, table_rows, shift, width, hist, pass_status,
-                         tickets, out_k(pass), out_v(pass), err);
-    else if (pass == 0)
-      hipLaunchKernelGGL(onesweep_kernel<kSrcKeysIota>, dim3(tiles), dim3(kSortThreads), 0, s,
-                         nullptr, in_k, nullptr, L.sg, table_rows, shift, width, hist,
-                         pass_status, tickets, out_k(pass), out_v(pass), err);
+    const PassArgs a = {ids, pass == 0 ? hashed : out_k(pass - 1),
+                        pass == 0 ? nullptr : out_v(pass - 1), table_rows, shift, width,
+                        hist + pass * kMaxBins, v.status + (int64_t)pass * L.num_tiles * kMaxBins,
+                        tickets + pass, out_k(pass), out_v(pass), err};
+    const int src = pass > 0 ? kSrcKeys : (ids != nullptr ? kSrcIds : kSrcKeysIota);
+    if (L.items == kSortItems)
+      launch_pass<kSortItems>(src, L, a, s);
     else
-      hipLaunchKernelGGL(onesweep_kernel<kSrcKeys>, dim3(tiles), dim3(kSortThreads), 0, s,
-                         nullptr, in_k, in_v, L.sg, table_rows, shift, width,
-                         hist + pass * kMaxBins, pass_status, tickets + pass, out_k(pass),
-                         out_v(pass), err);
+      launch_pass<kSortItems / 2>(src, L, a, s);
   }
   // distinct-row slots
   hipLaunchKernelGGL(range_slots_kernel, dim3((unsigned)p.slot_tiles), dim3(kSlotThreads), 0, s,

@@ -337,3 +337,21 @@ def test_random_sweep(oracle, seed):
     ids = random_ids(rng, n, rows)
     check_all_modes(oracle, ids, dim, rows, 500 + seed)
     release()
+
+
+@pytest.mark.parametrize("tiles,extra", [(63, 4093), (64, 1), (100, 17), (127, 3), (128, 9)])
+def test_sort_tile_sizes(oracle, tiles, extra):
+    """Sorts around the size where the plan switches from half-size tiles
+    (2048 keys, for sorts of fewer than 128 full tiles whose look-back words
+    fit the workspace) to full 4096-key tiles, each with a ragged last tile
+    and a few hot rows: every output mode bit for bit."""
+    rng = np.random.Generator(np.random.PCG64(tiles * 10 + extra))
+    n = tiles * 4096 + extra
+    rows = 3_000_017
+    ids = rng.integers(0, rows, n).astype(np.int64)
+    hot = rng.integers(0, rows, 4)
+    pick = rng.random(n) < 0.2
+    ids[pick] = hot[rng.integers(0, 4, int(pick.sum()))]
+    ids[rng.random(n) < 0.01] = -1
+    check_all_modes(oracle, ids, 8, rows, 700 + tiles)
+    release()
