@@ -527,6 +527,25 @@ def main():
 
     # whole-step timing (the driver's step): nothing between the calls
     ms_per_step = timed_steps(step)
+    schedule_check = None
+    if wl.grads == "rowsparse" and not signsgd:
+        # the timed schedule's last apply against the same batch planned and
+        # applied one call after another on one stream, bit for bit
+        last = args.warmup + args.steps - 1
+        ws_ref = torch.empty_like(ws)
+        uid_ref, uval_ref = torch.empty_like(uid), torch.empty_like(uval)
+        cnt_ref = torch.zeros_like(count)
+        E.engram_scatter_plan_tokens(tokens[last % N_BATCHES], wl.table_rows, D, *hargs,
+                                     workspace=ws_ref)
+        E.engram_scatter_apply(grads, ws_ref, wl.table_rows, unique_ids=uid_ref,
+                               unique_grads=uval_ref, num_unique=cnt_ref)
+        torch.cuda.synchronize()
+        u_ref = int(cnt_ref.item())
+        if not (int(count.item()) == u_ref and torch.equal(uid[:u_ref], uid_ref[:u_ref])
+                and torch.equal(uval[:u_ref].view(torch.int32), uval_ref[:u_ref].view(torch.int32))):
+            raise RuntimeError("the timed schedule's backward differs from the serial calls")
+        schedule_check = "last step bit-exact against serial calls"
+        del ws_ref, uid_ref, uval_ref, cnt_ref
     phase_ms, serial_ms = serial_phases(False)
     # the same work with separate calls, timed in the same process
     sep_ms = timed_steps(step_separate)
@@ -660,6 +679,7 @@ def main():
                    "backward": wl.grads, "accumulate": "f64" if backward else None,
                    "unique_rows": unique_rows, "token_batches_cycled": N_BATCHES},
         "serial_ms_per_step": serial_ms,
+        "schedule_check": schedule_check,
         "step_algorithmic_bytes": step_bytes,
         "step_gbps": step_gbps,
         "step_frac_of_peak": step_gbps / PEAK_HBM_GBS,
