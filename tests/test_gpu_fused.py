@@ -173,3 +173,55 @@ def test_token_plan_head_layouts(layout):
     assert torch.equal(uid_t[:u], uid_i[:u])
     assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
     assert torch.equal(uid_t[:u], torch.unique(ids))
+
+
+@pytest.mark.parametrize("overlap", [False, True])
+def test_plans_made_ahead_in_two_workspaces(overlap):
+    """The schedule the bench times: the next batch's token plan made on a
+    side stream into the other of two reused workspaces while this batch's
+    lookup and apply run.  Every step's row-sparse output equals a fresh
+    plan and apply of the same batch, bit for bit, so a reused workspace
+    carries nothing over from the plan it held before.  Per-head segments,
+    and (overlapping head ranges) one sort of all keys."""
+    wl = workloads.backward()
+    primes, offs = list(wl.primes), list(wl.offsets)
+    if overlap:
+        offs[1] = offs[0] + primes[0] // 3
+    args = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, wl.multipliers(), primes, offs)
+    rows, D = wl.table_rows, wl.dim
+    toks = [dev(wl.tokens(k)) for k in range(3)]
+    R = toks[0].numel() * len(primes)
+    table = workloads.make_table(rows, D, 5, "cuda")
+    grads = workloads.make_grads(R, D, 6, "cuda")
+    out = torch.empty((R, D), dtype=torch.bfloat16, device="cuda")
+    size = E.engram_scatter_add_workspace(R, rows, D, E.SCATTER_ROWSPARSE)
+    wss = [torch.empty(size, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    main, side = torch.cuda.current_stream(), torch.cuda.Stream()
+    ev_plan = [torch.cuda.Event() for _ in range(2)]
+    ev_apply = [torch.cuda.Event() for _ in range(2)]
+
+    def plan(k):
+        side.wait_event(ev_apply[k % 2])
+        E.engram_scatter_plan_tokens(toks[k % 3], rows, D, *args, workspace=wss[k % 2],
+                                     stream=side)
+        ev_plan[k % 2].record(side)
+
+    got = []
+    plan(0)
+    for k in range(6):
+        plan(k + 1)
+        E.engram_lookup(toks[k % 3], table, *args, out=out)
+        main.wait_event(ev_plan[k % 2])
+        got.append(E.engram_scatter_apply(grads, wss[k % 2], rows))
+        ev_apply[k % 2].record(main)
+    main.wait_stream(side)
+    for k, (uid, val, cnt) in enumerate(got):
+        ws = E.engram_scatter_plan_tokens(toks[k % 3], rows, D, *args)
+        uid_r, val_r, cnt_r = E.engram_scatter_apply(grads, ws, rows)
+        torch.cuda.synchronize()
+        u = int(cnt_r.item())
+        assert int(cnt.item()) == u and u > 0
+        assert torch.equal(uid[:u], uid_r[:u])
+        assert torch.equal(val[:u].view(torch.int32), val_r[:u].view(torch.int32))
+    del got, grads, table, out
+    release()
