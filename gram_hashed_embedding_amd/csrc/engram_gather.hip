@@ -100,26 +100,31 @@ __global__ __launch_bounds__(kGatherThreads) void zero_rows_kernel(const int64_t
   if (c % cpr == 0) count_errors(ids[c / cpr] != -1 ? 1 : 0, err);
 }
 
-// The fused forward (engram_lookup).  A block takes kLookRows consecutive
-// lookups.  Phase 1: its first kLookRows lanes compute one row each from the
-// tokens (lookup_row: the token's history in one round of loads, the order
-// mix, a Barrett remainder), so the hash costs one lane per row, and keep
-// them in LDS (and write them out when the caller asks).  Phase 2: as
-// gather_kernel, every lane moves 16-byte chunks of those rows, kUnroll at
-// a time (all loads before the stores).  The row ids never go through
-// memory.  N = ngram_size at compile time, so the history takes no more
-// registers than the order needs.  The slice form (one context-parallel
-// rank's forward, _forward_global_slice on the same page) is the same kernel
-// over a window of positions whose history may reach back before it.
-constexpr int kLookRows = 32;
+// The fused forward (engram_lookup).  A block takes rows_per_block
+// consecutive lookups.  Phase 1: its first rows_per_block lanes compute one
+// row each from the tokens (lookup_row: the token's history in one round of
+// loads, the order mix, a Barrett remainder), so the hash costs one lane per
+// row, and keep them in LDS (and write them out when the caller asks).
+// Phase 2: as gather_kernel, every lane moves 16-byte chunks of those rows,
+// kUnroll at a time (all loads before the stores).  The row ids never go
+// through memory.  A block moves about kLookChunks chunks: 32 rows at
+// head_dim 256 (measured best there), more rows for narrower rows (head_dim
+// 64: 128 rows), at most one per thread.  N = ngram_size at compile time, so
+// the history takes no more registers than the order needs.  The slice form
+// (one context-parallel rank's forward, _forward_global_slice on the same
+// page) is the same kernel over a window of positions whose history may
+// reach back before it.
+constexpr int kLookRows = 32;       // fewest rows per block
+constexpr int kLookChunks = 1024;   // 16-byte chunks per block, when rows allow
+constexpr int kLookRowsMax = kGatherThreads;
 
 template <int N>
 __global__ __launch_bounds__(kGatherThreads) void lookup_kernel(
-    const HashParams h, int64_t n, const u32x4 *__restrict__ table, int64_t cpr, int log2_cpr,
-    u32x4 *__restrict__ out, int64_t *__restrict__ rows_out) {
-  __shared__ int64_t s_row[kLookRows];
-  const int64_t row0 = (int64_t)blockIdx.x * kLookRows;
-  const int nrows = (int)min((int64_t)kLookRows, n - row0);
+    const HashParams h, int64_t n, int rows_per_block, const u32x4 *__restrict__ table,
+    int64_t cpr, int log2_cpr, u32x4 *__restrict__ out, int64_t *__restrict__ rows_out) {
+  __shared__ int64_t s_row[kLookRowsMax];
+  const int64_t row0 = (int64_t)blockIdx.x * rows_per_block;
+  const int nrows = (int)min((int64_t)rows_per_block, n - row0);
   if ((int)threadIdx.x < nrows) {
     const int64_t r = lookup_row<N>(h, row0 + threadIdx.x);  // inside its head's rows
     s_row[threadIdx.x] = r;
@@ -226,7 +231,10 @@ int lookup_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t bat
   if (d_table == nullptr || d_out == nullptr) return ENGRAM_EINVAL;
   if (!aligned16(d_table) || !aligned16(d_out)) return ENGRAM_EALIGN;
   const int64_t cpr = head_dim / 8;
-  const int64_t blocks = (n + kLookRows - 1) / kLookRows;
+  int64_t rows_per_block = kLookChunks / cpr;
+  rows_per_block = rows_per_block < kLookRows ? kLookRows : rows_per_block;
+  rows_per_block = rows_per_block > kLookRowsMax ? kLookRowsMax : rows_per_block;
+  const int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
   if (blocks > INT32_MAX) return ENGRAM_EINVAL;
   const u32x4 *tab = static_cast<const u32x4 *>(d_table);
   u32x4 *out = static_cast<u32x4 *>(d_out);
@@ -238,8 +246,8 @@ int lookup_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t bat
   switch (ngram_size) {
 #define ENGRAM_LOOKUP_CASE(N)                                                                 \
   case N:                                                                                     \
-    hipLaunchKernelGGL(lookup_kernel<N>, grid, block, 0, s, h, n, tab, cpr, log2_cpr, out,     \
-                       d_row_ids);                                                            \
+    hipLaunchKernelGGL(lookup_kernel<N>, grid, block, 0, s, h, n, (int)rows_per_block, tab,   \
+                       cpr, log2_cpr, out, d_row_ids);                                        \
     break;
     ENGRAM_LOOKUP_CASE(2)
     ENGRAM_LOOKUP_CASE(3)

@@ -36,10 +36,11 @@ def test_lookup_tiny_against_oracle(oracle):
 
 
 @pytest.mark.parametrize("n", range(2, 9))
-@pytest.mark.parametrize("dim", [8, 24, 256])
+@pytest.mark.parametrize("dim", [8, 24, 64, 128, 256])
 def test_lookup_every_order_and_width(oracle, n, dim):
     """Every ngram size (the kernel is compiled per size) and row widths with
-    1, 3 (not a power of two) and 32 chunks, against the separate calls."""
+    1, 3 (not a power of two), 8, 16 and 32 chunks (256, 256, 128, 64 and 32
+    rows per block, the last block ragged), against the separate calls."""
     J = 2
     H = (n - 1) * J
     primes = workloads.primes_above(3000, H)
