@@ -10,6 +10,7 @@ tensors' device (or the stream passed in), exactly like the C entry points.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import re
 from pathlib import Path
@@ -130,14 +131,33 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+# Host arrays of hash constants, kept per value: the library only reads them
+# during a call, so one array serves every call with the same constants and a
+# step does not rebuild them (the per-call host cost bounds small steps).
+_HOST_I64 = {}
+
+
 def _host_i64(values, length, what):
-    arr = (ctypes.c_int64 * max(length, 1))()
-    vals = [int(v) for v in (values.tolist() if hasattr(values, "tolist") else values)]
+    vals = tuple(values.tolist() if hasattr(values, "tolist") else values)
     if len(vals) != length:
         raise ValueError(f"{what} must have {length} entries, got {len(vals)}")
-    for i, v in enumerate(vals):
-        arr[i] = v
+    arr = _HOST_I64.get(vals)
+    if arr is None:
+        arr = (ctypes.c_int64 * max(length, 1))(*(int(v) for v in vals))
+        if len(_HOST_I64) >= 256:
+            _HOST_I64.clear()
+        _HOST_I64[vals] = arr
     return arr
+
+
+_SAME_DEVICE = contextlib.nullcontext()
+
+
+def _on(device):
+    """Make `device` current for a call (no switch when it already is)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return _SAME_DEVICE
+    return torch.cuda.device(device)
 
 
 def _device_tensor(t, dtype, what):
@@ -177,7 +197,7 @@ def engram_hash(tokens, ngram_size, heads_per_ngram, eos_id, multipliers, primes
     mult = _host_i64(multipliers, int(ngram_size), "multipliers")
     pr = _host_i64(primes, heads, "primes")
     off = _host_i64(offsets, heads, "offsets")
-    with torch.cuda.device(tokens.device):
+    with _on(tokens.device):
         status = _lib.engram_hash(_ptr(tokens), _ptr(seq_ids), batch, seq, int(ngram_size),
                                   int(heads_per_ngram), int(eos_id), mult, pr, off,
                                   int(table_rows), _ptr(out), _stream(tokens.device, stream))
@@ -213,7 +233,7 @@ def engram_hash_slice(tokens, seq_start, seq_end, ngram_size, heads_per_ngram, e
     mult = _host_i64(multipliers, int(ngram_size), "multipliers")
     pr = _host_i64(primes, heads, "primes")
     off = _host_i64(offsets, heads, "offsets")
-    with torch.cuda.device(tokens.device):
+    with _on(tokens.device):
         status = _lib.engram_hash_slice(_ptr(tokens), _ptr(seq_ids), batch, gseq, start, end,
                                         int(ngram_size), int(heads_per_ngram), int(eos_id),
                                         mult, pr, off, int(table_rows), _ptr(out),
@@ -247,7 +267,7 @@ def engram_gather(row_ids, table, out=None, err_count=None, stream=None):
         raise ValueError("out must hold n * head_dim values")
     if err_count is not None:
         _device_tensor(err_count, torch.int64, "err_count")
-    with torch.cuda.device(row_ids.device):
+    with _on(row_ids.device):
         status = _lib.engram_gather(_ptr(row_ids), n, _ptr(table), rows, dim, _ptr(out),
                                     _ptr(err_count), _stream(row_ids.device, stream))
     _check(status, "engram_gather")
@@ -262,8 +282,9 @@ def engram_scatter_add_workspace(n, table_rows, head_dim, mode=SCATTER_SORTED) -
 
 
 def _workspace(workspace, n, table_rows, dim, mode, device):
-    need = engram_scatter_add_workspace(n, table_rows, dim, mode)
+    """The caller's workspace (the library checks its size), or a new one."""
     if workspace is None:
+        need = engram_scatter_add_workspace(n, table_rows, dim, mode)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     _device_tensor(workspace, torch.uint8, "workspace")
     return workspace
@@ -284,7 +305,7 @@ def engram_scatter_add(row_ids, grads, grad_table, mode=SCATTER_SORTED, workspac
     ws = None
     if mode == SCATTER_SORTED:
         ws = _workspace(workspace, n, rows, dim, mode, row_ids.device)
-    with torch.cuda.device(row_ids.device):
+    with _on(row_ids.device):
         status = _lib.engram_scatter_add(_ptr(row_ids), n, _ptr(grads), dim, _ptr(grad_table),
                                          rows, int(mode), _ptr(ws),
                                          0 if ws is None else ws.numel(), _ptr(err_count),
@@ -318,7 +339,7 @@ def engram_scatter_add_rowsparse(row_ids, grads, table_rows, unique_ids=None, un
     if err_count is not None:
         _device_tensor(err_count, torch.int64, "err_count")
     ws = _workspace(workspace, n, table_rows, dim, SCATTER_ROWSPARSE, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         status = _lib.engram_scatter_add_rowsparse(_ptr(row_ids), n, _ptr(grads), dim,
                                                    int(table_rows), _ptr(unique_ids),
                                                    _ptr(unique_grads), _ptr(num_unique),
@@ -337,7 +358,7 @@ def engram_scatter_plan(row_ids, table_rows, head_dim, workspace=None, err_count
     ws = _workspace(workspace, n, table_rows, head_dim, SCATTER_ROWSPARSE, row_ids.device)
     if err_count is not None:
         _device_tensor(err_count, torch.int64, "err_count")
-    with torch.cuda.device(row_ids.device):
+    with _on(row_ids.device):
         status = _lib.engram_scatter_plan(_ptr(row_ids), n, int(table_rows), int(head_dim),
                                           _ptr(ws), ws.numel(), _ptr(err_count),
                                           _stream(row_ids.device, stream))
@@ -371,7 +392,7 @@ def engram_scatter_apply(grads, workspace, table_rows, grad_table=None, unique_i
         _device_tensor(num_unique, torch.int64, "num_unique")
         if unique_ids.numel() < n or unique_grads.numel() < n * dim:
             raise ValueError("unique_ids / unique_grads must hold n entries")
-    with torch.cuda.device(dev):
+    with _on(dev):
         status = _lib.engram_scatter_apply(_ptr(grads), n, dim, int(table_rows),
                                            _ptr(grad_table), _ptr(unique_ids),
                                            _ptr(unique_grads), _ptr(num_unique), _ptr(workspace),
@@ -398,7 +419,7 @@ def engram_signsgd_rowsparse(unique_ids, unique_grads, num_unique, table, lr, er
         raise ValueError("unique_grads must be [capacity, head_dim]")
     if err_count is not None:
         _device_tensor(err_count, torch.int64, "err_count")
-    with torch.cuda.device(table.device):
+    with _on(table.device):
         status = _lib.engram_signsgd_rowsparse(_ptr(unique_ids), _ptr(unique_grads),
                                                _ptr(num_unique), cap, dim, _ptr(table), rows,
                                                float(lr), _ptr(err_count),
@@ -417,7 +438,7 @@ def engram_scatter_apply_signsgd(grads, workspace, table, lr, stream=None):
     n = grads.numel() // dim
     if grads.numel() != n * dim:
         raise ValueError("grads must be [n, head_dim] with the table's head_dim")
-    with torch.cuda.device(table.device):
+    with _on(table.device):
         status = _lib.engram_scatter_apply_signsgd(_ptr(grads), n, dim, rows, _ptr(table),
                                                    float(lr), _ptr(workspace),
                                                    workspace.numel(),
@@ -456,7 +477,7 @@ def engram_ple_conv(x, weight, dilation, bias=None, seq_ids=None, halo=None, out
     _device_tensor(out, torch.bfloat16, "out")
     if out.shape != x.shape:
         raise ValueError("out must have the shape of x")
-    with torch.cuda.device(x.device):
+    with _on(x.device):
         status = _lib.engram_ple_conv(_ptr(x), _ptr(halo), hl, _ptr(seq_ids), _ptr(weight),
                                       _ptr(bias), batch, seq, ch, weight.shape[1],
                                       int(dilation), _ptr(out), _stream(x.device, stream))
@@ -500,7 +521,7 @@ def engram_lookup(tokens, table, ngram_size, heads_per_ngram, eos_id, multiplier
         _device_tensor(row_ids, torch.int64, "row_ids")
         if row_ids.numel() != batch * seq * heads:
             raise ValueError("row_ids must hold batch * seq * H ids")
-    with torch.cuda.device(tokens.device):
+    with _on(tokens.device):
         status = _lib.engram_lookup(_ptr(tokens), _ptr(seq_ids), batch, seq, int(ngram_size),
                                     int(heads_per_ngram), int(eos_id), mult, pr, off,
                                     _ptr(table), rows, dim, _ptr(out), _ptr(row_ids),
@@ -536,7 +557,7 @@ def engram_lookup_slice(tokens, seq_start, seq_end, table, ngram_size, heads_per
         _device_tensor(row_ids, torch.int64, "row_ids")
         if row_ids.numel() != batch * local * heads:
             raise ValueError("row_ids must hold batch * (seq_end - seq_start) * H ids")
-    with torch.cuda.device(tokens.device):
+    with _on(tokens.device):
         status = _lib.engram_lookup_slice(_ptr(tokens), _ptr(seq_ids), batch, gseq, start, end,
                                           int(ngram_size), int(heads_per_ngram), int(eos_id),
                                           mult, pr, off, _ptr(table), rows, dim, _ptr(out),
@@ -555,7 +576,7 @@ def engram_scatter_plan_tokens(tokens, table_rows, head_dim, ngram_size, heads_p
     batch, seq = tokens.shape
     n = batch * seq * heads
     ws = _workspace(workspace, n, table_rows, head_dim, SCATTER_ROWSPARSE, tokens.device)
-    with torch.cuda.device(tokens.device):
+    with _on(tokens.device):
         status = _lib.engram_scatter_plan_tokens(_ptr(tokens), _ptr(seq_ids), batch, seq,
                                                  int(ngram_size), int(heads_per_ngram),
                                                  int(eos_id), mult, pr, off, int(table_rows),
