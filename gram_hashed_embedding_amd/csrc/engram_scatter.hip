@@ -71,6 +71,7 @@ constexpr int kAtomicThreads = 256;
 constexpr int kAtomicUnroll = 4;
 
 constexpr int64_t kLongBlocks = 1024;  // most blocks that sum long runs
+constexpr int64_t kXcds = 8;           // XCDs of an MI355X (blocks go to them in turn)
 // Gradient tensors larger than this are read with non-temporal loads: half
 // the MI355X's 256 MB Infinity Cache, so a tensor that could still be cached
 // when the apply runs is read normally.
@@ -1014,10 +1015,21 @@ template <int L, int Q, int OUT, bool EXACT, bool NT>
 __global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
   if (OUT == kOutSparse && blockIdx.x == 0 && threadIdx.x == 0)
     *a.num_unique = (int64_t)*a.unique_total;
-  if (blockIdx.x < a.long_blocks)
+  if (blockIdx.x < a.long_blocks) {
     long_runs<L, Q, OUT, EXACT, NT>(a);
-  else
-    walk_range<L, Q, OUT, EXACT, NT>(a, (int64_t)blockIdx.x - a.long_blocks);
+  } else {
+    // Walker blocks take their ranges stripe by stripe: the GPU hands
+    // consecutive blocks to its kXcds XCDs in turn, so the blocks of stripe
+    // blk % kXcds all run on one XCD, which then walks one contiguous part
+    // of the sorted order (the keys at its range boundaries and the runs
+    // that cross into the next range stay in that XCD's L2).  The blocks
+    // past the last whole stripe keep their order.
+    const int64_t nb = (int64_t)gridDim.x - a.long_blocks;
+    const int64_t blk = (int64_t)blockIdx.x - a.long_blocks;
+    const int64_t full = nb / kXcds * kXcds;
+    walk_range<L, Q, OUT, EXACT, NT>(a, blk < full ? blk % kXcds * (nb / kXcds) + blk / kXcds
+                                                   : blk);
+  }
 }
 
 __global__ void write_zero_kernel(int64_t *p) { *p = 0; }
