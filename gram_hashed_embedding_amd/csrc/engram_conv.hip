@@ -158,7 +158,8 @@ __global__ __launch_bounds__(kConvThreads) void ple_conv_generic_kernel(const Co
   const uint16_t *wp = reinterpret_cast<const uint16_t *>(a.w) + qd * 4 * a.K;
   const int64_t *sr = a.seg != nullptr ? a.seg + b * (a.halo_len + a.seq) + a.halo_len : nullptr;
   float acc[4];
-  for (int c = 0; c < 4; ++c) acc[c] = a.bias != nullptr ? bf16_bits_to_f32(a.bias[qd * 4 + c]) : 0.0f;
+  for (int c = 0; c < 4; ++c)
+    acc[c] = a.bias != nullptr ? bf16_bits_to_f32(a.bias[qd * 4 + c]) : 0.0f;
   for (int k = 0; k < a.K; ++k) {
     const int64_t p = t - (int64_t)(a.K - 1 - k) * a.dil;
     bool ok = p >= -a.halo_len;

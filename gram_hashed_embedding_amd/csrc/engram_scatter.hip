@@ -76,7 +76,7 @@ constexpr int64_t kXcds = 8;           // XCDs of an MI355X (blocks go to them i
 // the MI355X's 256 MB Infinity Cache, so a tensor that could still be cached
 // when the apply runs is read normally.
 constexpr int64_t kStreamGradBytes = int64_t(128) << 20;
-constexpr int64_t kLongSpan = 64;      // fewest ranges per such block
+constexpr int64_t kLongSpan = 64;      // fewest ranges per long-run block
 // Global digit totals are kept in kHistCopies copies (a block adds to copy
 // blockIdx % kHistCopies) so the histogram's atomics do not all meet on the
 // same few hundred words; readers add the copies.
@@ -775,7 +775,8 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
   for (int q = 1; q < kRange; ++q) klast = q < live_count ? kk[q] : klast;
   int tail = 0;
 #pragma unroll
-  for (int q = 0; q < kRange; ++q) tail += (q < live_count && !(last_long && kk[q] == klast)) ? 1 : 0;
+  for (int q = 0; q < kRange; ++q)
+    tail += (q < live_count && !(last_long && kk[q] == klast)) ? 1 : 0;
 
   // The output row of every run that starts in [lead, tail), loaded beside
   // the gradient rows, so no write waits on a read (other positions re-read
@@ -856,7 +857,8 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
     for (int q0 = 0; q0 < m; q0 += 4) {
       uint2 g[4][Q];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) load_row<L, Q, EXACT, NT>(a, q0 + b < m ? nv[q0 + b] : 0u, lane, g[b]);
+      for (int b = 0; b < 4; ++b)
+        load_row<L, Q, EXACT, NT>(a, q0 + b < m ? nv[q0 + b] : 0u, lane, g[b]);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
         if (q0 + b < m) add_quads<Q>(acc, g[b]);
@@ -1322,8 +1324,10 @@ int plan_sorted(const int64_t *ids, const HashParams *hp, int64_t n, int64_t tab
   // pair the apply reads; the keys a plan from tokens hashes go to the other
   // buffer of the first pass.
   const bool end_in_a = p.passes % 2 == 1;
-  uint32_t *const last_k = end_in_a ? v.keys_a : v.keys_b, *const last_v = end_in_a ? v.vals_a : v.vals_b;
-  uint32_t *const other_k = end_in_a ? v.keys_b : v.keys_a, *const other_v = end_in_a ? v.vals_b : v.vals_a;
+  uint32_t *const last_k = end_in_a ? v.keys_a : v.keys_b,
+                 *const last_v = end_in_a ? v.vals_a : v.vals_b;
+  uint32_t *const other_k = end_in_a ? v.keys_b : v.keys_a,
+                 *const other_v = end_in_a ? v.vals_b : v.vals_a;
   auto out_k = [&](int pass) { return (L.passes - 1 - pass) % 2 == 0 ? last_k : other_k; };
   auto out_v = [&](int pass) { return (L.passes - 1 - pass) % 2 == 0 ? last_v : other_v; };
   uint32_t *const hashed = out_k(0) == last_k ? other_k : last_k;
@@ -1503,7 +1507,8 @@ extern "C" int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head
   int rc = check_sorted(n, table_rows, head_dim, &p);
   if (rc != ENGRAM_OK) return rc;
   const bool dense = d_grad_table != nullptr;
-  const bool sparse = d_unique_ids != nullptr || d_unique_grads != nullptr || d_num_unique != nullptr;
+  const bool sparse =
+      d_unique_ids != nullptr || d_unique_grads != nullptr || d_num_unique != nullptr;
   if (dense == sparse) return ENGRAM_EINVAL;  // exactly one output form
   if (sparse && (d_unique_ids == nullptr || d_unique_grads == nullptr || d_num_unique == nullptr))
     return ENGRAM_EINVAL;

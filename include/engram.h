@@ -272,8 +272,9 @@ int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
  *     ENGRAM_SCATTER_ROWSPARSE) bytes; d_err_count as elsewhere.
  *   engram_scatter_apply: the same n, head_dim, table_rows and workspace as
  *     the plan (made by either plan call), with the plan's work ordered
- *     before it (same stream, or an event).  Exactly one output form: d_grad_table (dense, accumulated), or
- *     all of d_unique_ids / d_unique_grads / d_num_unique (row-sparse).  The
+ *     before it (same stream, or an event).  Exactly one output form:
+ *     d_grad_table (dense, accumulated), or all of d_unique_ids /
+ *     d_unique_grads / d_num_unique (row-sparse).  The
  *     apply does not change the plan; it may run again on the same plan.  A
  *     workspace that holds no plan of these ids gives undefined results.
  * Errors: EINVAL (sizes, output form), EALIGN, EWORKSPACE.  n == 0: the plan
