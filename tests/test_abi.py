@@ -237,3 +237,22 @@ def test_lookup_slice_rejects():
     # empty slices and batches enqueue nothing
     assert look(start=2, end=2, table=None, out=None) == e.ENGRAM_OK
     assert look(batch=0, tokens=None, table=None, out=None) == e.ENGRAM_OK
+
+
+def test_host_constant_arrays():
+    """The binding keeps one host array per set of hash constants: the same
+    values (as a tuple, a list or a numpy array) give the same array, other
+    values another one, and an array always holds exactly its values."""
+    import numpy as np
+    a = e._host_i64((5, -7, 2 ** 63 - 1), 3, "x")
+    assert list(a) == [5, -7, 2 ** 63 - 1]
+    assert e._host_i64([5, -7, 2 ** 63 - 1], 3, "x") is a
+    assert e._host_i64(np.array([5, -7, 2 ** 63 - 1], dtype=np.int64), 3, "x") is a
+    b = e._host_i64((5, -7, 3), 3, "x")
+    assert b is not a and list(b) == [5, -7, 3] and list(a) == [5, -7, 2 ** 63 - 1]
+    with pytest.raises(ValueError):
+        e._host_i64((1, 2), 3, "x")
+    for k in range(300):            # the cache stays bounded
+        e._host_i64((k, k + 1), 2, "x")
+    assert len(e._HOST_I64) <= 256
+    assert list(e._host_i64((5, -7, 3), 3, "x")) == [5, -7, 3]
