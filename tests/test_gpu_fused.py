@@ -226,3 +226,53 @@ def test_plans_made_ahead_in_two_workspaces(overlap):
         assert torch.equal(val[:u].view(torch.int32), val_r[:u].view(torch.int32))
     del got, grads, table, out
     release()
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_token_plan_random_sweep(seed):
+    """Seeded random token plans against the plan of engram_hash's ids, bit
+    for bit: ngram sizes 2..8, up to 64 heads, token counts from 1 to about
+    40,000 (ragged tiles of either size), primes from tiny to 2^22, head
+    offsets in a random order with random gaps, and on some seeds two
+    heads' ranges overlapping (one sort of all keys)."""
+    rng = np.random.Generator(np.random.PCG64(4200 + seed))
+    n = int(rng.integers(2, 9))
+    J = int(rng.integers(1, 64 // (n - 1) + 1))
+    H = (n - 1) * J
+    lo = int(np.exp(rng.uniform(np.log(3), np.log(1 << 22))))
+    primes = workloads.primes_above(lo, H)
+    order = rng.permutation(H)
+    offs = [0] * H
+    at = 0
+    for h in order:
+        at += int(rng.integers(0, 50))
+        offs[h] = at
+        at += primes[h]
+    if seed % 3 == 2 and H > 1:
+        a, b = int(order[0]), int(order[1])
+        offs[b] = offs[a] + primes[a] // 2
+    rows = at + int(rng.integers(1, 100))
+    mult = workloads.seeded_multipliers(n, 300 + seed)
+    batch = int(rng.integers(1, 4))
+    seq = int(np.exp(rng.uniform(0, np.log(40000 // batch))))
+    tok = rng.integers(0, int(rng.integers(2, 5000)), (batch, seq)).astype(np.int64)
+    tok[rng.random(tok.shape) < 0.02] = 3
+    seg = workloads.random_segments(tok.shape, int(rng.integers(5, 500)), seed) if seed % 2 else None
+    sd = None if seg is None else dev(seg)
+    args = (n, J, 3, mult, primes, offs)
+    R = tok.size * H
+    dim = 8
+    grads = workloads.make_grads(R, dim, 50 + seed, "cuda")
+    ws_t = E.engram_scatter_plan_tokens(dev(tok), rows, dim, *args, seq_ids=sd)
+    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, rows)
+    ids = E.engram_hash(dev(tok), *args, rows, seq_ids=sd)
+    ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
+    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, rows)
+    torch.cuda.synchronize()
+    u = int(cnt_t.item())
+    assert u == int(cnt_i.item()) and u > 0
+    assert torch.equal(uid_t[:u], uid_i[:u])
+    assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
+    assert torch.equal(uid_t[:u], torch.unique(ids))
+    del grads, ws_t, ws_i
+    release()
