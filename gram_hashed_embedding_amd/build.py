@@ -2,7 +2,8 @@
 
     python -m gram_hashed_embedding_amd.build
 
-compiles every csrc/*.hip into gram_hashed_embedding_amd/libengram.so.
+compiles every csrc/*.hip (one hipcc process per source, in parallel) and
+links them into gram_hashed_embedding_amd/libengram.so.
 """
 from __future__ import annotations
 
@@ -10,6 +11,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 from pathlib import Path
 
 PKG = Path(__file__).resolve().parent
@@ -24,7 +27,6 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-Wall",
     # packed fp32 vector ops (v_pk_*_f32) are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -44,14 +46,34 @@ def sources() -> list[Path]:
     return sorted(CSRC.glob("*.hip"))
 
 
+def _jobs() -> int:
+    try:
+        return max(1, min(int(os.environ.get("MAX_JOBS", "0")) or os.cpu_count() or 1, 16))
+    except ValueError:
+        return 4
+
+
 def build(verbose: bool = False) -> Path:
     """Compile all HIP sources into LIBRARY (always rebuilds)."""
-    tmp = LIBRARY.with_suffix(".so.tmp")
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}",
-           *map(str, sources()), "-o", str(tmp)]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    cc = hipcc()
+    with tempfile.TemporaryDirectory(prefix="engram_build_") as tmpdir:
+        objs = []
+
+        def compile_one(src: Path) -> Path:
+            obj = Path(tmpdir) / (src.stem + ".o")
+            cmd = [cc, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(src), "-o", str(obj)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.run(cmd, check=True)
+            return obj
+
+        with ThreadPoolExecutor(max_workers=_jobs()) as pool:
+            objs = list(pool.map(compile_one, sources()))
+        tmp = LIBRARY.with_suffix(".so.tmp")
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *map(str, objs), "-o", str(tmp)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
     os.replace(tmp, LIBRARY)
     return LIBRARY
 
