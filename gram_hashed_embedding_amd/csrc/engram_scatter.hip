@@ -51,6 +51,8 @@
 //     contributions) do not serialise a walker.
 // Atomic path: one fp32 atomic add per gradient element into the dense
 // table (hardware float atomics in L2); order of additions not fixed.
+#include <mutex>
+
 #include "engram_hash_dev.h"
 
 namespace engram {
@@ -1458,6 +1460,37 @@ int atomic_scatter(const int64_t *ids, int64_t n, const void *grads, int64_t dim
   return launch_status();
 }
 
+// ------------------------------------------------------- static scratch ---
+// The workspace of engram_scatter_add_rowsparse_noalloc: a fixed device
+// array of the library (each device holds its own copy from the time the
+// library's code is loaded on it until the process ends), for callers that
+// cannot allocate.  Host code never uses the array's name as a device
+// address: the address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.
+constexpr size_t kStaticScratchBytes = ENGRAM_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint64_t scratch[kStaticScratchBytes / sizeof(uint64_t)];
+
+struct ScratchSlot {
+  std::once_flag once;
+  void *ptr = nullptr;
+  hipError_t rc = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, or null.
+void *static_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchSlot &slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot] {
+    void *p = nullptr;
+    slot.rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    slot.ptr = slot.rc == hipSuccess ? p : nullptr;
+  });
+  return slot.ptr;
+}
+
 }  // namespace
 }  // namespace engram
 
@@ -1622,3 +1655,32 @@ extern "C" int engram_scatter_plan_tokens(const int64_t *d_tokens, const int64_t
   return plan_sorted(nullptr, &hp, n, table_rows, p, d_workspace, nullptr, as_stream(stream));
 }
 
+
+extern "C" int engram_scatter_add_rowsparse_noalloc(const int64_t *d_row_ids, int64_t n,
+                                                    const void *d_grads, int64_t head_dim,
+                                                    int64_t table_rows, int64_t *d_unique_ids,
+                                                    float *d_unique_grads,
+                                                    int64_t *d_num_unique, int64_t *d_err_count,
+                                                    void *stream) {
+  Plan p;
+  int rc = check_sorted(n, table_rows, head_dim, &p);
+  if (rc != ENGRAM_OK) return rc;
+  if (d_num_unique == nullptr) return ENGRAM_EINVAL;
+  if (p.total > kStaticScratchBytes) return ENGRAM_EWORKSPACE;  // more ids than the array plans
+  hipStream_t s = as_stream(stream);
+  if (n == 0) {
+    hipLaunchKernelGGL(write_zero_kernel, dim3(1), dim3(1), 0, s, d_num_unique);
+    return launch_status();
+  }
+  if (d_row_ids == nullptr || d_grads == nullptr || d_unique_ids == nullptr ||
+      d_unique_grads == nullptr)
+    return ENGRAM_EINVAL;
+  if (!aligned16(d_grads) || !aligned16(d_unique_grads)) return ENGRAM_EALIGN;
+  void *ws = static_scratch();
+  if (ws == nullptr) return ENGRAM_EHIP;
+  if ((rc = plan_sorted(d_row_ids, nullptr, n, table_rows, p, ws, d_err_count, s)) != ENGRAM_OK)
+    return rc;
+  const ApplyOut o = {kOutSparse, nullptr, d_unique_ids, d_unique_grads, d_num_unique, nullptr,
+                      0.0f};
+  return apply_sorted(d_grads, n, head_dim, table_rows, p, ws, o, s);
+}

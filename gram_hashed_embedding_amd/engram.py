@@ -31,6 +31,7 @@ SCATTER_ATOMIC = 1
 SCATTER_ROWSPARSE = 2
 MAX_NGRAM = 8
 MAX_HEADS = 64
+NOALLOC_SCRATCH_BYTES = 32 << 20  # ENGRAM_NOALLOC_SCRATCH_BYTES
 
 if not LIBRARY.exists():
     raise ImportError(f"{LIBRARY} is missing: build it with "
@@ -81,6 +82,10 @@ _lib.engram_scatter_add_rowsparse.restype = ctypes.c_int
 _lib.engram_scatter_add_rowsparse.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
                                               ctypes.c_int64, _vp, _vp, _vp, _vp,
                                               ctypes.c_size_t, _vp, _vp]
+
+_lib.engram_scatter_add_rowsparse_noalloc.restype = ctypes.c_int
+_lib.engram_scatter_add_rowsparse_noalloc.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
+                                                      ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]
 
 _lib.engram_scatter_plan.restype = ctypes.c_int
 _lib.engram_scatter_plan.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
@@ -346,6 +351,34 @@ def engram_scatter_add_rowsparse(row_ids, grads, table_rows, unique_ids=None, un
                                                    _ptr(ws), ws.numel(), _ptr(err_count),
                                                    _stream(dev, stream))
     _check(status, "engram_scatter_add_rowsparse")
+    return unique_ids, unique_grads, num_unique
+
+
+def engram_scatter_add_rowsparse_noalloc(row_ids, grads, table_rows, unique_ids, unique_grads,
+                                         num_unique, err_count=None, stream=None):
+    """engram_scatter_add_rowsparse with the library's fixed device array as
+    its workspace: every output buffer is the caller's and nothing is
+    allocated.  Raises EngramError (workspace) when n ids need more than
+    NOALLOC_SCRATCH_BYTES of workspace.  Calls that overlap on one device race."""
+    _device_tensor(row_ids, torch.int64, "row_ids")
+    _device_tensor(grads, torch.bfloat16, "grads")
+    n = row_ids.numel()
+    dim = grads.shape[-1]
+    if grads.numel() != n * dim:
+        raise ValueError("grads must hold n * head_dim values")
+    _device_tensor(unique_ids, torch.int64, "unique_ids")
+    _device_tensor(unique_grads, torch.float32, "unique_grads")
+    _device_tensor(num_unique, torch.int64, "num_unique")
+    if unique_ids.numel() < n or unique_grads.numel() < n * dim:
+        raise ValueError("unique_ids / unique_grads must hold n entries")
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
+    dev = row_ids.device
+    with _on(dev):
+        status = _lib.engram_scatter_add_rowsparse_noalloc(
+            _ptr(row_ids), n, _ptr(grads), dim, int(table_rows), _ptr(unique_ids),
+            _ptr(unique_grads), _ptr(num_unique), _ptr(err_count), _stream(dev, stream))
+    _check(status, "engram_scatter_add_rowsparse_noalloc")
     return unique_ids, unique_grads, num_unique
 
 

@@ -14,7 +14,9 @@
  * - Pointers named d_* are device pointers (HIP device memory of the current
  *   device); pointers named h_* are host pointers.  The caller allocates and
  *   frees every buffer, workspace included.  The library never allocates,
- *   keeps no state between calls and is re-entrant.
+ *   keeps no state between calls and is re-entrant; the one exception is
+ *   engram_scatter_add_rowsparse_noalloc, whose workspace is a fixed device
+ *   array of the library (see there).
  * - Host arrays are read during the call only (copied into kernel
  *   arguments); the caller may reuse them as soon as the call returns.
  * - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
@@ -69,6 +71,9 @@ extern "C" {
 #define ENGRAM_SCATTER_SORTED 0    /* deterministic: sort + segmented sum    */
 #define ENGRAM_SCATTER_ATOMIC 1    /* fp32 atomic adds (order not fixed)     */
 #define ENGRAM_SCATTER_ROWSPARSE 2 /* workspace query of the row-sparse call */
+
+/* Bytes of the fixed device array engram_scatter_add_rowsparse_noalloc uses. */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* Human-readable text of a status code (static storage). */
 const char *engram_status_string(int status);
@@ -307,6 +312,33 @@ int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
                          int64_t table_rows, float *d_grad_table, int64_t *d_unique_ids,
                          float *d_unique_grads, int64_t *d_num_unique, void *d_workspace,
                          size_t workspace_bytes, void *stream);
+
+/*
+ * engram_scatter_add_rowsparse_noalloc -- engram_scatter_add_rowsparse
+ * without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same sums, outputs, limits and errors as
+ * engram_scatter_add_rowsparse; the sorted path's workspace is instead a
+ * fixed device array of the library of ENGRAM_NOALLOC_SCRATCH_BYTES bytes
+ * (each device the library runs on holds one copy until the process ends).
+ * The call allocates nothing.
+ *   Size limit: n ids fit when engram_scatter_add_workspace(n, table_rows,
+ *   head_dim, ENGRAM_SCATTER_ROWSPARSE) <= ENGRAM_NOALLOC_SCRATCH_BYTES
+ *   (about 1.9M ids of a 200M-row table); larger inputs return
+ *   ENGRAM_EWORKSPACE before anything is enqueued.
+ *   Every call on a device uses that device's one array, which keeps the last
+ *   call's contents (each call clears what it needs cleared): calls that
+ *   overlap on one device (other streams, other host threads) race and give
+ *   undefined results.  Order them on one stream, or use
+ *   engram_scatter_add_rowsparse with a workspace per stream.
+ * Errors: those of engram_scatter_add_rowsparse (EWORKSPACE: too many ids),
+ * and EHIP if the array's address cannot be found on the current device.
+ */
+int engram_scatter_add_rowsparse_noalloc(const int64_t *d_row_ids, int64_t n,
+                                         const void *d_grads, int64_t head_dim,
+                                         int64_t table_rows, int64_t *d_unique_ids,
+                                         float *d_unique_grads, int64_t *d_num_unique,
+                                         int64_t *d_err_count, void *stream);
 
 /*
  * engram_signsgd_rowsparse -- one SignSGD step on the rows a row-sparse

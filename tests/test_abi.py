@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
                           "engram_hash_slice", "engram_signsgd_rowsparse",
                           "engram_scatter_apply_signsgd", "engram_ple_conv",
                           "engram_lookup", "engram_scatter_plan_tokens",
-                          "engram_lookup_slice"}
+                          "engram_lookup_slice", "engram_scatter_add_rowsparse_noalloc"}
     for name in names:
         assert hasattr(e._lib, name), name
 
@@ -256,3 +256,24 @@ def test_host_constant_arrays():
         e._host_i64((k, k + 1), 2, "x")
     assert len(e._HOST_I64) <= 256
     assert list(e._host_i64((5, -7, 3), 3, "x")) == [5, -7, 3]
+
+
+def test_noalloc_limits():
+    """The allocation-free scatter-add takes any n whose workspace fits its
+    fixed array (the e2e batch does) and rejects larger ones before any
+    launch; its other checks are the row-sparse call's."""
+    w = e.engram_scatter_add_workspace
+    assert w(1572864, 200000000, 256, e.SCATTER_ROWSPARSE) <= e.NOALLOC_SCRATCH_BYTES
+    na = e._lib.engram_scatter_add_rowsparse_noalloc
+    n = 4_000_000
+    assert w(n, 200000000, 256, e.SCATTER_ROWSPARSE) > e.NOALLOC_SCRATCH_BYTES
+    assert na(ALIGNED, n, ALIGNED, 256, 200000000, ALIGNED, ALIGNED, ALIGNED, None, None) == \
+        e.ENGRAM_EWORKSPACE
+    assert na(ALIGNED, 100, ALIGNED, 12, 50, ALIGNED, ALIGNED, ALIGNED, None, None) == \
+        e.ENGRAM_EINVAL                                    # head_dim % 8
+    assert na(ALIGNED, 100, ALIGNED, 8, 50, ALIGNED, ALIGNED, None, None, None) == \
+        e.ENGRAM_EINVAL                                    # no count
+    assert na(None, 100, ALIGNED, 8, 50, ALIGNED, ALIGNED, ALIGNED, None, None) == \
+        e.ENGRAM_EINVAL
+    assert na(ALIGNED, 100, MISALIGNED, 8, 50, ALIGNED, ALIGNED, ALIGNED, None, None) == \
+        e.ENGRAM_EALIGN
