@@ -415,6 +415,9 @@ def main():
         ws = wss[0]
 
     side = torch.cuda.Stream(dev)  # default priority
+    # every plan and apply reports into one device counter, checked after the
+    # run: an expired wait or an apply without its plan would show there
+    err = torch.zeros(1, dtype=torch.int64, device=dev)
     hargs = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
     ev_plan = [torch.cuda.Event() for _ in range(2)]
     ev_apply = [torch.cuda.Event() for _ in range(2)]
@@ -428,7 +431,7 @@ def main():
         last read that workspace (batch k - 2) is done."""
         side.wait_event(ev_apply[k % 2])
         E.engram_scatter_plan_tokens(tokens[k % N_BATCHES], wl.table_rows, D, *hargs,
-                                     workspace=wss[k % 2], stream=side)
+                                     workspace=wss[k % 2], err_count=err, stream=side)
         ev_plan[k % 2].record(side)
         planned["next"] = k
 
@@ -461,7 +464,8 @@ def main():
             return
         ev_rows[k % 2].record(stream)
         side.wait_event(ev_rows[k % 2])
-        E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws, stream=side)
+        E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws, err_count=err,
+                              stream=side)
         ev_plan[k % 2].record(side)
         E.engram_gather(rows, table, out=out)
         stream.wait_event(ev_plan[k % 2])
@@ -469,12 +473,12 @@ def main():
 
     def apply_backward(ws):
         if signsgd:
-            E.engram_scatter_apply_signsgd(grads, ws, table, lr)
+            E.engram_scatter_apply_signsgd(grads, ws, table, lr, err_count=err)
         elif wl.grads == "rowsparse":
             E.engram_scatter_apply(grads, ws, wl.table_rows, unique_ids=uid, unique_grads=uval,
-                                   num_unique=count)
+                                   num_unique=count, err_count=err)
         else:
-            E.engram_scatter_apply(grads, ws, wl.table_rows, grad_table=gtab)
+            E.engram_scatter_apply(grads, ws, wl.table_rows, grad_table=gtab, err_count=err)
 
     def serial_step(k, ev, separate=False):
         """The calls of a step one after another on one stream, with events
@@ -491,9 +495,11 @@ def main():
         ev[2].record(stream)
         if backward:
             if separate:
-                E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws)
+                E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws,
+                                      err_count=err)
             else:
-                E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, workspace=ws)
+                E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, workspace=ws,
+                                             err_count=err)
             ev[3].record(stream)
             apply_backward(ws)
             ev[4].record(stream)
@@ -570,6 +576,8 @@ def main():
     sep_ms = timed_steps(step_separate)
     sep_phase_ms, _ = serial_phases(True)
 
+    if backward and int(err.item()) != 0:
+        raise RuntimeError(f"the step's plans or applies reported errors: {int(err.item())}")
     # distinct rows of one batch (the backward's U), read after timing
     unique_rows = 0
     if backward:

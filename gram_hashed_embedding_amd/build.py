@@ -2,8 +2,10 @@
 
     python -m gram_hashed_embedding_amd.build
 
-compiles every csrc/*.hip (one hipcc process per source, in parallel) and
-links them into gram_hashed_embedding_amd/libengram.so.
+compiles every csrc/*.hip with hipcc and the host-only csrc/*.cpp (the
+entry points and their argument checks, plain C++) with ROCm's clang++, one
+process per source, in parallel, and links them into
+gram_hashed_embedding_amd/libengram.so.
 """
 from __future__ import annotations
 
@@ -42,8 +44,18 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libengram.so)")
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra"]
+
+
 def sources() -> list[Path]:
-    return sorted(CSRC.glob("*.hip"))
+    return sorted(CSRC.glob("*.hip")) + sorted(CSRC.glob("*.cpp"))
+
+
+def host_cxx() -> str:
+    for cand in (os.environ.get("ENGRAM_CXX"), "/opt/rocm/llvm/bin/clang++", shutil.which("g++")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("no C++ compiler found for the host sources")
 
 
 def _jobs() -> int:
@@ -61,7 +73,11 @@ def build(verbose: bool = False) -> Path:
 
         def compile_one(src: Path) -> Path:
             obj = Path(tmpdir) / (src.stem + ".o")
-            cmd = [cc, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(src), "-o", str(obj)]
+            if src.suffix == ".cpp":
+                cmd = [host_cxx(), *HOST_FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(src),
+                       "-o", str(obj)]
+            else:
+                cmd = [cc, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", str(src), "-o", str(obj)]
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.run(cmd, check=True)

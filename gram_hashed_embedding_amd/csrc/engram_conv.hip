@@ -37,7 +37,6 @@ constexpr int kConvThreads = 256;
 constexpr int kConvQuads = kConvThreads;  // channel quads per block (1024 channels)
 constexpr int kT = 24;                    // positions per lane
 constexpr int kXcds = 8;                  // XCDs of an MI355X (blocks go round-robin)
-constexpr int kMaxKernel = 16;
 
 struct ConvArgs {
   const uint2 *x;     // [batch, seq, quads]
@@ -148,7 +147,7 @@ __global__ __launch_bounds__(kConvThreads) void ple_conv_k4_kernel(const ConvArg
   }
 }
 
-// Any K <= kMaxKernel and dilation: one lane per (position, channel quad),
+// Any K <= kConvMaxKernel and dilation: one lane per (position, channel quad),
 // each tap read from memory and checked against the segment ids directly.
 __global__ __launch_bounds__(kConvThreads) void ple_conv_generic_kernel(const ConvArgs a) {
   const int64_t i = (int64_t)blockIdx.x * kConvThreads + threadIdx.x;
@@ -177,46 +176,28 @@ __global__ __launch_bounds__(kConvThreads) void ple_conv_generic_kernel(const Co
 }  // namespace
 }  // namespace engram
 
-using namespace engram;
-
-extern "C" int engram_ple_conv(const void *d_x, const void *d_halo, int64_t halo_len,
-                               const int64_t *d_seq_ids, const void *d_weight,
-                               const void *d_bias, int64_t batch, int64_t seq, int64_t channels,
-                               int32_t kernel_size, int32_t dilation, void *d_out,
-                               void *stream) {
-  if (batch < 0 || seq < 0 || channels <= 0 || channels % 8 != 0 || halo_len < 0)
-    return ENGRAM_EINVAL;
-  if (kernel_size < 1 || kernel_size > kMaxKernel || dilation < 1) return ENGRAM_EINVAL;
-  if (halo_len > 0 && d_halo == nullptr) return ENGRAM_EINVAL;
-  if (seq > INT64_MAX / 2 - halo_len || channels > INT64_MAX / 8) return ENGRAM_EINVAL;
-  if (!mul_fits(batch, seq + halo_len, INT64_MAX / 8) ||
-      !mul_fits(batch * (seq + halo_len), channels * 2, INT64_MAX))
-    return ENGRAM_EINVAL;
-  if (batch == 0 || seq == 0) return ENGRAM_OK;
-  if (d_x == nullptr || d_weight == nullptr || d_out == nullptr) return ENGRAM_EINVAL;
-  if (!aligned16(d_x) || !aligned16(d_out) || (d_halo != nullptr && !aligned16(d_halo)))
-    return ENGRAM_EALIGN;
+int engram::launch_ple_conv(const ConvCall &c, void *stream) {
   ConvArgs a = {};
-  a.x = static_cast<const uint2 *>(d_x);
-  a.halo = static_cast<const uint2 *>(d_halo);
-  a.seg = d_seq_ids;
-  a.w = static_cast<const uint2 *>(d_weight);
-  a.bias = static_cast<const uint16_t *>(d_bias);
-  a.out = static_cast<uint2 *>(d_out);
-  a.batch = batch;
-  a.seq = seq;
-  a.quads = channels / 4;
-  a.halo_len = halo_len;
-  a.K = kernel_size;
-  a.dil = dilation;
-  a.tiles = (seq + kT - 1) / kT;
+  a.x = static_cast<const uint2 *>(c.x);
+  a.halo = static_cast<const uint2 *>(c.halo);
+  a.seg = c.seg;
+  a.w = static_cast<const uint2 *>(c.weight);
+  a.bias = static_cast<const uint16_t *>(c.bias);
+  a.out = static_cast<uint2 *>(c.out);
+  a.batch = c.batch;
+  a.seq = c.seq;
+  a.quads = c.channels / 4;
+  a.halo_len = c.halo_len;
+  a.K = c.K;
+  a.dil = c.dilation;
+  a.tiles = (c.seq + kT - 1) / kT;
   a.groups = (a.quads + kConvQuads - 1) / kConvQuads;
   hipStream_t s = as_stream(stream);
-  const int64_t blocks = batch * a.groups * a.tiles;
-  if (kernel_size == 4 && dilation <= 8) {
+  const int64_t blocks = c.batch * a.groups * a.tiles;
+  if (c.K == 4 && c.dilation <= 8) {
     if (blocks > INT32_MAX) return ENGRAM_EINVAL;
     const dim3 grid((unsigned)blocks), block(kConvThreads);
-    switch (dilation) {
+    switch (c.dilation) {
 #define ENGRAM_CONV_CASE(D) \
   case D: hipLaunchKernelGGL(ple_conv_k4_kernel<D>, grid, block, 0, s, a); break;
       ENGRAM_CONV_CASE(1)
@@ -230,7 +211,7 @@ extern "C" int engram_ple_conv(const void *d_x, const void *d_halo, int64_t halo
 #undef ENGRAM_CONV_CASE
     }
   } else {
-    const int64_t n = batch * seq * a.quads;
+    const int64_t n = c.batch * c.seq * a.quads;
     const int64_t gb = (n + kConvThreads - 1) / kConvThreads;
     if (gb > INT32_MAX) return ENGRAM_EINVAL;
     hipLaunchKernelGGL(ple_conv_generic_kernel, dim3((unsigned)gb), dim3(kConvThreads), 0, s, a);

@@ -152,25 +152,14 @@ __global__ __launch_bounds__(kGatherThreads) void lookup_kernel(
 }  // namespace
 }  // namespace engram
 
-using namespace engram;
-
-extern "C" int engram_gather(const int64_t *d_row_ids, int64_t n, const void *d_table,
-                             int64_t table_rows, int64_t head_dim, void *d_out,
-                             int64_t *d_err_count, void *stream) {
-  if (n < 0 || table_rows < 0 || head_dim <= 0 || head_dim % 8 != 0 || head_dim > kMaxDim)
-    return ENGRAM_EINVAL;
-  if (!mul_fits(table_rows, head_dim * 2, INT64_MAX) || !mul_fits(n, head_dim * 2, INT64_MAX))
-    return ENGRAM_EINVAL;
-  if (n == 0) return ENGRAM_OK;
-  if (d_row_ids == nullptr || d_table == nullptr || d_out == nullptr) return ENGRAM_EINVAL;
-  if (!aligned16(d_table) || !aligned16(d_out)) return ENGRAM_EALIGN;
-
+int engram::launch_gather(const int64_t *d_row_ids, int64_t n, const void *d_table,
+                          int64_t table_rows, int64_t head_dim, void *d_out, int64_t *d_err_count,
+                          void *stream) {
   const int64_t cpr = head_dim / 8;
   const int64_t total = n * cpr;
   const int64_t per_block = (int64_t)kGatherThreads * kUnroll;
   const int64_t blocks = (total + per_block - 1) / per_block;
   if (blocks > INT32_MAX) return ENGRAM_EINVAL;
-
   const u32x4 *tab = static_cast<const u32x4 *>(d_table);
   u32x4 *out = static_cast<u32x4 *>(d_out);
   hipStream_t s = as_stream(stream);
@@ -205,31 +194,10 @@ extern "C" int engram_gather(const int64_t *d_row_ids, int64_t n, const void *d_
   return launch_status();
 }
 
-namespace engram {
-namespace {
-
-// The fused forward over positions [start, end) of every row of tokens
-// [batch, stride]; shared by engram_lookup (the whole rows) and
-// engram_lookup_slice.
-int lookup_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
-                  int64_t stride, int64_t start, int64_t end, int32_t ngram_size,
-                  int32_t heads_per_ngram, int64_t eos_id, const int64_t *h_multipliers,
-                  const int64_t *h_primes, const int64_t *h_offsets, const void *d_table,
-                  int64_t table_rows, int64_t head_dim, void *d_out, int64_t *d_row_ids,
-                  void *stream) {
-  if (head_dim <= 0 || head_dim % 8 != 0 || head_dim > kMaxDim) return ENGRAM_EINVAL;
-  HashParams h;
-  int64_t tokens = 0;
-  const int rc = make_hash_params(d_tokens, d_seq_ids, batch, stride, start, end, ngram_size,
-                                  heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets,
-                                  table_rows, &h, &tokens);
-  if (rc != ENGRAM_OK) return rc;
-  const int64_t n = tokens * h.H;
-  if (!mul_fits(table_rows, head_dim * 2, INT64_MAX) || !mul_fits(n, head_dim * 2, INT64_MAX))
-    return ENGRAM_EINVAL;
-  if (n == 0) return ENGRAM_OK;
-  if (d_table == nullptr || d_out == nullptr) return ENGRAM_EINVAL;
-  if (!aligned16(d_table) || !aligned16(d_out)) return ENGRAM_EALIGN;
+// The fused forward over the positions hp describes (a whole row, or one
+// context-parallel slice of it), n = tokens * H lookups.
+int engram::launch_lookup(const HashParams &hp, int64_t n, const void *d_table,
+                          int64_t head_dim, void *d_out, int64_t *d_row_ids, void *stream) {
   const int64_t cpr = head_dim / 8;
   int64_t rows_per_block = kLookChunks / cpr;
   rows_per_block = rows_per_block < kLookRows ? kLookRows : rows_per_block;
@@ -243,10 +211,10 @@ int lookup_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t bat
   int log2_cpr = -1;
   for (int b = 0; b < 62; ++b)
     if (cpr == (int64_t)1 << b) log2_cpr = b;
-  switch (ngram_size) {
+  switch (hp.n) {
 #define ENGRAM_LOOKUP_CASE(N)                                                                 \
   case N:                                                                                     \
-    hipLaunchKernelGGL(lookup_kernel<N>, grid, block, 0, s, h, n, (int)rows_per_block, tab,   \
+    hipLaunchKernelGGL(lookup_kernel<N>, grid, block, 0, s, hp, n, (int)rows_per_block, tab,  \
                        cpr, log2_cpr, out, d_row_ids);                                        \
     break;
     ENGRAM_LOOKUP_CASE(2)
@@ -259,31 +227,4 @@ int lookup_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t bat
 #undef ENGRAM_LOOKUP_CASE
   }
   return launch_status();
-}
-
-}  // namespace
-}  // namespace engram
-
-extern "C" int engram_lookup(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
-                             int64_t seq, int32_t ngram_size, int32_t heads_per_ngram,
-                             int64_t eos_id, const int64_t *h_multipliers,
-                             const int64_t *h_primes, const int64_t *h_offsets,
-                             const void *d_table, int64_t table_rows, int64_t head_dim,
-                             void *d_out, int64_t *d_row_ids, void *stream) {
-  if (seq < 0) return ENGRAM_EINVAL;
-  return lookup_window(d_tokens, d_seq_ids, batch, seq, 0, seq, ngram_size, heads_per_ngram,
-                       eos_id, h_multipliers, h_primes, h_offsets, d_table, table_rows, head_dim,
-                       d_out, d_row_ids, stream);
-}
-
-extern "C" int engram_lookup_slice(const int64_t *d_tokens, const int64_t *d_seq_ids,
-                                   int64_t batch, int64_t global_seq, int64_t seq_start,
-                                   int64_t seq_end, int32_t ngram_size, int32_t heads_per_ngram,
-                                   int64_t eos_id, const int64_t *h_multipliers,
-                                   const int64_t *h_primes, const int64_t *h_offsets,
-                                   const void *d_table, int64_t table_rows, int64_t head_dim,
-                                   void *d_out, int64_t *d_row_ids, void *stream) {
-  return lookup_window(d_tokens, d_seq_ids, batch, global_seq, seq_start, seq_end, ngram_size,
-                       heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets, d_table,
-                       table_rows, head_dim, d_out, d_row_ids, stream);
 }

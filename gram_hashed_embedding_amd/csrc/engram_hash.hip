@@ -84,93 +84,12 @@ __global__ __launch_bounds__(kHashThreads) void hash_kernel(const HashArgs a) {
 }  // namespace
 }  // namespace engram
 
-namespace engram {
-namespace {
-
-int hash_window(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch, int64_t stride,
-                int64_t start, int64_t end, int32_t ngram_size, int32_t heads_per_ngram,
-                int64_t eos_id, const int64_t *h_multipliers, const int64_t *h_primes,
-                const int64_t *h_offsets, int64_t table_rows, int64_t *d_row_ids,
-                void *stream) {
-  HashArgs a = {};
-  int64_t total = 0;
-  const int rc = make_hash_params(d_tokens, d_seq_ids, batch, stride, start, end, ngram_size,
-                                  heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets,
-                                  table_rows, &a.p, &total);
-  if (rc != ENGRAM_OK) return rc;
-  if ((total + kHashTokens - 1) / kHashTokens > INT32_MAX) return ENGRAM_EINVAL;
-  if (total == 0) return ENGRAM_OK;
-  if (d_row_ids == nullptr) return ENGRAM_EINVAL;
-  a.rows = d_row_ids;
-  a.total_tokens = total;
-  const unsigned blocks = (unsigned)((total + kHashTokens - 1) / kHashTokens);
-  hipLaunchKernelGGL(hash_kernel, dim3(blocks), dim3(kHashThreads), 0, as_stream(stream), a);
+int engram::launch_hash(const HashParams &hp, int64_t tokens, int64_t *d_row_ids,
+                        void *stream) {
+  const int64_t blocks = (tokens + kHashTokens - 1) / kHashTokens;
+  if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+  const HashArgs a = {hp, d_row_ids, tokens};
+  hipLaunchKernelGGL(hash_kernel, dim3((unsigned)blocks), dim3(kHashThreads), 0,
+                     as_stream(stream), a);
   return launch_status();
-}
-
-}  // namespace
-
-int make_hash_params(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
-                     int64_t stride, int64_t start, int64_t end, int32_t ngram_size,
-                     int32_t heads_per_ngram, int64_t eos_id, const int64_t *h_multipliers,
-                     const int64_t *h_primes, const int64_t *h_offsets, int64_t table_rows,
-                     HashParams *hp, int64_t *tokens_out) {
-  if (batch < 0 || stride < 0 || table_rows < 0) return ENGRAM_EINVAL;
-  if (start < 0 || end < start || end > stride) return ENGRAM_EINVAL;
-  if (ngram_size < 2 || ngram_size > ENGRAM_MAX_NGRAM || heads_per_ngram < 1)
-    return ENGRAM_EINVAL;
-  const int64_t H = (int64_t)(ngram_size - 1) * heads_per_ngram;
-  if (H > ENGRAM_MAX_HEADS) return ENGRAM_EINVAL;
-  if (h_multipliers == nullptr || h_primes == nullptr || h_offsets == nullptr)
-    return ENGRAM_EINVAL;
-  if (!mul_fits(batch, stride, INT64_MAX)) return ENGRAM_EINVAL;
-  const int64_t local = end - start;
-  const int64_t total = batch * local;
-  if (!mul_fits(total, H * 8, INT64_MAX)) return ENGRAM_EINVAL;
-  *hp = HashParams{};
-  for (int64_t h = 0; h < H; ++h) {
-    const int64_t p = h_primes[h], off = h_offsets[h];
-    if (p <= 0 || off < 0 || off > table_rows - p) return ENGRAM_EINVAL;
-    hp->prime[h] = (uint64_t)p;
-    hp->magic[h] = UINT64_MAX / (uint64_t)p;
-    hp->offset[h] = off;
-  }
-  for (int k = 0; k < ngram_size; ++k) hp->mult[k] = (uint64_t)h_multipliers[k];
-  *tokens_out = total;
-  if (total > 0 && d_tokens == nullptr) return ENGRAM_EINVAL;
-  hp->tokens = d_tokens;
-  hp->seg = d_seq_ids;
-  hp->stride = stride;
-  hp->start = start;
-  hp->local = local;
-  hp->eos = eos_id;
-  hp->n = ngram_size;
-  hp->J = heads_per_ngram;
-  hp->H = (int32_t)H;
-  return ENGRAM_OK;
-}
-
-}  // namespace engram
-
-using namespace engram;
-
-extern "C" int engram_hash(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
-                           int64_t seq, int32_t ngram_size, int32_t heads_per_ngram,
-                           int64_t eos_id, const int64_t *h_multipliers,
-                           const int64_t *h_primes, const int64_t *h_offsets,
-                           int64_t table_rows, int64_t *d_row_ids, void *stream) {
-  if (seq < 0) return ENGRAM_EINVAL;
-  return hash_window(d_tokens, d_seq_ids, batch, seq, 0, seq, ngram_size, heads_per_ngram,
-                     eos_id, h_multipliers, h_primes, h_offsets, table_rows, d_row_ids, stream);
-}
-
-extern "C" int engram_hash_slice(const int64_t *d_tokens, const int64_t *d_seq_ids,
-                                 int64_t batch, int64_t global_seq, int64_t seq_start,
-                                 int64_t seq_end, int32_t ngram_size, int32_t heads_per_ngram,
-                                 int64_t eos_id, const int64_t *h_multipliers,
-                                 const int64_t *h_primes, const int64_t *h_offsets,
-                                 int64_t table_rows, int64_t *d_row_ids, void *stream) {
-  return hash_window(d_tokens, d_seq_ids, batch, global_seq, seq_start, seq_end, ngram_size,
-                     heads_per_ngram, eos_id, h_multipliers, h_primes, h_offsets, table_rows,
-                     d_row_ids, stream);
 }

@@ -19,32 +19,6 @@ namespace engram {
 
 constexpr int64_t kHashFill = 0;  // history token read where none is valid
 
-// Everything the hash needs, passed by value as kernel arguments (about 1.6 KB).
-struct HashParams {
-  const int64_t *tokens;  // [batch, stride]
-  const int64_t *seg;     // [batch, stride] packed segment ids, or null
-  int64_t stride;         // positions per row of tokens / seg
-  int64_t start;          // first hashed position of every row
-  int64_t local;          // hashed positions per row
-  int64_t eos;
-  int32_t n;  // ngram_size
-  int32_t J;  // heads_per_ngram
-  int32_t H;  // (n - 1) * J
-  int32_t pad;
-  uint64_t mult[ENGRAM_MAX_NGRAM];
-  uint64_t prime[ENGRAM_MAX_HEADS];
-  uint64_t magic[ENGRAM_MAX_HEADS];  // floor((2^64 - 1) / prime)
-  int64_t offset[ENGRAM_MAX_HEADS];
-};
-
-// Host side (engram_hash.hip): checks the arguments every hashing entry point
-// shares and fills *hp; *tokens_out receives batch * (end - start).
-int make_hash_params(const int64_t *d_tokens, const int64_t *d_seq_ids, int64_t batch,
-                     int64_t stride, int64_t start, int64_t end, int32_t ngram_size,
-                     int32_t heads_per_ngram, int64_t eos_id, const int64_t *h_multipliers,
-                     const int64_t *h_primes, const int64_t *h_offsets, int64_t table_rows,
-                     HashParams *hp, int64_t *tokens_out);
-
 // Floor remainder of a signed 64-bit x by p in [1, 2^63): Barrett reduction
 // of |x| with magic = floor((2^64-1)/p).  The estimate q = hi64(|x| * magic)
 // is floor(|x|/p) or one less, so one conditional subtraction finishes it.

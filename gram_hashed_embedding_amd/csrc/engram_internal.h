@@ -1,11 +1,11 @@
-// engram_internal.h -- helpers shared by the HIP translation units of
+// engram_internal.h -- device helpers shared by the HIP translation units of
 // libengram.so.  Not part of the public ABI (that is include/engram.h).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "engram.h"
+#include "engram_host.h"
 
 namespace engram {
 
@@ -17,22 +17,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));  // four bf16 values
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
-inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
 inline hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Status of the launches just enqueued on this thread.
 inline int launch_status() {
   return hipGetLastError() == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP;
-}
-
-// Widest row any entry point takes (2^30 values); keeps every byte count of
-// a row far from overflow.
-constexpr int64_t kMaxDim = int64_t(1) << 30;
-
-// a * b <= limit for non-negative a, b, without overflow.
-inline bool mul_fits(int64_t a, int64_t b, int64_t limit) {
-  return a == 0 || b <= limit / a;
 }
 
 // bf16 element e (0..7) of a 16-byte chunk, widened exactly to fp32.

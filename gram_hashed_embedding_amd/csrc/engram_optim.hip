@@ -76,23 +76,11 @@ __global__ __launch_bounds__(kOptThreads) void signsgd_rowsparse_kernel(
 }  // namespace
 }  // namespace engram
 
-using namespace engram;
-
-extern "C" int engram_signsgd_rowsparse(const int64_t *d_unique_ids, const float *d_unique_grads,
-                                        const int64_t *d_num_unique, int64_t capacity,
-                                        int64_t head_dim, void *d_table, int64_t table_rows,
-                                        float lr, int64_t *d_err_count, void *stream) {
-  if (capacity < 0 || table_rows < 0 || head_dim <= 0 || head_dim % 8 != 0 || head_dim > kMaxDim)
-    return ENGRAM_EINVAL;
+int engram::launch_signsgd(const int64_t *d_unique_ids, const float *d_unique_grads,
+                           const int64_t *d_num_unique, int64_t capacity, int64_t head_dim,
+                           void *d_table, int64_t table_rows, float lr, int64_t *d_err_count,
+                           void *stream) {
   const int64_t cpr = head_dim / 8;
-  if (!mul_fits(capacity, head_dim * 4, INT64_MAX / 2) ||
-      !mul_fits(table_rows, head_dim * 2, INT64_MAX))
-    return ENGRAM_EINVAL;
-  if (capacity == 0) return ENGRAM_OK;
-  if (d_unique_ids == nullptr || d_unique_grads == nullptr || d_num_unique == nullptr ||
-      d_table == nullptr)
-    return ENGRAM_EINVAL;
-  if (!aligned16(d_unique_grads) || !aligned16(d_table)) return ENGRAM_EALIGN;
   const int64_t per_block = (int64_t)kOptThreads * kOptUnroll;
   const int64_t blocks = (capacity * cpr + per_block - 1) / per_block;
   if (blocks > INT32_MAX) return ENGRAM_EINVAL;

@@ -17,93 +17,20 @@ from pathlib import Path
 
 import torch
 
+from . import abi
+from .abi import (ENGRAM_EALIGN, ENGRAM_EHIP, ENGRAM_EINVAL, ENGRAM_EWORKSPACE,  # noqa: F401
+                  ENGRAM_OK, ERR_NO_PLAN, ERR_STALLED, MAX_HEADS, MAX_NGRAM,
+                  NOALLOC_SCRATCH_BYTES, SCATTER_ATOMIC, SCATTER_ROWSPARSE, SCATTER_SORTED)
+
 _PKG = Path(__file__).resolve().parent
 LIBRARY = _PKG / "libengram.so"
 HEADER = _PKG.parent / "include" / "engram.h"
-
-ENGRAM_OK = 0
-ENGRAM_EINVAL = -1
-ENGRAM_EALIGN = -2
-ENGRAM_EWORKSPACE = -3
-ENGRAM_EHIP = -4
-SCATTER_SORTED = 0
-SCATTER_ATOMIC = 1
-SCATTER_ROWSPARSE = 2
-MAX_NGRAM = 8
-MAX_HEADS = 64
-NOALLOC_SCRATCH_BYTES = 32 << 20  # ENGRAM_NOALLOC_SCRATCH_BYTES
 
 if not LIBRARY.exists():
     raise ImportError(f"{LIBRARY} is missing: build it with "
                       "`python -m gram_hashed_embedding_amd.build` (hipcc, gfx950)")
 
-_lib = ctypes.CDLL(str(LIBRARY))
-_i64p = ctypes.POINTER(ctypes.c_int64)
-_vp = ctypes.c_void_p
-
-_lib.engram_status_string.restype = ctypes.c_char_p
-_lib.engram_status_string.argtypes = [ctypes.c_int]
-_lib.engram_abi_version.restype = ctypes.c_int
-_lib.engram_abi_version.argtypes = []
-_lib.engram_hash.restype = ctypes.c_int
-_lib.engram_hash.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
-                             ctypes.c_int32, ctypes.c_int64, _i64p, _i64p, _i64p,
-                             ctypes.c_int64, _vp, _vp]
-_lib.engram_hash_slice.restype = ctypes.c_int
-_lib.engram_hash_slice.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                   ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                   ctypes.c_int64, _i64p, _i64p, _i64p, ctypes.c_int64, _vp,
-                                   _vp]
-_lib.engram_lookup.restype = ctypes.c_int
-_lib.engram_lookup.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
-                               ctypes.c_int32, ctypes.c_int64, _i64p, _i64p, _i64p, _vp,
-                               ctypes.c_int64, ctypes.c_int64, _vp, _vp, _vp]
-_lib.engram_lookup_slice.restype = ctypes.c_int
-_lib.engram_lookup_slice.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                     ctypes.c_int64, _i64p, _i64p, _i64p, _vp, ctypes.c_int64,
-                                     ctypes.c_int64, _vp, _vp, _vp]
-_lib.engram_scatter_plan_tokens.restype = ctypes.c_int
-_lib.engram_scatter_plan_tokens.argtypes = [_vp, _vp, ctypes.c_int64, ctypes.c_int64,
-                                            ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
-                                            _i64p, _i64p, _i64p, ctypes.c_int64,
-                                            ctypes.c_int64, _vp, ctypes.c_size_t, _vp]
-_lib.engram_gather.restype = ctypes.c_int
-_lib.engram_gather.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
-                               _vp, _vp]
-_lib.engram_scatter_add_workspace.restype = ctypes.c_size_t
-_lib.engram_scatter_add_workspace.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
-                                              ctypes.c_int32]
-_lib.engram_scatter_add.restype = ctypes.c_int
-_lib.engram_scatter_add.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64, _vp,
-                                    ctypes.c_int64, ctypes.c_int32, _vp, ctypes.c_size_t, _vp,
-                                    _vp]
-_lib.engram_scatter_add_rowsparse.restype = ctypes.c_int
-_lib.engram_scatter_add_rowsparse.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
-                                              ctypes.c_int64, _vp, _vp, _vp, _vp,
-                                              ctypes.c_size_t, _vp, _vp]
-
-_lib.engram_scatter_add_rowsparse_noalloc.restype = ctypes.c_int
-_lib.engram_scatter_add_rowsparse_noalloc.argtypes = [_vp, ctypes.c_int64, _vp, ctypes.c_int64,
-                                                      ctypes.c_int64, _vp, _vp, _vp, _vp, _vp]
-
-_lib.engram_scatter_plan.restype = ctypes.c_int
-_lib.engram_scatter_plan.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
-                                     ctypes.c_size_t, _vp, _vp]
-_lib.engram_scatter_apply.restype = ctypes.c_int
-_lib.engram_scatter_apply.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _vp,
-                                      _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-_lib.engram_signsgd_rowsparse.restype = ctypes.c_int
-_lib.engram_signsgd_rowsparse.argtypes = [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64, _vp,
-                                          ctypes.c_int64, ctypes.c_float, _vp, _vp]
-_lib.engram_scatter_apply_signsgd.restype = ctypes.c_int
-_lib.engram_scatter_apply_signsgd.argtypes = [_vp, ctypes.c_int64, ctypes.c_int64,
-                                              ctypes.c_int64, _vp, ctypes.c_float, _vp,
-                                              ctypes.c_size_t, _vp]
-_lib.engram_ple_conv.restype = ctypes.c_int
-_lib.engram_ple_conv.argtypes = [_vp, _vp, ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64,
-                                 ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
-                                 _vp, _vp]
+_lib = abi.declare(ctypes.CDLL(str(LIBRARY)))
 
 
 class EngramError(RuntimeError):
@@ -400,10 +327,13 @@ def engram_scatter_plan(row_ids, table_rows, head_dim, workspace=None, err_count
 
 
 def engram_scatter_apply(grads, workspace, table_rows, grad_table=None, unique_ids=None,
-                         unique_grads=None, num_unique=None, stream=None):
+                         unique_grads=None, num_unique=None, err_count=None, stream=None):
     """Sums of `grads` (bf16 [n, head_dim]) per the plan in `workspace`: into
     grad_table (dense, in place) when given, else row-sparse (allocated when
-    not given); returns grad_table or (unique_ids, unique_grads, num_unique)."""
+    not given); returns grad_table or (unique_ids, unique_grads, num_unique).
+    err_count (int64 [1] on the device) receives ERR_NO_PLAN when the
+    workspace holds no complete plan of these sizes, ERR_STALLED for a plan
+    whose wait expired (nothing is written then)."""
     _device_tensor(grads, torch.bfloat16, "grads")
     _device_tensor(workspace, torch.uint8, "workspace")
     dim = grads.shape[-1]
@@ -425,11 +355,14 @@ def engram_scatter_apply(grads, workspace, table_rows, grad_table=None, unique_i
         _device_tensor(num_unique, torch.int64, "num_unique")
         if unique_ids.numel() < n or unique_grads.numel() < n * dim:
             raise ValueError("unique_ids / unique_grads must hold n entries")
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
     with _on(dev):
         status = _lib.engram_scatter_apply(_ptr(grads), n, dim, int(table_rows),
                                            _ptr(grad_table), _ptr(unique_ids),
                                            _ptr(unique_grads), _ptr(num_unique), _ptr(workspace),
-                                           workspace.numel(), _stream(dev, stream))
+                                           workspace.numel(), _ptr(err_count),
+                                           _stream(dev, stream))
     _check(status, "engram_scatter_apply")
     if grad_table is not None:
         return grad_table
@@ -461,7 +394,7 @@ def engram_signsgd_rowsparse(unique_ids, unique_grads, num_unique, table, lr, er
     return table
 
 
-def engram_scatter_apply_signsgd(grads, workspace, table, lr, stream=None):
+def engram_scatter_apply_signsgd(grads, workspace, table, lr, err_count=None, stream=None):
     """The planned backward of bf16 grads [n, head_dim] fused with one
     SignSGD step on the bf16 table (in place)."""
     _device_tensor(grads, torch.bfloat16, "grads")
@@ -471,10 +404,12 @@ def engram_scatter_apply_signsgd(grads, workspace, table, lr, stream=None):
     n = grads.numel() // dim
     if grads.numel() != n * dim:
         raise ValueError("grads must be [n, head_dim] with the table's head_dim")
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
     with _on(table.device):
         status = _lib.engram_scatter_apply_signsgd(_ptr(grads), n, dim, rows, _ptr(table),
                                                    float(lr), _ptr(workspace),
-                                                   workspace.numel(),
+                                                   workspace.numel(), _ptr(err_count),
                                                    _stream(table.device, stream))
     _check(status, "engram_scatter_apply_signsgd")
     return table
@@ -601,20 +536,23 @@ def engram_lookup_slice(tokens, seq_start, seq_end, table, ngram_size, heads_per
 
 def engram_scatter_plan_tokens(tokens, table_rows, head_dim, ngram_size, heads_per_ngram, eos_id,
                                multipliers, primes, offsets, seq_ids=None, workspace=None,
-                               stream=None):
+                               err_count=None, stream=None):
     """The backward's plan for the hashed ids of tokens, made from the tokens;
-    returns the workspace (allocated when not given)."""
+    returns the workspace (allocated when not given).  err_count (int64 [1]
+    on the device) receives ERR_STALLED should a bounded wait expire."""
     heads, mult, pr, off = _hash_args(tokens, ngram_size, heads_per_ngram, multipliers, primes,
                                       offsets, seq_ids)
     batch, seq = tokens.shape
     n = batch * seq * heads
     ws = _workspace(workspace, n, table_rows, head_dim, SCATTER_ROWSPARSE, tokens.device)
+    if err_count is not None:
+        _device_tensor(err_count, torch.int64, "err_count")
     with _on(tokens.device):
         status = _lib.engram_scatter_plan_tokens(_ptr(tokens), _ptr(seq_ids), batch, seq,
                                                  int(ngram_size), int(heads_per_ngram),
                                                  int(eos_id), mult, pr, off, int(table_rows),
                                                  int(head_dim), _ptr(ws), ws.numel(),
-                                                 _stream(tokens.device, stream))
+                                                 _ptr(err_count), _stream(tokens.device, stream))
     _check(status, "engram_scatter_plan_tokens")
     return ws
 

@@ -39,8 +39,8 @@
  * - The sorted scatter's kernels wait on one another's published counts
  *   with bounded waits.  Blocks take their tiles in launch order (an atomic
  *   ticket), so every wait is for a block already running and ends; should
- *   one ever expire, the call adds 2^40 to *d_err_count (when not NULL)
- *   instead of hanging, and its results are not valid.
+ *   one ever expire, the call adds ENGRAM_ERR_STALLED (2^40) to *d_err_count
+ *   (when not NULL) instead of hanging, and its results are not valid.
  * - Layouts are row-major and contiguous.  bf16 data is passed as void*.
  * - head_dim, wherever it is taken, is at most 2^30 (the sorted scatter and
  *   its plan: at most 2048); larger values are EINVAL.
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 1
+#define ENGRAM_ABI_VERSION 2
 
 #define ENGRAM_OK 0
 #define ENGRAM_EINVAL (-1)
@@ -71,6 +71,12 @@ extern "C" {
 #define ENGRAM_SCATTER_SORTED 0    /* deterministic: sort + segmented sum    */
 #define ENGRAM_SCATTER_ATOMIC 1    /* fp32 atomic adds (order not fixed)     */
 #define ENGRAM_SCATTER_ROWSPARSE 2 /* workspace query of the row-sparse call */
+
+/* Added to *d_err_count by the sorted scatter: a bounded wait of the plan
+ * expired (its results are not valid), or an apply found no complete plan of
+ * its n and table_rows in the workspace (it then wrote nothing; U = 0). */
+#define ENGRAM_ERR_STALLED ((int64_t)1 << 40)
+#define ENGRAM_ERR_NO_PLAN ((int64_t)1 << 41)
 
 /* Bytes of the fixed device array engram_scatter_add_rowsparse_noalloc uses. */
 #define ENGRAM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
@@ -227,7 +233,13 @@ size_t engram_scatter_add_workspace(int64_t n, int64_t table_rows,
  * aggregation per row) and [PR1] Validation (FP32 reduction defaults).
  *   mode ENGRAM_SCATTER_SORTED: S_r is summed in fp64, rounded once to fp32,
  *     then added with one fp32 add; deterministic run to run.  Needs the
- *     workspace and table_rows < 2^32 - 1, n < 2^32.
+ *     workspace and table_rows < 2^32 - 1, n < 2^32.  The fp64 sum is exact,
+ *     and S_r then the same as a sum in any other order, as long as the bits
+ *     of a row's terms and partial sums span at most 53 places (bf16 terms
+ *     within a factor of about 2^45 of each other, e.g. every N(0, 1)
+ *     gradient); past that the kernels' addition order (a fixed tree, not
+ *     ascending flat index) can round differently, in the last bits of an
+ *     fp64 sum that is then rounded to fp32.
  *   mode ENGRAM_SCATTER_ATOMIC: every gradient element is added to the
  *     table with an fp32 atomic add; the order of additions is not fixed.
  *     Needs no workspace.
@@ -279,9 +291,16 @@ int engram_scatter_add_rowsparse(const int64_t *d_row_ids, int64_t n,
  *     the plan (made by either plan call), with the plan's work ordered
  *     before it (same stream, or an event).  Exactly one output form:
  *     d_grad_table (dense, accumulated), or all of d_unique_ids /
- *     d_unique_grads / d_num_unique (row-sparse).  The
- *     apply does not change the plan; it may run again on the same plan.  A
- *     workspace that holds no plan of these ids gives undefined results.
+ *     d_unique_grads / d_num_unique (row-sparse).  The apply does not change
+ *     the plan; it may run again on the same plan.
+ *   The plan stamps the workspace with its n and table_rows when it
+ *   completes, and marks it when a bounded wait expired.  The apply first
+ *   checks both on the device: for a workspace that holds no complete plan of
+ *   its n and table_rows it writes nothing (a row-sparse apply writes U = 0)
+ *   and adds ENGRAM_ERR_NO_PLAN to *d_err_count; for a plan whose wait
+ *   expired, ENGRAM_ERR_STALLED.  A complete plan of other ids of the same
+ *   sizes cannot be told apart and gives those ids' sums.  Whatever the
+ *   workspace holds, the apply reads and writes only inside its buffers.
  * Errors: EINVAL (sizes, output form), EALIGN, EWORKSPACE.  n == 0: the plan
  * enqueues nothing; a row-sparse apply writes U = 0.
  */
@@ -297,8 +316,9 @@ int engram_scatter_plan(const int64_t *d_row_ids, int64_t n, int64_t table_rows,
  * engram_scatter_plan (table_rows, head_dim, the workspace of n ids).
  * Lets the backward's plan start from the tokens alone, beside a forward
  * done with engram_lookup.  Errors: those of both calls.  Hashed rows are
- * always inside the table, so there is no error counter (nor a place to
- * report an expired wait).
+ * always inside the table, so *d_err_count (when not NULL) only ever receives
+ * ENGRAM_ERR_STALLED, should a bounded wait expire; the workspace is then
+ * marked, and an apply of it writes nothing.
  */
 int engram_scatter_plan_tokens(const int64_t *d_tokens, const int64_t *d_seq_ids,
                                int64_t batch, int64_t seq, int32_t ngram_size,
@@ -306,12 +326,12 @@ int engram_scatter_plan_tokens(const int64_t *d_tokens, const int64_t *d_seq_ids
                                const int64_t *h_multipliers, const int64_t *h_primes,
                                const int64_t *h_offsets, int64_t table_rows,
                                int64_t head_dim, void *d_workspace, size_t workspace_bytes,
-                               void *stream);
+                               int64_t *d_err_count, void *stream);
 
 int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
                          int64_t table_rows, float *d_grad_table, int64_t *d_unique_ids,
                          float *d_unique_grads, int64_t *d_num_unique, void *d_workspace,
-                         size_t workspace_bytes, void *stream);
+                         size_t workspace_bytes, int64_t *d_err_count, void *stream);
 
 /*
  * engram_scatter_add_rowsparse_noalloc -- engram_scatter_add_rowsparse
@@ -377,13 +397,15 @@ int engram_signsgd_rowsparse(const int64_t *d_unique_ids, const float *d_unique_
  *   d_grads bf16 [n, head_dim]; d_table bf16 [table_rows, head_dim], updated
  *   in place; lr the learning rate; the workspace holds a plan of the n ids
  *   made by engram_scatter_plan or engram_scatter_plan_tokens (same n,
- *   head_dim and table_rows), ordered before this call.  d_grads and d_table
- *   16-byte aligned.
+ *   head_dim and table_rows), ordered before this call, checked on the
+ *   device as by engram_scatter_apply (d_err_count likewise).  d_grads and
+ *   d_table 16-byte aligned.
  * Errors: EINVAL, EALIGN, EWORKSPACE.  n == 0 enqueues nothing.
  */
 int engram_scatter_apply_signsgd(const void *d_grads, int64_t n, int64_t head_dim,
                                  int64_t table_rows, void *d_table, float lr,
-                                 void *d_workspace, size_t workspace_bytes, void *stream);
+                                 void *d_workspace, size_t workspace_bytes,
+                                 int64_t *d_err_count, void *stream);
 
 /*
  * engram_ple_conv -- the PLE causal dilated depthwise convolution with zero

@@ -102,11 +102,13 @@ def test_e2e_forward_backward(oracle):
     uid, uval, count = E.engram_scatter_add_rowsparse(rows.view(-1), grads, wl.table_rows,
                                                       err_count=err)
     # the plan the benchmark times (from the tokens) gives the same output
+    perr = torch.zeros(1, dtype=torch.int64, device="cuda")
     ws_t = E.engram_scatter_plan_tokens(dev(tok), wl.table_rows, wl.dim, wl.ngram_size,
                                         wl.heads_per_ngram, wl.eos_id, mult, wl.primes,
-                                        wl.offsets)
-    uid_t, uval_t, count_t = E.engram_scatter_apply(grads, ws_t, wl.table_rows)
+                                        wl.offsets, err_count=perr)
+    uid_t, uval_t, count_t = E.engram_scatter_apply(grads, ws_t, wl.table_rows, err_count=perr)
     torch.cuda.synchronize()
+    assert int(perr.item()) == 0
     ut = int(count_t.item())
     assert ut == int(count.item())
     assert torch.equal(uid_t[:ut], uid[:ut])

@@ -11,6 +11,33 @@ from tests.gpu_helpers import bits, dev, host_f32, needs_gpu, release
 pytestmark = needs_gpu
 E = pytest.importorskip("gram_hashed_embedding_amd.engram")
 
+# Every token plan and every apply of this file reports into an error
+# counter, and each test ends by checking that none was bumped (no wait of a
+# plan expired, and every apply found a complete plan of its sizes).
+_COUNTERS = []
+
+
+def plan_tokens(*args, **kwargs):
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _COUNTERS.append(err)
+    return E.engram_scatter_plan_tokens(*args, err_count=err, **kwargs)
+
+
+def apply(*args, **kwargs):
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _COUNTERS.append(err)
+    return E.engram_scatter_apply(*args, err_count=err, **kwargs)
+
+
+@pytest.fixture(autouse=True)
+def no_plan_errors():
+    _COUNTERS.clear()
+    yield
+    torch.cuda.synchronize()
+    bumped = [int(c.item()) for c in _COUNTERS if int(c.item()) != 0]
+    _COUNTERS.clear()
+    assert not bumped, f"error counters bumped: {bumped}"
+
 
 def hash_args(wl, mult):
     return (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
@@ -74,11 +101,11 @@ def test_token_plan_matches_id_plan_and_oracle(oracle, name, segments):
     sd = None if seg is None else dev(seg)
     R = tok.size * len(wl.primes)
     grads = workloads.make_grads(R, wl.dim, wl.seed + 9, "cuda")
-    ws_t = E.engram_scatter_plan_tokens(dev(tok), wl.table_rows, wl.dim, *args, seq_ids=sd)
-    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, wl.table_rows)
+    ws_t = plan_tokens(dev(tok), wl.table_rows, wl.dim, *args, seq_ids=sd)
+    uid_t, val_t, cnt_t = apply(grads, ws_t, wl.table_rows)
     ids = E.engram_hash(dev(tok), *args, wl.table_rows, seq_ids=sd)
     ws_i = E.engram_scatter_plan(ids.view(-1), wl.table_rows, wl.dim)
-    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, wl.table_rows)
+    uid_i, val_i, cnt_i = apply(grads, ws_i, wl.table_rows)
     torch.cuda.synchronize()
     u = int(cnt_t.item())
     assert u == int(cnt_i.item())
@@ -113,11 +140,11 @@ def test_token_plan_every_order(n, J):
     R = tok.size * H
     dim = 16
     grads = workloads.make_grads(R, dim, n + J, "cuda")
-    ws_t = E.engram_scatter_plan_tokens(dev(tok), rows, dim, *args, seq_ids=dev(seg))
-    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, rows)
+    ws_t = plan_tokens(dev(tok), rows, dim, *args, seq_ids=dev(seg))
+    uid_t, val_t, cnt_t = apply(grads, ws_t, rows)
     ids = E.engram_hash(dev(tok), *args, rows, seq_ids=dev(seg))
     ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
-    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, rows)
+    uid_i, val_i, cnt_i = apply(grads, ws_i, rows)
     torch.cuda.synchronize()
     u = int(cnt_t.item())
     assert u == int(cnt_i.item()) and u > 0
@@ -163,11 +190,11 @@ def test_token_plan_head_layouts(layout):
     R = tok.size * H
     dim = 8
     grads = workloads.make_grads(R, dim, 17, "cuda")
-    ws_t = E.engram_scatter_plan_tokens(dev(tok), rows, dim, *args, seq_ids=dev(seg))
-    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, rows)
+    ws_t = plan_tokens(dev(tok), rows, dim, *args, seq_ids=dev(seg))
+    uid_t, val_t, cnt_t = apply(grads, ws_t, rows)
     ids = E.engram_hash(dev(tok), *args, rows, seq_ids=dev(seg))
     ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
-    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, rows)
+    uid_i, val_i, cnt_i = apply(grads, ws_i, rows)
     torch.cuda.synchronize()
     u = int(cnt_t.item())
     assert u == int(cnt_i.item()) and u > 0
@@ -203,7 +230,7 @@ def test_plans_made_ahead_in_two_workspaces(overlap):
 
     def plan(k):
         side.wait_event(ev_apply[k % 2])
-        E.engram_scatter_plan_tokens(toks[k % 3], rows, D, *args, workspace=wss[k % 2],
+        plan_tokens(toks[k % 3], rows, D, *args, workspace=wss[k % 2],
                                      stream=side)
         ev_plan[k % 2].record(side)
 
@@ -213,12 +240,12 @@ def test_plans_made_ahead_in_two_workspaces(overlap):
         plan(k + 1)
         E.engram_lookup(toks[k % 3], table, *args, out=out)
         main.wait_event(ev_plan[k % 2])
-        got.append(E.engram_scatter_apply(grads, wss[k % 2], rows))
+        got.append(apply(grads, wss[k % 2], rows))
         ev_apply[k % 2].record(main)
     main.wait_stream(side)
     for k, (uid, val, cnt) in enumerate(got):
-        ws = E.engram_scatter_plan_tokens(toks[k % 3], rows, D, *args)
-        uid_r, val_r, cnt_r = E.engram_scatter_apply(grads, ws, rows)
+        ws = plan_tokens(toks[k % 3], rows, D, *args)
+        uid_r, val_r, cnt_r = apply(grads, ws, rows)
         torch.cuda.synchronize()
         u = int(cnt_r.item())
         assert int(cnt.item()) == u and u > 0
@@ -263,11 +290,11 @@ def test_token_plan_random_sweep(seed):
     R = tok.size * H
     dim = 8
     grads = workloads.make_grads(R, dim, 50 + seed, "cuda")
-    ws_t = E.engram_scatter_plan_tokens(dev(tok), rows, dim, *args, seq_ids=sd)
-    uid_t, val_t, cnt_t = E.engram_scatter_apply(grads, ws_t, rows)
+    ws_t = plan_tokens(dev(tok), rows, dim, *args, seq_ids=sd)
+    uid_t, val_t, cnt_t = apply(grads, ws_t, rows)
     ids = E.engram_hash(dev(tok), *args, rows, seq_ids=sd)
     ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
-    uid_i, val_i, cnt_i = E.engram_scatter_apply(grads, ws_i, rows)
+    uid_i, val_i, cnt_i = apply(grads, ws_i, rows)
     torch.cuda.synchronize()
     u = int(cnt_t.item())
     assert u == int(cnt_i.item()) and u > 0
