@@ -1,9 +1,12 @@
-"""The oracle under UBSan: int64 wraparound must be done without undefined
-signed overflow (the page's hash relies on wrapping).  The sanitized build
-runs in a child process, which aborts on the first undefined operation."""
+"""The oracle under UBSan and under ASan: int64 wraparound must be done
+without undefined signed overflow (the page's hash relies on wrapping), and
+no function may read or write outside its arrays.  Each sanitized build runs
+in a child process, which aborts on the first report."""
 import os
 import subprocess
 import sys
+
+import pytest
 
 from oracle import build
 from oracle.engram_oracle import SOURCE
@@ -27,13 +30,24 @@ print("sanitized-ok")
 """
 
 
-def _run_sanitized(tmp_path, flags, name):
+def _run_sanitized(tmp_path, flags, name, env=None):
     lib = build(SOURCE, tmp_path / name, extra_flags=flags)
     res = subprocess.run([sys.executable, "-c", CHILD.format(root=ROOT, lib=str(lib))],
-                         capture_output=True, text=True, timeout=600)
+                         capture_output=True, text=True, timeout=600,
+                         env=None if env is None else dict(os.environ, **env))
     assert res.returncode == 0 and "sanitized-ok" in res.stdout, res.stderr[-2000:]
 
 
 def test_oracle_under_ubsan(tmp_path):
     _run_sanitized(tmp_path, ("-O1", "-fsanitize=undefined", "-fno-sanitize-recover=all"),
                    "liboracle_ubsan.so")
+
+
+def test_oracle_under_asan(tmp_path):
+    asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], capture_output=True,
+                          text=True).stdout.strip()
+    if not (os.path.isabs(asan) and os.path.exists(asan)):
+        pytest.skip("gcc has no AddressSanitizer runtime here")
+    _run_sanitized(tmp_path, ("-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address"),
+                   "liboracle_asan.so",
+                   env={"LD_PRELOAD": asan, "ASAN_OPTIONS": "detect_leaks=0:abort_on_error=1"})
