@@ -39,10 +39,46 @@
  * fix the combining operation or the fill value, and no checkpoint is here.
  *
  * Build: gcc -O2 -std=c11 -shared -fPIC engram_oracle.c -o libengram_oracle.so
+ * The same source built with -fopenmp (the benchmark's all-core CPU
+ * baseline) spreads the independent work over threads: tokens of the hash,
+ * lookups of the gather, distinct rows of the scatter-add (each row still
+ * summed by one thread in ascending flat index, so every result is the same
+ * bit for bit).  Without -fopenmp the pragmas are empty and it is serial.
  */
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#define ORACLE_FOR_ROWS _Pragma("omp parallel for schedule(dynamic, 1024)")
+#define ORACLE_FOR_COUNT _Pragma("omp parallel for schedule(static) reduction(+ : bad)")
+#define ORACLE_PARALLEL_FOR _Pragma("omp parallel for schedule(static)")
+#else
+#define ORACLE_FOR_ROWS
+#define ORACLE_FOR_COUNT
+#define ORACLE_PARALLEL_FOR
+#endif
+
+/* Threads the parallel loops use (1 in a serial build). */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* Index of the calling thread in [0, oracle_threads()). */
+static int oracle_thread(void)
+{
+#ifdef _OPENMP
+    return omp_get_thread_num();
+#else
+    return 0;
+#endif
+}
 
 #define ORACLE_FILL 0
 #define ORACLE_MAX_ORDER 8
@@ -130,26 +166,26 @@ int oracle_hash(const int64_t *tokens, const int64_t *seq_ids,
         if (primes[h] <= 0)
             return -1;
 
-    for (int64_t b = 0; b < batch; ++b) {
+    /* one (b, t) after another: position f = b * seq + t */
+    ORACLE_PARALLEL_FOR
+    for (int64_t f = 0; f < batch * seq; ++f) {
+        const int64_t b = f / seq, t = f % seq;
         const int64_t *tok = tokens + b * seq;
         const int64_t *seg = seq_ids ? seq_ids + b * seq : NULL;
-        for (int64_t t = 0; t < seq; ++t) {
-            /* window[k] = token k positions back (k = 0: current token) */
-            int64_t window[ORACLE_MAX_ORDER];
-            window[0] = tok[t];
-            for (int k = 1; k < ngram_size; ++k)
-                window[k] = earlier_token(tok, seg, t, k, eos_id);
+        /* window[k] = token k positions back (k = 0: current token) */
+        int64_t window[ORACLE_MAX_ORDER];
+        window[0] = tok[t];
+        for (int k = 1; k < ngram_size; ++k)
+            window[k] = earlier_token(tok, seg, t, k, eos_id);
 
-            for (int g = 2; g <= ngram_size; ++g) {
-                /* order-g mix: wrapping sum over k < g of window[k] * m[k] */
-                int64_t mix = 0;
-                for (int k = 0; k < g; ++k)
-                    mix = wrapping_add(mix, wrapping_mul(window[k], multipliers[k]));
-                for (int j = 0; j < heads_per_ngram; ++j) {
-                    const int64_t h = (int64_t)(g - 2) * heads_per_ngram + j;
-                    row_ids[(b * seq + t) * H + h] =
-                        offsets[h] + positive_remainder(mix, primes[h]);
-                }
+        for (int g = 2; g <= ngram_size; ++g) {
+            /* order-g mix: wrapping sum over k < g of window[k] * m[k] */
+            int64_t mix = 0;
+            for (int k = 0; k < g; ++k)
+                mix = wrapping_add(mix, wrapping_mul(window[k], multipliers[k]));
+            for (int j = 0; j < heads_per_ngram; ++j) {
+                const int64_t h = (int64_t)(g - 2) * heads_per_ngram + j;
+                row_ids[f * H + h] = offsets[h] + positive_remainder(mix, primes[h]);
             }
         }
     }
@@ -170,6 +206,7 @@ int64_t oracle_gather(const int64_t *row_ids, int64_t n, const uint16_t *table,
                       int64_t table_rows, int64_t dim, uint16_t *out)
 {
     int64_t bad = 0;
+    ORACLE_FOR_COUNT
     for (int64_t i = 0; i < n; ++i) {
         const int64_t r = row_ids[i];
         uint16_t *dst = out + i * dim;
@@ -246,6 +283,22 @@ static row_ref *sorted_refs(const int64_t *row_ids, int64_t n, int64_t table_row
     return refs;
 }
 
+/* Start of every group of equal rows in the sorted list refs[0, m), and
+ * m after the last: starts[0 .. *groups].  Caller frees the list. */
+static int64_t *group_starts(const row_ref *refs, int64_t m, int64_t *groups)
+{
+    int64_t *starts = (int64_t *)malloc((size_t)(m + 1) * sizeof(int64_t));
+    int64_t g = 0;
+    if (starts == NULL)
+        return NULL;
+    for (int64_t q = 0; q < m; ++q)
+        if (q == 0 || refs[q].row != refs[q - 1].row)
+            starts[g++] = q;
+    starts[g] = m;
+    *groups = g;
+    return starts;
+}
+
 /* Sum of one group refs[begin, end) (all the same row) into acc[dim]. */
 static void sum_group(const row_ref *refs, int64_t begin, int64_t end,
                       const uint16_t *grads, int64_t dim, double *acc)
@@ -266,30 +319,29 @@ int64_t oracle_scatter_add_dense(const int64_t *row_ids, int64_t n,
                                  const uint16_t *grads, int64_t dim,
                                  float *grad_table, int64_t table_rows)
 {
-    int64_t m = 0, bad = 0;
+    int64_t m = 0, bad = 0, groups = 0;
     row_ref *refs = sorted_refs(row_ids, n, table_rows, &m, &bad);
-    double *acc = (double *)malloc((size_t)(dim > 0 ? dim : 1) * sizeof(double));
-    if (refs == NULL || acc == NULL) {
-        free(refs);
-        free(acc);
-        return -1;
-    }
-    int64_t begin = 0;
-    while (begin < m) {
-        int64_t end = begin + 1;
-        while (end < m && refs[end].row == refs[begin].row)
-            ++end;
-        sum_group(refs, begin, end, grads, dim, acc);
-        float *dst = grad_table + refs[begin].row * dim;
-        for (int64_t e = 0; e < dim; ++e) {
-            const float s = (float)acc[e];
-            dst[e] = dst[e] + s;
+    int64_t *starts = refs ? group_starts(refs, m, &groups) : NULL;
+    /* one fp64 accumulator row per thread */
+    double *accs = (double *)malloc((size_t)oracle_threads() * (size_t)(dim > 0 ? dim : 1) *
+                                    sizeof(double));
+    const int failed = refs == NULL || starts == NULL || accs == NULL;
+    if (!failed) {
+        ORACLE_FOR_ROWS
+        for (int64_t g = 0; g < groups; ++g) {
+            double *acc = accs + (int64_t)oracle_thread() * dim;
+            sum_group(refs, starts[g], starts[g + 1], grads, dim, acc);
+            float *dst = grad_table + refs[starts[g]].row * dim;
+            for (int64_t e = 0; e < dim; ++e) {
+                const float s = (float)acc[e];
+                dst[e] = dst[e] + s;
+            }
         }
-        begin = end;
     }
-    free(acc);
+    free(accs);
+    free(starts);
     free(refs);
-    return bad;
+    return failed ? -1 : bad;
 }
 
 /* Row-sparse form: the unique rows in ascending order with their fp32 sums:
@@ -300,30 +352,29 @@ int64_t oracle_scatter_add_rowsparse(const int64_t *row_ids, int64_t n,
                                      int64_t table_rows, int64_t *unique_ids,
                                      float *unique_grads, int64_t *num_unique)
 {
-    int64_t m = 0, bad = 0;
+    int64_t m = 0, bad = 0, groups = 0;
     row_ref *refs = sorted_refs(row_ids, n, table_rows, &m, &bad);
-    double *acc = (double *)malloc((size_t)(dim > 0 ? dim : 1) * sizeof(double));
-    if (refs == NULL || acc == NULL) {
-        free(refs);
-        free(acc);
-        return -1;
+    int64_t *starts = refs ? group_starts(refs, m, &groups) : NULL;
+    /* one fp64 accumulator row per thread */
+    double *accs = (double *)malloc((size_t)oracle_threads() * (size_t)(dim > 0 ? dim : 1) *
+                                    sizeof(double));
+    const int failed = refs == NULL || starts == NULL || accs == NULL;
+    if (!failed) {
+        /* group u is the u-th distinct row in ascending order */
+        ORACLE_FOR_ROWS
+        for (int64_t u = 0; u < groups; ++u) {
+            double *acc = accs + (int64_t)oracle_thread() * dim;
+            sum_group(refs, starts[u], starts[u + 1], grads, dim, acc);
+            unique_ids[u] = refs[starts[u]].row;
+            for (int64_t e = 0; e < dim; ++e)
+                unique_grads[u * dim + e] = (float)acc[e];
+        }
+        *num_unique = groups;
     }
-    int64_t u = 0, begin = 0;
-    while (begin < m) {
-        int64_t end = begin + 1;
-        while (end < m && refs[end].row == refs[begin].row)
-            ++end;
-        sum_group(refs, begin, end, grads, dim, acc);
-        unique_ids[u] = refs[begin].row;
-        for (int64_t e = 0; e < dim; ++e)
-            unique_grads[u * dim + e] = (float)acc[e];
-        ++u;
-        begin = end;
-    }
-    *num_unique = u;
-    free(acc);
+    free(accs);
+    free(starts);
     free(refs);
-    return bad;
+    return failed ? -1 : bad;
 }
 
 /* ---------------------------------------------------------------------- */

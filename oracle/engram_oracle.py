@@ -20,6 +20,9 @@ import numpy as np
 _HERE = Path(__file__).resolve().parent
 SOURCE = _HERE / "engram_oracle.c"
 LIBRARY = _HERE / "libengram_oracle.so"
+# the same source built with -fopenmp: the all-core CPU baseline
+LIBRARY_OMP = _HERE / "libengram_oracle_omp.so"
+OMP_FLAGS = ("-fopenmp",)
 
 _i64p = ctypes.POINTER(ctypes.c_int64)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
@@ -41,9 +44,16 @@ def _ptr(arr, ctype):
 class Oracle:
     """One loaded copy of the oracle library."""
 
+    @property
+    def threads(self) -> int:
+        """Threads its parallel loops use (1 for the serial build)."""
+        return int(self._lib.oracle_threads())
+
     def __init__(self, library: Path | str = LIBRARY):
         self.path = str(library)
         lib = ctypes.CDLL(self.path)
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_threads.argtypes = []
         lib.oracle_hash.restype = ctypes.c_int
         lib.oracle_hash.argtypes = [_i64p, _i64p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int64,
@@ -121,12 +131,18 @@ class Oracle:
         return out, int(bad)
 
     # -- scatter-add ----------------------------------------------------------
-    def scatter_add_dense(self, row_ids, grad_bits, grad_table):
-        """Accumulate into a copy of grad_table float32 [rows, dim]; returns
-        (new table, invalid count)."""
+    def scatter_add_dense(self, row_ids, grad_bits, grad_table, inplace=False):
+        """Accumulate into a copy of grad_table float32 [rows, dim] (into
+        grad_table itself when inplace, which must then be a C-contiguous
+        float32 array); returns (new table, invalid count)."""
         ids = np.ascontiguousarray(row_ids, dtype=np.int64).reshape(-1)
         grads = np.ascontiguousarray(grad_bits, dtype=np.uint16).reshape(ids.size, -1)
-        table = np.array(grad_table, dtype=np.float32, copy=True, order="C")
+        if inplace:
+            if grad_table.dtype != np.float32 or not grad_table.flags.c_contiguous:
+                raise ValueError("an in-place table must be C-contiguous float32")
+            table = grad_table
+        else:
+            table = np.array(grad_table, dtype=np.float32, copy=True, order="C")
         rows, dim = table.shape
         if grads.shape[1] != dim:
             raise ValueError("grad width differs from table width")
@@ -196,6 +212,7 @@ class Oracle:
 
 
 _default = None
+_default_omp = None
 
 
 def default_oracle() -> Oracle:
@@ -208,3 +225,21 @@ def default_oracle() -> Oracle:
             build()
         _default = Oracle(LIBRARY)
     return _default
+
+
+def build_all() -> None:
+    """Both builds of the oracle: serial, and with OpenMP."""
+    build()
+    build(SOURCE, LIBRARY_OMP, OMP_FLAGS)
+
+
+def openmp_oracle() -> Oracle:
+    """The oracle built with OpenMP (its parallel loops on every thread
+    OMP_NUM_THREADS allows); built on first use like default_oracle."""
+    global _default_omp
+    if _default_omp is None:
+        if (not LIBRARY_OMP.exists()
+                or os.path.getmtime(LIBRARY_OMP) < os.path.getmtime(SOURCE)):
+            build(SOURCE, LIBRARY_OMP, OMP_FLAGS)
+        _default_omp = Oracle(LIBRARY_OMP)
+    return _default_omp
