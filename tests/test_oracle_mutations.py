@@ -43,8 +43,7 @@ MUTANTS = {
     "fp32_accumulation": ("acc[e] += (double)bf16_bits_to_float(g[e]);",
                           "acc[e] = (float)((float)acc[e] + bf16_bits_to_float(g[e]));"),
     "overwrite_not_add": ("dst[e] = dst[e] + s;", "dst[e] = s;"),
-    "no_grouping": ("while (end < m && refs[end].row == refs[begin].row)",
-                    "while (end < m && 0)"),
+    "no_grouping": ("if (q == 0 || refs[q].row != refs[q - 1].row)", "if (1)"),
     "sgd_ascent": ("const float updated = w - step;", "const float updated = w + step;"),
     "sgd_truncating_bf16": ("u += 0x7fffu + keep_odd;", "u += 0u * keep_odd;"),
     "sgd_ties_away": ("u += 0x7fffu + keep_odd;", "u += 0x8000u + 0u * keep_odd;"),
