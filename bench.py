@@ -4,31 +4,39 @@ One step = one pass of the whole path over one token batch:
     engram_lookup (forward: the row ids hashed from the tokens and their
        table rows gathered, in one kernel)
     -> engram_scatter_plan_tokens + engram_scatter_apply (backward: per-row
-       fp32 sums, row-sparse; the same work as hashing, then
-       engram_scatter_add_rowsparse)
+       fp32 sums; the same work as hashing, then the one-call scatter-add)
 The plan (sorting the row ids) needs only the tokens, so the next batch's
 plan runs on a second stream while the current step's forward and backward
 run (a training loop knows its next batch), into the other of two
 workspaces; the apply waits for the forward and for its batch's plan.  The
 timed region holds exactly one plan, forward and apply per step (it ends
 when the plan made during the last step is done too); untimed steps run
-before it for --settle seconds (0.25 by default), then the W warm-up
-steps.  A serial pass of the
-same calls gives the per-phase times, and the same step with separate calls
-(engram_hash, then engram_scatter_plan of the ids beside engram_gather, then
-the apply) is timed beside it.
-on the end-to-end workload: tokens [8, 8192] (Zipf(1.1) ids, EOS w.p.
-1/4096), ngram_size 4, 8 heads per order (24 heads), a 200M x 256 bf16 table
-(102.4 GB, resident in HBM), upstream gradients [8, 8192, 24, 256] bf16.
+before it for --settle seconds (0.25 by default), then the W warm-up steps.
+A serial pass of the same calls gives the per-phase times, and the same step
+with separate calls (engram_hash, then engram_scatter_plan of the ids beside
+engram_gather, then the apply) is timed beside it.
+
+The default run measures the end-to-end workload -- tokens [8, 8192]
+(Zipf(1.1) ids, EOS w.p. 1/4096), ngram_size 4, 8 heads per order (24
+heads), a 200M x 256 bf16 table (102.4 GB, resident in HBM), upstream
+gradients [8, 8192, 24, 256] bf16, row-sparse fp32 gradients -- and prints
+it as the JSON line, with the other configurations of the benchmark nested
+under "other_configs", each with its own roofline and CPU baseline:
+    medium    forward only: tokens [4, 4096] uniform, 16 heads, 16.8M x 64 table
+    full      forward only: tokens [1, 32768] packed documents, Zipf(1.1),
+              32 heads, the 200M x 256 table (the e2e run's, reused)
+    backward  forward + dense fp32 backward: tokens [4, 4096] Zipf(1.2), 16
+              heads, 16.8M x 64 table; also the one-call scatter-add, sorted
+              against fp32 atomics, on the same ids and gradients
 Eight distinct token batches are cycled so one step does not warm the next.
 All inputs are resident in HBM before timing starts.
 
-Prints ONE JSON line.  `value` is row lookups per second over the whole
-forward + backward step.  The roofline entry is for the step's dominant
-kernel, timed with HIP events on the stream it runs on.  The CPU baseline
-is the oracle on the host, timed on the same workload's lookups.
+`value` is row lookups per second over the whole step.  The roofline entry
+is for the step's dominant kernel, timed with HIP events on the stream it
+runs on.  The CPU baseline is the oracle on the host: one core, and the same
+source built with OpenMP on every thread the process may use.
 
-    python bench.py [--steps K] [--warmup W]
+    python bench.py [--steps K] [--warmup W] [--no-other-configs]
                     [--workload e2e|e2e_signsgd|full|medium|backward|cp_slice|ple_conv]
 
 --workload ple_conv times the PLE causal dilated depthwise convolution
@@ -51,6 +59,7 @@ timed beside it.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -65,6 +74,11 @@ METRIC = ("row lookups/s and achieved HBM GB/s (% of peak), "
           "fwd hash+gather and bwd scatter")
 PEAK_HBM_GBS = 8000.0
 N_BATCHES = 8
+# Bytes of the host copy of a table the CPU baseline gathers from: a table
+# larger than this (the 102.4 GB ones) is copied in part, its first rows, and
+# the baseline's row ids are folded modulo their count.
+HOST_TABLE_BYTES = 8 << 30
+CPU_BUDGET_S = 6.0  # per CPU leg: repeat within this, at most 5 runs, median
 
 
 def log(*a):
@@ -97,7 +111,9 @@ def algorithmic_bytes(wl, unique_rows, separate=False):
 # The sources whose code a kernel of the hot path is built from: the
 # kernel's own file and the device headers it includes.
 KERNEL_HEADERS = ("gram_hashed_embedding_amd/csrc/engram_internal.h",
-                  "gram_hashed_embedding_amd/csrc/engram_hash_dev.h")
+                  "gram_hashed_embedding_amd/csrc/engram_hash_dev.h",
+                  "gram_hashed_embedding_amd/csrc/engram_host.h",
+                  "gram_hashed_embedding_amd/csrc/engram_scatter_dev.h")
 
 
 def code_digest(paths):
@@ -115,271 +131,156 @@ def code_digest(paths):
 
 
 def measured_traffic(call, wl):
-    """HBM bytes per launch of `call` from the committed rocprofv3 counter
-    summary (profiles/hbm_traffic.json), or None when it was taken on another
-    workload or the kernel's code has changed since."""
+    """HBM bytes per launch of `call` on workload wl from the committed
+    rocprofv3 counter summary (profiles/hbm_traffic.json), or None when no
+    counters were taken on that workload or the kernel's code has changed
+    since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if wl.name != "e2e" or not os.path.exists(path):
+    if not os.path.exists(path):
         return None
-    rec = json.load(open(path))["kernels"]
-    parts = {"lookup": ["lookup"], "gather": ["gather"], "scatter_apply": ["reduce"]}.get(call)
-    if parts is None:
+    rec = json.load(open(path)).get("workloads", {}).get(wl.name)
+    key = {"lookup": "lookup", "gather": "gather", "scatter_apply": "apply"}.get(call)
+    if rec is None or key not in rec["kernels"]:
         return None
-    total = 0.0
-    for key in parts:
-        k = rec[key]
-        if code_digest([k["source"], *KERNEL_HEADERS]) != k.get("code_sha256"):
-            return None
-        total += k["fetch_bytes"] + k["write_bytes"]
-    return total
+    k = rec["kernels"][key]
+    if code_digest([k["source"], *KERNEL_HEADERS]) != k.get("code_sha256"):
+        return None
+    return k["fetch_bytes"] + k["write_bytes"]
 
 
-def cpu_baseline(wl, tokens_host, mult, table, grads, budget_s=12.0):
-    """The oracle (single-threaded C) on the host cores, on the e2e batch:
-    hash, gather from a compact host copy of the table rows the batch
-    touches, and the row-sparse scatter-add.  Repeated within a time budget;
-    the median rate is reported."""
-    import torch
-    from oracle import default_oracle
+# ------------------------------------------------------------ CPU baseline --
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    oracle = default_oracle()
-    rows0 = oracle.hash(tokens_host[0], wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult,
-                        wl.primes, wl.offsets).reshape(-1)
-    uniq, local = np.unique(rows0, return_inverse=True)
-    compact = table.index_select(0, torch.from_numpy(uniq).to(table.device))
-    compact_bits = compact.view(torch.int16).cpu().numpy().view(np.uint16)
-    grad_bits = grads.view(torch.int16).cpu().numpy().view(np.uint16)
-    local = local.astype(np.int64)
-    rates, start = [], time.perf_counter()
-    while len(rates) < 5 and (not rates or time.perf_counter() - start < budget_s):
+
+def timed_runs(fn, budget_s=CPU_BUDGET_S):
+    """Seconds per run of fn: repeated until the budget is spent (at least
+    once, at most 5 times); the median."""
+    times, start = [], time.perf_counter()
+    while len(times) < 5 and (not times or time.perf_counter() - start < budget_s):
         t0 = time.perf_counter()
-        oracle.hash(tokens_host[0], wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult,
-                    wl.primes, wl.offsets)
-        oracle.gather(local, compact_bits)
-        if wl.grads == "rowsparse":
-            oracle.scatter_add_rowsparse(local, grad_bits, wl.dim, uniq.size)
-        rates.append(wl.lookups / (time.perf_counter() - t0))
-    return {"value": float(np.median(rates)), "unit": "lookups/s", "cores": 1,
-            "kind": "oracle",
-            "sample": (f"the full {wl.name} batch ({wl.lookups} lookups), "
-                       f"{len(rates)} runs, median; gather from a compact host copy of "
-                       f"the {uniq.size} table rows it touches; single-threaded C oracle")}
+        fn()
+        times.append(time.perf_counter() - t0)
+    return float(np.median(times)), len(times)
 
 
-def bench_cp_slice(args, torch, E, workloads, ranks=8):
-    """One context-parallel rank's forward: its slice of the replicated
-    sequence hashed (history read across the slice boundary) and looked up in
-    one pass (engram_lookup_slice); the two-call form (engram_hash_slice,
-    then engram_gather) is timed beside it."""
-    wl = workloads.full()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
-    mult = wl.multipliers()
-    S = wl.seq
-    a, b = (ranks - 1) * S // ranks, S
-    local = b - a
-    log(f"[bench] cp_slice: workload {wl.describe()}, slice [{a}, {b}) of {ranks}")
-    host = [wl.tokens(k, with_segments=True) for k in range(N_BATCHES)]
-    tokens = [torch.from_numpy(t).to(dev) for t, _ in host]
-    segs = [torch.from_numpy(s_).to(dev) for _, s_ in host]
-    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, dev)
-    R, D = wl.batch * local * wl.heads, wl.dim
-    rows = torch.empty((wl.batch, local, wl.heads), dtype=torch.int64, device=dev)
-    out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
-    hargs = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+def cpu_baseline(work, units, unit, sample):
+    """The oracle on this host: `work(oracle)` run by the serial build on one
+    core, and by the OpenMP build of the same source on every thread it may
+    use.  The all-core rate is `value`; the one-core rate is reported beside."""
+    from oracle import default_oracle, openmp_oracle
 
-    def step(k):
-        E.engram_lookup_slice(tokens[k % N_BATCHES], a, b, table, *hargs,
-                              seq_ids=segs[k % N_BATCHES], out=out)
-
-    def step_separate(k, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        E.engram_hash_slice(tokens[k % N_BATCHES], a, b, *hargs, wl.table_rows,
-                            seq_ids=segs[k % N_BATCHES], out=rows)
-        if ev is not None:
-            ev[1].record(stream)
-        E.engram_gather(rows, table, out=out)
-        if ev is not None:
-            ev[2].record(stream)
-
-    def timed(fn):
-        for k in range(args.warmup):
-            fn(k)
-        torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        for k in range(args.steps):
-            fn(k)
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1) / args.steps
-
-    ms = timed(step)
-    sep_ms = timed(step_separate)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        step_separate(k, evs[k])
-    torch.cuda.synchronize()
-    E.engram_hash_slice(tokens[0], a, b, *hargs, wl.table_rows, seq_ids=segs[0], out=rows)
-    hist = wl.ngram_size - 1
-    tok_bytes = 8 * wl.batch * (local + hist) * 2  # tokens + seg ids of the slice and its history
-    look_bytes = tok_bytes + 4 * D * R
-    look_gbps = look_bytes / (ms * 1e-3) / 1e9
-    phases = {"lookup": {"ms": ms, "algorithmic_bytes": look_bytes, "gbps": look_gbps,
-                         "frac_of_peak": look_gbps / PEAK_HBM_GBS}}
-    nbytes = {"hash": tok_bytes + 8 * R, "gather": 8 * R + 4 * D * R}
-    sep_phases = {}
-    for i, p_ in enumerate(("hash", "gather")):
-        pm = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
-        g = nbytes[p_] / (pm * 1e-3) / 1e9
-        sep_phases[p_] = {"ms": pm, "algorithmic_bytes": nbytes[p_], "gbps": g,
-                          "frac_of_peak": g / PEAK_HBM_GBS}
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import default_oracle
-        oracle = default_oracle()
-        t_host, s_host = host[0]
-        rates, start = [], time.perf_counter()
-        ids = rows.cpu().numpy()
-        uniq, loc = np.unique(ids.reshape(-1), return_inverse=True)
-        compact = table.index_select(0, torch.from_numpy(uniq).to(dev))
-        compact_bits = compact.view(torch.int16).cpu().numpy().view(np.uint16)
-        while len(rates) < 5 and (not rates or time.perf_counter() - start < 12.0):
-            c0 = time.perf_counter()
-            oracle.hash_global_slice(t_host, a, b, wl.ngram_size, wl.heads_per_ngram,
-                                     wl.eos_id, mult, wl.primes, wl.offsets, s_host)
-            oracle.gather(loc.astype(np.int64), compact_bits)
-            rates.append(R / (time.perf_counter() - c0))
-        cpu = {"value": float(np.median(rates)), "unit": "lookups/s", "cores": 1,
-               "kind": "oracle",
-               "sample": (f"one rank's slice ({R} lookups), {len(rates)} runs, median; the "
-                          "oracle hashes the whole replicated sequence and keeps the slice; "
-                          "gather from a compact host copy of the rows it touches")}
-    result = {
-        "metric": METRIC, "value": R / (ms * 1e-3), "unit": "lookups/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {**wl.describe(), "workload": "cp_slice", "cp_ranks": ranks,
-                   "slice": [a, b], "lookups": R, "segments": True,
-                   "step": "lookup_slice (hash and gather of the slice in one pass)"},
-        "phases": phases,
-        "separate_calls": {"ms_per_step": sep_ms, "value": R / (sep_ms * 1e-3),
-                           "step": "hash_slice+gather", "phases": sep_phases},
-        "roofline": {"bound": "hbm", "kernel": f"lookup_kernel<{wl.ngram_size}> "
-                     "(engram_lookup_slice)", "achieved": look_gbps, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": look_gbps / PEAK_HBM_GBS, "traffic": None},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(result), flush=True)
+    serial, par = default_oracle(), openmp_oracle()
+    t1, n1 = timed_runs(lambda: work(serial))
+    tn, nn = timed_runs(lambda: work(par))
+    return {"value": units / tn, "unit": unit, "cores": par.threads, "kind": "oracle",
+            "sample": f"{sample}; median of {nn} runs (one core: {n1})",
+            "single_core": {"value": units / t1, "cores": 1},
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "threads_allowed": len(os.sched_getaffinity(0))}
 
 
-def bench_ple_conv(args, torch, E, workloads):
-    """The PLE convolution over one batch of hidden states; a second pass
-    with the context-parallel halo (the preceding (K-1) * dilation rows)."""
-    wl = workloads.ple_conv()
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    stream = torch.cuda.current_stream(dev)
-    B, S, C, K, d = wl.batch, wl.seq, wl.channels, wl.kernel_size, wl.dilation
-    log(f"[bench] ple_conv: {wl.describe()}")
-    x = workloads.make_bf16((B, S, C), wl.seed, dev)
-    w = workloads.make_bf16((C, K), wl.seed + 1, dev, std=0.5)
-    bias = workloads.make_bf16((C,), wl.seed + 2, dev, std=0.5)
-    seg = torch.from_numpy(wl.segments()).to(dev)
-    H = wl.history
-    halo = workloads.make_bf16((B, H, C), wl.seed + 3, dev)
-    seg_h = torch.from_numpy(wl.segments(halo=H)).to(dev)
-    out = torch.empty_like(x)
-
-    def timed(fn, steps, warmup):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(steps):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / max(steps, 1)
-
-    plain = lambda: E.engram_ple_conv(x, w, d, bias=bias, seq_ids=seg, out=out)
-    with_halo = lambda: E.engram_ple_conv(x, w, d, bias=bias, seq_ids=seg_h, halo=halo, out=out)
-    timed(plain, 0, 20)       # bring the clocks up before either timing
-    timed(with_halo, 0, 20)
-    ms = timed(plain, args.steps, args.warmup)
-    ms_h = timed(with_halo, args.steps, args.warmup)
-    nbytes = 2 * B * S * C * 2 + 8 * B * S + 2 * C * (K + 1)
-    nbytes_h = nbytes + 2 * B * H * C + 8 * B * H
-    gbps, gbps_h = nbytes / (ms * 1e-3) / 1e9, nbytes_h / (ms_h * 1e-3) / 1e9
-    cpu = None
-    if not args.no_cpu_baseline:
-        from oracle import default_oracle
-        oracle = default_oracle()
-        xs = x[0:1, :, :256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        ws_ = w[:256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        bs = bias[:256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-        sg = seg[0:1].cpu().numpy()
-        rates, start = [], time.perf_counter()
-        while len(rates) < 5 and (not rates or time.perf_counter() - start < 12.0):
-            c0 = time.perf_counter()
-            oracle.ple_conv(xs, ws_, d, bs, sg)
-            rates.append(S * 256 / (time.perf_counter() - c0))
-        cpu = {"value": float(np.median(rates)), "unit": "position-channels/s", "cores": 1,
-               "kind": "oracle",
-               "sample": f"one row x 256 channels ({S * 256} outputs), {len(rates)} runs, "
-                         "median; single-threaded C oracle"}
-    result = {
-        "metric": "PLE conv position-channels/s and achieved HBM GB/s (% of peak)",
-        "value": B * S * C / (ms * 1e-3), "unit": "position-channels/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic",
-        "config": {**wl.describe(), "segments": "packed documents", "bias": True},
-        "algorithmic_bytes": nbytes, "gbps": gbps,
-        "with_cp_halo": {"halo_rows": H, "ms": ms_h, "algorithmic_bytes": nbytes_h,
-                         "gbps": gbps_h},
-        "roofline": {"bound": "hbm", "kernel": f"ple_conv_k4_kernel<{d}>", "achieved": gbps,
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBS,
-                     "traffic": None},
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(result), flush=True)
-
-
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="e2e",
-                    choices=["e2e", "e2e_signsgd", "full", "medium", "backward", "cp_slice",
-                             "ple_conv"])
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--settle", type=float, default=0.25,
-                    help="seconds of untimed steps before the warm-up steps")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path runs on a single MI355X with the whole table in HBM)",
-              file=sys.stderr)
-        sys.exit(2)
-
+def host_bits(t):
     import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
-    from gram_hashed_embedding_amd import engram as E
-    from gram_hashed_embedding_amd import workloads
 
-    if args.workload == "cp_slice":
-        return bench_cp_slice(args, torch, E, workloads)
-    if args.workload == "ple_conv":
-        return bench_ple_conv(args, torch, E, workloads)
-    signsgd = args.workload == "e2e_signsgd"
+def host_table(table):
+    """(uint16 bits of the table, or of as many of its first rows as fit in
+    HOST_TABLE_BYTES, and whether ids must be folded into those rows)."""
+    rows, dim = table.shape
+    fit = HOST_TABLE_BYTES // (2 * dim)
+    if rows <= fit:
+        return host_bits(table), False
+    return host_bits(table[:fit]), True
+
+
+def step_cpu_baseline(wl, tokens_host, mult, table, grads):
+    """The oracle's step on this workload's first token batch: the hash, the
+    gather and (when the workload has a backward) the scatter-add of the
+    upstream gradients into the workload's gradient form."""
+    import torch
+    tab_bits, folded = host_table(table)
+    hargs = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+    tok = tokens_host[0]
+    from oracle import default_oracle
+    rows = default_oracle().hash(tok, *hargs).reshape(-1)
+    gather_rows = rows % tab_bits.shape[0] if folded else rows
+    grad_bits = host_bits(grads) if grads is not None else None
+    dense = None
+    if wl.grads == "dense":
+        dense = np.zeros((wl.table_rows, wl.dim), dtype=np.float32)
+        dense.fill(0.0)  # touch every page before timing
+
+    def work(o):
+        o.hash(tok, *hargs)
+        o.gather(gather_rows, tab_bits)
+        if wl.grads == "rowsparse":
+            o.scatter_add_rowsparse(rows, grad_bits, wl.dim, wl.table_rows)
+        elif wl.grads == "dense":
+            o.scatter_add_dense(rows, grad_bits, dense, inplace=True)
+
+    what = {"rowsparse": "hash, gather and row-sparse scatter-add",
+            "dense": "hash, gather and dense fp32 scatter-add (into a host table of the "
+                     "workload's shape)",
+            "none": "hash and gather"}[wl.grads]
+    where = (f"gathering from a host copy of the table's first {tab_bits.shape[0]} rows "
+             f"({tab_bits.nbytes / 1e9:.1f} GB) with row ids folded modulo that count"
+             if folded else "gathering from a host copy of the whole table")
+    del torch
+    return cpu_baseline(work, wl.lookups, "lookups/s",
+                        f"the {wl.name} step on one token batch ({wl.lookups} lookups): {what}; "
+                        f"{where}")
+
+
+# --------------------------------------------------------------- HBM probe --
+def copy_probe_gbps(torch, dev, stream):
+    """The hand-written streaming copy (gram_hashed_embedding_amd/probe) over
+    2 GiB each way: what this GPU's HBM gives a plain 16-byte copy."""
+    path = os.path.join(ROOT, "gram_hashed_embedding_amd", "probe", "libengram_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.engram_probe_stream_copy.restype = ctypes.c_int
+    lib.engram_probe_stream_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                             ctypes.c_void_p]
+    nbytes = 2 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    s = ctypes.c_void_p(stream.cuda_stream)
+
+    def run():
+        rc = lib.engram_probe_stream_copy(ctypes.c_void_p(src.data_ptr()),
+                                          ctypes.c_void_p(dst.data_ptr()), nbytes // 16, s)
+        if rc != 0:
+            raise RuntimeError("copy probe launch failed")
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(10):
+        run()
+    b.record(stream)
+    torch.cuda.synchronize()
+    gbps = 2 * nbytes * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    return gbps
+
+
+# ------------------------------------------------------- the step benchmark --
+def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
+    """One workload's step (see the module docstring): the result dict.
+    `table` is an existing bf16 table of the workload's shape to reuse."""
+    signsgd = name == "e2e_signsgd"
     lr = 1e-6  # the learning rate of the pages' SignSGD runs
-    wl = workloads.get("e2e" if signsgd else args.workload)
+    wl = workloads.get("e2e" if signsgd else name)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
@@ -389,7 +290,9 @@ def main():
     tokens_host = [wl.tokens(k) for k in range(N_BATCHES)]
     tokens = [torch.from_numpy(t).to(dev) for t in tokens_host]
     t0 = time.perf_counter()
-    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, dev)
+    shared_table = table is not None and tuple(table.shape) == (wl.table_rows, wl.dim)
+    if not shared_table:
+        table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, dev)
     torch.cuda.synchronize()
     log(f"[bench] table {tuple(table.shape)} bf16 ready in {time.perf_counter() - t0:.1f}s")
 
@@ -397,6 +300,7 @@ def main():
     rows = torch.empty((wl.batch, wl.seq, wl.heads), dtype=torch.int64, device=dev)
     out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
     backward = wl.grads != "none"
+    grads = None
     if backward:
         grads = workloads.make_grads(R, D, wl.seed + 2, dev)
     if wl.grads == "rowsparse":  # (the SignSGD step's comparison uses these too)
@@ -561,13 +465,14 @@ def main():
         uid_ref, uval_ref = torch.empty_like(uid), torch.empty_like(uval)
         cnt_ref = torch.zeros_like(count)
         E.engram_scatter_plan_tokens(tokens[last % N_BATCHES], wl.table_rows, D, *hargs,
-                                     workspace=ws_ref)
+                                     workspace=ws_ref, err_count=err)
         E.engram_scatter_apply(grads, ws_ref, wl.table_rows, unique_ids=uid_ref,
-                               unique_grads=uval_ref, num_unique=cnt_ref)
+                               unique_grads=uval_ref, num_unique=cnt_ref, err_count=err)
         torch.cuda.synchronize()
         u_ref = int(cnt_ref.item())
         if not (int(count.item()) == u_ref and torch.equal(uid[:u_ref], uid_ref[:u_ref])
-                and torch.equal(uval[:u_ref].view(torch.int32), uval_ref[:u_ref].view(torch.int32))):
+                and torch.equal(uval[:u_ref].view(torch.int32),
+                                uval_ref[:u_ref].view(torch.int32))):
             raise RuntimeError("the timed schedule's backward differs from the serial calls")
         schedule_check = "last step bit-exact against serial calls"
         del ws_ref, uid_ref, uval_ref, cnt_ref
@@ -575,20 +480,25 @@ def main():
     # the same work with separate calls, timed in the same process
     sep_ms = timed_steps(step_separate)
     sep_phase_ms, _ = serial_phases(True)
-
     if backward and int(err.item()) != 0:
         raise RuntimeError(f"the step's plans or applies reported errors: {int(err.item())}")
-    # distinct rows of one batch (the backward's U), read after timing
-    unique_rows = 0
+
+    # distinct rows of each cycled batch (the backward's U), read after timing;
+    # the step's bytes use their mean, as the timed steps cycle the batches
+    unique_per_batch = []
     if backward:
-        E.engram_hash(tokens[0], *hargs, wl.table_rows, out=rows)
-        unique_rows = int(torch.unique(rows).numel())
+        for k in range(N_BATCHES):
+            E.engram_hash(tokens[k], *hargs, wl.table_rows, out=rows)
+            unique_per_batch.append(int(torch.unique(rows).numel()))
+    unique_rows = float(np.mean(unique_per_batch)) if unique_per_batch else 0
     nbytes = algorithmic_bytes(wl, unique_rows)
     sep_bytes = algorithmic_bytes(wl, unique_rows, separate=True)
     scatter_modes = None
     if wl.grads == "dense":
         # the one-call scatter-add, sorted (plan + apply) and fp32-atomic, side
         # by side on the same ids and gradients (the dense table accumulates)
+        E.engram_hash(tokens[0], *hargs, wl.table_rows, out=rows)
+
         def timed_call(fn, reps=max(args.steps, 3)):
             fn()
             torch.cuda.synchronize()
@@ -600,8 +510,8 @@ def main():
             torch.cuda.synchronize()
             return a_.elapsed_time(b_) / reps
         flat = rows.view(-1)
-        dense_bytes = 8 * R + 2 * D * R + 8 * D * unique_rows
-        scatter_modes = {"algorithmic_bytes": dense_bytes}
+        dense_bytes = 8 * R + 2 * D * R + 8 * D * unique_per_batch[0]
+        scatter_modes = {"algorithmic_bytes": dense_bytes, "unique_rows": unique_per_batch[0]}
         for name_, mode_ in (("sorted", E.SCATTER_SORTED), ("atomic", E.SCATTER_ATOMIC)):
             ms_ = timed_call(lambda: E.engram_scatter_add(
                 flat, grads, gtab, mode=mode_,
@@ -616,6 +526,7 @@ def main():
         sep_bytes["scatter_apply"] = nbytes["scatter_apply"]
         # the same step in two calls, for comparison (same plan, same stream)
         u0, u1, u2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        E.engram_hash(tokens[0], *hargs, wl.table_rows, out=rows)
         E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws)
         tw = []
         for k in range(max(args.steps // 2, 3)):
@@ -628,10 +539,12 @@ def main():
             torch.cuda.synchronize()
             tw.append((u0.elapsed_time(u1), u1.elapsed_time(u2)))
         a_ms, s_ms = (float(np.median([t[i] for t in tw])) for i in range(2))
+        u0_ = unique_per_batch[0]
         unfused = {"scatter_apply_ms": a_ms, "engram_signsgd_rowsparse_ms": s_ms,
                    "total_ms": a_ms + s_ms,
-                   "algorithmic_bytes": 2 * D * R + (4 * D + 8) * unique_rows
-                   + (8 + 4 * D + 4 * D) * unique_rows}
+                   "algorithmic_bytes": 2 * D * R + (4 * D + 8) * u0_
+                   + (8 + 4 * D + 4 * D) * u0_}
+
     def phase_table(pm, nb):
         out_ = {}
         for p_, ms in pm.items():
@@ -654,32 +567,20 @@ def main():
     if backward and phase_ms["scatter_apply"] > phase_ms["lookup"]:
         dominant = "scatter_apply"
         kernel = ("segment_reduce_kernel, SignSGD output (engram_scatter_apply_signsgd)"
-                  if signsgd else "segment_reduce_kernel (engram_scatter_apply)")
-    roofline = {"bound": "hbm", "kernel": kernel, "achieved": phases[dominant]["gbps"],
-                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": phases[dominant]["gbps"] / PEAK_HBM_GBS,
+                  if signsgd else f"segment_reduce_kernel, {wl.grads} output "
+                  "(engram_scatter_apply)")
+    # a forward-only step is the one lookup launch, back to back: its time
+    # per step is the kernel's own (an event pair around a single small
+    # launch also counts the launch)
+    achieved = phases[dominant]["gbps"] if backward else step_gbps
+    roofline = {"bound": "hbm", "kernel": kernel, "achieved": achieved,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                 "traffic": None if signsgd else measured_traffic(dominant, wl)}
 
-    # context: a plain device-to-device copy (torch copy_, 2 GiB read + 2 GiB
-    # written) shows what this GPU's HBM delivers to a streaming kernel
-    src = torch.empty(1 << 30, dtype=torch.int16, device=dev).fill_(1)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        dst.copy_(src)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        dst.copy_(src)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 2 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
-
-    cpu = None
-    if not args.no_cpu_baseline and wl.grads in ("rowsparse", "none"):
+    cpu_result = None
+    if cpu and not args.no_cpu_baseline and not signsgd:
         try:
-            cpu = cpu_baseline(wl, tokens_host, mult, table,
-                               grads if backward else None)
+            cpu_result = step_cpu_baseline(wl, tokens_host, mult, table, grads)
         except Exception as exc:  # the baseline must not hide the GPU number
             log(f"[bench] cpu baseline failed: {exc!r}")
 
@@ -704,7 +605,10 @@ def main():
                       " apply)" if backward else "")
                    + ("+signsgd(fused into the apply)" if signsgd else ""),
                    "backward": wl.grads, "accumulate": "f64" if backward else None,
-                   "unique_rows": unique_rows, "token_batches_cycled": N_BATCHES},
+                   "unique_rows": unique_rows, "unique_rows_per_batch": unique_per_batch,
+                   "token_batches_cycled": N_BATCHES,
+                   **({"table": "the e2e run's 200M x 256 bf16 table, reused"}
+                      if shared_table else {})},
         "serial_ms_per_step": serial_ms,
         "schedule_check": schedule_check,
         "step_algorithmic_bytes": step_bytes,
@@ -715,9 +619,231 @@ def main():
         **({"two_call_apply_and_signsgd": unfused} if unfused else {}),
         **({"scatter_add_sorted_vs_atomic": scatter_modes} if scatter_modes else {}),
         "roofline": roofline,
-        "hbm_copy_ceiling_gbps": copy_gbps,
+        "cpu_baseline": cpu_result,
+    }
+    return result, table
+
+
+def sub_config(res):
+    """The fields of a nested configuration's result."""
+    keep = ("metric", "value", "unit", "ms_per_step", "config", "step_algorithmic_bytes",
+            "step_gbps", "step_frac_of_peak", "phases", "separate_calls",
+            "scatter_add_sorted_vs_atomic", "roofline", "cpu_baseline")
+    return {k: res[k] for k in keep if k in res}
+
+
+def bench_cp_slice(args, torch, E, workloads, ranks=8):
+    """One context-parallel rank's forward: its slice of the replicated
+    sequence hashed (history read across the slice boundary) and looked up in
+    one pass (engram_lookup_slice); the two-call form (engram_hash_slice,
+    then engram_gather) is timed beside it."""
+    wl = workloads.full()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    mult = wl.multipliers()
+    S = wl.seq
+    a, b = (ranks - 1) * S // ranks, S
+    local = b - a
+    log(f"[bench] cp_slice: workload {wl.describe()}, slice [{a}, {b}) of {ranks}")
+    host = [wl.tokens(k, with_segments=True) for k in range(N_BATCHES)]
+    tokens = [torch.from_numpy(t).to(dev) for t, _ in host]
+    segs = [torch.from_numpy(s_).to(dev) for _, s_ in host]
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, dev)
+    R, D = wl.batch * local * wl.heads, wl.dim
+    rows = torch.empty((wl.batch, local, wl.heads), dtype=torch.int64, device=dev)
+    out = torch.empty((R, D), dtype=torch.bfloat16, device=dev)
+    hargs = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+
+    def step(k):
+        E.engram_lookup_slice(tokens[k % N_BATCHES], a, b, table, *hargs,
+                              seq_ids=segs[k % N_BATCHES], out=out)
+
+    def step_separate(k, ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        E.engram_hash_slice(tokens[k % N_BATCHES], a, b, *hargs, wl.table_rows,
+                            seq_ids=segs[k % N_BATCHES], out=rows)
+        if ev is not None:
+            ev[1].record(stream)
+        E.engram_gather(rows, table, out=out)
+        if ev is not None:
+            ev[2].record(stream)
+
+    def timed(fn):
+        for k in range(args.warmup):
+            fn(k)
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for k in range(args.steps):
+            fn(k)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    ms = timed(step)
+    sep_ms = timed(step_separate)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step_separate(k, evs[k])
+    torch.cuda.synchronize()
+    E.engram_hash_slice(tokens[0], a, b, *hargs, wl.table_rows, seq_ids=segs[0], out=rows)
+    hist = wl.ngram_size - 1
+    tok_bytes = 8 * wl.batch * (local + hist) * 2  # tokens + seg ids of the slice and its history
+    look_bytes = tok_bytes + 4 * D * R
+    look_gbps = look_bytes / (ms * 1e-3) / 1e9
+    phases = {"lookup": {"ms": ms, "algorithmic_bytes": look_bytes, "gbps": look_gbps,
+                         "frac_of_peak": look_gbps / PEAK_HBM_GBS}}
+    nbytes = {"hash": tok_bytes + 8 * R, "gather": 8 * R + 4 * D * R}
+    sep_phases = {}
+    for i, p_ in enumerate(("hash", "gather")):
+        pm = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+        g = nbytes[p_] / (pm * 1e-3) / 1e9
+        sep_phases[p_] = {"ms": pm, "algorithmic_bytes": nbytes[p_], "gbps": g,
+                          "frac_of_peak": g / PEAK_HBM_GBS}
+    cpu = None
+    if not args.no_cpu_baseline:
+        t_host, s_host = host[0]
+        ids = rows.cpu().numpy().reshape(-1)
+        tab_bits, folded = host_table(table)
+        gather_rows = ids % tab_bits.shape[0] if folded else ids
+
+        def work(o):
+            o.hash_global_slice(t_host, a, b, wl.ngram_size, wl.heads_per_ngram, wl.eos_id,
+                                mult, wl.primes, wl.offsets, s_host)
+            o.gather(gather_rows, tab_bits)
+        cpu = cpu_baseline(work, R, "lookups/s",
+                           f"one rank's slice ({R} lookups): the oracle hashes the whole "
+                           "replicated sequence and keeps the slice, then gathers from a host "
+                           f"copy of the table's first {tab_bits.shape[0]} rows with row ids "
+                           "folded modulo that count")
+    result = {
+        "metric": METRIC, "value": R / (ms * 1e-3), "unit": "lookups/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**wl.describe(), "workload": "cp_slice", "cp_ranks": ranks,
+                   "slice": [a, b], "lookups": R, "segments": True,
+                   "step": "lookup_slice (hash and gather of the slice in one pass)"},
+        "phases": phases,
+        "separate_calls": {"ms_per_step": sep_ms, "value": R / (sep_ms * 1e-3),
+                           "step": "hash_slice+gather", "phases": sep_phases},
+        "roofline": {"bound": "hbm", "kernel": f"lookup_kernel<{wl.ngram_size}> "
+                     "(engram_lookup_slice)", "achieved": look_gbps, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": look_gbps / PEAK_HBM_GBS, "traffic": None},
         "cpu_baseline": cpu,
     }
+    print(json.dumps(result), flush=True)
+
+
+def bench_ple_conv(args, torch, E, workloads):
+    """The PLE convolution over one batch of hidden states; a second pass
+    with the context-parallel halo (the preceding (K-1) * dilation rows)."""
+    wl = workloads.ple_conv()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    B, S, C, K, d = wl.batch, wl.seq, wl.channels, wl.kernel_size, wl.dilation
+    log(f"[bench] ple_conv: {wl.describe()}")
+    x = workloads.make_bf16((B, S, C), wl.seed, dev)
+    w = workloads.make_bf16((C, K), wl.seed + 1, dev, std=0.5)
+    bias = workloads.make_bf16((C,), wl.seed + 2, dev, std=0.5)
+    seg = torch.from_numpy(wl.segments()).to(dev)
+    H = wl.history
+    halo = workloads.make_bf16((B, H, C), wl.seed + 3, dev)
+    seg_h = torch.from_numpy(wl.segments(halo=H)).to(dev)
+    out = torch.empty_like(x)
+
+    def timed(fn, steps, warmup):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / max(steps, 1)
+
+    plain = lambda: E.engram_ple_conv(x, w, d, bias=bias, seq_ids=seg, out=out)
+    with_halo = lambda: E.engram_ple_conv(x, w, d, bias=bias, seq_ids=seg_h, halo=halo, out=out)
+    timed(plain, 0, 20)       # bring the clocks up before either timing
+    timed(with_halo, 0, 20)
+    ms = timed(plain, args.steps, args.warmup)
+    ms_h = timed(with_halo, args.steps, args.warmup)
+    nbytes = 2 * B * S * C * 2 + 8 * B * S + 2 * C * (K + 1)
+    nbytes_h = nbytes + 2 * B * H * C + 8 * B * H
+    gbps, gbps_h = nbytes / (ms * 1e-3) / 1e9, nbytes_h / (ms_h * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        xs = x[0:1, :, :256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        ws_ = w[:256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        bs = bias[:256].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        sg = seg[0:1].cpu().numpy()
+        cpu = cpu_baseline(lambda o: o.ple_conv(xs, ws_, d, bs, sg), S * 256,
+                           "position-channels/s",
+                           f"one row x 256 channels ({S * 256} outputs)")
+    result = {
+        "metric": "PLE conv position-channels/s and achieved HBM GB/s (% of peak)",
+        "value": B * S * C / (ms * 1e-3), "unit": "position-channels/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {**wl.describe(), "segments": "packed documents", "bias": True},
+        "algorithmic_bytes": nbytes, "gbps": gbps,
+        "with_cp_halo": {"halo_rows": H, "ms": ms_h, "algorithmic_bytes": nbytes_h,
+                         "gbps": gbps_h},
+        "roofline": {"bound": "hbm", "kernel": f"ple_conv_k4_kernel<{d}>", "achieved": gbps,
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbps / PEAK_HBM_GBS,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="e2e",
+                    choices=["e2e", "e2e_signsgd", "full", "medium", "backward", "cp_slice",
+                             "ple_conv"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="the e2e line alone, without the nested configurations")
+    ap.add_argument("--settle", type=float, default=0.25,
+                    help="seconds of untimed steps before the warm-up steps")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path runs on a single MI355X with the whole table in HBM)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gram_hashed_embedding_amd import engram as E
+    from gram_hashed_embedding_amd import workloads
+
+    if args.workload == "cp_slice":
+        return bench_cp_slice(args, torch, E, workloads)
+    if args.workload == "ple_conv":
+        return bench_ple_conv(args, torch, E, workloads)
+    result, table = bench_step(args, torch, E, workloads, args.workload)
+    dev = torch.device("cuda:0")
+    result["copy_probe_gbps"] = copy_probe_gbps(torch, dev, torch.cuda.current_stream(dev))
+    if args.workload == "e2e" and not args.no_other_configs:
+        others = {}
+        for name in ("medium", "full", "backward"):
+            res, _ = bench_step(args, torch, E, workloads, name,
+                                table=table if name == "full" else None)
+            others[name] = sub_config(res)
+            torch.cuda.empty_cache()
+        result["other_configs"] = others
+    del table
     print(json.dumps(result), flush=True)
 
 

@@ -22,6 +22,9 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 INCLUDE = ROOT / "include"
 LIBRARY = PKG / "libengram.so"
+# the HBM streaming-copy probe the benchmark reports beside the roofline
+PROBE_SOURCE = PKG / "probe" / "hbm_copy.hip"
+PROBE_LIBRARY = PKG / "probe" / "libengram_probe.so"
 ARCH = "gfx950"
 
 FLAGS = [
@@ -65,8 +68,20 @@ def _jobs() -> int:
         return 4
 
 
+def build_probe(verbose: bool = False) -> Path:
+    """Compile the HBM streaming-copy probe into PROBE_LIBRARY."""
+    tmp = PROBE_LIBRARY.with_suffix(".so.tmp")
+    cmd = [hipcc(), *FLAGS, "-shared", str(PROBE_SOURCE), "-o", str(tmp)]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, PROBE_LIBRARY)
+    return PROBE_LIBRARY
+
+
 def build(verbose: bool = False) -> Path:
-    """Compile all HIP sources into LIBRARY (always rebuilds)."""
+    """Compile all HIP sources into LIBRARY, and the probe (always rebuilds)."""
+    build_probe(verbose)
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="engram_build_") as tmpdir:
         objs = []
