@@ -28,6 +28,9 @@ under "other_configs", each with its own roofline and CPU baseline:
     backward  forward + dense fp32 backward: tokens [4, 4096] Zipf(1.2), 16
               heads, 16.8M x 64 table; also the one-call scatter-add, sorted
               against fp32 atomics, on the same ids and gradients
+    e2e_padtail  the e2e step on packs of whole documents whose row tails are
+              pad tokens in a segment of their own (hot rows of thousands of
+              terms per head), on the same table
 Eight distinct token batches are cycled so one step does not warm the next.
 All inputs are resident in HBM before timing starts.
 
@@ -201,16 +204,16 @@ def host_table(table):
     return host_bits(table[:fit]), True
 
 
-def step_cpu_baseline(wl, tokens_host, mult, table, grads):
+def step_cpu_baseline(wl, tokens_host, segs_host, mult, table, grads):
     """The oracle's step on this workload's first token batch: the hash, the
     gather and (when the workload has a backward) the scatter-add of the
     upstream gradients into the workload's gradient form."""
     import torch
     tab_bits, folded = host_table(table)
     hargs = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
-    tok = tokens_host[0]
+    tok, seg = tokens_host[0], segs_host[0]
     from oracle import default_oracle
-    rows = default_oracle().hash(tok, *hargs).reshape(-1)
+    rows = default_oracle().hash(tok, *hargs, seg).reshape(-1)
     gather_rows = rows % tab_bits.shape[0] if folded else rows
     grad_bits = host_bits(grads) if grads is not None else None
     dense = None
@@ -219,7 +222,7 @@ def step_cpu_baseline(wl, tokens_host, mult, table, grads):
         dense.fill(0.0)  # touch every page before timing
 
     def work(o):
-        o.hash(tok, *hargs)
+        o.hash(tok, *hargs, seg)
         o.gather(gather_rows, tab_bits)
         if wl.grads == "rowsparse":
             o.scatter_add_rowsparse(rows, grad_bits, wl.dim, wl.table_rows)
@@ -287,8 +290,14 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     mult = wl.multipliers()
     log(f"[bench] workload {wl.describe()}")
 
-    tokens_host = [wl.tokens(k) for k in range(N_BATCHES)]
+    # packed workloads carry their segment ids (the pad-tail one needs them:
+    # its tail is a segment of its own)
+    with_seg = wl.token_kind == "packed_pad"
+    drawn = [wl.tokens(k, with_segments=True) for k in range(N_BATCHES)]
+    tokens_host = [t for t, _ in drawn]
     tokens = [torch.from_numpy(t).to(dev) for t in tokens_host]
+    segs_host = [sg if with_seg else None for _, sg in drawn]
+    segs = [None if sg is None else torch.from_numpy(sg).to(dev) for sg in segs_host]
     t0 = time.perf_counter()
     shared_table = table is not None and tuple(table.shape) == (wl.table_rows, wl.dim)
     if not shared_table:
@@ -335,7 +344,8 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         last read that workspace (batch k - 2) is done."""
         side.wait_event(ev_apply[k % 2])
         E.engram_scatter_plan_tokens(tokens[k % N_BATCHES], wl.table_rows, D, *hargs,
-                                     workspace=wss[k % 2], err_count=err, stream=side)
+                                     seq_ids=segs[k % N_BATCHES], workspace=wss[k % 2],
+                                     err_count=err, stream=side)
         ev_plan[k % 2].record(side)
         planned["next"] = k
 
@@ -347,14 +357,14 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         follows the forward and waits for its own batch's plan, made during
         the step before.  Every step makes one plan, one forward and one
         apply."""
-        tok = tokens[k % N_BATCHES]
+        tok, sg = tokens[k % N_BATCHES], segs[k % N_BATCHES]
         if not backward:
-            E.engram_lookup(tok, table, *hargs, out=out)
+            E.engram_lookup(tok, table, *hargs, seq_ids=sg, out=out)
             return
         if planned["next"] != k:  # the first step: nothing planned yet
             plan_ahead(k)
         plan_ahead(k + 1)
-        E.engram_lookup(tok, table, *hargs, out=out)
+        E.engram_lookup(tok, table, *hargs, seq_ids=sg, out=out)
         stream.wait_event(ev_plan[k % 2])
         apply_backward(wss[k % 2])
         ev_apply[k % 2].record(stream)
@@ -362,7 +372,8 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     def step_separate(k):
         """The same step with separate calls (hash, then the plan of the ids
         beside the gather), for comparison."""
-        E.engram_hash(tokens[k % N_BATCHES], *hargs, wl.table_rows, out=rows)
+        E.engram_hash(tokens[k % N_BATCHES], *hargs, wl.table_rows, seq_ids=segs[k % N_BATCHES],
+                      out=rows)
         if not backward:
             E.engram_gather(rows, table, out=out)
             return
@@ -387,14 +398,14 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     def serial_step(k, ev, separate=False):
         """The calls of a step one after another on one stream, with events
         between them (per-phase times)."""
-        tok = tokens[k % N_BATCHES]
+        tok, sg = tokens[k % N_BATCHES], segs[k % N_BATCHES]
         ev[0].record(stream)
         if separate:
-            E.engram_hash(tok, *hargs, wl.table_rows, out=rows)
+            E.engram_hash(tok, *hargs, wl.table_rows, seq_ids=sg, out=rows)
             ev[1].record(stream)
             E.engram_gather(rows, table, out=out)
         else:
-            E.engram_lookup(tok, table, *hargs, out=out)
+            E.engram_lookup(tok, table, *hargs, seq_ids=sg, out=out)
             ev[1].record(stream)
         ev[2].record(stream)
         if backward:
@@ -402,8 +413,8 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
                 E.engram_scatter_plan(rows.view(-1), wl.table_rows, D, workspace=ws,
                                       err_count=err)
             else:
-                E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, workspace=ws,
-                                             err_count=err)
+                E.engram_scatter_plan_tokens(tok, wl.table_rows, D, *hargs, seq_ids=sg,
+                                             workspace=ws, err_count=err)
             ev[3].record(stream)
             apply_backward(ws)
             ev[4].record(stream)
@@ -465,7 +476,8 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         uid_ref, uval_ref = torch.empty_like(uid), torch.empty_like(uval)
         cnt_ref = torch.zeros_like(count)
         E.engram_scatter_plan_tokens(tokens[last % N_BATCHES], wl.table_rows, D, *hargs,
-                                     workspace=ws_ref, err_count=err)
+                                     seq_ids=segs[last % N_BATCHES], workspace=ws_ref,
+                                     err_count=err)
         E.engram_scatter_apply(grads, ws_ref, wl.table_rows, unique_ids=uid_ref,
                                unique_grads=uval_ref, num_unique=cnt_ref, err_count=err)
         torch.cuda.synchronize()
@@ -488,7 +500,7 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     unique_per_batch = []
     if backward:
         for k in range(N_BATCHES):
-            E.engram_hash(tokens[k], *hargs, wl.table_rows, out=rows)
+            E.engram_hash(tokens[k], *hargs, wl.table_rows, seq_ids=segs[k], out=rows)
             unique_per_batch.append(int(torch.unique(rows).numel()))
     unique_rows = float(np.mean(unique_per_batch)) if unique_per_batch else 0
     nbytes = algorithmic_bytes(wl, unique_rows)
@@ -497,7 +509,7 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     if wl.grads == "dense":
         # the one-call scatter-add, sorted (plan + apply) and fp32-atomic, side
         # by side on the same ids and gradients (the dense table accumulates)
-        E.engram_hash(tokens[0], *hargs, wl.table_rows, out=rows)
+        E.engram_hash(tokens[0], *hargs, wl.table_rows, seq_ids=segs[0], out=rows)
 
         def timed_call(fn, reps=max(args.steps, 3)):
             fn()
@@ -580,7 +592,7 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     cpu_result = None
     if cpu and not args.no_cpu_baseline and not signsgd:
         try:
-            cpu_result = step_cpu_baseline(wl, tokens_host, mult, table, grads)
+            cpu_result = step_cpu_baseline(wl, tokens_host, segs_host, mult, table, grads)
         except Exception as exc:  # the baseline must not hide the GPU number
             log(f"[bench] cpu baseline failed: {exc!r}")
 
@@ -608,7 +620,9 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
                    "unique_rows": unique_rows, "unique_rows_per_batch": unique_per_batch,
                    "token_batches_cycled": N_BATCHES,
                    **({"table": "the e2e run's 200M x 256 bf16 table, reused"}
-                      if shared_table else {})},
+                      if shared_table else {}),
+                   **({"segments": "packed documents; each row's tail after its last whole "
+                       "document is pad tokens in a segment of their own"} if with_seg else {})},
         "serial_ms_per_step": serial_ms,
         "schedule_check": schedule_check,
         "step_algorithmic_bytes": step_bytes,
@@ -809,8 +823,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="e2e",
-                    choices=["e2e", "e2e_signsgd", "full", "medium", "backward", "cp_slice",
-                             "ple_conv"])
+                    choices=["e2e", "e2e_signsgd", "e2e_padtail", "full", "medium", "backward",
+                             "cp_slice", "ple_conv"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-other-configs", action="store_true",
                     help="the e2e line alone, without the nested configurations")
@@ -837,9 +851,9 @@ def main():
     result["copy_probe_gbps"] = copy_probe_gbps(torch, dev, torch.cuda.current_stream(dev))
     if args.workload == "e2e" and not args.no_other_configs:
         others = {}
-        for name in ("medium", "full", "backward"):
+        for name in ("medium", "full", "backward", "e2e_padtail"):
             res, _ = bench_step(args, torch, E, workloads, name,
-                                table=table if name == "full" else None)
+                                table=table if name in ("full", "e2e_padtail") else None)
             others[name] = sub_config(res)
             torch.cuda.empty_cache()
         result["other_configs"] = others

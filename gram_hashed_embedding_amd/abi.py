@@ -17,7 +17,7 @@ SCATTER_ATOMIC = 1
 SCATTER_ROWSPARSE = 2
 MAX_NGRAM = 8
 MAX_HEADS = 64
-NOALLOC_SCRATCH_BYTES = 32 << 20  # ENGRAM_NOALLOC_SCRATCH_BYTES
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ENGRAM_NOALLOC_SCRATCH_BYTES
 ERR_STALLED = 1 << 40             # ENGRAM_ERR_STALLED
 ERR_NO_PLAN = 1 << 41             # ENGRAM_ERR_NO_PLAN
 

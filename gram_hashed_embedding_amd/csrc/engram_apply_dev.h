@@ -24,10 +24,15 @@
 // store, or the SignSGD step on the bf16 table row); a run cut by the
 // range's end but ending in the next range is finished by the same walker.
 // Runs longer than that (hot rows, found from three sorted keys per range)
-// are summed whole by the leading blocks of the same launch, a block per
-// run, its walkers taking interleaved ranges of the run and adding their
-// sums in a fixed order.  No work item waits on another, and hot rows
-// (hundreds of contributions) do not serialise a walker.
+// are summed by the leading blocks of the same launch in aligned chunks of
+// kChunk sorted positions: the block of a chunk sums the part of each long
+// run that lies in it, its walkers taking interleaved ranges and adding
+// their sums in a fixed order.  A long run inside one chunk is written at
+// once; one that crosses chunks leaves an fp64 partial-sum row in each, and
+// a second launch adds those in chunk order.  No work item waits on another,
+// hot rows do not serialise a walker, and a row that holds a large share of
+// all positions (a padding row) is spread over as many blocks as it has
+// chunks.
 #pragma once
 
 #include "engram_scatter_dev.h"
@@ -36,12 +41,12 @@ namespace engram {
 
 constexpr int kWalkThreads = 256;
 constexpr int64_t kLongBlocks = 1024;  // most blocks that sum long runs
+constexpr int64_t kCombineBlocks = 256;  // most blocks of the second launch
 constexpr int64_t kXcds = 8;           // XCDs of an MI355X (blocks go to them in turn)
 // Gradient tensors larger than this are read with non-temporal loads: half
 // the MI355X's 256 MB Infinity Cache, so a tensor that could still be cached
 // when the apply runs is read normally.
 constexpr int64_t kStreamGradBytes = int64_t(128) << 20;
-constexpr int64_t kLongSpan = 64;      // fewest ranges per long-run block
 
 // Lane layout.  A walker is L lanes.  A row of head_dim values is split into
 // quads of 4 values (8 bytes of bf16 input, 16 bytes of fp32 output); lane
@@ -65,8 +70,10 @@ struct WalkArgs {
   float *unique_grads;
   uint2 *table;         // SignSGD output: the bf16 table, [rows, dim / 4] quads
   float lr;
-  uint32_t long_blocks;  // leading blocks of the grid: they sum the long runs
-  int64_t long_span;     // ranges each of those blocks looks after
+  uint32_t *chunk_owner;   // per chunk: slot + 1 of the long run that leaves it, or 0
+  double *partials;        // per chunk: [2, dim] fp64 rows (run entering, run leaving)
+  int64_t num_chunks;
+  uint32_t long_blocks;    // leading blocks of the grid: they sum long runs by chunk
   const PlanScalars *plan;  // U, the stall flag and the stamp, from the plan
   int64_t *num_unique;      // row-sparse output count
   int64_t *err;             // error counter, or null
@@ -365,93 +372,13 @@ __device__ __forceinline__ void walk_range(const WalkArgs &a, int64_t blk) {
   emit_row<L, Q, OUT>(cur, u, a, lane, acc, cw, cg);
 }
 
-// One long run: the run that starts in range c0 and reaches range c0 + 2.
-template <int L, int Q, int OUT, bool EXACT, bool NT>
-__device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
-                                         double (&s_part)[kWalkThreads / L][L * 4]) {
-  constexpr int G = kWalkThreads / L;  // walkers per block
-  const int lane = threadIdx.x % L, g = threadIdx.x / L, wl = __lane_id();
-  const int64_t r0 = c0 * kRange;
-  const uint32_t u = a.head_off[c0 + 1] - 1;  // the last head of c0 (c0 + 2 exists)
-  const uint32_t key = a.keys[r0 + kRange - 1];
-  uint2 tw[Q];   // SignSGD: the run's bf16 table row
-  f32x4 tg[Q];   // dense: the run's fp32 gradient table row
-  if constexpr (OUT == kOutSignSGD)
-    load_quads<L, Q, EXACT>(a.table, table_row(a, key), a.quads, lane, tw);
-  if constexpr (OUT == kOutDense && Q == 1) load_grad_row<L, Q, EXACT>(a, table_row(a, key), lane, tg);
-  // start: range c0 is sorted, so the run begins after its smaller keys
-  int64_t start = r0;
-  const u32x4 *kp = reinterpret_cast<const u32x4 *>(a.keys + r0);
-#pragma unroll
-  for (int j = 0; j < kRange / 4; ++j) {
-    const u32x4 k4 = kp[j];
-    start += (k4.x != key) + (k4.y != key) + (k4.z != key) + (k4.w != key);
-  }
-  // stop: the first position past r0 + 2 * kRange (which holds key) whose
-  // key differs, 4 * kWave positions per step, each wavefront on its own
-  int64_t stop = -1;
-  for (int64_t p0 = r0 + 2 * kRange + 1; stop < 0; p0 += 4 * kWave) {
-    int leave_at = 4;  // first of this lane's 4 positions past the run
-#pragma unroll
-    for (int e = 3; e >= 0; --e) {
-      const int64_t p = p0 + 4 * wl + e;
-      leave_at = (p >= a.n || a.keys[p] != key) ? e : leave_at;
-    }
-    const unsigned long long leave = __ballot(leave_at < 4);
-    if (leave != 0ull) {
-      const int src = __ffsll((long long)leave) - 1;
-      stop = p0 + 4 * src + __shfl(leave_at, src, kWave);
-    }
-  }
-  const int64_t c1 = (stop - 1) / kRange;  // range of the run's last position
-  double acc[Q][4];
-  zero_acc<Q>(acc);
-  uint32_t vv[kRange];
-  if (Q == 1 && c0 + g <= c1) load_vals(a.vals, (c0 + g) * kRange, vv);
-  if constexpr (Q == 1) {
-    // a whole range of rows in flight, the next range's indices fetched
-    // while they arrive
-#pragma unroll 1
-    for (int64_t c = c0 + g; c <= c1; c += G) {
-      uint2 rows[kRange][Q];
-#pragma unroll
-      for (int q = 0; q < kRange; ++q) {
-        const int64_t p = c * kRange + q;
-        load_row<L, Q, EXACT, NT>(a, (p >= start && p < stop) ? vv[q] : 0u, lane, rows[q]);
-      }
-      if (c + G <= c1) load_vals(a.vals, (c + G) * kRange, vv);
-#pragma unroll
-      for (int q = 0; q < kRange; ++q) {
-        const int64_t p = c * kRange + q;
-        add_quads_if<Q>(acc, rows[q], p >= start && p < stop);
-      }
-    }
-  } else {
-    // wide rows: batches of kRange / Q rows, one batch at a time (a loop the
-    // compiler keeps rolled, so it cannot hoist every batch's loads at once)
-    constexpr int B = kRange / Q > 0 ? kRange / Q : 1;
-#pragma unroll 1
-    for (int64_t p0 = (c0 + g) * kRange; p0 <= c1 * kRange; p0 += (int64_t)G * kRange) {
-#pragma unroll 1
-      for (int b0 = 0; b0 < kRange; b0 += B) {
-        uint32_t idx[B];
-#pragma unroll
-        for (int qq = 0; qq < B; ++qq) idx[qq] = a.vals[p0 + b0 + qq];
-        uint2 rows[B][Q];
-#pragma unroll
-        for (int qq = 0; qq < B; ++qq) {
-          const int64_t p = p0 + b0 + qq;
-          load_row<L, Q, EXACT, NT>(a, (p >= start && p < stop) ? idx[qq] : 0u, lane, rows[qq]);
-        }
-#pragma unroll
-        for (int qq = 0; qq < B; ++qq) {
-          const int64_t p = p0 + b0 + qq;
-          add_quads_if<Q>(acc, rows[qq], p >= start && p < stop);
-        }
-      }
-    }
-  }
-  // walker 0 adds the other walkers' sums in walker order
+// Walker 0 adds the other walkers' sums to its own, in walker order (through
+// LDS, one quad of the row at a time).
+template <int L, int Q>
+__device__ __forceinline__ void block_combine(double (&acc)[Q][4],
+                                              double (&s_part)[kWalkThreads / L][L * 4]) {
+  constexpr int G = kWalkThreads / L;
+  const int lane = threadIdx.x % L, g = threadIdx.x / L;
 #pragma unroll
   for (int k = 0; k < Q; ++k) {
     if (g > 0)
@@ -465,89 +392,429 @@ __device__ __forceinline__ void long_run(const WalkArgs &a, int64_t c0,
         for (int e = 0; e < 4; ++e) acc[k][e] += s_part[h][lane * 4 + e];
     __syncthreads();
   }
-  if (g == 0) emit_row<L, Q, OUT>(key, u, a, lane, acc, tw, tg);
 }
 
-// Long runs (hot rows, longer than a range).  Block b checks which of the
-// ranges [b * long_span, (b + 1) * long_span) end in a long run (three keys
-// per range) and sums those runs in range order, the whole block on one run:
-// the run's end is found by a scan of the keys, the block's G walkers sum the
-// run's ranges c0 + g, c0 + g + G, ... (each range's indices fetched one
-// range ahead, its rows all in flight), and walker 0 adds the walkers' sums
-// in walker order before writing the row.  Fixed assignment and fixed order keep the result
-// deterministic.
-template <int L, int Q, int OUT, bool EXACT, bool NT>
-__device__ __forceinline__ void long_runs(const WalkArgs &a) {
-  __shared__ double s_part[kWalkThreads / L][L * 4];
-  __shared__ uint32_t s_list[kWalkThreads];
-  __shared__ int s_wave_count[kWalkThreads / kWave];
-  const int wl = __lane_id(), wave = threadIdx.x / kWave;
-  const int64_t first = (int64_t)blockIdx.x * a.long_span;
-  const int64_t last = min(a.num_ranges, first + a.long_span);
-  for (int64_t b0 = first; b0 < last; b0 += kWalkThreads) {
-    // this stretch's flagged ranges, in range order
-    const int64_t r = b0 + threadIdx.x;
-    bool flagged = false;
-    if (r < last) {
-      const int64_t at = r * kRange;
-      flagged = last_run_long(r, a.n, a.sentinel, a.keys[at > 0 ? at - 1 : 0],
-                              a.keys[min(at + kRange - 1, a.n - 1)],
-                              a.keys[min(at + 2 * kRange, a.n - 1)]);
-    }
-    const unsigned long long bal = __ballot(flagged);
-    if (wl == 0) s_wave_count[wave] = __popcll(bal);
-    __syncthreads();
-    int at = __popcll(bal & ((1ull << wl) - 1ull)), count = 0;
+// The partial-sum row of chunk j, side 0 (the long run entering the chunk)
+// or 1 (the long run leaving it).
+__device__ __forceinline__ f64x2 *partial_row(const WalkArgs &a, int64_t j, int side) {
+  return reinterpret_cast<f64x2 *>(a.partials + (2 * j + side) * a.dim);
+}
+
+// Walker 0's sum into a partial-sum row (fp64, exactly as held).
+template <int L, int Q>
+__device__ __forceinline__ void store_partial(const WalkArgs &a, f64x2 *row, int lane,
+                                              const double (&acc)[Q][4]) {
 #pragma unroll
-    for (int v = 0; v < kWalkThreads / kWave; ++v) {
-      at += v < wave ? s_wave_count[v] : 0;
-      count += s_wave_count[v];
-    }
-    if (flagged) s_list[at] = (uint32_t)r;
-    __syncthreads();
-    for (int i = 0; i < count; ++i) long_run<L, Q, OUT, EXACT, NT>(a, s_list[i], s_part);
-    __syncthreads();  // s_list and s_wave_count are rewritten for the next stretch
+  for (int k = 0; k < Q; ++k) {
+    const int64_t qd = lane + (int64_t)k * L;
+    if (qd >= a.quads) continue;
+    row[2 * qd] = f64x2{acc[k][0], acc[k][1]};
+    row[2 * qd + 1] = f64x2{acc[k][2], acc[k][3]};
   }
 }
 
-// The apply kernel: blocks [0, long_blocks) sum the long runs, the rest are
-// range walkers, kWalkThreads / L walkers per block.
+// Long-run blocks hold kGroupChunks chunks at a time in LDS: the keys of
+// each chunk with the two ranges before and after it, which the tests read
+// (positions P0 - kHalo .. P1 + kHalo - 1; 0xFFFFFFFF before the first
+// position, the drop key past the last), the flat indices, and per range
+// the chunk offsets of its first and last distinct-row starts and the slot
+// of its last distinct row.  Keys and indices arrive as 16-byte vectors.
+constexpr int kChunkRanges = (int)(kChunk / kRange);
+constexpr int kGroupChunks = 4;
+constexpr int kHalo = 2 * kRange;
+constexpr int kChunkKeys = kHalo + (int)kChunk + kHalo;
+
+template <int L>
+struct LongLds {
+  double part[kWalkThreads / L][L * 4];
+  alignas(16) uint32_t keys[kGroupChunks][kChunkKeys];
+  // indices; one row more, for the chunk after the group's last
+  alignas(16) uint32_t vals[kGroupChunks + 1][kChunk];
+  uint32_t slot[kGroupChunks][kChunkRanges];
+  uint32_t far_before[kGroupChunks];  // key at P0 - kChunk - 1 (0xFFFFFFFF: none)
+  uint32_t far_after[kGroupChunks];   // key at P0 + 2 kChunk (the drop key: none)
+  unsigned long long end_next;        // end of a run in the next chunk
+  uint16_t first[kGroupChunks][kChunkRanges];
+  uint16_t last[kGroupChunks][kChunkRanges];
+  uint32_t has_start[kGroupChunks];  // bit r: range r holds a distinct-row start
+  uint32_t flagged[kGroupChunks];    // bit r: range r's last run is long
+  uint32_t enters[kGroupChunks];     // a long run enters the chunk
+};
+
+// The sum of chunk offsets [s, e) of one row (flat indices from LDS) by the
+// whole block: walker g takes offsets s + 16 g .. s + 16 g + 15, then
+// s + 16 (g + G) ..., all 16 rows in flight at once (wide rows: in batches);
+// walker 0 then adds the walkers' sums in walker order.  The order of every
+// addition depends only on [s, e).  Walker 0's acc holds the sum on return.
+template <int L, int Q, bool EXACT, bool NT>
+__device__ __forceinline__ void block_sum_lds(const WalkArgs &a, const uint32_t *vals, int s,
+                                              int e, double (&acc)[Q][4],
+                                              double (&part)[kWalkThreads / L][L * 4]) {
+  constexpr int G = kWalkThreads / L;
+  constexpr int B = Q == 1 ? kRange : (kRange / Q > 0 ? kRange / Q : 1);  // rows in flight
+  const int lane = threadIdx.x % L, g = threadIdx.x / L;
+  zero_acc<Q>(acc);
+#pragma unroll 1
+  for (int b = s + kRange * g; b < e; b += kRange * G) {
+#pragma unroll 1
+    for (int b0 = 0; b0 < kRange; b0 += B) {
+      uint2 rows[B][Q];
+#pragma unroll
+      for (int q = 0; q < B; ++q) {
+        const int o = b + b0 + q;
+        load_row<L, Q, EXACT, NT>(a, o < e ? vals[o] : 0u, lane, rows[q]);
+      }
+#pragma unroll
+      for (int q = 0; q < B; ++q) add_quads_if<Q>(acc, rows[q], b + b0 + q < e);
+    }
+  }
+  block_combine<L, Q>(acc, part);
+}
+
+// Chunks [j0, j0 + cnt) into LDS (cnt <= kGroupChunks), then the tests of
+// every range of them: one round of loads for the whole group.  The key and
+// index buffers hold whole ranges, so a 16-byte vector that starts before
+// n is inside them (its positions past n read as the drop key).
+template <int L>
+__device__ __forceinline__ void load_group(const WalkArgs &a, int64_t j0, int cnt,
+                                           LongLds<L> &s) {
+  const int tid = threadIdx.x;
+  constexpr int kKeyVecs = kChunkKeys / 4, kValVecs = (int)kChunk / 4;
+  constexpr int kKeyIters = (kGroupChunks * kKeyVecs + kWalkThreads - 1) / kWalkThreads;
+  constexpr int kValIters = (kGroupChunks * kValVecs + kWalkThreads - 1) / kWalkThreads;
+  static_assert(kGroupChunks * kChunkRanges <= kWalkThreads, "one thread per range");
+  static_assert(kHalo % 4 == 0 && kChunkKeys % 4 == 0, "whole vectors");
+  const u32x4 *kv = reinterpret_cast<const u32x4 *>(a.keys);
+  const u32x4 *vv = reinterpret_cast<const u32x4 *>(a.vals);
+  u32x4 kx[kKeyIters] = {}, vx[kValIters] = {};
+#pragma unroll
+  for (int it = 0; it < kKeyIters; ++it) {
+    const int i = tid + it * kWalkThreads, k = i / kKeyVecs;
+    const int64_t p = (j0 + k) * kChunk - kHalo + 4 * (i - k * kKeyVecs);
+    if (i < cnt * kKeyVecs && p >= 0 && p < a.n) kx[it] = kv[p / 4];
+  }
+#pragma unroll
+  for (int it = 0; it < kValIters; ++it) {
+    const int i = tid + it * kWalkThreads, k = i / kValVecs;
+    const int64_t p = (j0 + k) * kChunk + 4 * (i - k * kValVecs);
+    if (i < cnt * kValVecs && p < a.n) vx[it] = vv[p / 4];
+  }
+#pragma unroll
+  for (int it = 0; it < kKeyIters; ++it) {
+    const int i = tid + it * kWalkThreads, k = i / kKeyVecs, o = 4 * (i - k * kKeyVecs);
+    const int64_t p = (j0 + k) * kChunk - kHalo + o;
+    if (i < cnt * kKeyVecs) {
+      u32x4 v = kx[it];
+      const uint32_t pre = 0xFFFFFFFFu;
+      v.x = p < 0 ? pre : (p < a.n ? v.x : a.sentinel);
+      v.y = p < 0 ? pre : (p + 1 < a.n ? v.y : a.sentinel);
+      v.z = p < 0 ? pre : (p + 2 < a.n ? v.z : a.sentinel);
+      v.w = p < 0 ? pre : (p + 3 < a.n ? v.w : a.sentinel);
+      *reinterpret_cast<u32x4 *>(&s.keys[k][o]) = v;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < kValIters; ++it) {
+    const int i = tid + it * kWalkThreads, k = i / kValVecs, o = 4 * (i - k * kValVecs);
+    if (i < cnt * kValVecs) *reinterpret_cast<u32x4 *>(&s.vals[k][o]) = vx[it];
+  }
+  {
+    const int k = tid / kChunkRanges, r = tid % kChunkRanges;
+    const int64_t c = (j0 + k) * kChunkRanges + r;  // this thread's range
+    const int64_t P0 = (j0 + k) * kChunk;
+    if (k < cnt && c + 1 < a.num_ranges) s.slot[k][r] = a.head_off[c + 1] - 1;
+    if (k < cnt && r == 1)
+      s.far_before[k] = P0 >= kChunk + 1 ? a.keys[P0 - kChunk - 1] : 0xFFFFFFFFu;
+    if (k < cnt && r == 2) s.far_after[k] = P0 + 2 * kChunk < a.n ? a.keys[P0 + 2 * kChunk] : a.sentinel;
+  }
+  __syncthreads();
+  // per range: distinct-row starts (key differs from the one before) and the
+  // walkers' long-run test; the first thread of a chunk tests the run that
+  // enters it
+  const int k = tid / kChunkRanges, r = tid % kChunkRanges;
+  bool has = false, flag = false, enter = false;
+  if (k < cnt) {
+    const int64_t c = (j0 + k) * kChunkRanges + r, P0 = (j0 + k) * kChunk;
+    const uint32_t *kk = &s.keys[k][kHalo + r * kRange];  // kk[q]: position 16 c + q
+    int first = kRange, last = -1;
+#pragma unroll
+    for (int q = 0; q < kRange; ++q) {
+      const bool st = kk[q] != kk[q - 1];
+      first = (st && first == kRange) ? q : first;
+      last = st ? q : last;
+    }
+    s.first[k][r] = (uint16_t)(r * kRange + first);
+    s.last[k][r] = (uint16_t)(r * kRange + (last < 0 ? 0 : last));
+    has = first < kRange;
+    flag = last_run_long(c, a.n, a.sentinel, kk[-1], kk[kRange - 1], kk[2 * kRange]);
+    if (r == 0) {
+      const uint32_t *k0 = &s.keys[k][kHalo];  // k0[o]: position P0 + o
+      enter = P0 > 0 && k0[0] != a.sentinel && k0[-1] == k0[0] &&
+              (k0[-kRange - 1] == k0[0] || (P0 + kRange < a.n && k0[kRange] == k0[0]));
+    }
+  }
+  const unsigned long long hb = __ballot(has), fb = __ballot(flag), eb = __ballot(enter);
+  if (tid % 64 == 0 && tid / kChunkRanges < kGroupChunks) {
+    const int k0 = tid / kChunkRanges;  // chunks k0 and k0 + 1 share this wavefront
+    s.has_start[k0] = (uint32_t)hb;
+    s.flagged[k0] = (uint32_t)fb;
+    s.enters[k0] = (uint32_t)(eb & 1u);
+    if (k0 + 1 < kGroupChunks) {
+      s.has_start[k0 + 1] = (uint32_t)(hb >> 32);
+      s.flagged[k0 + 1] = (uint32_t)(fb >> 32);
+      s.enters[k0 + 1] = (uint32_t)((eb >> 32) & 1u);
+    }
+  }
+  __syncthreads();
+}
+
+// The end of a run of `key` that holds P1 = (j + 1) * kChunk and ends in
+// chunk j + 1 (not past P1 + kChunk), as an offset from P1, with chunk j + 1's
+// flat indices put in LDS row k + 1 beside it.  When the group holds chunk
+// j + 1 (k + 1 < cnt) both come from LDS; else one round of loads.
+template <int L>
+__device__ __forceinline__ int next_chunk_end(const WalkArgs &a, int64_t j, int k, int cnt,
+                                              uint32_t key, LongLds<L> &s) {
+  if (k + 1 < cnt) {
+    const uint32_t has = s.has_start[k + 1];  // (no start at its offset 0: the run holds it)
+    return has != 0 ? (int)s.first[k + 1][__ffs((int)has) - 1]
+                    : (int)min(kChunk, a.n - (j + 1) * kChunk);
+  }
+  const int tid = threadIdx.x;
+  const int64_t P1 = (j + 1) * kChunk;
+  if (tid == 0) s.end_next = (unsigned long long)min(kChunk, a.n - P1);
+  __syncthreads();
+  static_assert(kChunk == 2 * kWalkThreads, "two positions a thread");
+  const int o = 2 * tid;
+  const int64_t p = P1 + o;
+  if (p < a.n) {  // the buffers hold whole ranges: p + 1 is inside them
+    const uint2 kk = *reinterpret_cast<const uint2 *>(a.keys + p);
+    const uint2 vv = *reinterpret_cast<const uint2 *>(a.vals + p);
+    s.vals[k + 1][o] = vv.x;
+    s.vals[k + 1][o + 1] = vv.y;
+    const int e = kk.x != key ? o : (p + 1 < a.n && kk.y != key ? o + 1 : -1);
+    if (e >= 0) atomicMin(&s.end_next, (unsigned long long)e);
+  }
+  __syncthreads();
+  return (int)s.end_next;
+}
+
+// One chunk of long-run work: positions [P0, P1) = [j * kChunk, ...) of the
+// sorted order, held in LDS slot k of a group of cnt.  The long runs there
+// are the one entering from the previous chunk and those starting in the
+// chunk's ranges that a walker leaves out.  The block sums each run's
+// positions; a run's end is the first distinct-row start after it (from the
+// per-range starts).  A run that ends in this chunk or the next is summed
+// whole by the chunk it starts in and written out at once (its output row
+// read while the sum's loads are in flight).  A run that spans three chunks
+// or more is split: every chunk it touches sums its own part into an fp64
+// partial row (side 0: the run entering the chunk; side 1: the run leaving
+// it, whose slot (+1) goes to chunk_owner[j], 0 when none) for the second
+// launch.  The chunks on both sides of a boundary agree on which runs are
+// split from the keys at P0 - kChunk - 1, P1 and P0 + 2 kChunk.
 template <int L, int Q, int OUT, bool EXACT, bool NT>
-__global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
-  // Only a complete plan of these n and table_rows, none of whose waits
-  // expired, is read; otherwise nothing is written (U = 0) and it is counted.
+__device__ __forceinline__ void long_chunk(const WalkArgs &a, int64_t j, int k, int cnt,
+                                           LongLds<L> &s) {
+  const int lane = threadIdx.x % L, g = threadIdx.x / L;
+  const int64_t P0 = j * kChunk;
+  const int len = (int)min(kChunk, a.n - P0);
+  const bool more = P0 + len < a.n;  // a chunk follows
+  const uint32_t has = s.has_start[k];
+  const uint32_t *kk = &s.keys[k][kHalo];  // kk[o]: position P0 + o
+  // the end (chunk offset) of a run that holds no distinct-row start in
+  // ranges r and up: the first start there, else the chunk's end
+  auto end_from = [&](int r) -> int {
+    const uint32_t m = r < kChunkRanges ? has >> r : 0u;
+    return m != 0 ? (int)s.first[k][r + __ffs((int)m) - 1] : len;
+  };
+  uint32_t owner = 0;  // slot + 1 of the split run that leaves the chunk
+  double acc[Q][4];
+  if (s.enters[k] != 0) {
+    // split when it started two chunks back or more, or leaves this chunk
+    // too; else the chunk before sums it whole
+    const uint32_t ekey = kk[0];
+    if (s.far_before[k] == ekey || (more && kk[len] == ekey)) {
+      block_sum_lds<L, Q, EXACT, NT>(a, s.vals[k], 0, end_from(0), acc, s.part);
+      if (g == 0) store_partial<L, Q>(a, partial_row(a, j, 0), lane, acc);
+    }
+  }
+  for (uint32_t m = s.flagged[k]; m != 0; m &= m - 1) {
+    const int r = __ffs((int)m) - 1;
+    const int start = s.last[k][r];
+    const uint32_t key = kk[start];
+    int end = end_from(r + 2);  // the run holds range r + 2's first position
+    const bool leaves = end == len && more && kk[len] == key;
+    const bool split = leaves && s.far_after[k] == key;
+    const uint32_t slot = s.slot[k][r];
+    uint2 tw[Q];   // SignSGD: the run's bf16 table row
+    f32x4 tg[Q];   // dense: the run's fp32 gradient table row
+    if (!split && g == 0) {
+      if constexpr (OUT == kOutSignSGD)
+        load_quads<L, Q, EXACT>(a.table, table_row(a, key), a.quads, lane, tw);
+      if constexpr (OUT == kOutDense && Q == 1)
+        load_grad_row<L, Q, EXACT>(a, table_row(a, key), lane, tg);
+    }
+    if (leaves && !split) end = len + next_chunk_end<L>(a, j, k, cnt, key, s);
+    // (offsets past len index LDS row k + 1: the next chunk's indices)
+    block_sum_lds<L, Q, EXACT, NT>(a, s.vals[k], start, end, acc, s.part);
+    if (g == 0) {
+      if (split)
+        store_partial<L, Q>(a, partial_row(a, j, 1), lane, acc);
+      else
+        emit_row<L, Q, OUT>(key, slot, a, lane, acc, tw, tg);
+    }
+    if (split) owner = slot + 1;
+  }
+  if (threadIdx.x == 0) a.chunk_owner[j] = owner;
+}
+
+// Long runs (hot rows, longer than a range), chunk by chunk.  Long block l
+// of nlong takes a contiguous share of the chunks, kGroupChunks at a time.
+template <int L, int Q, int OUT, bool EXACT, bool NT>
+__device__ __forceinline__ void long_chunks(const WalkArgs &a, int64_t l, int64_t nlong) {
+  static_assert(kChunkRanges == 32 && kWalkThreads % 64 == 0,
+                "a chunk's ranges are one half of a wavefront");
+  __shared__ LongLds<L> s;
+  const int64_t per = (a.num_chunks + nlong - 1) / nlong;
+  const int64_t first = l * per, last = min(first + per, a.num_chunks);
+  for (int64_t j0 = first; j0 < last; j0 += kGroupChunks) {
+    const int cnt = (int)min((int64_t)kGroupChunks, last - j0);
+    load_group<L>(a, j0, cnt, s);
+#pragma unroll 1
+    for (int k = 0; k < cnt; ++k) long_chunk<L, Q, OUT, EXACT, NT>(a, j0 + k, k, cnt, s);
+    __syncthreads();  // the group's LDS is rewritten next
+  }
+}
+
+// Whether the workspace holds a complete plan of these n and table_rows,
+// none of whose waits expired.  If not, nothing is written, and with
+// `report` block 0 says so (U = 0 for the row-sparse output, and the mark in
+// the error counter; the apply's second launch leaves that to the first).
+template <int OUT>
+__device__ __forceinline__ bool plan_ok(const WalkArgs &a, bool report) {
   const PlanScalars *pl = a.plan;
   const bool stalled = pl->stalled != 0;
-  if (stalled || pl->n != (uint64_t)a.n || pl->table_rows != (uint64_t)a.sentinel) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) {
-      if (OUT == kOutSparse) *a.num_unique = 0;
-      add_mark(a.err, stalled ? kStallMark : kNoPlanMark);
-    }
+  if (!stalled && pl->n == (uint64_t)a.n && pl->table_rows == (uint64_t)a.sentinel) return true;
+  if (report && blockIdx.x == 0 && threadIdx.x == 0) {
+    if (OUT == kOutSparse) *a.num_unique = 0;
+    add_mark(a.err, stalled ? kStallMark : kNoPlanMark);
+  }
+  return false;
+}
+
+// The apply kernel: blocks [0, long_blocks) sum the long runs chunk by chunk
+// (first, so that no long run is left for the end of the launch), the rest
+// are range walkers, kWalkThreads / L walkers per block.
+template <int L, int Q, int OUT, bool EXACT, bool NT>
+__global__ __launch_bounds__(kWalkThreads) void segment_reduce_kernel(const WalkArgs a) {
+  if (!plan_ok<OUT>(a, true)) return;
+  if (OUT == kOutSparse && blockIdx.x == 0 && threadIdx.x == 0)
+    *a.num_unique = (int64_t)a.plan->unique;
+  if (blockIdx.x < a.long_blocks) {
+    long_chunks<L, Q, OUT, EXACT, NT>(a, blockIdx.x, a.long_blocks);
     return;
   }
-  if (OUT == kOutSparse && blockIdx.x == 0 && threadIdx.x == 0) *a.num_unique = (int64_t)pl->unique;
-  if (blockIdx.x < a.long_blocks) {
-    long_runs<L, Q, OUT, EXACT, NT>(a);
-  } else {
-    // Walker blocks take their ranges stripe by stripe: the GPU hands
-    // consecutive blocks to its kXcds XCDs in turn, so the blocks of stripe
-    // blk % kXcds all run on one XCD, which then walks one contiguous part
-    // of the sorted order (the keys at its range boundaries and the runs
-    // that cross into the next range stay in that XCD's L2).  The blocks
-    // past the last whole stripe keep their order.
-    const int64_t nb = (int64_t)gridDim.x - a.long_blocks;
-    const int64_t blk = (int64_t)blockIdx.x - a.long_blocks;
-    const int64_t full = nb / kXcds * kXcds;
-    walk_range<L, Q, OUT, EXACT, NT>(a, blk < full ? blk % kXcds * (nb / kXcds) + blk / kXcds
-                                                   : blk);
+  // Walker blocks take their ranges stripe by stripe: the GPU hands
+  // consecutive blocks to its kXcds XCDs in turn, so the blocks of stripe
+  // blk % kXcds all run on one XCD, which then walks one contiguous part of
+  // the sorted order (the keys at its range boundaries and the runs that
+  // cross into the next range stay in that XCD's L2).  The blocks past the
+  // last whole stripe keep their order.
+  const int64_t nb = (int64_t)gridDim.x - a.long_blocks;
+  const int64_t blk = (int64_t)blockIdx.x - a.long_blocks;
+  const int64_t full = nb / kXcds * kXcds;
+  walk_range<L, Q, OUT, EXACT, NT>(a, blk < full ? blk % kXcds * (nb / kXcds) + blk / kXcds
+                                                 : blk);
+}
+
+// The apply's second launch: the long runs that cross chunks.  The run
+// leaving chunk j (chunk_owner[j] = its slot + 1) is the sum, in chunk order,
+// of chunk j's side-1 row and the side-0 rows of the chunks it enters, found
+// from the first key of each later chunk.  Block b looks after chunks b,
+// b + gridDim.x, ...: its threads read kWalkThreads of their owners at once
+// and list the non-zero ones, which the block then finishes one by one.
+// Walker g adds rows g, g + G, ... of a run and walker 0 adds the walkers'
+// sums in walker order, so the order of the additions is fixed.
+template <int L, int Q, int OUT, bool EXACT>
+__global__ __launch_bounds__(kWalkThreads) void combine_kernel(const WalkArgs a) {
+  constexpr int G = kWalkThreads / L;
+  __shared__ double s_part[kWalkThreads / L][L * 4];
+  __shared__ unsigned long long s_last;
+  __shared__ uint32_t s_list[kWalkThreads];
+  __shared__ uint32_t s_count;
+  if (!plan_ok<OUT>(a, false)) return;
+  const int lane = threadIdx.x % L, g = threadIdx.x / L, tid = threadIdx.x;
+  const int64_t stride = gridDim.x;
+  for (int64_t j0 = blockIdx.x; j0 < a.num_chunks; j0 += stride * kWalkThreads) {
+    if (tid == 0) s_count = 0;
+    __syncthreads();
+    {
+      const int64_t j = j0 + tid * stride;
+      if (j < a.num_chunks && a.chunk_owner[j] != 0) s_list[atomicAdd(&s_count, 1u)] = (uint32_t)tid;
+    }
+    __syncthreads();
+    const uint32_t count = s_count;
+#pragma unroll 1
+    for (uint32_t i0 = 0; i0 < count; ++i0) {
+      const int64_t j = j0 + (int64_t)s_list[i0] * stride;
+      const uint32_t owner = a.chunk_owner[j];
+      if (owner > (uint32_t)a.n || (j + 1) * kChunk >= a.n) {  // not from a plan of these ids
+        if (tid == 0) add_mark(a.err, kNoPlanMark);
+        continue;
+      }
+      const uint32_t key = a.keys[(j + 1) * kChunk - 1];
+      uint2 tw[Q];   // SignSGD: the run's bf16 table row
+      f32x4 tg[Q];   // dense: the run's fp32 gradient table row
+      if (g == 0) {  // read while the chunks are found and summed
+        if constexpr (OUT == kOutSignSGD)
+          load_quads<L, Q, EXACT>(a.table, table_row(a, key), a.quads, lane, tw);
+        if constexpr (OUT == kOutDense && Q == 1)
+          load_grad_row<L, Q, EXACT>(a, table_row(a, key), lane, tg);
+      }
+      // the last chunk the run enters: the chunks after j whose first key is
+      // the run's, kWalkThreads at a time
+      if (tid == 0) s_last = (unsigned long long)(j + 1);
+      __syncthreads();
+      for (int64_t base = j + 1;; base += kWalkThreads) {
+        const int64_t jj = base + tid;
+        const bool in = jj < a.num_chunks && a.keys[jj * kChunk] == key;
+        if (in) atomicMax(&s_last, (unsigned long long)jj);
+        // the run is contiguous: it goes on past this batch only if the
+        // batch's last chunk is in it
+        if (!__syncthreads_or(in && tid == kWalkThreads - 1)) break;
+      }
+      const int64_t jl = (int64_t)s_last;
+      double acc[Q][4];
+      zero_acc<Q>(acc);
+      // rows in order: chunk j side 1, then chunks j + 1 .. jl side 0
+#pragma unroll 1
+      for (int64_t i = g; i <= jl - j; i += G) {
+        const f64x2 *row = partial_row(a, j + i, i == 0 ? 1 : 0);
+#pragma unroll
+        for (int k = 0; k < Q; ++k) {
+          const int64_t qd = lane + (int64_t)k * L;
+          if (qd >= a.quads) continue;
+          const f64x2 lo = row[2 * qd], hi = row[2 * qd + 1];
+          acc[k][0] += lo.x;
+          acc[k][1] += lo.y;
+          acc[k][2] += hi.x;
+          acc[k][3] += hi.y;
+        }
+      }
+      block_combine<L, Q>(acc, s_part);  // (its barriers also settle s_last's reads)
+      if (g == 0) emit_row<L, Q, OUT>(key, owner - 1, a, lane, acc, tw, tg);
+    }
+    __syncthreads();  // s_list and s_count are rewritten next
   }
 }
 
 template <int L, int Q, int OUT>
-void launch_walkers(const WalkArgs &a, hipStream_t s) {
-  const int64_t threads = a.num_ranges * L;
-  const unsigned blocks =
-      a.long_blocks + (unsigned)((threads + kWalkThreads - 1) / kWalkThreads);
+void launch_walkers(WalkArgs a, hipStream_t s) {
+  const int64_t walker_blocks = (a.num_ranges * L + kWalkThreads - 1) / kWalkThreads;
+  // long blocks: about two chunks each, at most kLongBlocks
+  const int64_t nlong = (a.num_chunks + 1) / 2;
+  a.long_blocks = (uint32_t)(nlong < kLongBlocks ? nlong : kLongBlocks);
+  const unsigned blocks = (unsigned)(a.long_blocks + walker_blocks);
   const bool exact = a.quads == (int64_t)Q * L;
   if (exact && a.stream_grads)
     hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, true, true>), dim3(blocks),
@@ -561,6 +828,14 @@ void launch_walkers(const WalkArgs &a, hipStream_t s) {
   else
     hipLaunchKernelGGL((segment_reduce_kernel<L, Q, OUT, false, false>), dim3(blocks),
                        dim3(kWalkThreads), 0, s, a);
+  // the long runs that cross chunks: usually none, or a handful
+  const unsigned cblocks = (unsigned)(a.num_chunks < kCombineBlocks ? a.num_chunks : kCombineBlocks);
+  if (exact)
+    hipLaunchKernelGGL((combine_kernel<L, Q, OUT, true>), dim3(cblocks), dim3(kWalkThreads), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((combine_kernel<L, Q, OUT, false>), dim3(cblocks), dim3(kWalkThreads), 0,
+                       s, a);
 }
 
 // One quad (4 values) per lane: a walker is quads lanes wide, up to a whole

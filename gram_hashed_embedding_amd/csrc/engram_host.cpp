@@ -91,6 +91,12 @@ bool make_plan(int64_t n, int64_t table_rows, int64_t dim, Plan *p) {
   p->status = take((size_t)p->status_words * 8);
   p->counters = take(kSortCounters * 4);
   p->head_off = take((size_t)p->num_ranges * 4);
+  // per chunk of the sorted order: the slot of a long run that leaves it for
+  // the next chunk (+1; 0 when none), and two fp64 partial-sum rows (the
+  // long run that enters it, the long run that leaves it)
+  p->num_chunks = (n + kChunk - 1) / kChunk;
+  p->chunk_owner = take((size_t)p->num_chunks * 4);
+  p->partials = take((size_t)p->num_chunks * 2 * (size_t)dim * 8);
   p->total = off;
   return true;
 }

@@ -84,12 +84,22 @@ constexpr int kSlotTicketAt = 4;
 constexpr int kHistSets = kHistCopies > ENGRAM_MAX_HEADS ? kHistCopies : ENGRAM_MAX_HEADS;
 constexpr int kSortCounters = kTicketWords + kHistSets * 4 * kMaxBins;
 
+// Long runs: a distinct row whose run of sorted positions starts in one
+// 16-position range, covers the whole next range and reaches the one after
+// (the runs a range walker leaves out).  The apply sums them chunk by chunk
+// (kChunk sorted positions each, aligned), in parallel; a run that crosses
+// chunks leaves one fp64 partial-sum row in each chunk it touches, which the
+// apply's second launch adds up in chunk order.
+constexpr int64_t kChunk = 512;
+
 // Where the parts of the sorted path's workspace start (bytes, 256-aligned).
 struct Plan {
   int64_t num_tiles, num_ranges, slot_tiles;
   int bits, passes, per_pass;
   int64_t status_words;  // look-back words the workspace holds
-  size_t keys_a, vals_a, keys_b, vals_b, status, counters, head_off, scalars, total;
+  int64_t num_chunks;    // kChunk-position chunks of the sorted order
+  size_t keys_a, vals_a, keys_b, vals_b, status, counters, head_off, scalars, chunk_owner,
+      partials, total;
 };
 
 // The plan's scalars at Plan::scalars (the start of the workspace): written

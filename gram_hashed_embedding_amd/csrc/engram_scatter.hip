@@ -108,12 +108,10 @@ int engram::launch_apply(const void *grads, int64_t n, int64_t dim, int64_t tabl
   a.unique_grads = o.unique_grads;
   a.table = static_cast<uint2 *>(o.table);
   a.lr = o.lr;
-  // long-run blocks: at most kLongBlocks, each looking after at least
-  // kLongSpan ranges (a long run spans 3 ranges or more)
-  int64_t lb = p.num_ranges >= 3 ? (p.num_ranges + kLongSpan - 1) / kLongSpan : 0;
-  lb = lb < kLongBlocks ? lb : kLongBlocks;
-  a.long_blocks = (uint32_t)lb;
-  a.long_span = lb > 0 ? (p.num_ranges + lb - 1) / lb : 0;
+  a.chunk_owner = v.chunk_owner;
+  a.partials = v.partials;
+  a.num_chunks = p.num_chunks;
+  a.long_blocks = 0;  // set with the grid
   a.plan = v.scalars;
   a.num_unique = o.num_unique;
   a.err = err;

@@ -21,6 +21,8 @@ struct Views {
   uint64_t *status;
   uint32_t *counters, *head_off;
   PlanScalars *scalars;
+  uint32_t *chunk_owner;  // the apply's: long runs that leave each chunk
+  double *partials;       // the apply's: partial-sum rows of long runs
   const uint32_t *sorted_keys, *sorted_vals;  // where the last sort pass leaves them
 };
 
@@ -35,6 +37,8 @@ inline Views views_of(const Plan &p, void *ws) {
   v.counters = reinterpret_cast<uint32_t *>(base + p.counters);
   v.head_off = reinterpret_cast<uint32_t *>(base + p.head_off);
   v.scalars = reinterpret_cast<PlanScalars *>(base + p.scalars);
+  v.chunk_owner = reinterpret_cast<uint32_t *>(base + p.chunk_owner);
+  v.partials = reinterpret_cast<double *>(base + p.partials);
   // passes alternate a -> b -> a ...: an odd pass count ends in a
   v.sorted_keys = (p.passes % 2 == 1) ? v.keys_a : v.keys_b;
   v.sorted_vals = (p.passes % 2 == 1) ? v.vals_a : v.vals_b;

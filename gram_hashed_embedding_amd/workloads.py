@@ -31,6 +31,9 @@ import numpy as np
 
 VOCAB = 151936
 EOS_ID = 0
+# the pad token of the pad-tail workload: the last id of the vocabulary (the
+# rarest Zipf rank, so real tokens almost never equal it)
+PAD_ID = VOCAB - 1
 
 # Constants printed on the NeMo AutoModel API page
 # "nemo_automodel.components.models.qwen3_8_flash_next.engram", section Data.
@@ -154,6 +157,29 @@ def packed_documents(rng, batch, seq, zipf_s, mean_len=2048.0, sigma=1.0,
     return tokens, seg
 
 
+def packed_with_pad_tail(rng, batch, seq, zipf_s, mean_len=2048.0, sigma=1.0,
+                         eos_id=EOS_ID, pad_id=PAD_ID):
+    """Rows of packed documents as packed_documents draws them, except that a
+    row holds only whole documents: the rest of the row after the last one
+    that fits is padding, pad_id tokens in a segment of their own.  Returns
+    (tokens, segment ids)."""
+    tokens = zipf_tokens(rng, (batch, seq), zipf_s)
+    seg = np.empty((batch, seq), dtype=np.int64)
+    mu = math.log(mean_len) - 0.5 * sigma * sigma
+    for b in range(batch):
+        pos, doc = 0, 0
+        while True:
+            length = max(1, int(round(rng.lognormal(mu, sigma))))
+            if pos + length > seq:
+                break
+            seg[b, pos:pos + length] = doc
+            tokens[b, pos + length - 1] = eos_id
+            pos, doc = pos + length, doc + 1
+        tokens[b, pos:] = pad_id
+        seg[b, pos:] = doc
+    return tokens, seg
+
+
 def random_segments(shape, mean_length, seed):
     """Packed segment ids: each position starts a new segment with
     probability 1/mean_length (ids are running counts along each row)."""
@@ -176,7 +202,7 @@ class Workload:
     table_rows: int
     dim: int
     seed: int
-    token_kind: str            # "uniform" | "zipf" | "packed"
+    token_kind: str            # "uniform" | "zipf" | "packed" | "packed_pad"
     token_lo: int = 0
     token_hi: int = VOCAB
     zipf_s: float = 1.1
@@ -216,6 +242,8 @@ class Workload:
             tok = zipf_tokens(rng, shape, self.zipf_s)
         elif self.token_kind == "packed":
             tok, seg = packed_documents(rng, self.batch, self.seq, self.zipf_s)
+        elif self.token_kind == "packed_pad":
+            tok, seg = packed_with_pad_tail(rng, self.batch, self.seq, self.zipf_s)
         else:
             raise ValueError(self.token_kind)
         if self.eos_prob > 0:
@@ -265,8 +293,18 @@ def e2e() -> Workload:
                     "zipf", zipf_s=1.1, eos_prob=1 / 4096, grads="rowsparse")
 
 
+def e2e_padtail() -> Workload:
+    """The e2e shape with packs that end in a pad-token tail of their own
+    segment (the layer gives the tail padding its own sequence id): every
+    head then hashes the tail's tokens into one row, runs of thousands of
+    terms."""
+    primes = tuple(primes_at_most(8_333_333, 24))
+    return Workload("e2e_padtail", 8, 8192, 4, 8, primes, 200_000_000, 256, 1006,
+                    "packed_pad", zipf_s=1.1, grads="rowsparse")
+
+
 WORKLOADS = {"tiny": tiny, "medium": medium, "full": full,
-             "backward": backward, "e2e": e2e}
+             "backward": backward, "e2e": e2e, "e2e_padtail": e2e_padtail}
 
 
 def get(name: str) -> Workload:

@@ -79,7 +79,7 @@ extern "C" {
 #define ENGRAM_ERR_NO_PLAN ((int64_t)1 << 41)
 
 /* Bytes of the fixed device array engram_scatter_add_rowsparse_noalloc uses. */
-#define ENGRAM_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+#define ENGRAM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
 
 /* Human-readable text of a status code (static storage). */
 const char *engram_status_string(int status);
@@ -344,7 +344,7 @@ int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
  * The call allocates nothing.
  *   Size limit: n ids fit when engram_scatter_add_workspace(n, table_rows,
  *   head_dim, ENGRAM_SCATTER_ROWSPARSE) <= ENGRAM_NOALLOC_SCRATCH_BYTES
- *   (about 1.9M ids of a 200M-row table); larger inputs return
+ *   (about 2M ids of a 200M-row table at head_dim 256); larger inputs return
  *   ENGRAM_EWORKSPACE before anything is enqueued.
  *   Every call on a device uses that device's one array, which keeps the last
  *   call's contents (each call clears what it needs cleared): calls that

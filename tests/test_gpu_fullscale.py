@@ -140,3 +140,85 @@ def test_e2e_forward_backward(oracle):
     assert not np.array_equal(want_rows, before)
     del grads, table, ws
     release()
+
+
+def test_e2e_pad_tail_backward(oracle):
+    """The e2e shape on packs whose row tails are pad tokens in a segment of
+    their own: every head hashes the tail into one row, runs of thousands of
+    terms that the apply sums in chunks of 512 sorted positions.  The fused forward's ids, the plan
+    made from the tokens and its row-sparse apply, and the SignSGD apply, all
+    at full size against the oracle (the backward in full)."""
+    wl = workloads.e2e_padtail()
+    mult = wl.multipliers()
+    tok, seg = wl.tokens(0, with_segments=True)
+    args = (wl.ngram_size, wl.heads_per_ngram, wl.eos_id, mult, wl.primes, wl.offsets)
+    want_rows = oracle.hash(tok, *args, seg)
+    flat = want_rows.reshape(-1)
+    counts = np.unique(flat, return_counts=True)[1]
+    assert counts.max() > 4 * 512      # the tail's rows cross several chunks each
+    table = workloads.make_table(wl.table_rows, wl.dim, wl.seed, "cuda")
+    ids = torch.empty((tok.shape[0], tok.shape[1], wl.heads), dtype=torch.int64, device="cuda")
+    out = E.engram_lookup(dev(tok), table, *args, seq_ids=dev(seg), row_ids=ids)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), want_rows)
+    sampled_gather_check(oracle, want_rows, out, table, wl.seed)
+    del out, ids
+    release()
+    grads = workloads.make_grads(wl.lookups, wl.dim, wl.seed + 2, "cuda")
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = E.engram_scatter_plan_tokens(dev(tok), wl.table_rows, wl.dim, *args, seq_ids=dev(seg),
+                                      err_count=err)
+    uid, uval, cnt = E.engram_scatter_apply(grads, ws, wl.table_rows, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    want_uid, want_val, bad = oracle.scatter_add_rowsparse(flat, bits(grads), wl.dim,
+                                                           wl.table_rows)
+    u = int(cnt.item())
+    assert bad == 0 and u == want_uid.size
+    assert np.array_equal(uid[:u].cpu().numpy(), want_uid)
+    assert np.array_equal(host_f32(uval[:u]).view(np.uint32), want_val.view(np.uint32))
+    del uid, uval
+    # the same plan fused with one SignSGD step: every touched row
+    lr = 2.0 ** -6
+    touched = dev(want_uid)
+    before = bits(table.index_select(0, touched))
+    want_t, bad = oracle.signsgd_rowsparse(np.arange(u, dtype=np.int64), want_val, before, lr)
+    E.engram_scatter_apply_signsgd(grads, ws, table, lr, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(bits(table.index_select(0, touched)), want_t)
+    del grads, table, ws
+    release()
+
+
+def test_many_chunk_crossing_runs(oracle):
+    """48,000 long runs, each crossing a boundary of the apply's 512-position
+    chunks, over more chunks (about 66,000) than the apply's second launch
+    reads in one round: every distinct row id in full, and the sums of a
+    sample of rows against the oracle (a row's sum depends on its own
+    positions only, so the oracle sums just those)."""
+    rng = np.random.Generator(np.random.PCG64(4242))
+    rows, dim, n_runs = 1 << 24, 8, 48_000
+    lens = rng.integers(520, 900, size=n_runs)
+    keys = rng.permutation(rows)[:n_runs].astype(np.int64)
+    ids = rng.permutation(np.repeat(keys, lens))
+    assert ids.size > 256 * 256 * 512
+    grads = workloads.make_grads(ids.size, dim, 4243, "cuda")
+    err = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = E.engram_scatter_plan(dev(ids), rows, dim, err_count=err)
+    uid, uval, cnt = E.engram_scatter_apply(grads, ws, rows, err_count=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    want_uid = np.sort(keys)
+    u = int(cnt.item())
+    assert u == n_runs
+    assert np.array_equal(uid[:u].cpu().numpy(), want_uid)
+    picked = np.sort(rng.choice(want_uid, 512, replace=False))
+    where = np.nonzero(np.isin(ids, picked))[0]
+    sub_grads = bits(grads.index_select(0, dev(where.astype(np.int64))))
+    w_uid, w_val, bad = oracle.scatter_add_rowsparse(ids[where], sub_grads, dim, rows)
+    assert bad == 0 and np.array_equal(w_uid, picked)
+    got = host_f32(uval.index_select(0, dev(np.searchsorted(want_uid, picked).astype(np.int64))))
+    assert np.array_equal(got.view(np.uint32), w_val.view(np.uint32))
+    del grads, ws, uid, uval
+    release()

@@ -129,7 +129,8 @@ def test_dims(oracle, dim):
 
 @pytest.mark.parametrize("pattern", ["one_row", "two_rows", "runs_at_range_edges",
                                      "sorted_runs", "all_distinct", "max_key",
-                                     "every_length_sorted", "every_length_shuffled"])
+                                     "every_length_sorted", "every_length_shuffled",
+                                     "chunk_edges", "chunk_crossing"])
 def test_run_structure(oracle, pattern):
     """Runs longer than a walker range, runs ending exactly on range edges,
     a single hot row spanning thousands of ranges."""
@@ -148,6 +149,19 @@ def test_run_structure(oracle, pattern):
         ids = np.repeat(np.sort(rng.permutation(rows)[:600]), lens).astype(np.int64)
     elif pattern == "all_distinct":
         ids = rng.permutation(rows)[:70_000].astype(np.int64)
+    elif pattern == "chunk_edges":
+        # long runs of one chunk, just over one, and of many (a chunk of the
+        # apply is 512 sorted positions), among short ones
+        lens = np.concatenate([[511, 512, 513, 1023, 1024, 1025, 1536, 2049, 5000, 18, 17, 33],
+                               rng.integers(1, 40, size=400)])
+        ids = np.repeat(rng.permutation(rows)[:lens.size], lens).astype(np.int64)
+        ids = rng.permutation(ids)
+    elif pattern == "chunk_crossing":
+        # hundreds of long runs, each crossing one or two chunk boundaries:
+        # several for every block of the apply's second launch
+        lens = rng.integers(513, 1100, size=700)
+        ids = np.repeat(rng.permutation(rows)[:lens.size], lens).astype(np.int64)
+        ids = rng.permutation(ids)
     elif pattern.startswith("every_length"):
         # run lengths 1..50 in every phase against the sorted-order ranges
         lens = np.tile(np.arange(1, 51), 7)
@@ -354,4 +368,38 @@ def test_sort_tile_sizes(oracle, tiles, extra):
     ids[pick] = hot[rng.integers(0, 4, int(pick.sum()))]
     ids[rng.random(n) < 0.01] = -1
     check_all_modes(oracle, ids, 8, rows, 700 + tiles)
+    release()
+
+
+@pytest.mark.parametrize("dim", [8, 256, 512, 2048])
+def test_long_runs_every_width(oracle, dim):
+    """Long runs inside one chunk and across many, at row widths of one to
+    eight quads per lane, in every output form."""
+    rng = np.random.Generator(np.random.PCG64(dim))
+    rows = 70_000
+    lens = np.concatenate([[3000, 1025, 600, 512, 100, 40, 18], rng.integers(1, 30, size=300)])
+    ids = np.repeat(rng.permutation(rows)[:lens.size], lens).astype(np.int64)
+    ids = rng.permutation(ids)
+    check_all_modes(oracle, ids, dim, rows, 700 + dim)
+
+
+def test_apply_again_on_one_plan_with_chunks(oracle):
+    """A plan whose long runs cross several chunks, applied three times in a
+    row (each apply rewrites the per-chunk partial sums and owners the last
+    one left): every apply equals the oracle."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows, dim = 50_000, 64
+    lens = np.concatenate([[4000, 1500, 700], rng.integers(1, 50, size=500)])
+    ids = rng.permutation(np.repeat(rng.permutation(rows)[:lens.size], lens).astype(np.int64))
+    grads = workloads.make_grads(ids.size, dim, 78, "cuda")
+    want_uid, want_val, _ = oracle.scatter_add_rowsparse(ids, bits(grads), dim, rows)
+    ws = E.engram_scatter_plan(dev(ids), rows, dim)
+    for _ in range(3):
+        err = torch.zeros(1, dtype=torch.int64, device="cuda")
+        uid, uval, cnt = E.engram_scatter_apply(grads, ws, rows, err_count=err)
+        torch.cuda.synchronize()
+        u = int(cnt.item())
+        assert int(err.item()) == 0 and u == want_uid.size
+        assert np.array_equal(uid[:u].cpu().numpy(), want_uid)
+        assert np.array_equal(host_f32(uval[:u]).view(np.uint32), want_val.view(np.uint32))
     release()
