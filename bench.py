@@ -12,7 +12,15 @@ workspaces; the apply waits for the forward and for its batch's plan.  The
 timed region holds exactly one plan, forward and apply per step (it ends
 when the plan made during the last step is done too); untimed steps run
 before it for --settle seconds (0.25 by default), then the W warm-up steps.
-A serial pass of the same calls gives the per-phase times, and the same step
+The last timed step's backward is checked bit for bit against the same
+batch planned and applied one call after another.  With --graphs the step
+is also captured once per token batch as a HIP graph and replayed (one host
+launch per step, the same kernels and the same plan beside the forward and
+apply; checked the same way) and reported as graph_ms_per_step: on MI355X
+the replays measured slower than the calls launched one by one (e2e 0.721
+against 0.692 ms, the backward workload 89 against 83 us), since a replay
+ends only when all its branches have, and the next cannot start before.  A
+serial pass of the same calls gives the per-phase times, and the same step
 with separate calls (engram_hash, then engram_scatter_plan of the ids beside
 engram_gather, then the apply) is timed beside it.
 
@@ -465,12 +473,38 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
             ph["scatter_apply"] = mean(3, 4)
         return ph, mean(0, 4 if backward else 2)
 
-    # whole-step timing (the driver's step): nothing between the calls
-    ms_per_step = timed_steps(step)
-    schedule_check = None
-    if wl.grads == "rowsparse" and not signsgd:
-        # the timed schedule's last apply against the same batch planned and
-        # applied one call after another on one stream, bit for bit
+    def capture_steps():
+        """The step as HIP graphs, one per token batch: graph k makes batch
+        k + 1's plan (into workspace (k + 1) % 2) on a branch beside batch k's
+        forward and apply (which reads workspace k % 2), joined at its end.
+        Replays on one stream run one after another, so a graph's plan never
+        overlaps the apply that last read its workspace (N_BATCHES is even:
+        the batches and the workspaces cycle together).  The launches of a
+        step then cost one graph launch on the host."""
+        assert N_BATCHES % 2 == 0
+        torch.cuda.synchronize()
+        graphs = []
+        cap = torch.cuda.Stream(dev)  # default priority
+        for k in range(N_BATCHES):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                cur = torch.cuda.current_stream(dev)
+                side.wait_stream(cur)
+                with torch.cuda.stream(side):
+                    E.engram_scatter_plan_tokens(
+                        tokens[(k + 1) % N_BATCHES], wl.table_rows, D, *hargs,
+                        seq_ids=segs[(k + 1) % N_BATCHES], workspace=wss[(k + 1) % 2],
+                        err_count=err, stream=side)
+                E.engram_lookup(tokens[k], table, *hargs, seq_ids=segs[k], out=out)
+                apply_backward(wss[k % 2])
+                cur.wait_stream(side)
+            graphs.append(g)
+        torch.cuda.synchronize()
+        return graphs
+
+    def check_last():
+        """The timed schedule's last apply against the same batch planned and
+        applied one call after another on one stream, bit for bit."""
         last = last_step["k"]
         ws_ref = torch.empty_like(ws)
         uid_ref, uval_ref = torch.empty_like(uid), torch.empty_like(uval)
@@ -486,8 +520,31 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
                 and torch.equal(uval[:u_ref].view(torch.int32),
                                 uval_ref[:u_ref].view(torch.int32))):
             raise RuntimeError("the timed schedule's backward differs from the serial calls")
-        schedule_check = "last step bit-exact against serial calls"
         del ws_ref, uid_ref, uval_ref, cnt_ref
+
+    # whole-step timing (the driver's step): nothing between the calls,
+    # launched call by call ...
+    eager_ms = timed_steps(step)
+    checkable = wl.grads == "rowsparse" and not signsgd
+    if checkable:
+        check_last()
+    # ... and, on request, as one graph replay per step
+    graph_ms = None
+    if backward and args.graphs:
+        graphs = capture_steps()
+        # batch 0's plan, before graph 0 (which plans batch 1)
+        E.engram_scatter_plan_tokens(tokens[0], wl.table_rows, D, *hargs, seq_ids=segs[0],
+                                     workspace=wss[0], err_count=err)
+        torch.cuda.synchronize()
+        graph_ms = timed_steps(lambda k: graphs[k % N_BATCHES].replay())
+        if checkable:
+            check_last()
+        del graphs
+    ms_per_step = eager_ms
+    schedule = "launched call by call"
+    schedule_check = ("last step bit-exact against serial calls"
+                      + (", also replayed as graphs" if graph_ms is not None else "")
+                      if checkable else None)
     phase_ms, serial_ms = serial_phases(False)
     # the same work with separate calls, timed in the same process
     sep_ms = timed_steps(step_separate)
@@ -623,6 +680,9 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
                       if shared_table else {}),
                    **({"segments": "packed documents; each row's tail after its last whole "
                        "document is pad tokens in a segment of their own"} if with_seg else {})},
+        "schedule": schedule,
+        "eager_ms_per_step": eager_ms,
+        "graph_ms_per_step": graph_ms,
         "serial_ms_per_step": serial_ms,
         "schedule_check": schedule_check,
         "step_algorithmic_bytes": step_bytes,
@@ -640,7 +700,8 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
 
 def sub_config(res):
     """The fields of a nested configuration's result."""
-    keep = ("metric", "value", "unit", "ms_per_step", "config", "step_algorithmic_bytes",
+    keep = ("metric", "value", "unit", "ms_per_step", "config", "schedule",
+            "eager_ms_per_step", "graph_ms_per_step", "schedule_check", "step_algorithmic_bytes",
             "step_gbps", "step_frac_of_peak", "phases", "separate_calls",
             "scatter_add_sorted_vs_atomic", "roofline", "cpu_baseline")
     return {k: res[k] for k in keep if k in res}
@@ -830,6 +891,8 @@ def main():
                     help="the e2e line alone, without the nested configurations")
     ap.add_argument("--settle", type=float, default=0.25,
                     help="seconds of untimed steps before the warm-up steps")
+    ap.add_argument("--graphs", action="store_true",
+                    help="also time the backward steps captured as HIP graphs and replayed")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "

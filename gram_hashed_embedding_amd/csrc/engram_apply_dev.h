@@ -742,16 +742,16 @@ __global__ __launch_bounds__(kWalkThreads) void combine_kernel(const WalkArgs a)
   __shared__ unsigned long long s_last;
   __shared__ uint32_t s_list[kWalkThreads];
   __shared__ uint32_t s_count;
-  if (!plan_ok<OUT>(a, false)) return;
   const int lane = threadIdx.x % L, g = threadIdx.x / L, tid = threadIdx.x;
   const int64_t stride = gridDim.x;
   for (int64_t j0 = blockIdx.x; j0 < a.num_chunks; j0 += stride * kWalkThreads) {
+    // the owners, read beside the plan's stamp (one round trip)
+    const int64_t jt = j0 + tid * stride;
+    const uint32_t own = jt < a.num_chunks ? a.chunk_owner[jt] : 0u;
+    if (j0 == blockIdx.x && !plan_ok<OUT>(a, false)) return;
     if (tid == 0) s_count = 0;
     __syncthreads();
-    {
-      const int64_t j = j0 + tid * stride;
-      if (j < a.num_chunks && a.chunk_owner[j] != 0) s_list[atomicAdd(&s_count, 1u)] = (uint32_t)tid;
-    }
+    if (own != 0) s_list[atomicAdd(&s_count, 1u)] = (uint32_t)tid;
     __syncthreads();
     const uint32_t count = s_count;
 #pragma unroll 1
@@ -786,20 +786,33 @@ __global__ __launch_bounds__(kWalkThreads) void combine_kernel(const WalkArgs a)
       const int64_t jl = (int64_t)s_last;
       double acc[Q][4];
       zero_acc<Q>(acc);
-      // rows in order: chunk j side 1, then chunks j + 1 .. jl side 0
+      // rows in order: chunk j side 1, then chunks j + 1 .. jl side 0;
+      // walker g's rows g, g + G, ..., kRows of them in flight at a time
+      constexpr int kRows = 4;
 #pragma unroll 1
-      for (int64_t i = g; i <= jl - j; i += G) {
-        const f64x2 *row = partial_row(a, j + i, i == 0 ? 1 : 0);
+      for (int64_t i0 = g; i0 <= jl - j; i0 += (int64_t)G * kRows) {
+        f64x2 lo[kRows][Q], hi[kRows][Q];
 #pragma unroll
-        for (int k = 0; k < Q; ++k) {
-          const int64_t qd = lane + (int64_t)k * L;
-          if (qd >= a.quads) continue;
-          const f64x2 lo = row[2 * qd], hi = row[2 * qd + 1];
-          acc[k][0] += lo.x;
-          acc[k][1] += lo.y;
-          acc[k][2] += hi.x;
-          acc[k][3] += hi.y;
+        for (int u = 0; u < kRows; ++u) {
+          const int64_t i = i0 + (int64_t)u * G;
+          const f64x2 *row = partial_row(a, j + (i <= jl - j ? i : 0), i == 0 ? 1 : 0);
+#pragma unroll
+          for (int k = 0; k < Q; ++k) {
+            const int64_t qd = lane + (int64_t)k * L;
+            const bool ok = i <= jl - j && (EXACT || qd < a.quads);
+            lo[u][k] = ok ? row[2 * qd] : f64x2{0.0, 0.0};
+            hi[u][k] = ok ? row[2 * qd + 1] : f64x2{0.0, 0.0};
+          }
         }
+#pragma unroll
+        for (int u = 0; u < kRows; ++u)
+#pragma unroll
+          for (int k = 0; k < Q; ++k) {
+            acc[k][0] += lo[u][k].x;
+            acc[k][1] += lo[u][k].y;
+            acc[k][2] += hi[u][k].x;
+            acc[k][3] += hi[u][k].y;
+          }
       }
       block_combine<L, Q>(acc, s_part);  // (its barriers also settle s_last's reads)
       if (g == 0) emit_row<L, Q, OUT>(key, owner - 1, a, lane, acc, tw, tg);
