@@ -119,14 +119,6 @@ def algorithmic_bytes(wl, unique_rows, separate=False):
     return out
 
 
-# The sources whose code a kernel of the hot path is built from: the
-# kernel's own file and the device headers it includes.
-KERNEL_HEADERS = ("gram_hashed_embedding_amd/csrc/engram_internal.h",
-                  "gram_hashed_embedding_amd/csrc/engram_hash_dev.h",
-                  "gram_hashed_embedding_amd/csrc/engram_host.h",
-                  "gram_hashed_embedding_amd/csrc/engram_scatter_dev.h")
-
-
 def code_digest(paths):
     """sha256 of the code in `paths` (repository-relative) with comments and
     whitespace removed, so that edits to comments alone keep it."""
@@ -154,7 +146,7 @@ def measured_traffic(call, wl):
     if rec is None or key not in rec["kernels"]:
         return None
     k = rec["kernels"][key]
-    if code_digest([k["source"], *KERNEL_HEADERS]) != k.get("code_sha256"):
+    if code_digest(k["code_files"]) != k.get("code_sha256"):
         return None
     return k["fetch_bytes"] + k["write_bytes"]
 
