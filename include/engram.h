@@ -237,9 +237,11 @@ size_t engram_scatter_add_workspace(int64_t n, int64_t table_rows,
  *     and S_r then the same as a sum in any other order, as long as the bits
  *     of a row's terms and partial sums span at most 53 places (bf16 terms
  *     within a factor of about 2^45 of each other, e.g. every N(0, 1)
- *     gradient); past that the kernels' addition order (a fixed tree, not
- *     ascending flat index) can round differently, in the last bits of an
- *     fp64 sum that is then rounded to fp32.
+ *     gradient); past that a row of many terms, which the kernels sum in
+ *     interleaved 16-term pieces combined in a fixed order (a short row is
+ *     summed in ascending flat index), can round differently from a
+ *     sequential sum, in the last bits of an fp64 sum that is then rounded
+ *     to fp32; the result is still the same run to run.
  *   mode ENGRAM_SCATTER_ATOMIC: every gradient element is added to the
  *     table with an fp32 atomic add; the order of additions is not fixed.
  *     Needs no workspace.
