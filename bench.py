@@ -12,8 +12,12 @@ workspaces; the apply waits for the forward and for its batch's plan.  The
 timed region holds exactly one plan, forward and apply per step (it ends
 when the plan made during the last step is done too); untimed steps run
 before it for --settle seconds (0.25 by default), then the W warm-up steps.
-The last timed step's backward is checked bit for bit against the same
-batch planned and applied one call after another.  With --graphs the step
+A step with a backward is timed twice: each step's calls and events
+enqueued by one native call (engram_run_ops, the binding's Schedule, built
+once per token batch), which is the line's time, and the same calls made
+one by one through the binding (eager_ms_per_step).  The last timed step's
+backward is checked bit for bit against the same batch planned and applied
+one call after another, in both.  With --graphs the step
 is also captured once per token batch as a HIP graph and replayed (one host
 launch per step, the same kernels and the same plan beside the forward and
 apply; checked the same way) and reported as graph_ms_per_step: on MI355X
@@ -369,6 +373,43 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         apply_backward(wss[k % 2])
         ev_apply[k % 2].record(stream)
 
+    scheds = None
+
+    def build_schedules():
+        """The step of each token batch as one engram_run_ops schedule: the
+        same calls and events as step() (the next batch's plan on the side
+        stream after the apply that last read its workspace; the fused
+        forward; the apply after this batch's plan), enqueued by one native
+        call instead of one binding call and one torch event call each."""
+        out_ = []
+        for k in range(N_BATCHES):
+            nk = (k + 1) % N_BATCHES
+            sc = E.Schedule()
+            sc.wait(ev_apply[nk % 2], stream=side)
+            sc.plan_tokens(tokens[nk], wl.table_rows, D, *hargs, seq_ids=segs[nk],
+                           workspace=wss[nk % 2], err_count=err, stream=side)
+            sc.record(ev_plan[nk % 2], stream=side)
+            sc.lookup(tokens[k], table, *hargs, seq_ids=segs[k], out=out, stream=stream)
+            sc.wait(ev_plan[k % 2], stream=stream)
+            if signsgd:
+                sc.apply_signsgd(grads, wss[k % 2], table, lr, err_count=err, stream=stream)
+            elif wl.grads == "rowsparse":
+                sc.apply(grads, wss[k % 2], wl.table_rows, unique_ids=uid, unique_grads=uval,
+                         num_unique=count, err_count=err, stream=stream)
+            else:
+                sc.apply(grads, wss[k % 2], wl.table_rows, grad_table=gtab, err_count=err,
+                         stream=stream)
+            sc.record(ev_apply[k % 2], stream=stream)
+            out_.append(sc)
+        return out_
+
+    def step_scheduled(k):
+        """step(k), enqueued as the prebuilt schedule of its token batch."""
+        if planned["next"] != k:  # the first step: nothing planned yet
+            plan_ahead(k)
+        scheds[k % N_BATCHES].run()
+        planned["next"] = k + 1
+
     def step_separate(k):
         """The same step with separate calls (hash, then the plan of the ids
         beside the gather), for comparison."""
@@ -443,7 +484,7 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         for k in range(k, k + args.steps):
             fn(k)
         last_step["k"] = k
-        if fn is step and backward:
+        if fn in (step, step_scheduled) and backward:
             # the plan made during the last step (the next batch's) is part
             # of the timed work: the stop mark waits for it too
             stream.wait_event(ev_plan[planned["next"] % 2])
@@ -515,11 +556,20 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         del ws_ref, uid_ref, uval_ref, cnt_ref
 
     # whole-step timing (the driver's step): nothing between the calls,
-    # launched call by call ...
+    # launched call by call through the binding ...
     eager_ms = timed_steps(step)
     checkable = wl.grads == "rowsparse" and not signsgd
     if checkable:
         check_last()
+    # ... and each step enqueued by one native call (engram_run_ops)
+    sched_ms = None
+    if backward:
+        scheds = build_schedules()
+        planned["next"] = None
+        torch.cuda.synchronize()
+        sched_ms = timed_steps(step_scheduled)
+        if checkable:
+            check_last()
     # ... and, on request, as one graph replay per step
     graph_ms = None
     if backward and args.graphs:
@@ -532,11 +582,12 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         if checkable:
             check_last()
         del graphs
-    ms_per_step = eager_ms
-    schedule = "launched call by call"
-    schedule_check = ("last step bit-exact against serial calls"
-                      + (", also replayed as graphs" if graph_ms is not None else "")
-                      if checkable else None)
+    ms_per_step = sched_ms if sched_ms is not None else eager_ms
+    schedule = ("each step's calls and events enqueued by one engram_run_ops call"
+                if sched_ms is not None else "launched call by call")
+    schedule_check = ("last step bit-exact against serial calls, in the scheduled and the "
+                      "call-by-call runs" + (", and replayed as graphs" if graph_ms is not None
+                                             else "") if checkable else None)
     phase_ms, serial_ms = serial_phases(False)
     # the same work with separate calls, timed in the same process
     sep_ms = timed_steps(step_separate)
@@ -674,6 +725,7 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
                        "document is pad tokens in a segment of their own"} if with_seg else {})},
         "schedule": schedule,
         "eager_ms_per_step": eager_ms,
+        "scheduled_ms_per_step": sched_ms,
         "graph_ms_per_step": graph_ms,
         "serial_ms_per_step": serial_ms,
         "schedule_check": schedule_check,
@@ -693,7 +745,8 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
 def sub_config(res):
     """The fields of a nested configuration's result."""
     keep = ("metric", "value", "unit", "ms_per_step", "config", "schedule",
-            "eager_ms_per_step", "graph_ms_per_step", "schedule_check", "step_algorithmic_bytes",
+            "eager_ms_per_step", "scheduled_ms_per_step", "graph_ms_per_step", "schedule_check",
+            "step_algorithmic_bytes",
             "step_gbps", "step_frac_of_peak", "phases", "separate_calls",
             "scatter_add_sorted_vs_atomic", "roofline", "cpu_baseline")
     return {k: res[k] for k in keep if k in res}

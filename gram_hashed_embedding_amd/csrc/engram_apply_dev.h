@@ -25,11 +25,12 @@
 // range's end but ending in the next range is finished by the same walker.
 // Runs longer than that (hot rows, found from three sorted keys per range)
 // are summed by the leading blocks of the same launch in aligned chunks of
-// kChunk sorted positions: the block of a chunk sums the part of each long
-// run that lies in it, its walkers taking interleaved ranges and adding
-// their sums in a fixed order.  A long run inside one chunk is written at
-// once; one that crosses chunks leaves an fp64 partial-sum row in each, and
-// a second launch adds those in chunk order.  No work item waits on another,
+// kChunk sorted positions: the block of a chunk sums each long run that
+// starts there, its walkers taking interleaved 16-position pieces and adding
+// their sums in a fixed order.  A long run that ends in its first chunk or
+// the next is written at once; one that spans three chunks or more leaves an
+// fp64 partial-sum row in each chunk it touches, and a second launch
+// (combine_kernel) adds those in chunk order.  No work item waits on another,
 // hot rows do not serialise a walker, and a row that holds a large share of
 // all positions (a padding row) is spread over as many blocks as it has
 // chunks.
@@ -611,7 +612,9 @@ __device__ __forceinline__ int next_chunk_end(const WalkArgs &a, int64_t j, int 
 // partial row (side 0: the run entering the chunk; side 1: the run leaving
 // it, whose slot (+1) goes to chunk_owner[j], 0 when none) for the second
 // launch.  The chunks on both sides of a boundary agree on which runs are
-// split from the keys at P0 - kChunk - 1, P1 and P0 + 2 kChunk.
+// split from the keys at P0 - kChunk - 1, P1 and P0 + 2 kChunk.  Block-uniform
+// control flow throughout (every value it branches on comes from LDS after a
+// barrier).
 template <int L, int Q, int OUT, bool EXACT, bool NT>
 __device__ __forceinline__ void long_chunk(const WalkArgs &a, int64_t j, int k, int cnt,
                                            LongLds<L> &s) {

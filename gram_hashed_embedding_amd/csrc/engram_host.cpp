@@ -452,3 +452,50 @@ extern "C" int engram_ple_conv(const void *d_x, const void *d_halo, int64_t halo
                       batch, seq, channels, kernel_size, dilation};
   return launch_ple_conv(c, stream);
 }
+
+// ------------------------------------------------------------ the executor --
+extern "C" int engram_run_ops(const engram_op *ops, int64_t count, int64_t *failed_index) {
+  if (failed_index != nullptr) *failed_index = -1;
+  if (count < 0 || (count > 0 && ops == nullptr)) return ENGRAM_EINVAL;
+  for (int64_t i = 0; i < count; ++i) {
+    const engram_op &o = ops[i];
+    int st = ENGRAM_EINVAL;
+    switch (o.op) {
+      case ENGRAM_OP_LOOKUP:
+        st = engram_lookup(o.d_tokens, o.d_seq_ids, o.batch, o.seq, o.ngram_size,
+                           o.heads_per_ngram, o.eos_id, o.h_multipliers, o.h_primes, o.h_offsets,
+                           o.d_table, o.table_rows, o.head_dim, o.d_out, o.d_row_ids, o.stream);
+        break;
+      case ENGRAM_OP_PLAN_TOKENS:
+        st = engram_scatter_plan_tokens(o.d_tokens, o.d_seq_ids, o.batch, o.seq, o.ngram_size,
+                                        o.heads_per_ngram, o.eos_id, o.h_multipliers,
+                                        o.h_primes, o.h_offsets, o.table_rows, o.head_dim,
+                                        o.d_workspace, o.workspace_bytes, o.d_err_count,
+                                        o.stream);
+        break;
+      case ENGRAM_OP_APPLY:
+        st = engram_scatter_apply(o.d_grads, o.n, o.head_dim, o.table_rows, o.d_grad_table,
+                                  o.d_unique_ids, o.d_unique_grads, o.d_num_unique,
+                                  o.d_workspace, o.workspace_bytes, o.d_err_count, o.stream);
+        break;
+      case ENGRAM_OP_APPLY_SIGNSGD:
+        st = engram_scatter_apply_signsgd(o.d_grads, o.n, o.head_dim, o.table_rows,
+                                          o.d_table_rw, o.lr, o.d_workspace, o.workspace_bytes,
+                                          o.d_err_count, o.stream);
+        break;
+      case ENGRAM_OP_RECORD:
+        st = o.event != nullptr ? engram::record_event(o.event, o.stream) : ENGRAM_EINVAL;
+        break;
+      case ENGRAM_OP_WAIT:
+        st = o.event != nullptr ? engram::wait_event(o.stream, o.event) : ENGRAM_EINVAL;
+        break;
+      default:
+        break;
+    }
+    if (st != ENGRAM_OK) {
+      if (failed_index != nullptr) *failed_index = i;
+      return st;
+    }
+  }
+  return ENGRAM_OK;
+}

@@ -178,5 +178,9 @@ int launch_ple_conv(const ConvCall &c, void *stream);
 // Device address of the current device's copy of the library's fixed
 // scratch array (engram_scatter_add_rowsparse_noalloc), or null.
 void *static_scratch();
+// hipEventRecord(event, stream) and hipStreamWaitEvent(stream, event, 0)
+// for engram_run_ops (event non-null).
+int record_event(void *event, void *stream);
+int wait_event(void *stream, void *event);
 
 }  // namespace engram

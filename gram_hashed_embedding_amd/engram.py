@@ -556,3 +556,136 @@ def engram_scatter_plan_tokens(tokens, table_rows, head_dim, ngram_size, heads_p
     _check(status, "engram_scatter_plan_tokens")
     return ws
 
+
+
+# ---------------------------------------------------------------- schedules --
+class Schedule:
+    """A list of the library's calls and stream-event operations, built once
+    and enqueued with one native call per run (engram_run_ops): what a
+    training loop submits for a step, without the binding's and torch's
+    per-call host cost each time.  Each method appends one operation with the
+    arguments of the call of the same name (checked as that call checks
+    them); ``stream`` defaults to the current stream when the operation is
+    added.  The schedule holds raw pointers, so it keeps a reference to
+    every tensor, constant array, stream and event it was given; a schedule
+    must be rebuilt whenever one of them would be replaced."""
+
+    def __init__(self):
+        self._ops = []
+        self._keep = []
+        self._array = None
+
+    def _add(self, keep, **fields):
+        o = abi.EngramOp()
+        for k, v in fields.items():
+            setattr(o, k, v)
+        self._ops.append(o)
+        self._keep.extend(keep)
+        self._array = None
+        return self
+
+    @staticmethod
+    def _sp(device, stream):
+        s = stream if stream is not None else torch.cuda.current_stream(device)
+        return s, s.cuda_stream
+
+    def lookup(self, tokens, table, ngram_size, heads_per_ngram, eos_id, multipliers, primes,
+               offsets, out, seq_ids=None, row_ids=None, stream=None):
+        heads, mult, pr, off = _hash_args(tokens, ngram_size, heads_per_ngram, multipliers,
+                                          primes, offsets, seq_ids)
+        _device_tensor(table, torch.bfloat16, "table")
+        _device_tensor(out, torch.bfloat16, "out")
+        if row_ids is not None:
+            _device_tensor(row_ids, torch.int64, "row_ids")
+        s, sp = self._sp(tokens.device, stream)
+        batch, seq = tokens.shape
+        return self._add(
+            [tokens, seq_ids, table, out, row_ids, mult, pr, off, s],
+            op=abi.OP_LOOKUP, stream=sp, d_tokens=tokens.data_ptr(),
+            d_seq_ids=None if seq_ids is None else seq_ids.data_ptr(), batch=batch, seq=seq,
+            ngram_size=int(ngram_size), heads_per_ngram=int(heads_per_ngram),
+            eos_id=int(eos_id), h_multipliers=mult, h_primes=pr, h_offsets=off,
+            d_table=table.data_ptr(), table_rows=table.shape[0], head_dim=table.shape[1],
+            d_out=out.data_ptr(), d_row_ids=None if row_ids is None else row_ids.data_ptr())
+
+    def plan_tokens(self, tokens, table_rows, head_dim, ngram_size, heads_per_ngram, eos_id,
+                    multipliers, primes, offsets, workspace, seq_ids=None, err_count=None,
+                    stream=None):
+        heads, mult, pr, off = _hash_args(tokens, ngram_size, heads_per_ngram, multipliers,
+                                          primes, offsets, seq_ids)
+        _device_tensor(workspace, torch.uint8, "workspace")
+        if err_count is not None:
+            _device_tensor(err_count, torch.int64, "err_count")
+        s, sp = self._sp(tokens.device, stream)
+        batch, seq = tokens.shape
+        return self._add(
+            [tokens, seq_ids, workspace, err_count, mult, pr, off, s],
+            op=abi.OP_PLAN_TOKENS, stream=sp, d_tokens=tokens.data_ptr(),
+            d_seq_ids=None if seq_ids is None else seq_ids.data_ptr(), batch=batch, seq=seq,
+            ngram_size=int(ngram_size), heads_per_ngram=int(heads_per_ngram),
+            eos_id=int(eos_id), h_multipliers=mult, h_primes=pr, h_offsets=off,
+            table_rows=int(table_rows), head_dim=int(head_dim),
+            d_workspace=workspace.data_ptr(), workspace_bytes=workspace.numel(),
+            d_err_count=None if err_count is None else err_count.data_ptr())
+
+    def apply(self, grads, workspace, table_rows, grad_table=None, unique_ids=None,
+              unique_grads=None, num_unique=None, err_count=None, stream=None):
+        _device_tensor(grads, torch.bfloat16, "grads")
+        _device_tensor(workspace, torch.uint8, "workspace")
+        for t, dt, what in ((grad_table, torch.float32, "grad_table"),
+                            (unique_ids, torch.int64, "unique_ids"),
+                            (unique_grads, torch.float32, "unique_grads"),
+                            (num_unique, torch.int64, "num_unique"),
+                            (err_count, torch.int64, "err_count")):
+            if t is not None:
+                _device_tensor(t, dt, what)
+        s, sp = self._sp(grads.device, stream)
+        p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        return self._add(
+            [grads, workspace, grad_table, unique_ids, unique_grads, num_unique, err_count, s],
+            op=abi.OP_APPLY, stream=sp, d_grads=grads.data_ptr(), n=grads.shape[0],
+            head_dim=grads.shape[1], table_rows=int(table_rows),
+            d_grad_table=p(grad_table), d_unique_ids=p(unique_ids),
+            d_unique_grads=p(unique_grads), d_num_unique=p(num_unique),
+            d_workspace=workspace.data_ptr(), workspace_bytes=workspace.numel(),
+            d_err_count=p(err_count))
+
+    def apply_signsgd(self, grads, workspace, table, lr, err_count=None, stream=None):
+        _device_tensor(grads, torch.bfloat16, "grads")
+        _device_tensor(workspace, torch.uint8, "workspace")
+        _device_tensor(table, torch.bfloat16, "table")
+        if err_count is not None:
+            _device_tensor(err_count, torch.int64, "err_count")
+        s, sp = self._sp(grads.device, stream)
+        return self._add(
+            [grads, workspace, table, err_count, s],
+            op=abi.OP_APPLY_SIGNSGD, stream=sp, d_grads=grads.data_ptr(), n=grads.shape[0],
+            head_dim=grads.shape[1], table_rows=table.shape[0], d_table_rw=table.data_ptr(),
+            lr=float(lr), d_workspace=workspace.data_ptr(), workspace_bytes=workspace.numel(),
+            d_err_count=None if err_count is None else err_count.data_ptr())
+
+    def _event_op(self, op, event, stream):
+        s, sp = self._sp(torch.device("cuda", torch.cuda.current_device()), stream)
+        if not event.cuda_event:  # torch creates an event when it is first recorded
+            event.record(s)
+        return self._add([event, s], op=op, stream=sp, event=event.cuda_event)
+
+    def record(self, event, stream=None):
+        """event.record(stream), in the schedule."""
+        return self._event_op(abi.OP_RECORD, event, stream)
+
+    def wait(self, event, stream=None):
+        """stream.wait_event(event), in the schedule."""
+        return self._event_op(abi.OP_WAIT, event, stream)
+
+    def __len__(self):
+        return len(self._ops)
+
+    def run(self):
+        """Enqueue every operation, in order (engram_run_ops)."""
+        if self._array is None:
+            self._array = (abi.EngramOp * max(len(self._ops), 1))(*self._ops)
+        failed = ctypes.c_int64(-1)
+        status = _lib.engram_run_ops(self._array, len(self._ops), ctypes.byref(failed))
+        if status != ENGRAM_OK:
+            raise EngramError(status, f"engram_run_ops (operation {failed.value})")

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 2
+#define ENGRAM_ABI_VERSION 3
 
 #define ENGRAM_OK 0
 #define ENGRAM_EINVAL (-1)
@@ -441,6 +441,82 @@ int engram_ple_conv(const void *d_x, const void *d_halo, int64_t halo_len,
                     const int64_t *d_seq_ids, const void *d_weight, const void *d_bias,
                     int64_t batch, int64_t seq, int64_t channels, int32_t kernel_size,
                     int32_t dilation, void *d_out, void *stream);
+
+/*
+ * engram_run_ops -- enqueue a list of this library's calls and stream-event
+ * operations in one call, in order: what a training loop submits for one
+ * step (say, the next batch's plan on a side stream, the forward on the main
+ * stream, and later the apply after the plan's event), without a round trip
+ * through the caller's language per call.  Each operation is exactly the
+ * entry point it names, with that entry point's checks and errors; only the
+ * host's per-call cost differs.  The pages count host-side round trips per
+ * lookup as the cost to avoid ([API] Qwen3_8_FlashNextEngramTableConfig,
+ * strict_validation); with small batches the submission of a step's kernels
+ * is what sets its pace.
+ *   op ENGRAM_OP_LOOKUP: engram_lookup(d_tokens, d_seq_ids, batch, seq,
+ *     ngram_size, heads_per_ngram, eos_id, h_multipliers, h_primes,
+ *     h_offsets, d_table, table_rows, head_dim, d_out, d_row_ids, stream).
+ *   op ENGRAM_OP_PLAN_TOKENS: engram_scatter_plan_tokens(d_tokens, d_seq_ids,
+ *     batch, seq, ngram_size, heads_per_ngram, eos_id, h_multipliers,
+ *     h_primes, h_offsets, table_rows, head_dim, d_workspace,
+ *     workspace_bytes, d_err_count, stream).
+ *   op ENGRAM_OP_APPLY: engram_scatter_apply(d_grads, n, head_dim,
+ *     table_rows, d_grad_table, d_unique_ids, d_unique_grads, d_num_unique,
+ *     d_workspace, workspace_bytes, d_err_count, stream).
+ *   op ENGRAM_OP_APPLY_SIGNSGD: engram_scatter_apply_signsgd(d_grads, n,
+ *     head_dim, table_rows, d_table_rw, lr, d_workspace, workspace_bytes,
+ *     d_err_count, stream).
+ *   op ENGRAM_OP_RECORD: hipEventRecord(event, stream).
+ *   op ENGRAM_OP_WAIT: hipStreamWaitEvent(stream, event, 0).
+ *   Fields an operation does not name are ignored.  ops[0 .. count) are
+ *   read during the call only; every pointer in them must stay valid as the
+ *   named entry point requires (device buffers until the work completes).
+ *   event is a hipEvent_t the caller created; stream a hipStream_t (NULL:
+ *   the null stream).
+ * Returns ENGRAM_OK when every operation was enqueued.  Otherwise the
+ * status of the first operation that failed (EINVAL, EALIGN, EWORKSPACE,
+ * EHIP; EINVAL also for an unknown op code, or a RECORD or WAIT without an
+ * event); the operations before it stay enqueued and the later ones are
+ * not.  EINVAL with nothing enqueued for count < 0, or ops NULL with
+ * count > 0.  *failed_index, when failed_index is not NULL, receives the
+ * index of the operation that failed, or -1 (success, or an invalid list).
+ */
+#define ENGRAM_OP_LOOKUP 1
+#define ENGRAM_OP_PLAN_TOKENS 2
+#define ENGRAM_OP_APPLY 3
+#define ENGRAM_OP_APPLY_SIGNSGD 4
+#define ENGRAM_OP_RECORD 5
+#define ENGRAM_OP_WAIT 6
+
+typedef struct engram_op {
+  int32_t op;                 /* ENGRAM_OP_* */
+  int32_t ngram_size;         /* LOOKUP, PLAN_TOKENS */
+  int32_t heads_per_ngram;    /* LOOKUP, PLAN_TOKENS */
+  float lr;                   /* APPLY_SIGNSGD */
+  void *stream;               /* every op: the hipStream_t it is enqueued on */
+  void *event;                /* RECORD, WAIT: a hipEvent_t */
+  const int64_t *d_tokens;    /* LOOKUP, PLAN_TOKENS */
+  const int64_t *d_seq_ids;   /* LOOKUP, PLAN_TOKENS (NULL: no segments) */
+  int64_t batch, seq, eos_id; /* LOOKUP, PLAN_TOKENS */
+  const int64_t *h_multipliers, *h_primes, *h_offsets; /* LOOKUP, PLAN_TOKENS (host) */
+  int64_t table_rows;         /* LOOKUP, PLAN_TOKENS, APPLY, APPLY_SIGNSGD */
+  int64_t head_dim;           /* LOOKUP, PLAN_TOKENS, APPLY, APPLY_SIGNSGD */
+  const void *d_table;        /* LOOKUP */
+  void *d_out;                /* LOOKUP */
+  int64_t *d_row_ids;         /* LOOKUP (NULL: not written) */
+  void *d_workspace;          /* PLAN_TOKENS, APPLY, APPLY_SIGNSGD */
+  size_t workspace_bytes;
+  const void *d_grads;        /* APPLY, APPLY_SIGNSGD */
+  int64_t n;                  /* APPLY, APPLY_SIGNSGD */
+  float *d_grad_table;        /* APPLY (dense output), or NULL */
+  int64_t *d_unique_ids;      /* APPLY (row-sparse output), or NULL */
+  float *d_unique_grads;
+  int64_t *d_num_unique;
+  void *d_table_rw;           /* APPLY_SIGNSGD: the bf16 table */
+  int64_t *d_err_count;       /* PLAN_TOKENS, APPLY, APPLY_SIGNSGD (or NULL) */
+} engram_op;
+
+int engram_run_ops(const engram_op *ops, int64_t count, int64_t *failed_index);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def _ws(lib, n, rows, dim, mode):
 
 
 def case_status_strings_and_version(lib):
-    assert lib.engram_abi_version() == 2
+    assert lib.engram_abi_version() == abi.ABI_VERSION == 3
     assert lib.engram_status_string(0) == b"ok"
     for code in (-1, -2, -3, -4):
         assert lib.engram_status_string(code) not in (b"ok", b"unknown status")
@@ -265,6 +265,59 @@ def case_noalloc_limits(lib):
         abi.ENGRAM_EINVAL
     assert na(ALIGNED, 100, MISALIGNED, 8, 50, ALIGNED, ALIGNED, ALIGNED, None, None) == \
         abi.ENGRAM_EALIGN
+
+
+def _op(**fields):
+    o = abi.EngramOp()
+    for k, v in fields.items():
+        setattr(o, k, v)
+    return o
+
+
+def _hash_op(op, **fields):
+    """A lookup or token-plan op with valid hash arguments (3 orders, 2 heads
+    per order, a 36-row table) and fake buffers."""
+    base = dict(op=op, d_tokens=FAKE.value, batch=1, seq=4, ngram_size=3, heads_per_ngram=2,
+                h_multipliers=_arr((1, 2, 3)), h_primes=_arr((5, 7, 11, 13)),
+                h_offsets=_arr((0, 5, 12, 23)), table_rows=36, head_dim=8,
+                d_table=ALIGNED.value, d_out=ALIGNED.value, d_workspace=ALIGNED.value,
+                workspace_bytes=0)
+    base.update(fields)
+    return _op(**base)
+
+
+def case_run_ops_rejects(lib):
+    failed = ctypes.c_int64(99)
+    ref = ctypes.byref(failed)
+    assert lib.engram_run_ops(None, 0, ref) == abi.ENGRAM_OK and failed.value == -1
+    assert lib.engram_run_ops(None, 1, ref) == abi.ENGRAM_EINVAL and failed.value == -1
+    ops = (abi.EngramOp * 1)()
+    assert lib.engram_run_ops(ops, -1, ref) == abi.ENGRAM_EINVAL and failed.value == -1
+    bad_first = [
+        _op(op=0), _op(op=7), _op(op=-1),                      # unknown op codes
+        _op(op=abi.OP_RECORD), _op(op=abi.OP_WAIT),            # no event
+        _hash_op(abi.OP_LOOKUP, ngram_size=1),                 # engram_lookup's own checks
+        _hash_op(abi.OP_LOOKUP, d_out=None),
+        _hash_op(abi.OP_PLAN_TOKENS, heads_per_ngram=0),       # engram_scatter_plan_tokens's
+        _hash_op(abi.OP_PLAN_TOKENS, workspace_bytes=16),      # workspace too small: EWORKSPACE
+        _op(op=abi.OP_APPLY, n=8, head_dim=7, table_rows=36),  # engram_scatter_apply's
+        _op(op=abi.OP_APPLY_SIGNSGD, n=8, head_dim=8, table_rows=36),  # no table
+    ]
+    for o in bad_first:
+        one = (abi.EngramOp * 1)(o)
+        failed.value = 99
+        rc = lib.engram_run_ops(one, 1, ref)
+        assert rc in (abi.ENGRAM_EINVAL, abi.ENGRAM_EWORKSPACE), (o.op, rc)
+        assert failed.value == 0, o.op
+    # empty calls succeed without launching; the first failure's index comes back
+    ok_empty = [_hash_op(abi.OP_LOOKUP, batch=0), _hash_op(abi.OP_PLAN_TOKENS, batch=0),
+                _op(op=abi.OP_APPLY, n=0, head_dim=8, table_rows=36, d_grad_table=ALIGNED.value)]
+    lst = (abi.EngramOp * 5)(*ok_empty, _op(op=abi.OP_WAIT), _op(op=abi.OP_LOOKUP))
+    failed.value = 99
+    assert lib.engram_run_ops(lst, 5, ref) == abi.ENGRAM_EINVAL and failed.value == 3
+    failed.value = 99
+    assert lib.engram_run_ops(lst, 3, ref) == abi.ENGRAM_OK and failed.value == -1
+    assert lib.engram_run_ops(lst, 3, None) == abi.ENGRAM_OK
 
 
 CASES = [v for k, v in sorted(globals().items()) if k.startswith("case_")]

@@ -79,4 +79,14 @@ int launch_ple_conv(const ConvCall &c, void *) {
 // A fake, 256-aligned address: the stand-in launchers never dereference it.
 void *static_scratch() { return reinterpret_cast<void *>(uintptr_t(1) << 20); }
 
+int record_event(void *event, void *) {
+  require(event != nullptr);
+  return ENGRAM_OK;
+}
+
+int wait_event(void *, void *event) {
+  require(event != nullptr);
+  return ENGRAM_OK;
+}
+
 }  // namespace engram

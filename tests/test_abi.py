@@ -13,7 +13,7 @@ EXPORTED = {"engram_status_string", "engram_abi_version", "engram_hash", "engram
             "engram_scatter_plan", "engram_scatter_apply", "engram_hash_slice",
             "engram_signsgd_rowsparse", "engram_scatter_apply_signsgd", "engram_ple_conv",
             "engram_lookup", "engram_scatter_plan_tokens", "engram_lookup_slice",
-            "engram_scatter_add_rowsparse_noalloc"}
+            "engram_scatter_add_rowsparse_noalloc", "engram_run_ops"}
 
 
 def test_every_declared_symbol_is_exported():
@@ -51,3 +51,26 @@ def test_host_constant_arrays():
     assert len(e._HOST_I64) <= 256
     assert list(e._host_i64((5, -7, 3), 3, "x")) == [5, -7, 3]
 
+
+
+def test_op_struct_layout_matches_the_header(tmp_path):
+    """The binding's engram_op (abi.EngramOp) has the header's size and
+    field offsets, as a C compiler lays the struct out."""
+    import ctypes
+    import os
+    import subprocess
+    from gram_hashed_embedding_amd import abi
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    fields = [f for f, _ in abi.EngramOp._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text("#include <stddef.h>\n#include <stdio.h>\n#include \"engram.h\"\n"
+                   "int main(void) {\n  printf(\"%zu\\n\", sizeof(engram_op));\n"
+                   + "".join(f'  printf("%zu\\n", offsetof(engram_op, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(root, "include"), str(src), "-o",
+                    str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                          text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(abi.EngramOp)
+    assert got[1:] == [getattr(abi.EngramOp, f).offset for f in fields]
