@@ -438,6 +438,146 @@ __global__ __launch_bounds__(kHeadThreads) void plan_hash_heads_kernel(
   }
 }
 
+// ---------------------------------------------------- small plan in LDS ---
+// A plan from tokens sorted in per-head segments of at most kLdsSortKeys
+// keys (a small batch): one block per segment hashes its head's keys, sorts
+// them in LDS with the same stable LSD passes as the one-sweep sort (the
+// keys in (wave, round, lane) order, ranked by wavefront multi-split, each
+// pass's digit offsets by a block scan), and writes the segment's sorted
+// keys and flat indices.  The block of segment 0 also clears the slot scan's
+// look-back state and the plan's scalars.  One launch does what the clear,
+// the hash and one launch per sort pass do for large segments; the slot
+// scan follows.  Keys and indices pass through one LDS buffer in turn.
+// Measured on MI355X (plan alone, 16 heads): 21.8 against 43.9 us at 1024
+// keys per head, 24.2 against 42.9 at 4096, 36.5 against 44.3 at 8192; at
+// 16384 keys per head one block per head is slower than the multi-block
+// sort (60.4 against 50.8 us), so larger segments take that.
+constexpr int kLdsSortThreads = 1024;
+constexpr int kLdsSortWaves = kLdsSortThreads / kWave;
+constexpr int kLdsSortKeys = kLdsSortThreads * 8;
+
+template <int N, int ITEMS>
+__global__ __launch_bounds__(kLdsSortThreads) void plan_heads_lds_kernel(
+    const HashParams hp, const SortSegs sg, int passes, int per_pass, int bits,
+    uint32_t *keys_out, uint32_t *vals_out, uint64_t *slot_status, int64_t slot_words,
+    uint32_t *slot_ticket, PlanScalars *plan) {
+  static_assert(kLdsSortThreads * ITEMS <= kLdsSortKeys, "a segment fits the buffer");
+  __shared__ uint32_t s_buf[kLdsSortThreads * ITEMS];
+  __shared__ uint32_t s_cnt[kLdsSortWaves][kMaxBins];  // per-wave counts -> wave offsets
+  __shared__ uint32_t s_local[kMaxBins];               // start of each digit
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t seg = blockIdx.x;
+  const int h = (int)sg.head[seg];
+  const int order = h / hp.J;  // g - 2
+  const uint32_t kbase = sg.base[seg];
+  const int len = (int)sg.len;
+  if (seg == 0) {
+    for (int64_t i = tid; i < slot_words; i += kLdsSortThreads) slot_status[i] = 0;
+    if (tid == 0) {
+      *slot_ticket = 0;
+      *plan = PlanScalars{};  // no complete plan until the slot scan stamps it
+    }
+  }
+  // item i of this thread sits at segment position pos(i): (wave, round, lane)
+  auto pos = [&](int i) { return wave * (ITEMS * kWave) + i * kWave + lane; };
+  // the keys, B tokens at a time with their history loads in flight, into
+  // LDS at their positions (so the history registers are free again before
+  // the sort's), then into registers; a key's flat index follows from its
+  // position
+  constexpr int B = 4;
+#pragma unroll
+  for (int i0 = 0; i0 < ITEMS; i0 += B) {
+    uint64_t mix[B][ENGRAM_MAX_NGRAM - 1];
+#pragma unroll
+    for (int b = 0; b < B; ++b) token_mixes<N>(hp, min(pos(i0 + b), len - 1), mix[b]);
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      uint64_t m = mix[b][0];
+#pragma unroll
+      for (int k = 1; k < N - 1; ++k) m = order == k ? mix[b][k] : m;
+      s_buf[pos(i0 + b)] = (uint32_t)head_row(hp, m, h);
+    }
+  }
+  uint32_t key[ITEMS], val[ITEMS];
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    key[i] = s_buf[pos(i)];  // (this thread's own positions: no barrier needed)
+    val[i] = (uint32_t)((int64_t)pos(i) * sg.stride + h);
+  }
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int q = 0; q < passes; ++q) {
+    const int shift = q * per_pass;
+    const int width = bits - shift < per_pass ? bits - shift : per_pass;
+    const uint32_t mask = (1u << width) - 1u;
+    const int bins = 1 << width;
+    for (int d = tid; d < kLdsSortWaves * kMaxBins; d += kLdsSortThreads) (&s_cnt[0][0])[d] = 0;
+    __syncthreads();
+    uint32_t rank[ITEMS];
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const bool valid = pos(i) < len;
+      const uint32_t d = ((key[i] - kbase) >> shift) & mask;
+      unsigned long long peers = __ballot(valid);
+      for (int b = 0; b < width; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const unsigned long long bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      rank[i] = 0;
+      if (valid) {
+        const uint32_t prior = s_cnt[wave][d];
+        rank[i] = prior + (uint32_t)__popcll(peers & below);
+        if ((peers & below) == 0ull) s_cnt[wave][d] = prior + (uint32_t)__popcll(peers);
+      }
+    }
+    __syncthreads();
+    // per digit: the waves' offsets and the digit's total, then the digits'
+    // starts by a block scan
+    uint32_t total = 0;
+    if (tid < bins) {
+      for (int w = 0; w < kLdsSortWaves; ++w) {
+        const uint32_t c = s_cnt[w][tid];
+        s_cnt[w][tid] = total;
+        total += c;
+      }
+    }
+    uint32_t all;
+    const uint32_t start = block_exclusive_scan<kLdsSortThreads>(tid < bins ? total : 0u, all);
+    if (tid < bins) s_local[tid] = start;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i) {
+      const uint32_t d = ((key[i] - kbase) >> shift) & mask;
+      rank[i] += s_local[d] + s_cnt[wave][d];
+    }
+    // keys, then flat indices, through LDS into the pass's order
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (pos(i) < len) s_buf[rank[i]] = key[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (pos(i) < len) key[i] = s_buf[pos(i)];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (pos(i) < len) s_buf[rank[i]] = val[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ITEMS; ++i)
+      if (pos(i) < len) val[i] = s_buf[pos(i)];
+    __syncthreads();  // s_buf and s_cnt are rewritten by the next pass
+  }
+  const int64_t seg0 = seg * sg.len;
+#pragma unroll
+  for (int i = 0; i < ITEMS; ++i) {
+    if (pos(i) < len) {
+      keys_out[seg0 + pos(i)] = key[i];
+      vals_out[seg0 + pos(i)] = val[i];
+    }
+  }
+}
+
 // ------------------------------------------------------------ row slots ---
 // Slot of every range's first distinct row: the number of distinct-row heads
 // (first positions of a valid row) in all earlier ranges; the last tile also
@@ -654,6 +794,36 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
   uint32_t *hist = v.counters + kTicketWords;  // [copy][segment][4][kMaxBins]
   SortLayout L = whole_sort(p, n);
   const bool heads = ids == nullptr && head_sort(*hp, n / hp->H, p, &L);
+  if (heads && L.sg.len <= kLdsSortKeys) {
+    // small segments: one kernel sorts every head's keys in LDS, into the
+    // buffers the apply reads (those the last pass of a sort would fill)
+    uint32_t *const keys_dst = p.passes % 2 == 1 ? v.keys_a : v.keys_b;
+    uint32_t *const vals_dst = p.passes % 2 == 1 ? v.vals_a : v.vals_b;
+    const int items = L.sg.len <= 4 * kLdsSortThreads ? 4 : 8;
+    const dim3 grid((unsigned)L.sg.count), block(kLdsSortThreads);
+    switch (hp->n * 100 + items) {
+#define ENGRAM_PLAN_LDS_CASE(N, I)                                                             \
+  case N * 100 + I:                                                                            \
+    hipLaunchKernelGGL((plan_heads_lds_kernel<N, I>), grid, block, 0, s, *hp, L.sg, L.passes,   \
+                       L.per_pass, L.bits, keys_dst, vals_dst, v.status,                       \
+                       p.slot_tiles, tickets + kSlotTicketAt, v.scalars);                      \
+    break;
+#define ENGRAM_PLAN_LDS_N(N) ENGRAM_PLAN_LDS_CASE(N, 4) ENGRAM_PLAN_LDS_CASE(N, 8)
+      ENGRAM_PLAN_LDS_N(2)
+      ENGRAM_PLAN_LDS_N(3)
+      ENGRAM_PLAN_LDS_N(4)
+      ENGRAM_PLAN_LDS_N(5)
+      ENGRAM_PLAN_LDS_N(6)
+      ENGRAM_PLAN_LDS_N(7)
+      ENGRAM_PLAN_LDS_N(8)
+#undef ENGRAM_PLAN_LDS_N
+#undef ENGRAM_PLAN_LDS_CASE
+    }
+    hipLaunchKernelGGL(range_slots_kernel, dim3((unsigned)p.slot_tiles), dim3(kSlotThreads), 0,
+                       s, v.sorted_keys, n, (uint32_t)table_rows, p.num_ranges, v.status,
+                       tickets + kSlotTicketAt, v.head_off, v.scalars, err);
+    return launch_status();
+  }
   const int64_t sort_words = (int64_t)L.passes * L.num_tiles * kMaxBins;
   const int64_t status_len = sort_words + p.slot_tiles;
   const int64_t counters_len = kTicketWords + (int64_t)L.sg.copies * L.sg.count * 4 * kMaxBins;

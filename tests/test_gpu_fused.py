@@ -153,6 +153,44 @@ def test_token_plan_every_order(n, J):
     assert torch.equal(uid_t[:u], torch.unique(ids))
 
 
+@pytest.mark.parametrize("tokens", [1, 100, 4095, 4096, 4097, 8191, 8192, 8193, 9000])
+def test_token_plan_sizes_keep_the_sort_order(tokens):
+    """Small per-head segments are sorted by one block per head in LDS, larger
+    ones by the multi-block sort: around both switches the plan from the
+    tokens holds exactly the order of the plan of engram_hash's ids (equal
+    rows in ascending flat index).  The gradients make the sums depend on
+    that order: small terms with +-2^40 entries scattered among them, so a
+    different order of any row's terms would change the result's bits."""
+    n, J = 3, 4
+    H = (n - 1) * J
+    primes = workloads.primes_above(3000, H)
+    offs = workloads.cumulative_offsets(primes)
+    rows = sum(primes)
+    mult = workloads.seeded_multipliers(n, 90)
+    rng = np.random.Generator(np.random.PCG64(tokens))
+    tok = np.minimum(rng.zipf(1.3, (1, tokens)), 60).astype(np.int64)   # hot rows
+    args = (n, J, 0, mult, primes, offs)
+    R, dim = tok.size * H, 16
+    exp = rng.integers(127 - 6, 127 + 7, (R, dim)).astype(np.uint16)
+    gb = ((rng.integers(0, 2, (R, dim)).astype(np.uint16) << 15) | (exp << 7)
+          | rng.integers(0, 128, (R, dim)).astype(np.uint16))
+    big = rng.random((R, dim)) < 0.02
+    gb[big] = (np.uint16((127 + 40) << 7) | (rng.integers(0, 2, int(big.sum())).astype(np.uint16)
+                                              << 15))
+    grads = torch.from_numpy(gb.view(np.int16)).to("cuda").view(torch.bfloat16)
+    ws_t = plan_tokens(dev(tok), rows, dim, *args)
+    uid_t, val_t, cnt_t = apply(grads, ws_t, rows)
+    ids = E.engram_hash(dev(tok), *args, rows)
+    ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
+    uid_i, val_i, cnt_i = apply(grads, ws_i, rows)
+    torch.cuda.synchronize()
+    u = int(cnt_t.item())
+    assert u == int(cnt_i.item()) and u > 0
+    assert torch.equal(uid_t[:u], uid_i[:u])
+    assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
+    release()
+
+
 @pytest.mark.parametrize("layout", ["ascending", "descending", "shuffled", "gap",
                                     "overlapping", "shared"])
 def test_token_plan_head_layouts(layout):
