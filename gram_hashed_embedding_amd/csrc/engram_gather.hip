@@ -105,11 +105,14 @@ __global__ __launch_bounds__(kGatherThreads) void zero_rows_kernel(const int64_t
 // row each from the tokens (lookup_row: the token's history in one round of
 // loads, the order mix, a Barrett remainder), so the hash costs one lane per
 // row, and keep them in LDS (and write them out when the caller asks).
-// Phase 2: as gather_kernel, every lane moves 16-byte chunks of those rows,
-// kUnroll at a time (all loads before the stores).  The row ids never go
-// through memory.  A block moves about kLookChunks chunks: 32 rows at
-// head_dim 256 (measured best there), more rows for narrower rows (head_dim
-// 64: 128 rows), at most one per thread.  N = ngram_size at compile time, so
+// Phase 2: every lane moves kLookUnroll 16-byte chunks of those rows (all
+// loads before the stores), so a block's kLookChunks chunks take one round
+// trip.  The row ids never go through memory.  A block moves about
+// kLookChunks chunks: 32 rows at head_dim 256 (measured best there), more
+// rows for narrower rows (head_dim 64: 128 rows), at most one per thread.
+// Four chunks per lane (one round) against two (two rounds) measured, in one
+// process: e2e 265.4 against 269.9 us, full-scale 171.2 against 175.6,
+// medium 11.5 against 12.4.  N = ngram_size at compile time, so
 // the history takes no more registers than the order needs.  The slice form
 // (one context-parallel rank's forward, _forward_global_slice on the same
 // page) is the same kernel over a window of positions whose history may
@@ -117,6 +120,7 @@ __global__ __launch_bounds__(kGatherThreads) void zero_rows_kernel(const int64_t
 constexpr int kLookRows = 32;       // fewest rows per block
 constexpr int kLookChunks = 1024;   // 16-byte chunks per block, when rows allow
 constexpr int kLookRowsMax = kGatherThreads;
+constexpr int kLookUnroll = kLookChunks / kGatherThreads;  // chunks per lane
 
 template <int N>
 __global__ __launch_bounds__(kGatherThreads) void lookup_kernel(
@@ -133,16 +137,16 @@ __global__ __launch_bounds__(kGatherThreads) void lookup_kernel(
   __syncthreads();
   const int64_t nchunks = (int64_t)nrows * cpr;
   u32x4 *dst = out + row0 * cpr;
-  for (int64_t k0 = threadIdx.x; k0 < nchunks; k0 += (int64_t)kGatherThreads * kUnroll) {
-    u32x4 v[kUnroll];
+  for (int64_t k0 = threadIdx.x; k0 < nchunks; k0 += (int64_t)kGatherThreads * kLookUnroll) {
+    u32x4 v[kLookUnroll];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kLookUnroll; ++u) {
       const int64_t k = min(k0 + (int64_t)u * kGatherThreads, nchunks - 1);
       const int64_t rl = log2_cpr >= 0 ? k >> log2_cpr : k / cpr;
       v[u] = table[s_row[rl] * cpr + (k - rl * cpr)];
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < kLookUnroll; ++u) {
       const int64_t k = k0 + (int64_t)u * kGatherThreads;
       if (k < nchunks) __builtin_nontemporal_store(v[u], &dst[k]);
     }
