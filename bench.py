@@ -12,12 +12,12 @@ workspaces; the apply waits for the forward and for its batch's plan.  The
 timed region holds exactly one plan, forward and apply per step (it ends
 when the plan made during the last step is done too); untimed steps run
 before it for --settle seconds (0.25 by default), then the W warm-up steps.
-A step with a backward is timed twice: each step's calls and events
-enqueued by one native call (engram_run_ops, the binding's Schedule, built
-once per token batch), which is the line's time, and the same calls made
-one by one through the binding (eager_ms_per_step).  The last timed step's
-backward is checked bit for bit against the same batch planned and applied
-one call after another, in both.  With --graphs the step
+Every step is timed twice: each step's calls and events enqueued by one
+native call (engram_run_ops, the binding's Schedule, built once per token
+batch), which is the line's time, and the same calls made one by one
+through the binding (eager_ms_per_step).  The last timed step's backward is
+checked bit for bit against the same batch planned and applied one call
+after another, in both.  With --graphs the step
 is also captured once per token batch as a HIP graph and replayed (one host
 launch per step, the same kernels and the same plan beside the forward and
 apply; checked the same way) and reported as graph_ms_per_step: on MI355X
@@ -405,6 +405,9 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
 
     def step_scheduled(k):
         """step(k), enqueued as the prebuilt schedule of its token batch."""
+        if not backward:  # the forward alone: one operation
+            scheds[k % N_BATCHES].run()
+            return
         if planned["next"] != k:  # the first step: nothing planned yet
             plan_ahead(k)
         scheds[k % N_BATCHES].run()
@@ -562,14 +565,16 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     if checkable:
         check_last()
     # ... and each step enqueued by one native call (engram_run_ops)
-    sched_ms = None
     if backward:
         scheds = build_schedules()
-        planned["next"] = None
-        torch.cuda.synchronize()
-        sched_ms = timed_steps(step_scheduled)
-        if checkable:
-            check_last()
+    else:
+        scheds = [E.Schedule().lookup(tokens[k], table, *hargs, seq_ids=segs[k], out=out,
+                                      stream=stream) for k in range(N_BATCHES)]
+    planned["next"] = None
+    torch.cuda.synchronize()
+    sched_ms = timed_steps(step_scheduled)
+    if checkable:
+        check_last()
     # ... and, on request, as one graph replay per step
     graph_ms = None
     if backward and args.graphs:
@@ -582,9 +587,9 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
         if checkable:
             check_last()
         del graphs
-    ms_per_step = sched_ms if sched_ms is not None else eager_ms
+    ms_per_step = sched_ms
     schedule = ("each step's calls and events enqueued by one engram_run_ops call"
-                if sched_ms is not None else "launched call by call")
+                if backward else "each step's lookup enqueued by one engram_run_ops call")
     schedule_check = ("last step bit-exact against serial calls, in the scheduled and the "
                       "call-by-call runs" + (", and replayed as graphs" if graph_ms is not None
                                              else "") if checkable else None)
