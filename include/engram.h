@@ -346,7 +346,7 @@ int engram_scatter_apply(const void *d_grads, int64_t n, int64_t head_dim,
  * The call allocates nothing.
  *   Size limit: n ids fit when engram_scatter_add_workspace(n, table_rows,
  *   head_dim, ENGRAM_SCATTER_ROWSPARSE) <= ENGRAM_NOALLOC_SCRATCH_BYTES
- *   (about 2M ids of a 200M-row table at head_dim 256); larger inputs return
+ *   (2,525,312 ids of a 200M-row table at head_dim 256); larger inputs return
  *   ENGRAM_EWORKSPACE before anything is enqueued.
  *   Every call on a device uses that device's one array, which keeps the last
  *   call's contents (each call clears what it needs cleared): calls that
