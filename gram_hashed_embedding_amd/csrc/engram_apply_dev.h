@@ -40,8 +40,8 @@
 
 namespace engram {
 
-constexpr int kWalkThreads = 256;
-constexpr int64_t kLongBlocks = 1024;  // most blocks that sum long runs
+// (kWalkThreads, kLongBlocks and walker_lanes, the launch's shape, are in
+// engram_host.h, where the entry points check the grid before any launch.)
 constexpr int64_t kCombineBlocks = 256;  // most blocks of the second launch
 constexpr int64_t kXcds = 8;           // XCDs of an MI355X (blocks go to them in turn)
 // Gradient tensors larger than this are read with non-temporal loads: half
@@ -827,7 +827,8 @@ __global__ __launch_bounds__(kWalkThreads) void combine_kernel(const WalkArgs a)
 template <int L, int Q, int OUT>
 void launch_walkers(WalkArgs a, hipStream_t s) {
   const int64_t walker_blocks = (a.num_ranges * L + kWalkThreads - 1) / kWalkThreads;
-  // long blocks: about two chunks each, at most kLongBlocks
+  // long blocks: about two chunks each, at most kLongBlocks (the grid is
+  // apply_blocks(), which the entry points have checked)
   const int64_t nlong = (a.num_chunks + 1) / 2;
   a.long_blocks = (uint32_t)(nlong < kLongBlocks ? nlong : kLongBlocks);
   const unsigned blocks = (unsigned)(a.long_blocks + walker_blocks);
@@ -861,15 +862,18 @@ void launch_walkers(WalkArgs a, hipStream_t s) {
 template <int OUT>
 void dispatch_walkers(const WalkArgs &a, hipStream_t s) {
   const int64_t q = a.quads;
-  if (q <= 2) launch_walkers<2, 1, OUT>(a, s);
-  else if (q <= 4) launch_walkers<4, 1, OUT>(a, s);
-  else if (q <= 8) launch_walkers<8, 1, OUT>(a, s);
-  else if (q <= 16) launch_walkers<16, 1, OUT>(a, s);
-  else if (q <= 32) launch_walkers<32, 1, OUT>(a, s);
-  else if (q <= 64) launch_walkers<64, 1, OUT>(a, s);
-  else if (q <= 128) launch_walkers<64, 2, OUT>(a, s);
-  else if (q <= 256) launch_walkers<64, 4, OUT>(a, s);
-  else launch_walkers<64, 8, OUT>(a, s);
+  switch (walker_lanes(q)) {
+    case 2: launch_walkers<2, 1, OUT>(a, s); return;
+    case 4: launch_walkers<4, 1, OUT>(a, s); return;
+    case 8: launch_walkers<8, 1, OUT>(a, s); return;
+    case 16: launch_walkers<16, 1, OUT>(a, s); return;
+    case 32: launch_walkers<32, 1, OUT>(a, s); return;
+    default:  // a whole wavefront: 1, 2, 4 or 8 quads a lane
+      if (q <= 64) launch_walkers<64, 1, OUT>(a, s);
+      else if (q <= 128) launch_walkers<64, 2, OUT>(a, s);
+      else if (q <= 256) launch_walkers<64, 4, OUT>(a, s);
+      else launch_walkers<64, 8, OUT>(a, s);
+  }
 }
 
 

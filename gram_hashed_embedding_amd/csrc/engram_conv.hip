@@ -195,7 +195,7 @@ int engram::launch_ple_conv(const ConvCall &c, void *stream) {
   hipStream_t s = as_stream(stream);
   const int64_t blocks = c.batch * a.groups * a.tiles;
   if (c.K == 4 && c.dilation <= 8) {
-    if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+    if (!grid_fits(blocks, kConvThreads)) return ENGRAM_EINVAL;
     const dim3 grid((unsigned)blocks), block(kConvThreads);
     switch (c.dilation) {
 #define ENGRAM_CONV_CASE(D) \
@@ -213,7 +213,7 @@ int engram::launch_ple_conv(const ConvCall &c, void *stream) {
   } else {
     const int64_t n = c.batch * c.seq * a.quads;
     const int64_t gb = (n + kConvThreads - 1) / kConvThreads;
-    if (gb > INT32_MAX) return ENGRAM_EINVAL;
+    if (!grid_fits(gb, kConvThreads)) return ENGRAM_EINVAL;
     hipLaunchKernelGGL(ple_conv_generic_kernel, dim3((unsigned)gb), dim3(kConvThreads), 0, s, a);
   }
   return launch_status();

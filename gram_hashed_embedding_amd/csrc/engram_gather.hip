@@ -163,13 +163,13 @@ int engram::launch_gather(const int64_t *d_row_ids, int64_t n, const void *d_tab
   const int64_t total = n * cpr;
   const int64_t per_block = (int64_t)kGatherThreads * kUnroll;
   const int64_t blocks = (total + per_block - 1) / per_block;
-  if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+  if (!grid_fits(blocks, kGatherThreads)) return ENGRAM_EINVAL;
   const u32x4 *tab = static_cast<const u32x4 *>(d_table);
   u32x4 *out = static_cast<u32x4 *>(d_out);
   hipStream_t s = as_stream(stream);
   if (table_rows == 0) {
     const int64_t zb = (total + kGatherThreads - 1) / kGatherThreads;
-    if (zb > INT32_MAX) return ENGRAM_EINVAL;
+    if (!grid_fits(zb, kGatherThreads)) return ENGRAM_EINVAL;
     hipLaunchKernelGGL(zero_rows_kernel, dim3((unsigned)zb), dim3(kGatherThreads), 0, s,
                        d_row_ids, n, cpr, out, d_err_count);
     return launch_status();
@@ -207,7 +207,7 @@ int engram::launch_lookup(const HashParams &hp, int64_t n, const void *d_table,
   rows_per_block = rows_per_block < kLookRows ? kLookRows : rows_per_block;
   rows_per_block = rows_per_block > kLookRowsMax ? kLookRowsMax : rows_per_block;
   const int64_t blocks = (n + rows_per_block - 1) / rows_per_block;
-  if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+  if (!grid_fits(blocks, kGatherThreads)) return ENGRAM_EINVAL;
   const u32x4 *tab = static_cast<const u32x4 *>(d_table);
   u32x4 *out = static_cast<u32x4 *>(d_out);
   const dim3 grid((unsigned)blocks), block(kGatherThreads);

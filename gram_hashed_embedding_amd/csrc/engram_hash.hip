@@ -19,8 +19,10 @@
 // combined by a wrapping sum of token * multiplier; multiplier k scales the
 // token k positions back; a position with no valid history token reads 0.
 //
-// Design.  One block covers 64 consecutive tokens of the flattened
-// [batch, slice] array.  Phase 1: one lane per token computes the running
+// Design.  A block covers 64 consecutive tokens of the flattened
+// [batch, slice] array at a time (the blocks stride over the array when it
+// holds more tokens than one grid's worth: a grid stays within 2^32 work-items).
+// Phase 1: one lane per token computes the running
 // order mixes M_2..M_n of its token (token_mixes in engram_hash_dev.h: the
 // token's whole history loaded at once, then a walk back through it) and
 // keeps them in LDS.  Phase 2: the block's 64 * H outputs are one contiguous
@@ -51,33 +53,35 @@ __global__ __launch_bounds__(kHashThreads) void hash_kernel(const HashArgs a) {
   __shared__ int64_t s_off[ENGRAM_MAX_HEADS];
 
   const int tid = threadIdx.x;
-  const int64_t tok0 = (int64_t)blockIdx.x * kHashTokens;
   for (int h = tid; h < a.p.H; h += kHashThreads) {
     s_prime[h] = a.p.prime[h];
     s_magic[h] = a.p.magic[h];
     s_off[h] = a.p.offset[h];
   }
-
-  // Phase 1: the order mixes of one token per lane.
-  if (tid < kHashTokens && tok0 + tid < a.total_tokens) {
-    uint64_t mix[ENGRAM_MAX_NGRAM - 1];
-    token_mixes(a.p, tok0 + tid, mix);
+  for (int64_t tok0 = (int64_t)blockIdx.x * kHashTokens; tok0 < a.total_tokens;
+       tok0 += (int64_t)gridDim.x * kHashTokens) {
+    // Phase 1: the order mixes of one token per lane.
+    if (tid < kHashTokens && tok0 + tid < a.total_tokens) {
+      uint64_t mix[ENGRAM_MAX_NGRAM - 1];
+      token_mixes(a.p, tok0 + tid, mix);
 #pragma unroll
-    for (int k = 0; k < ENGRAM_MAX_NGRAM - 1; ++k)
-      if (k < a.p.n - 1) s_mix[tid][k] = mix[k];
-  }
-  __syncthreads();
+      for (int k = 0; k < ENGRAM_MAX_NGRAM - 1; ++k)
+        if (k < a.p.n - 1) s_mix[tid][k] = mix[k];
+    }
+    __syncthreads();
 
-  // Phase 2: contiguous, coalesced row-id stores.
-  const int64_t ntok = min((int64_t)kHashTokens, a.total_tokens - tok0);
-  const int nout = (int)ntok * a.p.H;
-  int64_t *out = a.rows + tok0 * a.p.H;
-  for (int o = tid; o < nout; o += kHashThreads) {
-    const int tl = o / a.p.H;
-    const int h = o - tl * a.p.H;
-    const int order = h / a.p.J;  // g - 2
-    const int64_t x = (int64_t)s_mix[tl][order];
-    out[o] = s_off[h] + (int64_t)floor_mod(x, s_prime[h], s_magic[h]);
+    // Phase 2: contiguous, coalesced row-id stores.
+    const int64_t ntok = min((int64_t)kHashTokens, a.total_tokens - tok0);
+    const int nout = (int)ntok * a.p.H;
+    int64_t *out = a.rows + tok0 * a.p.H;
+    for (int o = tid; o < nout; o += kHashThreads) {
+      const int tl = o / a.p.H;
+      const int h = o - tl * a.p.H;
+      const int order = h / a.p.J;  // g - 2
+      const int64_t x = (int64_t)s_mix[tl][order];
+      out[o] = s_off[h] + (int64_t)floor_mod(x, s_prime[h], s_magic[h]);
+    }
+    __syncthreads();  // s_mix is rewritten for the next tokens
   }
 }
 
@@ -86,8 +90,9 @@ __global__ __launch_bounds__(kHashThreads) void hash_kernel(const HashArgs a) {
 
 int engram::launch_hash(const HashParams &hp, int64_t tokens, int64_t *d_row_ids,
                         void *stream) {
-  const int64_t blocks = (tokens + kHashTokens - 1) / kHashTokens;
-  if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+  const int64_t need = (tokens + kHashTokens - 1) / kHashTokens;
+  const int64_t most = kMaxGridItems / kHashThreads;
+  const int64_t blocks = need < most ? need : most;
   const HashArgs a = {hp, d_row_ids, tokens};
   hipLaunchKernelGGL(hash_kernel, dim3((unsigned)blocks), dim3(kHashThreads), 0,
                      as_stream(stream), a);

@@ -107,8 +107,16 @@ using namespace engram;
 
 namespace {
 
+// The sorted path's sizes: 32-bit keys and flat indices, and the apply's
+// grid inside the launch limit.  That grid (walkers of 2 to 64 lanes per 16
+// ids) is the only one of the path that can pass the limit below n = 2^32:
+// the plan's kernels take at most about one thread per 4 ids.
+bool sorted_fits(const Plan &p, int64_t n, int64_t table_rows, int64_t head_dim) {
+  return sorted_limits_ok(n, table_rows) && grid_fits(apply_blocks(p, head_dim), kWalkThreads);
+}
+
 int check_sorted(int64_t n, int64_t table_rows, int64_t head_dim, Plan *p) {
-  if (!make_plan(n, table_rows, head_dim, p) || !sorted_limits_ok(n, table_rows))
+  if (!make_plan(n, table_rows, head_dim, p) || !sorted_fits(*p, n, table_rows, head_dim))
     return ENGRAM_EINVAL;
   return ENGRAM_OK;
 }
@@ -238,7 +246,7 @@ extern "C" size_t engram_scatter_add_workspace(int64_t n, int64_t table_rows, in
   if (!make_plan(n, table_rows, head_dim, &p)) return (size_t)-1;
   if (mode == ENGRAM_SCATTER_ATOMIC) return 0;
   if (mode != ENGRAM_SCATTER_SORTED && mode != ENGRAM_SCATTER_ROWSPARSE) return (size_t)-1;
-  if (!sorted_limits_ok(n, table_rows)) return (size_t)-1;
+  if (!sorted_fits(p, n, table_rows, head_dim)) return (size_t)-1;
   return p.total;
 }
 
@@ -274,7 +282,6 @@ extern "C" int engram_scatter_plan_tokens(const int64_t *d_tokens, const int64_t
   Plan p;
   if ((rc = check_sorted(n, table_rows, head_dim, &p)) != ENGRAM_OK) return rc;
   if (n == 0) return ENGRAM_OK;
-  if ((tokens + 63) / 64 > INT32_MAX) return ENGRAM_EINVAL;
   if ((rc = check_workspace(p, d_workspace, workspace_bytes)) != ENGRAM_OK) return rc;
   return launch_plan(nullptr, &hp, n, table_rows, p, d_workspace, d_err_count, stream);
 }
@@ -326,7 +333,8 @@ extern "C" int engram_scatter_add(const int64_t *d_row_ids, int64_t n, const voi
   Plan p;
   if (!make_plan(n, table_rows, head_dim, &p)) return ENGRAM_EINVAL;
   if (mode != ENGRAM_SCATTER_SORTED && mode != ENGRAM_SCATTER_ATOMIC) return ENGRAM_EINVAL;
-  if (mode == ENGRAM_SCATTER_SORTED && !sorted_limits_ok(n, table_rows)) return ENGRAM_EINVAL;
+  if (mode == ENGRAM_SCATTER_SORTED && !sorted_fits(p, n, table_rows, head_dim))
+    return ENGRAM_EINVAL;
   if (n == 0) return ENGRAM_OK;
   if (d_row_ids == nullptr || d_grads == nullptr || d_grad_table == nullptr)
     return ENGRAM_EINVAL;

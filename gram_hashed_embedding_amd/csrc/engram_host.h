@@ -28,6 +28,16 @@ inline bool mul_fits(int64_t a, int64_t b, int64_t limit) { return a == 0 || b <
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Work-items of one launch (blocks times threads per block): the dispatch
+// packet holds that count in 32 bits, so a grid must stay at or below
+// 2^32 - 1 of them.  Every launcher checks its grids with grid_fits before
+// enqueuing anything (ENGRAM_EINVAL when one does not fit), or strides its
+// blocks over the work so that no size needs more.
+constexpr int64_t kMaxGridItems = int64_t(0xFFFFFFFF);
+inline bool grid_fits(int64_t blocks, int64_t threads) {
+  return blocks >= 0 && blocks <= kMaxGridItems / threads;
+}
+
 // Number of bits of x (0 for 0).
 inline int bit_width_u64(uint64_t x) {
   int b = 0;
@@ -92,6 +102,19 @@ constexpr int kSortCounters = kTicketWords + kHistSets * 4 * kMaxBins;
 // apply's second launch adds up in chunk order.
 constexpr int64_t kChunk = 512;
 
+// The apply's launch: blocks of kWalkThreads threads, the first
+// min((chunks + 1) / 2, kLongBlocks) summing long runs, then the range
+// walkers, one per kRange sorted positions, walker_lanes(head_dim / 4)
+// lanes each (one 4-value quad of the row per lane, the quad count rounded
+// up to a power of two, at most one wavefront).
+constexpr int kWalkThreads = 256;
+constexpr int64_t kLongBlocks = 1024;
+inline int64_t walker_lanes(int64_t quads) {
+  int64_t l = 2;
+  while (l < quads && l < 64) l *= 2;
+  return l;
+}
+
 // Where the parts of the sorted path's workspace start (bytes, 256-aligned).
 struct Plan {
   int64_t num_tiles, num_ranges, slot_tiles;
@@ -101,6 +124,13 @@ struct Plan {
   size_t keys_a, vals_a, keys_b, vals_b, status, counters, head_off, scalars, chunk_owner,
       partials, total;
 };
+
+// Blocks of the apply's first launch for a plan of rows head_dim wide.
+inline int64_t apply_blocks(const Plan &p, int64_t head_dim) {
+  const int64_t nlong = (p.num_chunks + 1) / 2;
+  const int64_t walkers = p.num_ranges * walker_lanes(head_dim / 4);
+  return (nlong < kLongBlocks ? nlong : kLongBlocks) + (walkers + kWalkThreads - 1) / kWalkThreads;
+}
 
 // The plan's scalars at Plan::scalars (the start of the workspace): written
 // by the plan, read by the apply.

@@ -83,7 +83,7 @@ int engram::launch_signsgd(const int64_t *d_unique_ids, const float *d_unique_gr
   const int64_t cpr = head_dim / 8;
   const int64_t per_block = (int64_t)kOptThreads * kOptUnroll;
   const int64_t blocks = (capacity * cpr + per_block - 1) / per_block;
-  if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+  if (!grid_fits(blocks, kOptThreads)) return ENGRAM_EINVAL;
   const dim3 grid((unsigned)blocks), block(kOptThreads);
   hipStream_t s = as_stream(stream);
   const f32x4 *g = reinterpret_cast<const f32x4 *>(d_unique_grads);

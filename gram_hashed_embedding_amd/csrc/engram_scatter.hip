@@ -115,6 +115,8 @@ int engram::launch_apply(const void *grads, int64_t n, int64_t dim, int64_t tabl
   a.plan = v.scalars;
   a.num_unique = o.num_unique;
   a.err = err;
+  // (the entry points have checked this grid before enqueuing anything)
+  if (!grid_fits(apply_blocks(p, dim), kWalkThreads)) return ENGRAM_EINVAL;
   hipStream_t s = as_stream(stream);
   if (o.mode == kOutSparse)
     walk_sparse(a, s);
@@ -138,7 +140,7 @@ int engram::launch_scatter_atomic(const int64_t *ids, int64_t n, const void *gra
   const int64_t total = n * cpr;
   const int64_t per_block = (int64_t)kAtomicThreads * kAtomicUnroll;
   const int64_t blocks = (total + per_block - 1) / per_block;
-  if (blocks > INT32_MAX) return ENGRAM_EINVAL;
+  if (!grid_fits(blocks, kAtomicThreads)) return ENGRAM_EINVAL;
   const u32x4 *g = static_cast<const u32x4 *>(grads);
   const dim3 grid((unsigned)blocks), block(kAtomicThreads);
   switch (cpr) {

@@ -338,10 +338,10 @@ __global__ __launch_bounds__(kSortThreads) void onesweep_kernel(
 
 // ---------------------------------------------------------- plan from tokens
 // The first kernel of a plan made from the tokens: the row of every lookup
-// is computed as the hash kernel does (64 tokens per block; one lane per
-// token computes its order mixes, then the block's 64 * H outputs in flat
-// order), written as its 32-bit sort key, and counted into every pass's
-// digit histogram.  Hashed rows are always inside the table.
+// is computed as the hash kernel does (64 tokens at a time per block; one
+// lane per token computes its order mixes, then the block's 64 * H outputs
+// in flat order), written as its 32-bit sort key, and counted into every
+// pass's digit histogram.  Hashed rows are always inside the table.
 __global__ __launch_bounds__(kSortThreads) void plan_hash_kernel(const HashParams hp,
                                                                  int64_t total_tokens,
                                                                  int passes, int per_pass,
@@ -351,31 +351,34 @@ __global__ __launch_bounds__(kSortThreads) void plan_hash_kernel(const HashParam
   __shared__ uint64_t s_mix[kTokens][ENGRAM_MAX_NGRAM - 1];
   __shared__ uint32_t s_hist[4][kMaxBins];
   const int tid = threadIdx.x;
-  const int64_t tok0 = (int64_t)blockIdx.x * kTokens;
   for (int d = tid; d < 4 * kMaxBins; d += kSortThreads) (&s_hist[0][0])[d] = 0;
-  if (tid < kTokens && tok0 + tid < total_tokens) {
-    uint64_t mix[ENGRAM_MAX_NGRAM - 1];
-    token_mixes(hp, tok0 + tid, mix);
+  // (blocks stride over the tokens when there are more than one grid's worth)
+  for (int64_t tok0 = (int64_t)blockIdx.x * kTokens; tok0 < total_tokens;
+       tok0 += (int64_t)gridDim.x * kTokens) {
+    if (tid < kTokens && tok0 + tid < total_tokens) {
+      uint64_t mix[ENGRAM_MAX_NGRAM - 1];
+      token_mixes(hp, tok0 + tid, mix);
 #pragma unroll
-    for (int k = 0; k < ENGRAM_MAX_NGRAM - 1; ++k)
-      if (k < hp.n - 1) s_mix[tid][k] = mix[k];
-  }
-  __syncthreads();
-  const int ntok = (int)min((int64_t)kTokens, total_tokens - tok0);
-  const int nout = ntok * hp.H;
-  uint32_t *out = keys + tok0 * hp.H;
-  for (int o = tid; o < nout; o += kSortThreads) {
-    const int tl = o / hp.H;
-    const int h = o - tl * hp.H;
-    const uint32_t k = (uint32_t)head_row(hp, s_mix[tl][h / hp.J], h);
-    out[o] = k;
-    for (int q = 0; q < passes; ++q) {
-      const int shift = q * per_pass;
-      const int width = bits - shift < per_pass ? bits - shift : per_pass;
-      atomicAdd(&s_hist[q][(k >> shift) & ((1u << width) - 1u)], 1u);
+      for (int k = 0; k < ENGRAM_MAX_NGRAM - 1; ++k)
+        if (k < hp.n - 1) s_mix[tid][k] = mix[k];
     }
+    __syncthreads();
+    const int ntok = (int)min((int64_t)kTokens, total_tokens - tok0);
+    const int nout = ntok * hp.H;
+    uint32_t *out = keys + tok0 * hp.H;
+    for (int o = tid; o < nout; o += kSortThreads) {
+      const int tl = o / hp.H;
+      const int h = o - tl * hp.H;
+      const uint32_t k = (uint32_t)head_row(hp, s_mix[tl][h / hp.J], h);
+      out[o] = k;
+      for (int q = 0; q < passes; ++q) {
+        const int shift = q * per_pass;
+        const int width = bits - shift < per_pass ? bits - shift : per_pass;
+        atomicAdd(&s_hist[q][(k >> shift) & ((1u << width) - 1u)], 1u);
+      }
+    }
+    __syncthreads();  // s_mix is rewritten for the next tokens
   }
-  __syncthreads();
   uint32_t *copy = hist + (int64_t)(blockIdx.x % kHistCopies) * 4 * kMaxBins;
   for (int d = tid; d < passes * kMaxBins; d += kSortThreads) {
     const uint32_t c = (&s_hist[0][0])[d];
@@ -794,6 +797,17 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
   uint32_t *hist = v.counters + kTicketWords;  // [copy][segment][4][kMaxBins]
   SortLayout L = whole_sort(p, n);
   const bool heads = ids == nullptr && head_sort(*hp, n / hp->H, p, &L);
+  const int64_t sort_words = (int64_t)L.passes * L.num_tiles * kMaxBins;
+  const int64_t status_len = sort_words + p.slot_tiles;
+  const int64_t counters_len = kTicketWords + (int64_t)L.sg.copies * L.sg.count * 4 * kMaxBins;
+  const int64_t clear_len = status_len > counters_len ? status_len : counters_len;
+  // every grid inside the launch limit, checked before anything is enqueued
+  // (below n = 2^32 they all are; the token hash of a flat plan strides)
+  const int64_t head_chunks = (L.sg.len + kHeadTokens - 1) / kHeadTokens;
+  if (!grid_fits(p.num_tiles, kSortThreads) || !grid_fits(L.num_tiles, kSortThreads) ||
+      !grid_fits(p.slot_tiles, kSlotThreads) || !grid_fits((clear_len + 255) / 256, 256) ||
+      !grid_fits(L.sg.count * head_chunks, kHeadThreads))
+    return ENGRAM_EINVAL;
   if (heads && L.sg.len <= kLdsSortKeys) {
     // small segments: one kernel sorts every head's keys in LDS, into the
     // buffers the apply reads (those the last pass of a sort would fill)
@@ -824,10 +838,6 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
                        tickets + kSlotTicketAt, v.head_off, v.scalars, err);
     return launch_status();
   }
-  const int64_t sort_words = (int64_t)L.passes * L.num_tiles * kMaxBins;
-  const int64_t status_len = sort_words + p.slot_tiles;
-  const int64_t counters_len = kTicketWords + (int64_t)L.sg.copies * L.sg.count * 4 * kMaxBins;
-  const int64_t clear_len = status_len > counters_len ? status_len : counters_len;
   hipLaunchKernelGGL(sort_clear_kernel, dim3((unsigned)((clear_len + 255) / 256)), dim3(256), 0,
                      s, v.status, status_len, v.counters, (int)counters_len, v.scalars);
   // The passes alternate between the two key/index buffers and end in the
@@ -845,7 +855,7 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
     hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)p.num_tiles), dim3(kSortThreads), 0,
                        s, ids, n, table_rows, L.passes, L.per_pass, L.bits, hist, err);
   } else if (heads) {
-    const int64_t chunks = (L.sg.len + kHeadTokens - 1) / kHeadTokens;
+    const int64_t chunks = head_chunks;
     const dim3 grid((unsigned)(L.sg.count * chunks));
     switch (hp->n) {
 #define ENGRAM_PLAN_HEADS_CASE(N)                                                             \
@@ -864,7 +874,8 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
     }
   } else {  // keys in flat order
     const int64_t tokens = n / hp->H;
-    hipLaunchKernelGGL(plan_hash_kernel, dim3((unsigned)((tokens + 63) / 64)),
+    const int64_t need = (tokens + 63) / 64, most = kMaxGridItems / kSortThreads;
+    hipLaunchKernelGGL(plan_hash_kernel, dim3((unsigned)(need < most ? need : most)),
                        dim3(kSortThreads), 0, s, *hp, tokens, L.passes, L.per_pass, L.bits,
                        hashed, hist);
   }

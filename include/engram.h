@@ -44,6 +44,15 @@
  * - Layouts are row-major and contiguous.  bf16 data is passed as void*.
  * - head_dim, wherever it is taken, is at most 2^30 (the sorted scatter and
  *   its plan: at most 2048); larger values are EINVAL.
+ * - A kernel launch holds at most 2^32 - 1 threads (the dispatch packet
+ *   counts them in 32 bits).  The hash kernels stride over any number of
+ *   tokens; a call whose other kernels would need a larger launch returns
+ *   EINVAL before enqueuing anything.  That bounds engram_gather to
+ *   n * head_dim <= 8 * 8,589,934,080, engram_lookup(_slice) to n lookups <=
+ *   16,777,215 * r (r = 1024 / (head_dim / 8) rows, clamped to [32, 256]),
+ *   and the sorted scatter (every call that plans or applies) to n <=
+ *   4,294,704,896 at head_dim 40..64, 2,147,352,448 at 72..128 and
+ *   1,073,676,224 above 128 (the workspace query returns (size_t)-1 there).
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H

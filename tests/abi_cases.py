@@ -125,6 +125,34 @@ def case_scatter_rejects(lib):
         abi.ENGRAM_EWORKSPACE
 
 
+# The largest n the sorted path takes at each walker width (its apply launch
+# holds at most 2^32 - 1 threads: 16 ids a walker of head_dim / 4 lanes, as a
+# power of two up to 64; below 40 values the 32-bit ids bind first).
+SORTED_LAUNCH_LIMITS = [(8, 4294967294), (32, 4294967294), (64, 4294704896),
+                        (128, 2147352448), (136, 1073676224), (256, 1073676224),
+                        (2048, 1073676224)]
+
+
+def case_sorted_launch_limits(lib):
+    w = lib.engram_scatter_add_workspace
+    for dim, most in SORTED_LAUNCH_LIMITS:
+        assert w(most, 1000, dim, abi.SCATTER_ROWSPARSE) != BAD_SIZE, dim
+        assert w(most + 1, 1000, dim, abi.SCATTER_ROWSPARSE) == BAD_SIZE, dim
+        assert w(most + 1, 1000, dim, abi.SCATTER_SORTED) == BAD_SIZE, dim
+    n, big = 1073676224 + 1, 1 << 62
+    assert lib.engram_scatter_plan(ALIGNED, n, 1000, 256, ALIGNED, big, None, None) == \
+        abi.ENGRAM_EINVAL
+    assert lib.engram_scatter_apply(ALIGNED, n, 256, 1000, ALIGNED, None, None, None, ALIGNED,
+                                    big, None, None) == abi.ENGRAM_EINVAL
+    assert lib.engram_scatter_apply_signsgd(ALIGNED, n, 256, 1000, ALIGNED, 0.5, ALIGNED, big,
+                                            None, None) == abi.ENGRAM_EINVAL
+    assert lib.engram_scatter_add(ALIGNED, n, ALIGNED, 256, ALIGNED, 1000, abi.SCATTER_SORTED,
+                                  ALIGNED, big, None, None) == abi.ENGRAM_EINVAL
+    assert lib.engram_scatter_add_rowsparse(ALIGNED, n, ALIGNED, 256, 1000, ALIGNED, ALIGNED,
+                                            ALIGNED, ALIGNED, big, None, None) == \
+        abi.ENGRAM_EINVAL
+
+
 def case_plan_apply_reject(lib):
     ws = _ws(lib, 100, 50, 8, 2)
     pl, ap = lib.engram_scatter_plan, lib.engram_scatter_apply

@@ -42,9 +42,10 @@ int launch_plan(const int64_t *d_row_ids, const HashParams *hp, int64_t n, int64
   return ENGRAM_OK;
 }
 
-int launch_apply(const void *d_grads, int64_t n, int64_t head_dim, int64_t, const Plan &,
+int launch_apply(const void *d_grads, int64_t n, int64_t head_dim, int64_t, const Plan &p,
                  void *d_workspace, const ApplyOut &o, int64_t *, void *) {
   require(n > 0 && d_grads != nullptr && d_workspace != nullptr && head_dim % 8 == 0);
+  require(grid_fits(apply_blocks(p, head_dim), kWalkThreads));
   require(o.mode == kOutSignSGD ? o.table != nullptr
           : o.mode == kOutDense ? o.grad_table != nullptr
                                 : o.unique_ids != nullptr && o.unique_grads != nullptr &&

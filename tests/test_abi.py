@@ -28,6 +28,24 @@ def test_abi_case(case):
     case(e._lib)
 
 
+def test_launch_limits_of_the_gather_and_lookup():
+    """Sizes whose kernel launch would pass 2^32 - 1 threads are refused by
+    the library's launchers before any HIP call (the fake, aligned addresses
+    are never read)."""
+    lib, A = e._lib, abi_cases.ALIGNED
+    most_blocks = (2 ** 32 - 1) // 256
+    # gather, head_dim 8: 512 ids per 256-thread block; a table of no rows: 256
+    assert lib.engram_gather(A, most_blocks * 512 + 1, A, 1000, 8, A, None, None) == \
+        e.ENGRAM_EINVAL
+    assert lib.engram_gather(A, most_blocks * 256 + 1, A, 0, 8, A, None, None) == \
+        e.ENGRAM_EINVAL
+    # fused lookup, head_dim 8: 256 lookups per block (one head: ngram 2, one head per order)
+    one = abi_cases._arr((1, 3))
+    seq = most_blocks * 256 + 1
+    assert lib.engram_lookup(A, None, 1, seq, 2, 1, 0, one, abi_cases._arr((5,)),
+                             abi_cases._arr((0,)), A, 5, 8, A, None, None) == e.ENGRAM_EINVAL
+
+
 def test_binding_raises_on_bad_workspace_query():
     with pytest.raises(e.EngramError):
         e.engram_scatter_add_workspace(10, 50, 12, 0)

@@ -1,4 +1,6 @@
-"""The sorted scatter-add past 2^31 ids, near the largest input it takes
+"""Inputs past 2^31 lookups.
+
+The sorted scatter-add near the largest input it takes
 (n < 2^32 - 1: its plan keeps 32-bit sorted keys, flat indices, positions
 and slots).  N = 2^31 + 2^20 + 123 ids into a table of M = 1,000,003 rows:
 id i is row i mod M, so every row holds about 2,150 positions spread over
@@ -11,11 +13,22 @@ counted twice changes a result.  Checked: the dense table's column totals
 against fp64 totals of the gradients (torch on the device), and 512
 sampled rows (the first, the last, and the row of position 2^31 among
 them) against the oracle, which sums each row's gradient rows copied to
-the host.  About 100 GB of device memory."""
+the host.  About 100 GB of device memory.
+
+The forward (hash and fused lookup) over one row of 2^30 + 77 tokens with
+two heads (a bigram and a trigram head): 2^31 + 154 lookups, and a hash
+grid the kernel covers by striding (64 tokens of 256 threads a block would
+take more than 2^32 - 1 threads in one launch).  Every output
+row is compared with torch's index_select of the hashed ids, and the ids
+and output rows of 4,096 sampled positions (the first, the last, and those
+on both sides of lookup index 2^31 among them) with the oracle, which
+hashes each sampled position's window of tokens and gathers from a host
+copy of the rows it names.  About 60 GB of device memory."""
 import numpy as np
 import pytest
 import torch
 
+from gram_hashed_embedding_amd import workloads
 from tests.gpu_helpers import bits, dev, host_f32, needs_gpu, release
 
 pytestmark = needs_gpu
@@ -62,4 +75,54 @@ def test_sorted_scatter_past_2_31_ids(oracle):
     got = host_f32(gtab.index_select(0, dev(rows)))
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
     del ids, grads, gtab, pos_d
+    release()
+
+
+T = (1 << 30) + 77  # tokens of the forward: two heads, 2^31 + 154 lookups
+COMPARE = 1 << 24   # output rows per index_select comparison
+
+
+def test_forward_past_2_31_lookups(oracle):
+    n, J, eos = 3, 1, 0
+    mult = [3, 1_000_003, 7919 * 65537]
+    primes, offs = [999_983, 1_000_003], [0, 999_983]
+    hargs = (n, J, eos, mult, primes, offs)
+    rows_total = sum(primes)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(2031)
+    tok = torch.randint(0, 50_000, (1, T), generator=gen, device="cuda", dtype=torch.int64)
+    table = workloads.make_table(rows_total, D, 2031, "cuda")
+    print(f"lookup of {T} tokens x 2 heads", flush=True)
+    out = E.engram_lookup(tok, table, *hargs)
+    ids = E.engram_hash(tok, *hargs, rows_total)
+    torch.cuda.synchronize()
+    flat_ids, flat_out = ids.view(-1), out.view(-1, D)
+    for c0 in range(0, flat_ids.numel(), COMPARE):
+        c1 = min(c0 + COMPARE, flat_ids.numel())
+        want = table.index_select(0, flat_ids[c0:c1])
+        assert torch.equal(flat_out[c0:c1].view(torch.int16), want.view(torch.int16)), c0
+        del want
+
+    rng = np.random.Generator(np.random.PCG64(2031))
+    ts = np.unique(np.concatenate([np.array([0, 1, 2, (1 << 30) - 1, 1 << 30, T - 1]),
+                                   rng.choice(T, 4090, replace=False)]))
+    # the oracle's rows of each sampled position, from the n tokens ending there
+    # (the history reaches n - 1 tokens back; positions 0 and 1 from the row's start)
+    tok_row = tok[0]
+    want_ids = np.empty((ts.size, 2), dtype=np.int64)
+    for k, t in enumerate(ts[ts < n - 1]):
+        want_ids[k] = oracle.hash(tok_row[:t + 1].cpu().numpy()[None], *hargs)[0, -1]
+    late = ts >= n - 1
+    win = dev(ts[late][:, None] + np.arange(-(n - 1), 1))
+    windows = tok_row.index_select(0, win.view(-1)).view(-1, n).cpu().numpy()
+    want_ids[late] = oracle.hash(windows, *hargs)[:, -1]
+    ts_d = dev(ts)
+    assert np.array_equal(ids[0].index_select(0, ts_d).cpu().numpy(), want_ids)
+    uniq, local = np.unique(want_ids.reshape(-1), return_inverse=True)
+    small_table = bits(table.index_select(0, dev(uniq)))
+    want_rows, bad = oracle.gather(local.astype(np.int64), small_table)
+    assert bad == 0
+    got = bits(out[0].index_select(0, ts_d).reshape(-1, D))
+    assert np.array_equal(got, want_rows)
+    del tok, table, out, ids, flat_ids, flat_out
     release()
