@@ -75,6 +75,7 @@ struct WalkArgs {
   double *partials;        // per chunk: [2, dim] fp64 rows (run entering, run leaving)
   int64_t num_chunks;
   uint32_t long_blocks;    // leading blocks of the grid: they sum long runs by chunk
+  uint32_t long_group;     // consecutive chunks a long block takes at a time
   const PlanScalars *plan;  // U, the stall flag and the stamp, from the plan
   int64_t *num_unique;      // row-sparse output count
   int64_t *err;             // error counter, or null
@@ -421,7 +422,7 @@ __device__ __forceinline__ void store_partial(const WalkArgs &a, f64x2 *row, int
 // the chunk offsets of its first and last distinct-row starts and the slot
 // of its last distinct row.  Keys and indices arrive as 16-byte vectors.
 constexpr int kChunkRanges = (int)(kChunk / kRange);
-constexpr int kGroupChunks = 4;
+constexpr int kGroupChunks = kLongGroup;
 constexpr int kHalo = 2 * kRange;
 constexpr int kChunkKeys = kHalo + (int)kChunk + kHalo;
 
@@ -672,16 +673,17 @@ __device__ __forceinline__ void long_chunk(const WalkArgs &a, int64_t j, int k, 
 }
 
 // Long runs (hot rows, longer than a range), chunk by chunk.  Long block l
-// of nlong takes a contiguous share of the chunks, kGroupChunks at a time.
+// of nlong takes the groups of a.long_group consecutive chunks l, l + nlong,
+// l + 2 nlong, ... (a.long_group <= kGroupChunks), so a stretch of hot
+// chunks (a padding row) is spread over all long blocks.
 template <int L, int Q, int OUT, bool EXACT, bool NT>
 __device__ __forceinline__ void long_chunks(const WalkArgs &a, int64_t l, int64_t nlong) {
   static_assert(kChunkRanges == 32 && kWalkThreads % 64 == 0,
                 "a chunk's ranges are one half of a wavefront");
   __shared__ LongLds<L> s;
-  const int64_t per = (a.num_chunks + nlong - 1) / nlong;
-  const int64_t first = l * per, last = min(first + per, a.num_chunks);
-  for (int64_t j0 = first; j0 < last; j0 += kGroupChunks) {
-    const int cnt = (int)min((int64_t)kGroupChunks, last - j0);
+  const int64_t per = a.long_group;
+  for (int64_t j0 = l * per; j0 < a.num_chunks; j0 += nlong * per) {
+    const int cnt = (int)min(per, a.num_chunks - j0);
     load_group<L>(a, j0, cnt, s);
 #pragma unroll 1
     for (int k = 0; k < cnt; ++k) long_chunk<L, Q, OUT, EXACT, NT>(a, j0 + k, k, cnt, s);
@@ -827,10 +829,9 @@ __global__ __launch_bounds__(kWalkThreads) void combine_kernel(const WalkArgs a)
 template <int L, int Q, int OUT>
 void launch_walkers(WalkArgs a, hipStream_t s) {
   const int64_t walker_blocks = (a.num_ranges * L + kWalkThreads - 1) / kWalkThreads;
-  // long blocks: about two chunks each, at most kLongBlocks (the grid is
-  // apply_blocks(), which the entry points have checked)
-  const int64_t nlong = (a.num_chunks + 1) / 2;
-  a.long_blocks = (uint32_t)(nlong < kLongBlocks ? nlong : kLongBlocks);
+  // (the grid is apply_blocks(), which the entry points have checked)
+  a.long_blocks = (uint32_t)long_blocks(a.num_chunks);
+  a.long_group = (uint32_t)long_group(a.num_chunks);
   const unsigned blocks = (unsigned)(a.long_blocks + walker_blocks);
   const bool exact = a.quads == (int64_t)Q * L;
   if (exact && a.stream_grads)

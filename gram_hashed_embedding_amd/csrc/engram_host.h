@@ -103,12 +103,25 @@ constexpr int kSortCounters = kTicketWords + kHistSets * 4 * kMaxBins;
 constexpr int64_t kChunk = 512;
 
 // The apply's launch: blocks of kWalkThreads threads, the first
-// min((chunks + 1) / 2, kLongBlocks) summing long runs, then the range
-// walkers, one per kRange sorted positions, walker_lanes(head_dim / 4)
-// lanes each (one 4-value quad of the row per lane, the quad count rounded
-// up to a power of two, at most one wavefront).
+// long_blocks(chunks) summing long runs, then the range walkers, one per
+// kRange sorted positions, walker_lanes(head_dim / 4) lanes each (one 4-value
+// quad of the row per lane, the quad count rounded up to a power of two, at
+// most one wavefront).  Long blocks take groups of long_group(chunks)
+// consecutive chunks (at most kLongGroup), the groups dealt out to them in
+// turn: one chunk each while there are at most kLongBlocks chunks, and never
+// more than kLongBlocks of them, so that at any size they share the GPU with
+// the walkers from the start.
 constexpr int kWalkThreads = 256;
-constexpr int64_t kLongBlocks = 1024;
+constexpr int kLongGroup = 4;
+constexpr int64_t kLongBlocks = 256;
+inline int64_t long_blocks(int64_t num_chunks) {
+  return num_chunks < kLongBlocks ? num_chunks : kLongBlocks;
+}
+inline int64_t long_group(int64_t num_chunks) {
+  const int64_t nlong = long_blocks(num_chunks);
+  const int64_t per = nlong > 0 ? (num_chunks + nlong - 1) / nlong : 1;
+  return per < kLongGroup ? per : kLongGroup;
+}
 inline int64_t walker_lanes(int64_t quads) {
   int64_t l = 2;
   while (l < quads && l < 64) l *= 2;
@@ -127,9 +140,8 @@ struct Plan {
 
 // Blocks of the apply's first launch for a plan of rows head_dim wide.
 inline int64_t apply_blocks(const Plan &p, int64_t head_dim) {
-  const int64_t nlong = (p.num_chunks + 1) / 2;
   const int64_t walkers = p.num_ranges * walker_lanes(head_dim / 4);
-  return (nlong < kLongBlocks ? nlong : kLongBlocks) + (walkers + kWalkThreads - 1) / kWalkThreads;
+  return long_blocks(p.num_chunks) + (walkers + kWalkThreads - 1) / kWalkThreads;
 }
 
 // The plan's scalars at Plan::scalars (the start of the workspace): written

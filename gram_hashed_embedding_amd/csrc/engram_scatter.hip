@@ -112,6 +112,7 @@ int engram::launch_apply(const void *grads, int64_t n, int64_t dim, int64_t tabl
   a.partials = v.partials;
   a.num_chunks = p.num_chunks;
   a.long_blocks = 0;  // set with the grid
+  a.long_group = 1;
   a.plan = v.scalars;
   a.num_unique = o.num_unique;
   a.err = err;

@@ -51,8 +51,8 @@
  *   n * head_dim <= 8 * 8,589,934,080, engram_lookup(_slice) to n lookups <=
  *   16,777,215 * r (r = 1024 / (head_dim / 8) rows, clamped to [32, 256]),
  *   and the sorted scatter (every call that plans or applies) to n <=
- *   4,294,704,896 at head_dim 40..64, 2,147,352,448 at 72..128 and
- *   1,073,676,224 above 128 (the workspace query returns (size_t)-1 there).
+ *   4,294,901,504 at head_dim 40..64, 2,147,450,752 at 72..128 and
+ *   1,073,725,376 above 128 (the workspace query returns (size_t)-1 there).
  */
 #ifndef ENGRAM_H
 #define ENGRAM_H

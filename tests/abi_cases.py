@@ -128,9 +128,9 @@ def case_scatter_rejects(lib):
 # The largest n the sorted path takes at each walker width (its apply launch
 # holds at most 2^32 - 1 threads: 16 ids a walker of head_dim / 4 lanes, as a
 # power of two up to 64; below 40 values the 32-bit ids bind first).
-SORTED_LAUNCH_LIMITS = [(8, 4294967294), (32, 4294967294), (64, 4294704896),
-                        (128, 2147352448), (136, 1073676224), (256, 1073676224),
-                        (2048, 1073676224)]
+SORTED_LAUNCH_LIMITS = [(8, 4294967294), (32, 4294967294), (64, 4294901504),
+                        (128, 2147450752), (136, 1073725376), (256, 1073725376),
+                        (2048, 1073725376)]
 
 
 def case_sorted_launch_limits(lib):
@@ -139,7 +139,7 @@ def case_sorted_launch_limits(lib):
         assert w(most, 1000, dim, abi.SCATTER_ROWSPARSE) != BAD_SIZE, dim
         assert w(most + 1, 1000, dim, abi.SCATTER_ROWSPARSE) == BAD_SIZE, dim
         assert w(most + 1, 1000, dim, abi.SCATTER_SORTED) == BAD_SIZE, dim
-    n, big = 1073676224 + 1, 1 << 62
+    n, big = 1073725376 + 1, 1 << 62
     assert lib.engram_scatter_plan(ALIGNED, n, 1000, 256, ALIGNED, big, None, None) == \
         abi.ENGRAM_EINVAL
     assert lib.engram_scatter_apply(ALIGNED, n, 256, 1000, ALIGNED, None, None, None, ALIGNED,
