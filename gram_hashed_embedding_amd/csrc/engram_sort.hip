@@ -390,7 +390,8 @@ __global__ __launch_bounds__(kSortThreads) void plan_hash_kernel(const HashParam
 // block takes kHeadTokens tokens of one head (segment s hashes head head[s];
 // a segment is `chunks` blocks), writes each key at its segment's position
 // (segment s, token t: s * tokens + t) and counts its digits (of key -
-// base[s]) into the segment's histograms, one flush per block.  A thread
+// base[s], from bit `lo` up) into the segment's histograms, one flush per
+// block.  A thread
 // takes kHeadItems tokens with all their history loads in flight together.
 // Blocks of kSortThreads threads, like the sort's, so the plan gets its
 // share of the GPU beside a forward running on another stream (blocks of
@@ -403,7 +404,7 @@ constexpr int kHeadTokens = kHeadThreads * kHeadItems;
 template <int N>
 __global__ __launch_bounds__(kHeadThreads) void plan_hash_heads_kernel(
     const HashParams hp, const SortSegs sg, int64_t chunks, int passes, int per_pass, int bits,
-    uint32_t *keys, uint32_t *hist) {
+    int lo, uint32_t *keys, uint32_t *hist) {
   __shared__ uint32_t s_hist[4][kMaxBins];
   const int tid = threadIdx.x;
   const int64_t seg = blockIdx.x / chunks;
@@ -428,7 +429,7 @@ __global__ __launch_bounds__(kHeadThreads) void plan_hash_heads_kernel(
     const uint32_t key = (uint32_t)head_row(hp, m, h);
     out[t] = key;
     for (int q = 0; q < passes; ++q) {
-      const int shift = q * per_pass;
+      const int shift = lo + q * per_pass;
       const int width = bits - shift < per_pass ? bits - shift : per_pass;
       atomicAdd(&s_hist[q][((key - kbase) >> shift) & ((1u << width) - 1u)], 1u);
     }
@@ -577,6 +578,206 @@ __global__ __launch_bounds__(kLdsSortThreads) void plan_heads_lds_kernel(
     if (pos(i) < len) {
       keys_out[seg0 + pos(i)] = key[i];
       vals_out[seg0 + pos(i)] = val[i];
+    }
+  }
+}
+
+// ------------------------------------------- buckets after a top pass ---
+// A per-head plan of more than kLdsSortKeys keys a head on 17 to 24 bits
+// sorts in two steps: one one-sweep pass on the bits above the low
+// kBucketLow (stable, so every bucket -- the keys of one head whose top
+// digit is equal -- holds its keys in flat order), then this kernel sorts
+// each bucket on the low kBucketLow bits, in place, with two stable LSD
+// passes of 8 bits.  One block per (segment, top digit): the bucket's start
+// is the sum of the segment's top-digit counts below it.  A bucket of at
+// most kBucketKeys keys is sorted in LDS (the keys in (wave, round, lane)
+// order, as few rounds as it needs, ranked by wavefront multi-split, each
+// pass's digit starts by a block scan), read and written once.  A larger one
+// (a hot row's run) is sorted through global memory by the same block: per
+// pass, its digit totals, then tile after tile ranked as above and written
+// at its digits' running offsets, into the segment's scratch copy and back.
+// The result is the order the full LSD sort gives: stable passes over all
+// bits, low first.
+constexpr int kBucketLow = 16;  // bits the buckets are sorted on
+constexpr int kBucketThreads = 256;
+constexpr int kBucketWaves = kBucketThreads / kWave;
+constexpr int kBucketItems = 8;
+constexpr int kBucketKeys = kBucketThreads * kBucketItems;
+static_assert(kBucketThreads == kMaxBins && kBucketLow == 16,
+              "one thread per digit of a top pass of at most 8 bits, and of an 8-bit pass");
+
+// Ranks of one tile's keys by digit ((key - kbase) >> shift) & mask.  Item
+// i (i < rounds) of a thread sits at tile position (wave * rounds + i) * 64
+// + lane, and positions below `count` hold keys.  rank[i] receives the
+// item's place among its wave's keys of its digit, s_cnt[w][d] the start of
+// wave w's keys of digit d among the tile's, and (threads below `bins`)
+// *total the tile's count of digit tid.  Ends with a barrier.
+__device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[kBucketItems], int count,
+                                                  int rounds, uint32_t kbase, int shift, int width,
+                                                  uint32_t (&s_cnt)[kBucketWaves][kMaxBins],
+                                                  uint32_t (&rank)[kBucketItems],
+                                                  uint32_t *total) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const uint32_t mask = (1u << width) - 1u;
+  const int bins = 1 << width;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  for (int d = tid; d < kBucketWaves * kMaxBins; d += kBucketThreads) (&s_cnt[0][0])[d] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kBucketItems; ++i) {
+    if (i >= rounds) break;  // (block-uniform)
+    const bool valid = (wave * rounds + i) * kWave + lane < count;
+    const uint32_t d = ((key[i] - kbase) >> shift) & mask;
+    unsigned long long peers = __ballot(valid);
+    for (int b = 0; b < width; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const unsigned long long bal = __ballot(bit);
+      peers &= bit ? bal : ~bal;
+    }
+    rank[i] = 0;
+    if (valid) {
+      const uint32_t prior = s_cnt[wave][d];
+      rank[i] = prior + (uint32_t)__popcll(peers & below);
+      if ((peers & below) == 0ull) s_cnt[wave][d] = prior + (uint32_t)__popcll(peers);
+    }
+  }
+  __syncthreads();
+  if (tid < bins) {
+    uint32_t t = 0;
+    for (int w = 0; w < kBucketWaves; ++w) {
+      const uint32_t c = s_cnt[w][tid];
+      s_cnt[w][tid] = t;
+      t += c;
+    }
+    *total = t;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
+    const SortSegs sg, int top_bits, const uint32_t *hist, uint32_t *keys, uint32_t *vals,
+    uint32_t *tmp_keys, uint32_t *tmp_vals) {
+  constexpr int low_bits = kBucketLow;
+  __shared__ uint2 s_buf[kBucketKeys];  // (key, flat index) pairs
+  __shared__ uint32_t s_cnt[kBucketWaves][kMaxBins];
+  __shared__ uint32_t s_start[kMaxBins];  // start of each digit (tile, or bucket's running)
+  __shared__ uint32_t s_bucket[2];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int64_t seg = blockIdx.x >> top_bits;
+  const int top = (int)(blockIdx.x & ((1u << top_bits) - 1u));
+  uint32_t all;
+  // the top pass's digit totals
+  const uint32_t c = tid < (1 << top_bits) ? hist[seg * 4 * kMaxBins + tid] : 0u;
+  const uint32_t before = block_exclusive_scan<kBucketThreads>(c, all);
+  if (tid == top) {
+    s_bucket[0] = before;
+    s_bucket[1] = c;
+  }
+  __syncthreads();
+  const int64_t b0 = seg * sg.len + s_bucket[0];
+  const uint32_t m = s_bucket[1];
+  if (m < 2) return;  // (block-uniform)
+  const uint32_t kbase = sg.base[seg];
+  const int w0 = (low_bits + 1) / 2;
+  // rounds of 64 keys a wave: as few as the tile needs, so a small bucket's
+  // keys are spread over all the waves
+  int rounds = kBucketItems;
+  auto pos = [&](int i) { return (wave * rounds + i) * kWave + lane; };
+  uint32_t key[kBucketItems], val[kBucketItems], rank[kBucketItems];
+  uint32_t total = 0;
+  if (m <= (uint32_t)kBucketKeys) {
+    rounds = (int)((m + kBucketThreads - 1) / kBucketThreads);
+#pragma unroll
+    for (int i = 0; i < kBucketItems; ++i) {
+      if (i >= rounds) break;
+      const int64_t q = b0 + min((uint32_t)pos(i), m - 1);
+      key[i] = keys[q];
+      val[i] = vals[q];
+    }
+    for (int pass = 0; pass < 2; ++pass) {
+      const int shift = pass == 0 ? 0 : w0;
+      const int width = pass == 0 ? w0 : low_bits - w0;
+      bucket_tile_ranks(key, (int)m, rounds, kbase, shift, width, s_cnt, rank, &total);
+      const uint32_t start = block_exclusive_scan<kBucketThreads>(tid < (1 << width) ? total
+                                                                                      : 0u, all);
+      if (tid < (1 << width)) s_start[tid] = start;
+      __syncthreads();
+      const uint32_t mask = (1u << width) - 1u;
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        if (i >= rounds) break;
+        const uint32_t d = ((key[i] - kbase) >> shift) & mask;
+        rank[i] += s_start[d] + s_cnt[wave][d];
+      }
+      // keys with their flat indices through LDS into the pass's order
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        if (i >= rounds) break;
+        if ((uint32_t)pos(i) < m) s_buf[rank[i]] = uint2{key[i], val[i]};
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        if (i >= rounds) break;
+        if ((uint32_t)pos(i) < m) {
+          const uint2 kv = s_buf[pos(i)];
+          key[i] = kv.x;
+          val[i] = kv.y;
+        }
+      }
+      __syncthreads();  // s_buf, s_cnt and s_start are rewritten by the next pass
+    }
+#pragma unroll
+    for (int i = 0; i < kBucketItems; ++i) {
+      if (i >= rounds) break;
+      if ((uint32_t)pos(i) < m) {
+        keys[b0 + pos(i)] = key[i];
+        vals[b0 + pos(i)] = val[i];
+      }
+    }
+    return;
+  }
+  // a bucket larger than the LDS buffer: each pass from one copy of the
+  // bucket's positions to the other (keys -> scratch -> keys)
+  for (int pass = 0; pass < 2; ++pass) {
+    const uint32_t *src_k = pass == 0 ? keys : tmp_keys, *src_v = pass == 0 ? vals : tmp_vals;
+    uint32_t *dst_k = pass == 0 ? tmp_keys : keys, *dst_v = pass == 0 ? tmp_vals : vals;
+    const int shift = pass == 0 ? 0 : w0;
+    const int width = pass == 0 ? w0 : low_bits - w0;
+    const uint32_t mask = (1u << width) - 1u;
+    const int bins = 1 << width;
+    // the bucket's digit totals, then each digit's start
+    s_start[tid] = 0;
+    __syncthreads();
+    for (uint32_t p = tid; p < m; p += kBucketThreads)
+      atomicAdd(&s_start[((src_k[b0 + p] - kbase) >> shift) & mask], 1u);
+    __syncthreads();
+    const uint32_t cnt = tid < bins ? s_start[tid] : 0u;
+    __syncthreads();
+    const uint32_t start = block_exclusive_scan<kBucketThreads>(cnt, all);
+    s_start[tid] = start;
+    __syncthreads();
+    for (uint32_t t0 = 0; t0 < m; t0 += kBucketKeys) {
+      const int count = (int)min((uint32_t)kBucketKeys, m - t0);
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        const int64_t q = b0 + t0 + min(pos(i), count - 1);
+        key[i] = src_k[q];
+        val[i] = src_v[q];
+      }
+      bucket_tile_ranks(key, count, rounds, kbase, shift, width, s_cnt, rank, &total);
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        if (pos(i) < count) {
+          const uint32_t d = ((key[i] - kbase) >> shift) & mask;
+          const int64_t q = b0 + s_start[d] + s_cnt[wave][d] + rank[i];
+          dst_k[q] = key[i];
+          dst_v[q] = val[i];
+        }
+      }
+      __syncthreads();  // every read of s_start and s_cnt is done
+      if (tid < bins) s_start[tid] += total;
+      __syncthreads();
     }
   }
 }
@@ -797,6 +998,12 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
   uint32_t *hist = v.counters + kTicketWords;  // [copy][segment][4][kMaxBins]
   SortLayout L = whole_sort(p, n);
   const bool heads = ids == nullptr && head_sort(*hp, n / hp->H, p, &L);
+  // per-head segments too large for the LDS plan, on 17 to 24 bits: one
+  // sort pass on the bits above the low kBucketLow, then each bucket on them
+  const bool buckets = heads && L.sg.len > kLdsSortKeys && L.bits > kBucketLow &&
+                       L.bits <= kBucketLow + 8;
+  const int top_bits = L.bits - kBucketLow;
+  if (buckets) L.passes = 1;
   const int64_t sort_words = (int64_t)L.passes * L.num_tiles * kMaxBins;
   const int64_t status_len = sort_words + p.slot_tiles;
   const int64_t counters_len = kTicketWords + (int64_t)L.sg.copies * L.sg.count * 4 * kMaxBins;
@@ -861,7 +1068,8 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
 #define ENGRAM_PLAN_HEADS_CASE(N)                                                             \
   case N:                                                                                     \
     hipLaunchKernelGGL(plan_hash_heads_kernel<N>, grid, dim3(kHeadThreads), 0, s, *hp, L.sg,    \
-                       chunks, L.passes, L.per_pass, L.bits, hashed, hist);                   \
+                       chunks, L.passes, buckets ? top_bits : L.per_pass, L.bits,             \
+                       buckets ? kBucketLow : 0, hashed, hist);                               \
     break;
       ENGRAM_PLAN_HEADS_CASE(2)
       ENGRAM_PLAN_HEADS_CASE(3)
@@ -880,8 +1088,9 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
                        hashed, hist);
   }
   for (int pass = 0; pass < L.passes; ++pass) {
-    const int shift = pass * L.per_pass;
-    const int width = L.bits - shift < L.per_pass ? L.bits - shift : L.per_pass;
+    const int shift = buckets ? kBucketLow : pass * L.per_pass;
+    const int width = buckets ? top_bits
+                              : (L.bits - shift < L.per_pass ? L.bits - shift : L.per_pass);
     const PassArgs a = {ids, pass == 0 ? hashed : out_k(pass - 1),
                         pass == 0 ? nullptr : out_v(pass - 1), table_rows, shift, width,
                         hist + pass * kMaxBins, v.status + (int64_t)pass * L.num_tiles * kMaxBins,
@@ -892,6 +1101,10 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
     else
       launch_pass<kSortItems / 2>(src, L, a, s);
   }
+  if (buckets)  // the top pass wrote the pair the apply reads; the hashed keys are scratch
+    hipLaunchKernelGGL(bucket_sort_kernel, dim3((unsigned)(L.sg.count << top_bits)),
+                       dim3(kBucketThreads), 0, s, L.sg, top_bits, hist, last_k, last_v, other_k,
+                       other_v);
   // distinct-row slots
   hipLaunchKernelGGL(range_slots_kernel, dim3((unsigned)p.slot_tiles), dim3(kSlotThreads), 0, s,
                      v.sorted_keys, n, (uint32_t)table_rows, p.num_ranges, v.status + sort_words,

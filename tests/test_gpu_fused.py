@@ -191,6 +191,51 @@ def test_token_plan_sizes_keep_the_sort_order(tokens):
     release()
 
 
+@pytest.mark.parametrize("case", ["zipf_21", "hot_21", "zipf_17", "hot_24", "zipf_25"])
+def test_token_plan_buckets_keep_the_sort_order(case):
+    """Per-head segments of more than 8192 keys on 17 to 24 bits are sorted by
+    one pass on the top 8 bits and then bucket by bucket (in LDS, or through
+    global memory for a bucket of more than 2048 keys: the "hot" cases hold a
+    row of about 5,000 terms per head); 25 bits keep the passes of the full
+    sort.  Either way the plan from the tokens holds exactly the order of the
+    plan of engram_hash's ids, with gradients whose sums depend on the order
+    of every row's terms (as in the test above)."""
+    kind, b = case.split("_")
+    n, J = 3, 2
+    H = (n - 1) * J
+    primes = workloads.primes_above(1 << (int(b) - 1), H)
+    offs = workloads.cumulative_offsets(primes)
+    rows = sum(primes)
+    mult = workloads.seeded_multipliers(n, 91)
+    rng = np.random.Generator(np.random.PCG64(int(b) * 7 + len(kind)))
+    tok = np.minimum(rng.zipf(1.2, (2, 6100)), 5000).astype(np.int64)
+    if kind == "hot":
+        tok[rng.random(tok.shape) < 0.7] = 5
+    args = (n, J, 0, mult, primes, offs)
+    R, dim = tok.size * H, 16
+    exp = rng.integers(127 - 6, 127 + 7, (R, dim)).astype(np.uint16)
+    gb = ((rng.integers(0, 2, (R, dim)).astype(np.uint16) << 15) | (exp << 7)
+          | rng.integers(0, 128, (R, dim)).astype(np.uint16))
+    big = rng.random((R, dim)) < 0.02
+    gb[big] = (np.uint16((127 + 40) << 7) | (rng.integers(0, 2, int(big.sum())).astype(np.uint16)
+                                              << 15))
+    grads = torch.from_numpy(gb.view(np.int16)).to("cuda").view(torch.bfloat16)
+    ws_t = plan_tokens(dev(tok), rows, dim, *args)
+    uid_t, val_t, cnt_t = apply(grads, ws_t, rows)
+    ids = E.engram_hash(dev(tok), *args, rows)
+    ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
+    uid_i, val_i, cnt_i = apply(grads, ws_i, rows)
+    torch.cuda.synchronize()
+    u = int(cnt_t.item())
+    assert u == int(cnt_i.item()) and u > 0
+    if kind == "hot":  # the hottest row outgrows the LDS buffer
+        assert int(torch.unique(ids, return_counts=True)[1].max()) > 4096
+    assert torch.equal(uid_t[:u], uid_i[:u])
+    assert torch.equal(uid_t[:u], torch.unique(ids))
+    assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
+    release()
+
+
 @pytest.mark.parametrize("layout", ["ascending", "descending", "shuffled", "gap",
                                     "overlapping", "shared"])
 def test_token_plan_head_layouts(layout):
