@@ -191,7 +191,8 @@ def test_token_plan_sizes_keep_the_sort_order(tokens):
     release()
 
 
-@pytest.mark.parametrize("case", ["zipf_21", "hot_21", "zipf_17", "hot_24", "zipf_25"])
+@pytest.mark.parametrize("case", ["zipf_21", "hot_21", "zipf_17", "hot_24", "zipf_25", "same_21",
+                                  "short_21"])
 def test_token_plan_buckets_keep_the_sort_order(case):
     """Per-head segments of more than 8192 keys on 17 to 24 bits are sorted by
     one pass on the top 8 bits and then bucket by bucket (in LDS, or through
@@ -199,7 +200,9 @@ def test_token_plan_buckets_keep_the_sort_order(case):
     row of about 5,000 terms per head); 25 bits keep the passes of the full
     sort.  Either way the plan from the tokens holds exactly the order of the
     plan of engram_hash's ids, with gradients whose sums depend on the order
-    of every row's terms (as in the test above)."""
+    of every row's terms (as in the test above).  "same": every token alike,
+    so each head's keys are one row in one bucket; "short": 8193 tokens, one
+    past the LDS plan's limit."""
     kind, b = case.split("_")
     n, J = 3, 2
     H = (n - 1) * J
@@ -208,9 +211,12 @@ def test_token_plan_buckets_keep_the_sort_order(case):
     rows = sum(primes)
     mult = workloads.seeded_multipliers(n, 91)
     rng = np.random.Generator(np.random.PCG64(int(b) * 7 + len(kind)))
-    tok = np.minimum(rng.zipf(1.2, (2, 6100)), 5000).astype(np.int64)
+    shape = (1, 8193) if kind == "short" else (2, 6100)
+    tok = np.minimum(rng.zipf(1.2, shape), 5000).astype(np.int64)
     if kind == "hot":
         tok[rng.random(tok.shape) < 0.7] = 5
+    if kind == "same":
+        tok[:] = 7
     args = (n, J, 0, mult, primes, offs)
     R, dim = tok.size * H, 16
     exp = rng.integers(127 - 6, 127 + 7, (R, dim)).astype(np.uint16)
@@ -228,7 +234,7 @@ def test_token_plan_buckets_keep_the_sort_order(case):
     torch.cuda.synchronize()
     u = int(cnt_t.item())
     assert u == int(cnt_i.item()) and u > 0
-    if kind == "hot":  # the hottest row outgrows the LDS buffer
+    if kind in ("hot", "same"):  # the hottest row outgrows the LDS buffer
         assert int(torch.unique(ids, return_counts=True)[1].max()) > 4096
     assert torch.equal(uid_t[:u], uid_i[:u])
     assert torch.equal(uid_t[:u], torch.unique(ids))
