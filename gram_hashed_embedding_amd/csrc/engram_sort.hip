@@ -738,22 +738,42 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
     return;
   }
   // a bucket larger than the LDS buffer: each pass from one copy of the
-  // bucket's positions to the other (keys -> scratch -> keys)
+  // bucket's positions to the other (keys -> scratch -> keys).  A pass whose
+  // keys all share one digit keeps their order and is skipped (a bucket of
+  // one hot row needs no pass at all); after an odd number of passes the
+  // bucket is copied back.
+  bool in_tmp = false;
   for (int pass = 0; pass < 2; ++pass) {
-    const uint32_t *src_k = pass == 0 ? keys : tmp_keys, *src_v = pass == 0 ? vals : tmp_vals;
-    uint32_t *dst_k = pass == 0 ? tmp_keys : keys, *dst_v = pass == 0 ? tmp_vals : vals;
+    const uint32_t *src_k = in_tmp ? tmp_keys : keys, *src_v = in_tmp ? tmp_vals : vals;
+    uint32_t *dst_k = in_tmp ? keys : tmp_keys, *dst_v = in_tmp ? vals : tmp_vals;
     const int shift = pass == 0 ? 0 : w0;
     const int width = pass == 0 ? w0 : low_bits - w0;
     const uint32_t mask = (1u << width) - 1u;
     const int bins = 1 << width;
-    // the bucket's digit totals, then each digit's start
+    // the bucket's digit totals, kBucketKeys keys a round with every load in
+    // flight, then each digit's start; a bucket of one row (every key alike)
+    // is already in order
     s_start[tid] = 0;
     __syncthreads();
-    for (uint32_t p = tid; p < m; p += kBucketThreads)
-      atomicAdd(&s_start[((src_k[b0 + p] - kbase) >> shift) & mask], 1u);
-    __syncthreads();
+    const uint32_t first = src_k[b0];
+    bool differs = false;
+    for (uint32_t p0 = 0; p0 < m; p0 += kBucketKeys) {
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
+        key[i] = q < m ? src_k[b0 + q] : first;
+      }
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        if (p0 + (uint32_t)(i * kBucketThreads + tid) < m) {
+          atomicAdd(&s_start[((key[i] - kbase) >> shift) & mask], 1u);
+          differs = differs || key[i] != first;
+        }
+      }
+    }
+    if (!__syncthreads_or(differs)) break;  // (only at the first pass: the keys do not change)
     const uint32_t cnt = tid < bins ? s_start[tid] : 0u;
-    __syncthreads();
+    if (__syncthreads_or(cnt == m)) continue;  // one digit: the pass keeps the order
     const uint32_t start = block_exclusive_scan<kBucketThreads>(cnt, all);
     s_start[tid] = start;
     __syncthreads();
@@ -778,6 +798,25 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
       __syncthreads();  // every read of s_start and s_cnt is done
       if (tid < bins) s_start[tid] += total;
       __syncthreads();
+    }
+    in_tmp = !in_tmp;
+  }
+  if (in_tmp) {
+    for (uint32_t p0 = 0; p0 < m; p0 += kBucketKeys) {
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
+        key[i] = q < m ? tmp_keys[b0 + q] : 0u;
+        val[i] = q < m ? tmp_vals[b0 + q] : 0u;
+      }
+#pragma unroll
+      for (int i = 0; i < kBucketItems; ++i) {
+        const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
+        if (q < m) {
+          keys[b0 + q] = key[i];
+          vals[b0 + q] = val[i];
+        }
+      }
     }
   }
 }
