@@ -49,8 +49,10 @@ All inputs are resident in HBM before timing starts.
 `value` is row lookups per second over the whole step.  The roofline entry
 is for the step's dominant call, timed with HIP events on the stream it
 runs on: the forward as the step itself, the apply (its two launches) as
-back-to-back calls on one plan ("apply_back_to_back_ms").  The CPU baseline is the oracle on the host: one core, and the same
-source built with OpenMP on every thread the process may use.
+back-to-back calls on two batches' plans in turn ("apply_back_to_back_ms";
+the fused SignSGD apply as a single call).
+The CPU baseline is the oracle on the host: one core, and the same source
+built with OpenMP on every thread the process may use.
 
     python bench.py [--steps K] [--warmup W] [--no-other-configs]
                     [--workload e2e|e2e_signsgd|full|medium|backward|cp_slice|ple_conv]
@@ -678,21 +680,27 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
                       "step_algorithmic_bytes": sum(sep_bytes.values()),
                       "phases": phase_table(sep_phase_ms, sep_bytes)}
 
-    # the apply's own duration: back-to-back calls on one plan between two
-    # events on its stream (an event pair around a single call also counts
+    # the apply's own duration: back-to-back calls between two events on its
+    # stream (an event pair around a single call also counts
     # the host's submission of it whenever the GPU is ahead of the host, as on
     # the small backward workload)
+    # (The fused SignSGD apply runs slower back to back than in the step, 473
+    # against 421 us on one box, whose rocprofv3 average was 403 + 7 us: its
+    # roofline keeps the single call's time.)
     apply_b2b_ms = None
     if backward:
-        E.engram_scatter_plan_tokens(tokens[0], wl.table_rows, D, *hargs, seq_ids=segs[0],
-                                     workspace=wss[0], err_count=err)
+        # two batches' plans, applied in turn: consecutive applies touch
+        # different rows, as consecutive steps do
+        for k in range(2):
+            E.engram_scatter_plan_tokens(tokens[k], wl.table_rows, D, *hargs, seq_ids=segs[k],
+                                         workspace=wss[k], err_count=err)
         apply_backward(wss[0])
         torch.cuda.synchronize()
         a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = max(args.steps, 10)
         a_.record(stream)
-        for _ in range(reps):
-            apply_backward(wss[0])
+        for k in range(reps):
+            apply_backward(wss[k % 2])
         b_.record(stream)
         torch.cuda.synchronize()
         apply_b2b_ms = a_.elapsed_time(b_) / reps
@@ -709,7 +717,7 @@ def bench_step(args, torch, E, workloads, name, table=None, cpu=True):
     # a forward-only step is the one lookup launch, back to back: its time
     # per step is the kernel's own (an event pair around a single small
     # launch also counts the launch)
-    if dominant == "scatter_apply":
+    if dominant == "scatter_apply" and not signsgd:
         achieved = nbytes["scatter_apply"] / (apply_b2b_ms * 1e-3) / 1e9
     else:
         achieved = phases[dominant]["gbps"] if backward else step_gbps
