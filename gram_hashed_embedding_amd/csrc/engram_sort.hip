@@ -391,8 +391,8 @@ __global__ __launch_bounds__(kSortThreads) void plan_hash_kernel(const HashParam
 // a segment is `chunks` blocks), writes each key at its segment's position
 // (segment s, token t: s * tokens + t) and counts its digits (of key -
 // base[s], from bit `lo` up) into the segment's histograms, one flush per
-// block.  A thread
-// takes kHeadItems tokens with all their history loads in flight together.
+// block.  A thread takes kHeadItems tokens with all their history loads in
+// flight together.
 // Blocks of kSortThreads threads, like the sort's, so the plan gets its
 // share of the GPU beside a forward running on another stream (blocks of
 // 1024 threads wait there for a whole compute unit to drain).  N =
