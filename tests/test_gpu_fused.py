@@ -242,6 +242,46 @@ def test_token_plan_buckets_keep_the_sort_order(case):
     release()
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_token_plan_buckets_random_sweep(seed):
+    """A seeded sweep over the bucket plan's inputs: orders, heads per order,
+    17 to 24 bits, 8193 to 16000 tokens a head, Zipf skew and a hot token's
+    share; the plan from the tokens holds the order of the plan of the ids
+    (sums that depend on the order of every row's terms)."""
+    rng = np.random.Generator(np.random.PCG64(7000 + seed))
+    n, J = int(rng.integers(2, 5)), int(rng.integers(1, 4))
+    H = (n - 1) * J
+    bits = int(rng.integers(17, 25))
+    primes = workloads.primes_above((1 << (bits - 1)) + int(rng.integers(0, 1 << (bits - 2))), H)
+    offs = workloads.cumulative_offsets(primes)
+    rows = sum(primes)
+    mult = workloads.seeded_multipliers(n, 100 + seed)
+    batch = int(rng.integers(1, 3))
+    seq = int(rng.integers(8193 // batch + 1, 16000 // batch))
+    tok = np.minimum(rng.zipf(1.05 + rng.random(), (batch, seq)), 3000).astype(np.int64)
+    tok[rng.random(tok.shape) < rng.random() * 0.5] = 11
+    args = (n, J, 0, mult, primes, offs)
+    R, dim = tok.size * H, 8
+    exp = rng.integers(127 - 6, 127 + 7, (R, dim)).astype(np.uint16)
+    gb = ((rng.integers(0, 2, (R, dim)).astype(np.uint16) << 15) | (exp << 7)
+          | rng.integers(0, 128, (R, dim)).astype(np.uint16))
+    big = rng.random((R, dim)) < 0.02
+    gb[big] = (np.uint16((127 + 40) << 7) | (rng.integers(0, 2, int(big.sum())).astype(np.uint16)
+                                              << 15))
+    grads = torch.from_numpy(gb.view(np.int16)).to("cuda").view(torch.bfloat16)
+    ws_t = plan_tokens(dev(tok), rows, dim, *args)
+    uid_t, val_t, cnt_t = apply(grads, ws_t, rows)
+    ids = E.engram_hash(dev(tok), *args, rows)
+    ws_i = E.engram_scatter_plan(ids.view(-1), rows, dim)
+    uid_i, val_i, cnt_i = apply(grads, ws_i, rows)
+    torch.cuda.synchronize()
+    u = int(cnt_t.item())
+    assert u == int(cnt_i.item()) and u > 0
+    assert torch.equal(uid_t[:u], uid_i[:u])
+    assert torch.equal(val_t[:u].view(torch.int32), val_i[:u].view(torch.int32))
+    release()
+
+
 @pytest.mark.parametrize("layout", ["ascending", "descending", "shuffled", "gap",
                                     "overlapping", "shared"])
 def test_token_plan_head_layouts(layout):
