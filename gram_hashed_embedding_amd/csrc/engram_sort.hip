@@ -126,11 +126,12 @@ __global__ __launch_bounds__(256) void sort_clear_kernel(uint64_t *status, int64
   if (i == 0) *plan = PlanScalars{};  // no complete plan until the last kernel stamps it
 }
 
-// hist[copy][pass][digit] += number of keys with that digit.  One block per
-// kSortTile ids, all of a thread's loads in flight before any is counted.
+// hist[copy][pass][digit] += number of keys with that digit (digits from bit
+// `lo` up).  One block per kSortTile ids, all of a thread's loads in flight
+// before any is counted.
 __global__ __launch_bounds__(kSortThreads) void sort_histogram_kernel(
     const int64_t *ids, int64_t n, int64_t table_rows, int passes, int per_pass, int bits,
-    uint32_t *hist, int64_t *err) {
+    int lo, uint32_t *hist, int64_t *err) {
   __shared__ uint32_t s_hist[4][kMaxBins];
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * kSortTile + tid;
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kSortThreads) void sort_histogram_kernel(
     if (base + (int64_t)i * kSortThreads >= n) continue;
     const uint32_t k = make_key(id[i], table_rows, bad);
     for (int q = 0; q < passes; ++q) {
-      const int shift = q * per_pass;
+      const int shift = lo + q * per_pass;
       const int width = bits - shift < per_pass ? bits - shift : per_pass;
       atomicAdd(&s_hist[q][(k >> shift) & ((1u << width) - 1u)], 1u);
     }
@@ -583,28 +584,31 @@ __global__ __launch_bounds__(kLdsSortThreads) void plan_heads_lds_kernel(
 }
 
 // ------------------------------------------- buckets after a top pass ---
-// A per-head plan of more than kLdsSortKeys keys a head on 17 to 24 bits
-// sorts in two steps: one one-sweep pass on the bits above the low
-// kBucketLow (stable, so every bucket -- the keys of one head whose top
-// digit is equal -- holds its keys in flat order), then this kernel sorts
-// each bucket on the low kBucketLow bits, in place, with two stable LSD
-// passes of 8 bits.  One block per (segment, top digit): the bucket's start
-// is the sum of the segment's top-digit counts below it.  A bucket of at
-// most kBucketKeys keys is sorted in LDS (the keys in (wave, round, lane)
-// order, as few rounds as it needs, ranked by wavefront multi-split, each
-// pass's digit starts by a block scan), read and written once.  A larger one
-// (a hot row's run) is sorted through global memory by the same block: per
-// pass, its digit totals, then tile after tile ranked as above and written
-// at its digits' running offsets, into the segment's scratch copy and back.
-// The result is the order the full LSD sort gives: stable passes over all
-// bits, low first.
-constexpr int kBucketLow = 16;  // bits the buckets are sorted on
+// Two plans sort in two steps: a per-head plan of more than kLdsSortKeys
+// keys a head on 17 to 24 bits (buckets on its low 16 bits), and a plan of
+// at most kIdBucketKeys ids (buckets on all but the top bits of the keys,
+// 9 to 24 bits).  First one one-sweep pass on the top bits (stable, so every
+// bucket -- the keys of one segment whose top digit is equal -- holds its
+// keys in flat order), then this kernel sorts each bucket on the low bits,
+// in place, with two or three stable LSD passes of at most 8 bits.  One
+// block per (segment, top digit): the bucket's start is the sum of the
+// segment's top-digit counts below it (over the histogram's copies).  A
+// bucket of at most 256 * ITEMS keys is sorted in LDS (the keys in (wave,
+// round, lane) order, as few rounds as it needs, ranked by wavefront
+// multi-split, each pass's digit starts by a block scan), read and written
+// once.  A larger one (a hot row's run) is sorted through global memory by
+// the same block: per pass, its digit totals, then tile after tile ranked as
+// above and written at its digits' running offsets, into the segment's
+// scratch copy and back.  The result is the order the full LSD sort gives:
+// stable passes over all bits, low first.
+constexpr int kBucketLow = 16;  // bits a per-head plan's buckets are sorted on
+constexpr int kBucketMaxLow = 24;
+constexpr int64_t kIdBucketKeys = 262144;  // most ids sorted by buckets
 constexpr int kBucketThreads = 256;
 constexpr int kBucketWaves = kBucketThreads / kWave;
-constexpr int kBucketItems = 8;
-constexpr int kBucketKeys = kBucketThreads * kBucketItems;
-static_assert(kBucketThreads == kMaxBins && kBucketLow == 16,
-              "one thread per digit of a top pass of at most 8 bits, and of an 8-bit pass");
+constexpr int kBucketItems = 8;        // keys a thread holds: a per-head plan's buckets
+constexpr int kIdBucketItems = 16;     // and a plan of ids' (larger buckets, fewer blocks)
+static_assert(kBucketThreads == kMaxBins, "one thread per digit of a pass of at most 8 bits");
 
 // Ranks of one tile's keys by digit ((key - kbase) >> shift) & mask.  Item
 // i (i < rounds) of a thread sits at tile position (wave * rounds + i) * 64
@@ -612,10 +616,11 @@ static_assert(kBucketThreads == kMaxBins && kBucketLow == 16,
 // item's place among its wave's keys of its digit, s_cnt[w][d] the start of
 // wave w's keys of digit d among the tile's, and (threads below `bins`)
 // *total the tile's count of digit tid.  Ends with a barrier.
-__device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[kBucketItems], int count,
+template <int ITEMS>
+__device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[ITEMS], int count,
                                                   int rounds, uint32_t kbase, int shift, int width,
                                                   uint32_t (&s_cnt)[kBucketWaves][kMaxBins],
-                                                  uint32_t (&rank)[kBucketItems],
+                                                  uint32_t (&rank)[ITEMS],
                                                   uint32_t *total) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint32_t mask = (1u << width) - 1u;
@@ -624,21 +629,22 @@ __device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[kBucketI
   for (int d = tid; d < kBucketWaves * kMaxBins; d += kBucketThreads) (&s_cnt[0][0])[d] = 0;
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kBucketItems; ++i) {
-    if (i >= rounds) break;  // (block-uniform)
-    const bool valid = (wave * rounds + i) * kWave + lane < count;
-    const uint32_t d = ((key[i] - kbase) >> shift) & mask;
-    unsigned long long peers = __ballot(valid);
-    for (int b = 0; b < width; ++b) {
-      const bool bit = (d >> b) & 1u;
-      const unsigned long long bal = __ballot(bit);
-      peers &= bit ? bal : ~bal;
-    }
+  for (int i = 0; i < ITEMS; ++i) {
     rank[i] = 0;
-    if (valid) {
-      const uint32_t prior = s_cnt[wave][d];
-      rank[i] = prior + (uint32_t)__popcll(peers & below);
-      if ((peers & below) == 0ull) s_cnt[wave][d] = prior + (uint32_t)__popcll(peers);
+    if (i < rounds) {  // (block-uniform)
+      const bool valid = (wave * rounds + i) * kWave + lane < count;
+      const uint32_t d = ((key[i] - kbase) >> shift) & mask;
+      unsigned long long peers = __ballot(valid);
+      for (int b = 0; b < width; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const unsigned long long bal = __ballot(bit);
+        peers &= bit ? bal : ~bal;
+      }
+      if (valid) {
+        const uint32_t prior = s_cnt[wave][d];
+        rank[i] = prior + (uint32_t)__popcll(peers & below);
+        if ((peers & below) == 0ull) s_cnt[wave][d] = prior + (uint32_t)__popcll(peers);
+      }
     }
   }
   __syncthreads();
@@ -654,10 +660,11 @@ __device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[kBucketI
   __syncthreads();
 }
 
+template <int ITEMS>
 __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
-    const SortSegs sg, int top_bits, const uint32_t *hist, uint32_t *keys, uint32_t *vals,
-    uint32_t *tmp_keys, uint32_t *tmp_vals) {
-  constexpr int low_bits = kBucketLow;
+    const SortSegs sg, int top_bits, int low_bits, const uint32_t *hist, uint32_t *keys,
+    uint32_t *vals, uint32_t *tmp_keys, uint32_t *tmp_vals) {
+  constexpr int kBucketKeys = kBucketThreads * ITEMS;  // the LDS buffer's pairs
   __shared__ uint2 s_buf[kBucketKeys];  // (key, flat index) pairs
   __shared__ uint32_t s_cnt[kBucketWaves][kMaxBins];
   __shared__ uint32_t s_start[kMaxBins];  // start of each digit (tile, or bucket's running)
@@ -666,8 +673,11 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
   const int64_t seg = blockIdx.x >> top_bits;
   const int top = (int)(blockIdx.x & ((1u << top_bits) - 1u));
   uint32_t all;
-  // the top pass's digit totals
-  const uint32_t c = tid < (1 << top_bits) ? hist[seg * 4 * kMaxBins + tid] : 0u;
+  // the top pass's digit totals, summed over the histogram's copies
+  uint32_t c = 0;
+  if (tid < (1 << top_bits))
+    for (int cp = 0; cp < sg.copies; ++cp)
+      c += hist[((int64_t)cp * sg.count + seg) * 4 * kMaxBins + tid];
   const uint32_t before = block_exclusive_scan<kBucketThreads>(c, all);
   if (tid == top) {
     s_bucket[0] = before;
@@ -678,25 +688,27 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
   const uint32_t m = s_bucket[1];
   if (m < 2) return;  // (block-uniform)
   const uint32_t kbase = sg.base[seg];
-  const int w0 = (low_bits + 1) / 2;
+  // the low bits in npass LSD passes of w bits (the last one narrower)
+  const int npass = (low_bits + 7) / 8;
+  const int w = (low_bits + npass - 1) / npass;
   // rounds of 64 keys a wave: as few as the tile needs, so a small bucket's
   // keys are spread over all the waves
-  int rounds = kBucketItems;
+  int rounds = ITEMS;
   auto pos = [&](int i) { return (wave * rounds + i) * kWave + lane; };
-  uint32_t key[kBucketItems], val[kBucketItems], rank[kBucketItems];
+  uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
   uint32_t total = 0;
   if (m <= (uint32_t)kBucketKeys) {
     rounds = (int)((m + kBucketThreads - 1) / kBucketThreads);
 #pragma unroll
-    for (int i = 0; i < kBucketItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
       if (i >= rounds) break;
       const int64_t q = b0 + min((uint32_t)pos(i), m - 1);
       key[i] = keys[q];
       val[i] = vals[q];
     }
-    for (int pass = 0; pass < 2; ++pass) {
-      const int shift = pass == 0 ? 0 : w0;
-      const int width = pass == 0 ? w0 : low_bits - w0;
+    for (int pass = 0; pass < npass; ++pass) {
+      const int shift = pass * w;
+      const int width = low_bits - shift < w ? low_bits - shift : w;
       bucket_tile_ranks(key, (int)m, rounds, kbase, shift, width, s_cnt, rank, &total);
       const uint32_t start = block_exclusive_scan<kBucketThreads>(tid < (1 << width) ? total
                                                                                       : 0u, all);
@@ -704,20 +716,20 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
       __syncthreads();
       const uint32_t mask = (1u << width) - 1u;
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         if (i >= rounds) break;
         const uint32_t d = ((key[i] - kbase) >> shift) & mask;
         rank[i] += s_start[d] + s_cnt[wave][d];
       }
       // keys with their flat indices through LDS into the pass's order
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         if (i >= rounds) break;
         if ((uint32_t)pos(i) < m) s_buf[rank[i]] = uint2{key[i], val[i]};
       }
       __syncthreads();
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         if (i >= rounds) break;
         if ((uint32_t)pos(i) < m) {
           const uint2 kv = s_buf[pos(i)];
@@ -728,7 +740,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
       __syncthreads();  // s_buf, s_cnt and s_start are rewritten by the next pass
     }
 #pragma unroll
-    for (int i = 0; i < kBucketItems; ++i) {
+    for (int i = 0; i < ITEMS; ++i) {
       if (i >= rounds) break;
       if ((uint32_t)pos(i) < m) {
         keys[b0 + pos(i)] = key[i];
@@ -743,11 +755,11 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
   // one hot row needs no pass at all); after an odd number of passes the
   // bucket is copied back.
   bool in_tmp = false;
-  for (int pass = 0; pass < 2; ++pass) {
+  for (int pass = 0; pass < npass; ++pass) {
     const uint32_t *src_k = in_tmp ? tmp_keys : keys, *src_v = in_tmp ? tmp_vals : vals;
     uint32_t *dst_k = in_tmp ? keys : tmp_keys, *dst_v = in_tmp ? vals : tmp_vals;
-    const int shift = pass == 0 ? 0 : w0;
-    const int width = pass == 0 ? w0 : low_bits - w0;
+    const int shift = pass * w;
+    const int width = low_bits - shift < w ? low_bits - shift : w;
     const uint32_t mask = (1u << width) - 1u;
     const int bins = 1 << width;
     // the bucket's digit totals, kBucketKeys keys a round with every load in
@@ -759,12 +771,12 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
     bool differs = false;
     for (uint32_t p0 = 0; p0 < m; p0 += kBucketKeys) {
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
         key[i] = q < m ? src_k[b0 + q] : first;
       }
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         if (p0 + (uint32_t)(i * kBucketThreads + tid) < m) {
           atomicAdd(&s_start[((key[i] - kbase) >> shift) & mask], 1u);
           differs = differs || key[i] != first;
@@ -780,14 +792,14 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
     for (uint32_t t0 = 0; t0 < m; t0 += kBucketKeys) {
       const int count = (int)min((uint32_t)kBucketKeys, m - t0);
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         const int64_t q = b0 + t0 + min(pos(i), count - 1);
         key[i] = src_k[q];
         val[i] = src_v[q];
       }
       bucket_tile_ranks(key, count, rounds, kbase, shift, width, s_cnt, rank, &total);
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         if (pos(i) < count) {
           const uint32_t d = ((key[i] - kbase) >> shift) & mask;
           const int64_t q = b0 + s_start[d] + s_cnt[wave][d] + rank[i];
@@ -804,13 +816,13 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
   if (in_tmp) {
     for (uint32_t p0 = 0; p0 < m; p0 += kBucketKeys) {
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
         key[i] = q < m ? tmp_keys[b0 + q] : 0u;
         val[i] = q < m ? tmp_vals[b0 + q] : 0u;
       }
 #pragma unroll
-      for (int i = 0; i < kBucketItems; ++i) {
+      for (int i = 0; i < ITEMS; ++i) {
         const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
         if (q < m) {
           keys[b0 + q] = key[i];
@@ -1037,11 +1049,20 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
   uint32_t *hist = v.counters + kTicketWords;  // [copy][segment][4][kMaxBins]
   SortLayout L = whole_sort(p, n);
   const bool heads = ids == nullptr && head_sort(*hp, n / hp->H, p, &L);
-  // per-head segments too large for the LDS plan, on 17 to 24 bits: one
-  // sort pass on the bits above the low kBucketLow, then each bucket on them
-  const bool buckets = heads && L.sg.len > kLdsSortKeys && L.bits > kBucketLow &&
-                       L.bits <= kBucketLow + 8;
-  const int top_bits = L.bits - kBucketLow;
+  // one sort pass on the top bits, then each bucket on the rest: per-head
+  // segments too large for the LDS plan, on 17 to 24 bits (the low 16 bits
+  // in the buckets); and at most kIdBucketKeys ids, about 512 a bucket, on
+  // 9 to 24 bits below the top digit
+  int top_bits = 0;
+  if (heads && L.sg.len > kLdsSortKeys && L.bits > kBucketLow && L.bits <= kBucketLow + 8)
+    top_bits = L.bits - kBucketLow;
+  if (ids != nullptr && n > kSortTile && n <= kIdBucketKeys) {
+    const int want = bit_width_u64((uint64_t)(n - 1) / 512);  // about 512 ids a bucket
+    const int top = want < 8 ? want : 8;
+    if (L.bits - top >= 9 && L.bits - top <= kBucketMaxLow) top_bits = top;
+  }
+  const bool buckets = top_bits > 0;
+  const int low_bits = L.bits - top_bits;
   if (buckets) L.passes = 1;
   const int64_t sort_words = (int64_t)L.passes * L.num_tiles * kMaxBins;
   const int64_t status_len = sort_words + p.slot_tiles;
@@ -1099,7 +1120,8 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
   uint32_t *const hashed = out_k(0) == last_k ? other_k : last_k;
   if (ids != nullptr) {  // one block per kSortTile ids, whatever the sort's tiles
     hipLaunchKernelGGL(sort_histogram_kernel, dim3((unsigned)p.num_tiles), dim3(kSortThreads), 0,
-                       s, ids, n, table_rows, L.passes, L.per_pass, L.bits, hist, err);
+                       s, ids, n, table_rows, L.passes, buckets ? top_bits : L.per_pass, L.bits,
+                       buckets ? low_bits : 0, hist, err);
   } else if (heads) {
     const int64_t chunks = head_chunks;
     const dim3 grid((unsigned)(L.sg.count * chunks));
@@ -1108,7 +1130,7 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
   case N:                                                                                     \
     hipLaunchKernelGGL(plan_hash_heads_kernel<N>, grid, dim3(kHeadThreads), 0, s, *hp, L.sg,    \
                        chunks, L.passes, buckets ? top_bits : L.per_pass, L.bits,             \
-                       buckets ? kBucketLow : 0, hashed, hist);                               \
+                       buckets ? low_bits : 0, hashed, hist);                                 \
     break;
       ENGRAM_PLAN_HEADS_CASE(2)
       ENGRAM_PLAN_HEADS_CASE(3)
@@ -1127,7 +1149,7 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
                        hashed, hist);
   }
   for (int pass = 0; pass < L.passes; ++pass) {
-    const int shift = buckets ? kBucketLow : pass * L.per_pass;
+    const int shift = buckets ? low_bits : pass * L.per_pass;
     const int width = buckets ? top_bits
                               : (L.bits - shift < L.per_pass ? L.bits - shift : L.per_pass);
     const PassArgs a = {ids, pass == 0 ? hashed : out_k(pass - 1),
@@ -1141,9 +1163,16 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
       launch_pass<kSortItems / 2>(src, L, a, s);
   }
   if (buckets)  // the top pass wrote the pair the apply reads; the hashed keys are scratch
-    hipLaunchKernelGGL(bucket_sort_kernel, dim3((unsigned)(L.sg.count << top_bits)),
-                       dim3(kBucketThreads), 0, s, L.sg, top_bits, hist, last_k, last_v, other_k,
-                       other_v);
+  {
+    if (ids != nullptr)
+      hipLaunchKernelGGL(bucket_sort_kernel<kIdBucketItems>, dim3(1u << top_bits),
+                         dim3(kBucketThreads), 0, s, L.sg, top_bits, low_bits, hist, last_k, last_v,
+                         other_k, other_v);
+    else
+      hipLaunchKernelGGL(bucket_sort_kernel<kBucketItems>, dim3((unsigned)(L.sg.count << top_bits)),
+                         dim3(kBucketThreads), 0, s, L.sg, top_bits, low_bits, hist, last_k, last_v,
+                         other_k, other_v);
+  }
   // distinct-row slots
   hipLaunchKernelGGL(range_slots_kernel, dim3((unsigned)p.slot_tiles), dim3(kSlotThreads), 0, s,
                      v.sorted_keys, n, (uint32_t)table_rows, p.num_ranges, v.status + sort_words,

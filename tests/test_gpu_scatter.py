@@ -504,3 +504,40 @@ def test_apply_again_on_one_plan_with_chunks(oracle):
         assert np.array_equal(uid[:u].cpu().numpy(), want_uid)
         assert np.array_equal(host_f32(uval[:u]).view(np.uint32), want_val.view(np.uint32))
     release()
+
+
+# (n, table_rows, hot): a plan of at most 262,144 ids sorts one pass on the
+# top bits, then each bucket (about 512 ids) on the 9 to 24 bits below; hot
+# rows past the 4096-key LDS buffer take the bucket's global-memory passes.
+@pytest.mark.parametrize("n, rows, hot", [(4097, 1 << 12 | 5, 0), (20000, 20_000_000, 0),
+                                          (100_000, 16_778_782, 6000),
+                                          (262_144, 3_000_000_000, 0),
+                                          (262_144, 16_778_782, 300)])
+def test_id_plan_buckets_keep_the_sort_order(n, rows, hot):
+    """The plan of n ids sorted by buckets holds the order of the full
+    radix sort: the same ids followed by enough padding (-1, skipped) to
+    pass 262,144 ids, which the passes of the full sort plan, give the same
+    row-sparse sums bit for bit, with gradients whose sums depend on the
+    order of every row's terms (+-2^40 among small terms)."""
+    rng = np.random.Generator(np.random.PCG64(n + hot))
+    ids = np.minimum(rng.zipf(1.2, n), rows - 1).astype(np.int64)
+    ids = (ids * 2654435761) % rows  # spread the Zipf ranks over the table
+    if hot:
+        ids[rng.choice(n, hot, replace=False)] = rows // 3
+    dim = 8
+    pad = 262_145 - n
+    exp = rng.integers(127 - 6, 127 + 7, (n + pad, dim)).astype(np.uint16)
+    gb = ((rng.integers(0, 2, (n + pad, dim)).astype(np.uint16) << 15) | (exp << 7)
+          | rng.integers(0, 128, (n + pad, dim)).astype(np.uint16))
+    big = rng.random((n + pad, dim)) < 0.02
+    gb[big] = (np.uint16((127 + 40) << 7) | (rng.integers(0, 2, int(big.sum())).astype(np.uint16)
+                                              << 15))
+    grads = torch.from_numpy(gb.view(np.int16)).to("cuda").view(torch.bfloat16)
+    uid_b, val_b, err_b = run_sparse(ids, grads[:n].contiguous(), rows)
+    padded = np.concatenate([ids, np.full(pad, -1, np.int64)])
+    uid_f, val_f, err_f = run_sparse(padded, grads, rows)
+    assert err_b == 0 and err_f == 0
+    assert np.array_equal(uid_b, np.unique(ids))
+    assert np.array_equal(uid_b, uid_f)
+    assert np.array_equal(val_b.view(np.uint32), val_f.view(np.uint32))
+    release()
