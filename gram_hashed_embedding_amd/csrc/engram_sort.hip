@@ -604,11 +604,14 @@ __global__ __launch_bounds__(kLdsSortThreads) void plan_heads_lds_kernel(
 constexpr int kBucketLow = 16;  // bits a per-head plan's buckets are sorted on
 constexpr int kBucketMaxLow = 24;
 constexpr int64_t kIdBucketKeys = 262144;  // most ids sorted by buckets
+// A per-head plan's buckets: blocks of 256 threads holding 8 keys each (many
+// small buckets); a plan of ids': 1024 threads holding 4 (fewer, larger
+// buckets, each sorted by more waves).  Both hold up to 2048 or 4096 keys in
+// LDS, and have at least one thread per digit of a pass of at most 8 bits.
 constexpr int kBucketThreads = 256;
-constexpr int kBucketWaves = kBucketThreads / kWave;
-constexpr int kBucketItems = 8;        // keys a thread holds: a per-head plan's buckets
-constexpr int kIdBucketItems = 16;     // and a plan of ids' (larger buckets, fewer blocks)
-static_assert(kBucketThreads == kMaxBins, "one thread per digit of a pass of at most 8 bits");
+constexpr int kBucketItems = 8;
+constexpr int kIdBucketThreads = 1024;
+constexpr int kIdBucketItems = 4;
 
 // Ranks of one tile's keys by digit ((key - kbase) >> shift) & mask.  Item
 // i (i < rounds) of a thread sits at tile position (wave * rounds + i) * 64
@@ -616,17 +619,17 @@ static_assert(kBucketThreads == kMaxBins, "one thread per digit of a pass of at 
 // item's place among its wave's keys of its digit, s_cnt[w][d] the start of
 // wave w's keys of digit d among the tile's, and (threads below `bins`)
 // *total the tile's count of digit tid.  Ends with a barrier.
-template <int ITEMS>
+template <int NT, int ITEMS>
 __device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[ITEMS], int count,
                                                   int rounds, uint32_t kbase, int shift, int width,
-                                                  uint32_t (&s_cnt)[kBucketWaves][kMaxBins],
+                                                  uint32_t (&s_cnt)[(NT / kWave)][kMaxBins],
                                                   uint32_t (&rank)[ITEMS],
                                                   uint32_t *total) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const uint32_t mask = (1u << width) - 1u;
   const int bins = 1 << width;
   const unsigned long long below = (1ull << lane) - 1ull;
-  for (int d = tid; d < kBucketWaves * kMaxBins; d += kBucketThreads) (&s_cnt[0][0])[d] = 0;
+  for (int d = tid; d < (NT / kWave) * kMaxBins; d += NT) (&s_cnt[0][0])[d] = 0;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < ITEMS; ++i) {
@@ -650,7 +653,7 @@ __device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[ITEMS], 
   __syncthreads();
   if (tid < bins) {
     uint32_t t = 0;
-    for (int w = 0; w < kBucketWaves; ++w) {
+    for (int w = 0; w < (NT / kWave); ++w) {
       const uint32_t c = s_cnt[w][tid];
       s_cnt[w][tid] = t;
       t += c;
@@ -660,13 +663,14 @@ __device__ __forceinline__ void bucket_tile_ranks(const uint32_t (&key)[ITEMS], 
   __syncthreads();
 }
 
-template <int ITEMS>
-__global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
+template <int NT, int ITEMS>
+__global__ __launch_bounds__(NT) void bucket_sort_kernel(
     const SortSegs sg, int top_bits, int low_bits, const uint32_t *hist, uint32_t *keys,
     uint32_t *vals, uint32_t *tmp_keys, uint32_t *tmp_vals) {
-  constexpr int kBucketKeys = kBucketThreads * ITEMS;  // the LDS buffer's pairs
+  static_assert(NT >= kMaxBins && NT % kWave == 0, "a thread per digit, whole waves");
+  constexpr int kBucketKeys = NT * ITEMS;  // the LDS buffer's pairs
   __shared__ uint2 s_buf[kBucketKeys];  // (key, flat index) pairs
-  __shared__ uint32_t s_cnt[kBucketWaves][kMaxBins];
+  __shared__ uint32_t s_cnt[(NT / kWave)][kMaxBins];
   __shared__ uint32_t s_start[kMaxBins];  // start of each digit (tile, or bucket's running)
   __shared__ uint32_t s_bucket[2];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -678,7 +682,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
   if (tid < (1 << top_bits))
     for (int cp = 0; cp < sg.copies; ++cp)
       c += hist[((int64_t)cp * sg.count + seg) * 4 * kMaxBins + tid];
-  const uint32_t before = block_exclusive_scan<kBucketThreads>(c, all);
+  const uint32_t before = block_exclusive_scan<NT>(c, all);
   if (tid == top) {
     s_bucket[0] = before;
     s_bucket[1] = c;
@@ -698,7 +702,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
   uint32_t key[ITEMS], val[ITEMS], rank[ITEMS];
   uint32_t total = 0;
   if (m <= (uint32_t)kBucketKeys) {
-    rounds = (int)((m + kBucketThreads - 1) / kBucketThreads);
+    rounds = (int)((m + NT - 1) / NT);
 #pragma unroll
     for (int i = 0; i < ITEMS; ++i) {
       if (i >= rounds) break;
@@ -709,8 +713,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
     for (int pass = 0; pass < npass; ++pass) {
       const int shift = pass * w;
       const int width = low_bits - shift < w ? low_bits - shift : w;
-      bucket_tile_ranks(key, (int)m, rounds, kbase, shift, width, s_cnt, rank, &total);
-      const uint32_t start = block_exclusive_scan<kBucketThreads>(tid < (1 << width) ? total
+      bucket_tile_ranks<NT, ITEMS>(key, (int)m, rounds, kbase, shift, width, s_cnt, rank, &total);
+      const uint32_t start = block_exclusive_scan<NT>(tid < (1 << width) ? total
                                                                                       : 0u, all);
       if (tid < (1 << width)) s_start[tid] = start;
       __syncthreads();
@@ -765,19 +769,19 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
     // the bucket's digit totals, kBucketKeys keys a round with every load in
     // flight, then each digit's start; a bucket of one row (every key alike)
     // is already in order
-    s_start[tid] = 0;
+    if (tid < kMaxBins) s_start[tid] = 0;
     __syncthreads();
     const uint32_t first = src_k[b0];
     bool differs = false;
     for (uint32_t p0 = 0; p0 < m; p0 += kBucketKeys) {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
+        const uint32_t q = p0 + (uint32_t)(i * NT + tid);
         key[i] = q < m ? src_k[b0 + q] : first;
       }
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        if (p0 + (uint32_t)(i * kBucketThreads + tid) < m) {
+        if (p0 + (uint32_t)(i * NT + tid) < m) {
           atomicAdd(&s_start[((key[i] - kbase) >> shift) & mask], 1u);
           differs = differs || key[i] != first;
         }
@@ -786,8 +790,8 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
     if (!__syncthreads_or(differs)) break;  // (only at the first pass: the keys do not change)
     const uint32_t cnt = tid < bins ? s_start[tid] : 0u;
     if (__syncthreads_or(cnt == m)) continue;  // one digit: the pass keeps the order
-    const uint32_t start = block_exclusive_scan<kBucketThreads>(cnt, all);
-    s_start[tid] = start;
+    const uint32_t start = block_exclusive_scan<NT>(cnt, all);
+    if (tid < kMaxBins) s_start[tid] = start;
     __syncthreads();
     for (uint32_t t0 = 0; t0 < m; t0 += kBucketKeys) {
       const int count = (int)min((uint32_t)kBucketKeys, m - t0);
@@ -797,7 +801,7 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
         key[i] = src_k[q];
         val[i] = src_v[q];
       }
-      bucket_tile_ranks(key, count, rounds, kbase, shift, width, s_cnt, rank, &total);
+      bucket_tile_ranks<NT, ITEMS>(key, count, rounds, kbase, shift, width, s_cnt, rank, &total);
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
         if (pos(i) < count) {
@@ -817,13 +821,13 @@ __global__ __launch_bounds__(kBucketThreads) void bucket_sort_kernel(
     for (uint32_t p0 = 0; p0 < m; p0 += kBucketKeys) {
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
+        const uint32_t q = p0 + (uint32_t)(i * NT + tid);
         key[i] = q < m ? tmp_keys[b0 + q] : 0u;
         val[i] = q < m ? tmp_vals[b0 + q] : 0u;
       }
 #pragma unroll
       for (int i = 0; i < ITEMS; ++i) {
-        const uint32_t q = p0 + (uint32_t)(i * kBucketThreads + tid);
+        const uint32_t q = p0 + (uint32_t)(i * NT + tid);
         if (q < m) {
           keys[b0 + q] = key[i];
           vals[b0 + q] = val[i];
@@ -1165,13 +1169,13 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
   if (buckets)  // the top pass wrote the pair the apply reads; the hashed keys are scratch
   {
     if (ids != nullptr)
-      hipLaunchKernelGGL(bucket_sort_kernel<kIdBucketItems>, dim3(1u << top_bits),
-                         dim3(kBucketThreads), 0, s, L.sg, top_bits, low_bits, hist, last_k, last_v,
-                         other_k, other_v);
+      hipLaunchKernelGGL((bucket_sort_kernel<kIdBucketThreads, kIdBucketItems>),
+                         dim3(1u << top_bits), dim3(kIdBucketThreads), 0, s, L.sg, top_bits,
+                         low_bits, hist, last_k, last_v, other_k, other_v);
     else
-      hipLaunchKernelGGL(bucket_sort_kernel<kBucketItems>, dim3((unsigned)(L.sg.count << top_bits)),
-                         dim3(kBucketThreads), 0, s, L.sg, top_bits, low_bits, hist, last_k, last_v,
-                         other_k, other_v);
+      hipLaunchKernelGGL((bucket_sort_kernel<kBucketThreads, kBucketItems>),
+                         dim3((unsigned)(L.sg.count << top_bits)), dim3(kBucketThreads), 0, s,
+                         L.sg, top_bits, low_bits, hist, last_k, last_v, other_k, other_v);
   }
   // distinct-row slots
   hipLaunchKernelGGL(range_slots_kernel, dim3((unsigned)p.slot_tiles), dim3(kSlotThreads), 0, s,
