@@ -1166,8 +1166,7 @@ int engram::launch_plan(const int64_t *ids, const HashParams *hp, int64_t n, int
     else
       launch_pass<kSortItems / 2>(src, L, a, s);
   }
-  if (buckets)  // the top pass wrote the pair the apply reads; the hashed keys are scratch
-  {
+  if (buckets) {  // the top pass wrote the pair the apply reads; the other is scratch
     if (ids != nullptr)
       hipLaunchKernelGGL((bucket_sort_kernel<kIdBucketThreads, kIdBucketItems>),
                          dim3(1u << top_bits), dim3(kIdBucketThreads), 0, s, L.sg, top_bits,
